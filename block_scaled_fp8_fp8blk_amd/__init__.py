@@ -1,0 +1,168 @@
+"""Python binding of libfp8blk.so (the FP8-blk dense linear for MI355X).
+
+Argument marshalling only: every function here forwards device pointers,
+sizes and the caller's stream to the C ABI declared in include/fp8blk.h, and
+every step of the computation runs in the library's HIP kernels. PyTorch is
+used for device memory and streams only. If the shared library has not been
+built, the first call raises: there is no fallback of any kind.
+
+Tensors must be contiguous CUDA (HIP) tensors of these dtypes:
+  codes, scales_e8m0      torch.uint8
+  scales_f32, y           torch.float32
+  x_bf16, w_bf16, out     torch.bfloat16, torch.int16 or torch.uint16 (bf16 bit patterns)
+  ws                      any dtype, or None when the op needs no workspace
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
+
+OK, ERR_ARG, ERR_SCALE_FF, ERR_NAN_CODE, ERR_INEXACT, ERR_WORKSPACE, ERR_HIP = range(7)
+OP_LOAD_CHECK, OP_DEQUANT_BF16, OP_GEMV, OP_BF16_TWIN = range(4)
+MIN_COLS, MAX_COLS, MAX_M = 16, 65536, 16
+
+# Every symbol include/fp8blk.h declares.
+EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
+           "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin")
+
+_lib = None
+
+
+class Fp8BlkError(RuntimeError):
+    def __init__(self, status: int, where: str, first_bad: int = -1):
+        self.status = status
+        self.first_bad = first_bad
+        msg = f"{where}: {fp8blk_strerror(status)} (status {status})"
+        if first_bad >= 0:
+            msg += f", first bad index {first_bad}"
+        super().__init__(msg)
+
+
+def load():
+    """Load libfp8blk.so (built by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    L.fp8blk_abi_version.argtypes, L.fp8blk_abi_version.restype = [], i32
+    L.fp8blk_strerror.argtypes, L.fp8blk_strerror.restype = [i32], ctypes.c_char_p
+    L.fp8blk_workspace_bytes.argtypes, L.fp8blk_workspace_bytes.restype = [i32, i64, i64, i64], sz
+    L.fp8blk_load_check.argtypes = [vp, vp, i64, i64, vp, vp, sz, ctypes.POINTER(i64), vp]
+    L.fp8blk_load_check.restype = i32
+    L.fp8blk_dequant_bf16.argtypes, L.fp8blk_dequant_bf16.restype = [vp, vp, i64, i64, vp, vp], i32
+    L.fp8blk_gemv.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, sz, vp]
+    L.fp8blk_gemv.restype = i32
+    L.bf16_gemv_twin.argtypes = [vp, i64, i64, vp, i64, vp, vp, sz, vp]
+    L.bf16_gemv_twin.restype = i32
+    _lib = L
+    return L
+
+
+def fp8blk_abi_version() -> int:
+    return load().fp8blk_abi_version()
+
+
+def fp8blk_strerror(status: int) -> str:
+    return load().fp8blk_strerror(status).decode()
+
+
+def fp8blk_workspace_bytes(op: int, rows: int, cols: int, M: int = 1) -> int:
+    return load().fp8blk_workspace_bytes(op, rows, cols, M)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtypes, name):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t.data_ptr()
+
+
+def _bf16_dtypes():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _dev(ws, None, "ws"), ws.numel() * ws.element_size()
+
+
+def fp8blk_load_check(codes, scales_e8m0, scales_f32_out, ws, stream=None, check=True):
+    """Validate codes/scales and decode the f32 scale grid. Waits on the stream.
+    Returns (status, first_bad); raises Fp8BlkError on a refusal if check."""
+    import torch
+    rows, cols = codes.shape
+    wsp, wsb = _ws(ws)
+    fb = ctypes.c_int64(-1)
+    st = load().fp8blk_load_check(_dev(codes, (torch.uint8,), "codes"),
+                                  _dev(scales_e8m0, (torch.uint8,), "scales_e8m0"), rows, cols,
+                                  _dev(scales_f32_out, (torch.float32,), "scales_f32_out"), wsp, wsb,
+                                  ctypes.byref(fb), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_load_check", fb.value)
+    return st, fb.value
+
+
+def fp8blk_dequant_bf16(codes, scales_f32, out_bf16, stream=None, check=True):
+    import torch
+    rows, cols = codes.shape
+    st = load().fp8blk_dequant_bf16(_dev(codes, (torch.uint8,), "codes"),
+                                    _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
+                                    _dev(out_bf16, _bf16_dtypes(), "out_bf16"), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_dequant_bf16")
+    return st
+
+
+def fp8blk_gemv(codes, scales_f32, x_bf16, y, ws=None, stream=None, check=True):
+    """y[M, rows] = decode(codes, scales) @ x^T, in the library's fixed order."""
+    import torch
+    rows, cols = codes.shape
+    M = x_bf16.shape[0]
+    wsp, wsb = _ws(ws)
+    st = load().fp8blk_gemv(_dev(codes, (torch.uint8,), "codes"),
+                            _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
+                            _dev(x_bf16, _bf16_dtypes(), "x_bf16"), M,
+                            _dev(y, (torch.float32,), "y"), wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv")
+    return st
+
+
+def bf16_gemv_twin(w_bf16, x_bf16, y, ws=None, stream=None, check=True):
+    """The bf16-slab twin of fp8blk_gemv (same order, same bits)."""
+    rows, cols = w_bf16.shape
+    M = x_bf16.shape[0]
+    wsp, wsb = _ws(ws)
+    import torch
+    st = load().bf16_gemv_twin(_dev(w_bf16, _bf16_dtypes(), "w_bf16"), rows, cols,
+                               _dev(x_bf16, _bf16_dtypes(), "x_bf16"), M,
+                               _dev(y, (torch.float32,), "y"), wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "bf16_gemv_twin")
+    return st
+
+
+def raw_call(name: str, *args):
+    """Call an exported symbol with raw ctypes arguments (pointers as ints).
+    Used by tests that exercise the C ABI's argument checks directly."""
+    return getattr(load(), name)(*args)

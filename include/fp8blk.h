@@ -1,0 +1,186 @@
+/*
+ * fp8blk.h -- C ABI of libfp8blk.so: the block-scaled FP8 ("FP8-blk") dense
+ * linear, read as stored, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (docs.rs pages of the memra-engine crate):
+ *   - "Module dsv4_gpu" page, struct Fp8Dense: a linear is held as e4m3
+ *     codes [rows, cols] plus a 128x128 grid of e8m0 block scales. Every
+ *     scale is a power of two, the grid is decoded to f32 once at load, and
+ *     a 0xFF scale is refused there. The GEMV forms e4m3(code) * scale in
+ *     registers; that is the same f32 value the bf16 dequant slab holds, and
+ *     the accumulation order is the bf16 kernel's, so the two give identical
+ *     bits.
+ *   - same page, module header (rungs paragraph): dequantization to bf16
+ *     refuses any element that is not exactly a bf16 value; activations enter
+ *     as bf16; products accumulate in f32.
+ *   - same page, enum DW: the GEMV takes raw pointers to either the bf16 slab
+ *     or the stored FP8 pair, rebuilt per call by the caller.
+ *   - same page, structs StepWs / VerifyWs: work buffers are allocated once
+ *     by the owner, never per step; the verify panel is the decode arena
+ *     widened to several rows.
+ *   - "Struct Dsv4Gpu" page, field dense_fp8: decode and verify read the
+ *     FP8-blk linears as stored (e4m3 + f32 block scales) through the twin
+ *     GEMVs, halving the dense weight bytes.
+ *   - "Struct Dsv4Gpu" page, method spec_greedy_batched_with: a batched
+ *     kernel gives the same bits as its single-position twin.
+ *   - "dflash.rs" source page, fn bf16_to_f32: a bf16 pattern widens to f32
+ *     by becoming the high 16 bits.
+ *
+ * Formats (this library's reading of the pages' "e4m3" and "e8m0"):
+ *   e4m3 = OCP FP8 E4M3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
+ *          subnormals, no infinities, 0x7F and 0xFF are NaN.
+ *   e8m0 = 2^(code - 127); 0xFF is refused.
+ *   bf16 = the high 16 bits of an IEEE binary32, passed as uint16_t patterns.
+ *
+ * Layouts (all row-major and contiguous, no strides):
+ *   codes       uint8_t  [rows, cols]  rows = output features, cols = reduction
+ *   scales_e8m0 uint8_t  [ceil(rows/128), ceil(cols/128)]; element (r, c) uses
+ *                                      entry [r/128][c/128]
+ *   scales_f32  float    same grid, as produced by fp8blk_load_check
+ *   w_bf16      uint16_t [rows, cols]  bf16 dequant slab
+ *   x_bf16      uint16_t [M, cols]     activation panel, M = 1 (decode) .. 16
+ *   y           float    [M, rows]
+ *
+ * Reduction order (fixed; depends on cols only, never on rows, M, the launch
+ * plan or the device). For each output (m, r):
+ *   - segment t covers columns [1024 t, 1024 t + 1024); lane l = 0..63 owns
+ *     the 16-column chunk q = 64 t + l;
+ *   - lane partial: fused multiply-add over the chunk's 16 columns in
+ *     increasing order, starting from +0.0 (+0.0 for a chunk past the end);
+ *   - segment sum: pairwise tree over the 64 lane partials, pairing lanes that
+ *     differ in bit 5, then 4, 3, 2, 1, 0;
+ *   - y = segment 0, then y += segment t for t = 1, 2, ... in order.
+ *   Hence fp8blk_gemv == bf16_gemv_twin bitwise on load-checked weights, row m
+ *   of an M-row call == the M = 1 call on x[m] bitwise. Each product w * x is
+ *   exact in f32 (at most 4 x 8 significant bits) as long as it stays out of
+ *   the f32 subnormal range, so for such inputs the only error is in the sums:
+ *   |y - exact| <= gamma_d * sum_c |w x|, d = 16 + 6 + ceil(cols/1024) - 1,
+ *   gamma_d = d u / (1 - d u), u = 2^-24; d <= 85 and gamma_d < 5.1e-6 for
+ *   every cols up to FP8BLK_MAX_COLS.
+ *
+ * Ownership and threading: the caller owns every buffer (device memory unless
+ * stated). The library allocates and frees nothing, keeps no per-call global
+ * state and is safe to call from several host threads. All device work is
+ * enqueued on the caller's stream `stream` (NULL = the null stream).
+ *
+ * Errors: every entry point returns an fp8blk_status. It never aborts, throws
+ * or prints. On an error return the outputs are unspecified. fp8blk_dequant_bf16,
+ * fp8blk_gemv and bf16_gemv_twin do not re-validate the weights: they assume
+ * fp8blk_load_check accepted them (validation happens once, at load).
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream (the same type as hipStream_t). */
+typedef struct ihipStream_t *fp8blk_stream_t;
+
+typedef enum fp8blk_status {
+    FP8BLK_OK = 0,
+    FP8BLK_ERR_ARG = 1,       /* null pointer, bad shape, misalignment, M out of range */
+    FP8BLK_ERR_SCALE_FF = 2,  /* a scale code is 0xFF */
+    FP8BLK_ERR_NAN_CODE = 3,  /* a weight code is 0x7F or 0xFF (NaN) */
+    FP8BLK_ERR_INEXACT = 4,   /* e4m3(code) * scale is not exactly a bf16 value */
+    FP8BLK_ERR_WORKSPACE = 5, /* ws is NULL or ws_bytes is below fp8blk_workspace_bytes */
+    FP8BLK_ERR_HIP = 6        /* a HIP launch or runtime call failed */
+} fp8blk_status;
+
+/* Operation ids for fp8blk_workspace_bytes. */
+typedef enum fp8blk_op {
+    FP8BLK_OP_LOAD_CHECK = 0,
+    FP8BLK_OP_DEQUANT_BF16 = 1,
+    FP8BLK_OP_GEMV = 2,
+    FP8BLK_OP_BF16_TWIN = 3
+} fp8blk_op;
+
+/* Shape limits. cols must be a multiple of 16 (one 16-byte code load). */
+#define FP8BLK_MIN_COLS 16
+#define FP8BLK_MAX_COLS 65536
+#define FP8BLK_MAX_M 16
+
+/* Version of this ABI; bumped on any incompatible change. */
+int fp8blk_abi_version(void);
+
+/* Static text for a status code. */
+const char *fp8blk_strerror(int status);
+
+/* Bytes of device workspace `op` needs for this shape (0 = none; ws may then
+ * be NULL). Returns 0 for an unknown op. Pure host function. */
+size_t fp8blk_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M);
+
+/*
+ * Load-time check and scale-grid decode ("Module dsv4_gpu" page, Fp8Dense and
+ * the rungs paragraph). Checks, in this order of precedence:
+ *   FP8BLK_ERR_SCALE_FF  some scale code is 0xFF; *first_bad = lowest
+ *                        row-major index into the scale grid;
+ *   FP8BLK_ERR_NAN_CODE  some code is 0x7F or 0xFF; *first_bad = lowest
+ *                        row-major element index r * cols + c;
+ *   FP8BLK_ERR_INEXACT   some e4m3(code) * 2^(scale - 127) is not a finite
+ *                        bf16 value (too small for bf16's 2^-133 spacing, or
+ *                        past its largest finite value); *first_bad as above.
+ * On FP8BLK_OK, scales_f32_out holds 2^(code - 127) exactly for every grid
+ * entry (2^-127 as an f32 subnormal) and *first_bad = -1.
+ *   codes, scales_e8m0, scales_f32_out: device pointers, layouts above;
+ *     codes 16-byte aligned, scales_f32_out 4-byte aligned.
+ *   rows >= 1; 16 <= cols <= FP8BLK_MAX_COLS; cols % 16 == 0.
+ *   ws: device, >= fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK, ...) bytes,
+ *     8-byte aligned; its contents on entry do not matter.
+ *   first_bad: HOST pointer, may be NULL.
+ * Unlike the other entry points this one waits for `stream` to finish before
+ * returning, since it returns a verdict.
+ */
+int fp8blk_load_check(const uint8_t *codes, const uint8_t *scales_e8m0, int64_t rows,
+                      int64_t cols, float *scales_f32_out, void *ws, size_t ws_bytes,
+                      int64_t *first_bad, fp8blk_stream_t stream);
+
+/*
+ * The bf16 dequant slab ("Module dsv4_gpu" page, rungs paragraph and
+ * DenseBf16): out_bf16[r, c] = bf16 pattern of e4m3(codes[r, c]) *
+ * scales_f32[r/128][c/128]. Exact (no rounding) for weights accepted by
+ * fp8blk_load_check; for others the output is unspecified.
+ *   codes, out_bf16: device, 16-byte aligned; scales_f32: device, 4-byte aligned.
+ *   rows >= 1; 16 <= cols <= FP8BLK_MAX_COLS; cols % 16 == 0.
+ * Enqueued on `stream`; does not wait.
+ */
+int fp8blk_dequant_bf16(const uint8_t *codes, const float *scales_f32, int64_t rows,
+                        int64_t cols, uint16_t *out_bf16, fp8blk_stream_t stream);
+
+/*
+ * The FP8-blk GEMV, weights read as stored ("Module dsv4_gpu" page, Fp8Dense;
+ * "Struct Dsv4Gpu" page, dense_fp8 and spec_greedy_batched_with):
+ *   y[m, r] = sum over c of (e4m3(codes[r, c]) * scales_f32[r/128][c/128]) * x[m, c]
+ * decoded in registers, f32 accumulation in the reduction order above.
+ *   codes, x_bf16: device, 16-byte aligned; scales_f32, y: device, 4-byte aligned.
+ *   rows >= 1; 16 <= cols <= FP8BLK_MAX_COLS; cols % 16 == 0; 1 <= M <= FP8BLK_MAX_M.
+ *   ws/ws_bytes: fp8blk_workspace_bytes(FP8BLK_OP_GEMV, ...) bytes (currently
+ *     0: ws may be NULL).
+ * y must not overlap the inputs. Enqueued on `stream`; does not wait.
+ */
+int fp8blk_gemv(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,
+                const uint16_t *x_bf16, int64_t M, float *y, void *ws, size_t ws_bytes,
+                fp8blk_stream_t stream);
+
+/*
+ * The bf16-slab twin of fp8blk_gemv ("Module dsv4_gpu" page, Fp8Dense and DW;
+ * "dflash.rs" page, bf16_to_f32): the same y, with weights read from the bf16
+ * dequant slab and widened to f32, in the same reduction order with the same
+ * instructions. On weights accepted by fp8blk_load_check,
+ * bf16_gemv_twin(fp8blk_dequant_bf16(codes, scales)) == fp8blk_gemv(codes,
+ * scales) bit for bit.
+ *   w_bf16, x_bf16: device, 16-byte aligned; y: device, 4-byte aligned.
+ *   Shape limits, ws and stream as for fp8blk_gemv.
+ */
+int bf16_gemv_twin(const uint16_t *w_bf16, int64_t rows, int64_t cols, const uint16_t *x_bf16,
+                   int64_t M, float *y, void *ws, size_t ws_bytes, fp8blk_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

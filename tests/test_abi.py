@@ -1,0 +1,91 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-only logic (status text, workspace sizes, argument
+refusals that return before any device work) behaves as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_fp8blk_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([a-z_0-9]+)\s*\([^;{]*\)\s*;", text))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fb.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return fb.load()
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    assert {"fp8blk_load_check", "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin"} <= names
+    assert names == set(fb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # C linkage: the names are not mangled
+    out = os.popen(f"nm -D --defined-only {fb.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_host_helpers(lib):
+    assert fb.fp8blk_abi_version() == 1
+    for st in range(7):
+        assert fb.fp8blk_strerror(st)
+    assert fb.fp8blk_strerror(99) == "unknown status"
+    assert fb.fp8blk_workspace_bytes(fb.OP_LOAD_CHECK, 4096, 4096) >= 24
+    assert fb.fp8blk_workspace_bytes(fb.OP_GEMV, 4096, 4096, 16) == 0
+    assert fb.fp8blk_workspace_bytes(77, 1, 16) == 0
+
+
+P = 1 << 12  # a fake, 4096-aligned address: never dereferenced, every call below refuses first
+
+
+@pytest.mark.parametrize("rows,cols,M", [(0, 16, 1), (4, 8, 1), (4, 24, 1), (4, 65552, 1),
+                                         (4, 16, 0), (4, 16, 17), (-1, 16, 1)])
+def test_gemv_refuses_bad_shapes(lib, rows, cols, M):
+    assert lib.fp8blk_gemv(P, P, rows, cols, P, M, P, None, 0, None) == fb.ERR_ARG
+    assert lib.bf16_gemv_twin(P, rows, cols, P, M, P, None, 0, None) == fb.ERR_ARG
+
+
+def test_refuses_null_and_misaligned_pointers(lib):
+    assert lib.fp8blk_gemv(None, P, 4, 16, P, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv(P, None, 4, 16, P, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv(P, P, 4, 16, None, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv(P, P, 4, 16, P, 1, None, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv(P + 8, P, 4, 16, P, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv(P, P, 4, 16, P + 2, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv(P, P + 2, 4, 16, P, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.bf16_gemv_twin(P + 4, 4, 16, P, 1, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_dequant_bf16(P, P, 4, 16, P + 8, None) == fb.ERR_ARG
+    assert lib.fp8blk_dequant_bf16(None, P, 4, 16, P, None) == fb.ERR_ARG
+
+
+def test_load_check_refuses_before_device_work(lib):
+    fb_idx = ctypes.c_int64(123)
+    assert lib.fp8blk_load_check(P, P, 4, 17, P, P, 256, ctypes.byref(fb_idx), None) == fb.ERR_ARG
+    assert fb_idx.value == -1
+    assert lib.fp8blk_load_check(P, P, 4, 16, P, None, 256, None, None) == fb.ERR_WORKSPACE
+    assert lib.fp8blk_load_check(P, P, 4, 16, P, P, 8, None, None) == fb.ERR_WORKSPACE
+    assert lib.fp8blk_load_check(P, P, 4, 16, P, P + 4, 256, None, None) == fb.ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fb, "_lib", None)
+    monkeypatch.setattr(fb, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fb.load()
