@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8-blk GEMV on one MI355X.
+
+Metric: effective weight GB/s (codes + f32 block-scale grid read per second)
+and its fraction of the MI355X HBM3E peak (8.0 TB/s).
+
+Default workload (one "step"): the whole-step dense sweep -- 43 layers x
+[q 4096x4096, kv 1024x4096, o 4096x4096, gate 2048x4096, up 2048x4096,
+down 4096x2048] plus the 129280x4096 head: 259 distinct FP8-blk linears
+(~3.2 GB of codes, far above the 256 MB Infinity Cache, so every step reads
+cold from HBM), M=1, launched back to back on one stream. Inputs are drawn
+on the device with seeded generators and are resident in HBM before timing.
+
+Output: one JSON line. Besides the headline it carries
+  roofline      the GEMV kernel's algorithmic bytes / its average launch
+                duration (HIP events around every launch, instrumented pass),
+                against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle's double-precision GEMV over the same sweep;
+  per_config    cold-cache medians for the single-linear workloads (decode
+                shape, projection pair, verify panel at M=2..16), FP8 arm and
+                bf16 twin.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "FP8-blk GEMV effective weight GB/s (% of HBM peak), M=1 and M=16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--mode", choices=("graph", "stream"), default="graph",
+                   help="replay the sweep's 259 launches from a captured HIP graph, or enqueue them one by one")
+    p.add_argument("--arm", choices=("fp8", "bf16"), default="fp8", help="time the FP8 arm or the bf16 twin")
+    p.add_argument("--layers", type=int, default=43, help="layers in the sweep (default: the full 43)")
+    p.add_argument("--no-extra", action="store_true", help="skip the per-config cold-cache table")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--reps", type=int, default=15, help="cold-cache repetitions per config")
+    return p.parse_args()
+
+
+class Sweep:
+    """The sweep's linears on the device, load-checked, with prepared calls."""
+
+    def __init__(self, torch, fb, inputs, dev, layers, arm):
+        self.plan = inputs.sweep_plan(layers)
+        self.dev = dev
+        self.xs = {c: inputs.device_x(c, 1, 7 + c, dev) for c in sorted({l.cols for l in self.plan.linears})}
+        ws = torch.empty(fb.fp8blk_workspace_bytes(fb.OP_LOAD_CHECK, 1, 16), dtype=torch.uint8, device=dev)
+        self.lins = []
+        for spec in self.plan.linears:
+            codes, scales = inputs.device_linear(spec.rows, spec.cols, spec.seed, dev)
+            grid = torch.empty(scales.shape, dtype=torch.float32, device=dev)
+            fb.fp8blk_load_check(codes, scales, grid, ws)  # raises on any refusal
+            y = torch.empty((1, spec.rows), dtype=torch.float32, device=dev)
+            w = codes
+            if arm == "bf16":
+                w = torch.empty((spec.rows, spec.cols), dtype=torch.int16, device=dev)
+                fb.fp8blk_dequant_bf16(codes, grid, w)
+                del codes
+            self.lins.append(dict(spec=spec, w=w, grid=grid, x=self.xs[spec.cols], y=y, scales=scales))
+        torch.cuda.synchronize()
+        self.arm = arm
+        self.weight_bytes = self.plan.weight_bytes()  # FP8 codes + f32 grid, the metric's bytes
+        self.read_bytes = sum(self.algo_bytes(l["spec"]) for l in self.lins)
+
+    def algo_bytes(self, spec):
+        """Algorithmic bytes of one launch: weights (codes or bf16 slab), f32
+        grid (FP8 arm), x (bf16) and y (f32)."""
+        gr, gc = -(-spec.rows // 128), -(-spec.cols // 128)
+        wb = spec.rows * spec.cols * (1 if self.arm == "fp8" else 2)
+        return wb + (4 * gr * gc if self.arm == "fp8" else 0) + 2 * spec.cols + 4 * spec.rows
+
+    def calls(self, fb, stream=None):
+        out = []
+        for l in self.lins:
+            if self.arm == "fp8":
+                out.append(fb.prepared("fp8blk_gemv", l["w"], l["grid"], l["x"], l["y"], stream=stream))
+            else:
+                out.append(fb.prepared("bf16_gemv_twin", l["w"], l["x"], l["y"], stream=stream))
+        return out
+
+
+def run_calls(calls):
+    for c in calls:
+        st = c()
+        if st != 0:
+            raise RuntimeError(f"GEMV launch returned status {st}")
+
+
+def time_sweep(torch, fb, sw, steps, warmup, mode):
+    """Wall time of `steps` whole sweeps on one stream, events around all of them."""
+    stream = torch.cuda.current_stream()
+    graph = None
+    if mode == "graph":
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            run_calls(sw.calls(fb))  # warm the code objects before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            run_calls(sw.calls(fb, stream=cap))
+        torch.cuda.synchronize()
+        step = graph.replay
+    else:
+        calls = sw.calls(fb)
+        step = lambda: run_calls(calls)  # noqa: E731
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def launch_durations(torch, fb, sw, passes=2):
+    """Per-launch GPU durations: an event pair around every launch, on the
+    launching stream. Returns a list of (spec, seconds)."""
+    stream = torch.cuda.current_stream()
+    calls = sw.calls(fb)
+    out = []
+    for _ in range(passes):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+        for c, (a, b) in zip(calls, evs):
+            a.record(stream)
+            if c() != 0:
+                raise RuntimeError("GEMV launch failed")
+            b.record(stream)
+        torch.cuda.synchronize()
+        out = [(l["spec"], a.elapsed_time(b) / 1e3) for l, (a, b) in zip(sw.lins, evs)]  # keep the last pass
+    return out
+
+
+def per_config(torch, fb, inputs, dev, reps):
+    """Cold-cache medians for the single-linear workloads, FP8 arm and bf16 twin."""
+    # Cold cache without dirty lines: read 1 GiB of other data before each rep
+    # (a write flush would leave write-backs competing with the timed reads).
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    rows_out = []
+
+    def timed(call):
+        ts = []
+        for r in range(reps):
+            flush.sum()  # 1 GiB read: evicts the 256 MB Infinity Cache and the L2s
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            if call() != 0:
+                raise RuntimeError("launch failed")
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        ts.sort()
+        return statistics.median(ts), ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+
+    def add(name, L, Ms):
+        codes = torch.from_numpy(L.codes).to(dev)
+        scales = torch.from_numpy(L.scales).to(dev)
+        grid = torch.empty(scales.shape, dtype=torch.float32, device=dev)
+        fb.fp8blk_load_check(codes, scales, grid, ws)
+        slab = torch.empty((L.rows, L.cols), dtype=torch.int16, device=dev)
+        fb.fp8blk_dequant_bf16(codes, grid, slab)
+        xall = torch.from_numpy(L.x.view("int16")).to(dev)
+        wbytes = L.weight_bytes()
+        for M in Ms:
+            x = xall[:M].contiguous()
+            y = torch.empty((M, L.rows), dtype=torch.float32, device=dev)
+            med, p10, p90 = timed(fb.prepared("fp8blk_gemv", codes, grid, x, y))
+            tmed, _, _ = timed(fb.prepared("bf16_gemv_twin", slab, x, y))
+            rows_out.append(dict(linear=name, rows=L.rows, cols=L.cols, M=M, us=round(med * 1e6, 2),
+                                 us_p10=round(p10 * 1e6, 2), us_p90=round(p90 * 1e6, 2),
+                                 weight_GBps=round(wbytes / med / 1e9, 1),
+                                 pct_hbm_peak=round(100 * wbytes / med / 1e9 / HBM_PEAK_GBS, 1),
+                                 twin_us=round(tmed * 1e6, 2),
+                                 twin_GBps=round(2 * L.rows * L.cols / tmed / 1e9, 1)))
+            log(f"  {name} M={M}: {rows_out[-1]['us']} us, {rows_out[-1]['weight_GBps']} GB/s "
+                f"({rows_out[-1]['pct_hbm_peak']}%), twin {rows_out[-1]['twin_GBps']} GB/s")
+
+    add("decode_4096x4096", inputs.decode_shape(), [1])
+    for L in inputs.projection_pair():
+        add(L.name, L, [1])
+    for L in inputs.verify_panel():
+        add(L.name, L, [1] + list(inputs.VERIFY_M))
+    del flush
+    return rows_out
+
+
+def cpu_baseline(torch, sw, oracle):
+    """The oracle's double GEMV (O6) over the sweep's linears, timed on the host
+    cores (inputs copied to host memory first, outside the timing)."""
+    nthreads = min(16, os.cpu_count() or 1)
+    host = []
+    for l in sw.lins:
+        if sw.arm != "fp8":
+            return None
+        host.append((l["w"].cpu().numpy(), l["scales"].cpu().numpy(), l["x"].cpu().numpy().view("uint16")))
+    times = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        for codes, scales, x in host:
+            oracle.gemv_f64(codes, scales, x, nthreads=nthreads)
+        times.append(time.perf_counter() - t0)
+    t = min(times)
+    return {"value": round(sw.weight_bytes / t / 1e9, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"the full sweep ({len(host)} linears, {sw.weight_bytes / 1e9:.2f} GB of weights), double "
+                      f"GEMV over {nthreads} host threads, best of 2 passes of {t:.2f} s each or more"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world > 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the FP8-blk "
+              f"GEMV is a single-GPU kernel here, and sharding it over GPUs is a design note, not a run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp8_fp8blk_amd as fb
+    from block_scaled_fp8_fp8blk_amd import inputs
+
+    fb.load()
+    dev = torch.device("cuda:0")
+    log(f"setting up the sweep ({args.layers} layers + head, arm {args.arm})")
+    t0 = time.perf_counter()
+    sw = Sweep(torch, fb, inputs, dev, args.layers, args.arm)
+    log(f"  {len(sw.lins)} linears, {sw.weight_bytes / 1e9:.3f} GB weights, set up in {time.perf_counter() - t0:.1f} s")
+
+    secs, wall = time_sweep(torch, fb, sw, args.steps, args.warmup, args.mode)
+    ms_per_step = secs / args.steps * 1e3
+    value = sw.weight_bytes * args.steps / secs / 1e9
+    log(f"sweep: {ms_per_step:.4f} ms/step, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak), "
+        f"host wall {wall:.3f} s")
+
+    durs = launch_durations(torch, fb, sw)
+    ksum = sum(d for _, d in durs)
+    n = len(durs)
+    bytes_total = sw.read_bytes
+    achieved = bytes_total / ksum / 1e9
+    head = [d for s, d in durs if s.name == "head"]
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_gemv<fp8, M<=1>" if args.arm == "fp8" else "k_gemv<bf16, M<=1>",
+            "launches": n, "avg_launch_us": round(ksum / n * 1e6, 3),
+            "avg_algo_bytes_per_launch": int(bytes_total / n),
+            "sum_kernel_ms_per_step": round(ksum * 1e3, 4),
+            "head_us": round(head[0] * 1e6, 2) if head else None}
+    log(f"roofline: avg launch {roof['avg_launch_us']} us, {achieved:.1f} GB/s algorithmic "
+        f"({100 * roof['frac']:.1f}%), sum of kernels {roof['sum_kernel_ms_per_step']} ms/step")
+
+    extra = None
+    if not args.no_extra:
+        log("per-config cold-cache table")
+        extra = per_config(torch, fb, inputs, dev, args.reps)
+
+    cpu = None
+    if not args.no_cpu and args.arm == "fp8":
+        import oracle
+        log("CPU oracle baseline over the sweep")
+        cpu = cpu_baseline(torch, sw, oracle)
+        if cpu:
+            log(f"  oracle: {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    m16 = [r for r in (extra or []) if r["M"] == 16 and r["rows"] == 12288]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, drawn on the device; e4m3 codes of N(0,1)*0.05, e8m0 scales in [124,130], "
+                "x = bf16 of N(0,1))",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": f"whole-step dense sweep: {args.layers} x [q 4096x4096, kv 1024x4096, o 4096x4096, "
+                               f"gate 2048x4096, up 2048x4096, down 4096x2048] + head 129280x4096; "
+                               f"{len(sw.lins)} distinct FP8-blk linears, M=1, back to back on one stream",
+                   "arm": args.arm, "launch": args.mode, "M": 1, "linears": len(sw.lins),
+                   "weight_bytes_per_step": sw.weight_bytes, "cold_cache": "working set 12x the 256 MB MALL"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "m16_verify_12288x4096": ({"weight_GBps": m16[0]["weight_GBps"], "pct_hbm_peak": m16[0]["pct_hbm_peak"],
+                                   "us": m16[0]["us"]} if m16 else None),
+        "per_config": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -166,3 +166,27 @@ def raw_call(name: str, *args):
     """Call an exported symbol with raw ctypes arguments (pointers as ints).
     Used by tests that exercise the C ABI's argument checks directly."""
     return getattr(load(), name)(*args)
+
+
+def prepared(name: str, *tensors_and_sizes, stream=None):
+    """Marshal an entry point's arguments once and return a zero-argument
+    callable that enqueues it and returns its status. For launch-bound loops
+    (benchmarks, graph capture), where per-call tensor inspection would
+    dominate. Supported: "fp8blk_gemv" (codes, scales_f32, x_bf16, y) and
+    "bf16_gemv_twin" (w_bf16, x_bf16, y); no workspace (these need none)."""
+    import torch
+    fn = getattr(load(), name)
+    s = _stream(stream)
+    if name == "fp8blk_gemv":
+        codes, grid, x, y = tensors_and_sizes
+        rows, cols = codes.shape
+        args = (_dev(codes, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows, cols,
+                _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], _dev(y, (torch.float32,), "y"), None, 0, s)
+    elif name == "bf16_gemv_twin":
+        w, x, y = tensors_and_sizes
+        rows, cols = w.shape
+        args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
+                _dev(y, (torch.float32,), "y"), None, 0, s)
+    else:
+        raise ValueError(f"prepared: unsupported entry point {name!r}")
+    return lambda: fn(*args)

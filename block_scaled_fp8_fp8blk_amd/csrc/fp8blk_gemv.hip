@@ -20,7 +20,7 @@
 // 4 waves. The waves of a workgroup form 4/sw row streams of sw waves each;
 // the sw waves of a stream split the segments of its rows (split-K) and meet
 // in LDS, where one wave adds the segment sums in order. Each wave handles R
-// consecutive rows, so one x chunk feeds R rows.
+// consecutive rows, so one widened x chunk feeds R rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +42,7 @@ struct GemvArgs {
     int64_t rows;
     int K, M, T, GC;
     int sw;              // waves per row stream: 1, 2 or 4
+    int sw_log2;         // log2(sw)
     int tpw;             // segments per wave, ceil(T / sw)
 };
 
@@ -61,11 +62,25 @@ struct Fetch<kFp8> {
     __device__ __forceinline__ static Raw load(const GemvArgs& a, int64_t r, int q) {
         const uint8_t* p = static_cast<const uint8_t*>(a.w) + r * a.K + (int64_t)q * kChunk;
         Raw raw;
-        raw.c = *reinterpret_cast<const uint4*>(p);
+        raw.c = load_stream16(p);
         raw.s = a.grid[(r >> 7) * a.GC + (q >> 3)];  // chunk q lies in column block q / 8
         return raw;
     }
-    __device__ __forceinline__ static void weights(const Raw& raw, float* w) { decode16_fp8(raw.c, raw.s, w); }
+    __device__ __forceinline__ static void weights(const Raw& raw, float* w) { decode16_fp8_scaled(raw.c, raw.s, w); }
+    // Rows r0 .. r0 + n - 1 (clamped to the last row) of chunk q, into
+    // raw[i][u]. n <= 4 rows starting at a multiple of n share one 128-row
+    // block, hence one scale load.
+    template <int N, int TPW>
+    __device__ __forceinline__ static void load_rows(const GemvArgs& a, int64_t r0, int n, int q, Raw (&raw)[N][TPW],
+                                                     int u) {
+        const uint8_t* base = static_cast<const uint8_t*>(a.w) + (int64_t)q * kChunk;
+        const float s = a.grid[(min(r0, a.rows - 1) >> 7) * a.GC + (q >> 3)];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            raw[i][u].c = load_stream16(base + min(r0 + i, a.rows - 1) * a.K);
+            raw[i][u].s = s;
+        }
+    }
 };
 
 template <>
@@ -76,124 +91,276 @@ struct Fetch<kBf16> {
     __device__ __forceinline__ static Raw load(const GemvArgs& a, int64_t r, int q) {
         const uint16_t* p = static_cast<const uint16_t*>(a.w) + r * a.K + (int64_t)q * kChunk;
         Raw raw;
-        raw.lo = *reinterpret_cast<const uint4*>(p);
-        raw.hi = *reinterpret_cast<const uint4*>(p + 8);
+        raw.lo = load_stream16(p);
+        raw.hi = load_stream16(p + 8);
         return raw;
     }
     __device__ __forceinline__ static void weights(const Raw& raw, float* w) {
         widen8_bf16(raw.lo, w);
         widen8_bf16(raw.hi, w + 8);
     }
+    template <int N, int TPW>
+    __device__ __forceinline__ static void load_rows(const GemvArgs& a, int64_t r0, int n, int q, Raw (&raw)[N][TPW],
+                                                     int u) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) raw[i][u] = load(a, min(r0 + i, a.rows - 1), q);
+    }
 };
 
-template <int KIND, int MT, int R>
-__global__ __launch_bounds__(kThreads) void k_gemv(const GemvArgs a) {
-    using F = Fetch<KIND>;
-    extern __shared__ float part[];  // [row stream][segment][R * MT], used when sw > 1
+// Row-of-lane layout of a transposed reduction: value j of a group of four
+// ends in row kRowOf4[j] of its register; the mapping is its own inverse.
+__device__ __forceinline__ int value_in_row(int row) { return row == 1 ? 2 : row == 2 ? 1 : row; }
 
-    const int wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
-    const int streams = kWaves / a.sw;
-    const int rs = wave / a.sw, sp = wave % a.sw;
-    const int64_t r0 = ((int64_t)blockIdx.x * streams + rs) * R;
+// Panel kernel: an activation panel of M <= MT rows (also M = 1 when a row has
+// more than 16 segments). A wave owns R consecutive rows and walks its
+// segments in order, prefetching the next segment's codes while it computes
+// the current one. Per segment, each lane decodes its chunk of the R rows
+// once, then for every activation row m widens that row's x chunk and runs the
+// R fused multiply-add chains; the R * MT lane partials go through the
+// transposing reductions (tree64xV). A value keeps the same register and row
+// in every segment, so the running sums over segments are plain register adds,
+// and the lanes of a row store their own results. With sw > 1 each segment's
+// sums go to LDS and the first wave of the row stream adds them in order.
+template <int KIND, int MT, int R>
+__global__ __launch_bounds__(kThreads) void k_panel(const GemvArgs a) {
+    constexpr int V = R * MT;
+    constexpr int VP = V < 4 ? 4 : V;
+    constexpr int G = VP / 4;
+    using F = Fetch<KIND>;
+    extern __shared__ float part[];  // [row stream][segment][VP], used when sw > 1
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const int lane = threadIdx.x % kLanes;
+    const int rs = wave >> a.sw_log2, sp = wave & ((1 << a.sw_log2) - 1);
+    const int64_t r0 = (((int64_t)blockIdx.x << (2 - a.sw_log2)) + rs) * R;
     const int tb = sp * a.tpw;
     const int te = min(a.T, tb + a.tpw);
+    const int last_q = a.K / kChunk - 1;
+    const int vrow = value_in_row(lane >> 4);  // value j held by this lane's row
 
-    float y[R][MT];
+    float y[G];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) y[i][m] = 0.0f;
+    for (int g = 0; g < G; ++g) y[g] = 0.0f;
 
+    typename F::Raw raw[R][1];
+    if (tb < te) F::load_rows(a, r0, R, min(tb * kLanes + lane, last_q), raw, 0);
     for (int t = tb; t < te; ++t) {
+        typename F::Raw nxt[R][1];
+        if (t + 1 < te) F::load_rows(a, r0, R, min((t + 1) * kLanes + lane, last_q), nxt, 0);
         const int q = t * kLanes + lane;
-        const bool active = q * kChunk < a.K;
-        float acc[R][MT];
+        const bool live = q <= last_q;
+        const int qc = min(q, last_q);
+        float w[R][kChunk];
 #pragma unroll
-        for (int i = 0; i < R; ++i)
+        for (int i = 0; i < R; ++i) F::weights(raw[i][0], w[i]);
+        float v[VP];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
-        if (active) {
-            float w[R][kChunk];
+        for (int k = 0; k < VP; ++k) v[k] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const int64_t r = min(r0 + i, a.rows - 1);
-                F::weights(F::load(a, r, q), w[i]);
-            }
+        for (int m = 0; m < MT; ++m) {
+            if (m < a.M) {
+                const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.K + (int64_t)qc * kChunk);
+                float xf[kChunk];
+                widen8_bf16(xp[0], xf);
+                widen8_bf16(xp[1], xf + 8);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < a.M) {
-                    const uint16_t* xp = a.x + (int64_t)m * a.K + (int64_t)q * kChunk;
-                    float xv[kChunk];
-                    widen8_bf16(*reinterpret_cast<const uint4*>(xp), xv);
-                    widen8_bf16(*reinterpret_cast<const uint4*>(xp + 8), xv + 8);
+                for (int i = 0; i < R; ++i) {
+                    float s = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        float s = 0.0f;
-#pragma unroll
-                        for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[i][j], xv[j], s);
-                        acc[i][m] = s;
-                    }
+                    for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[i][j], xf[j], s);
+                    v[i * MT + m] = live ? s : 0.0f;
                 }
             }
         }
+        float red[G];
+        tree64xV<VP>(v, red);
+        if (a.sw_log2 == 0) {
 #pragma unroll
-        for (int i = 0; i < R; ++i)
+            for (int g = 0; g < G; ++g) y[g] = (t == 0) ? red[g] : y[g] + red[g];
+        } else if ((lane & 15) == 0) {
+            float* dst = part + ((int64_t)rs * a.T + t) * VP;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float P = tree64(acc[i][m]);
-                if (a.sw == 1) {
-                    y[i][m] = (t == 0) ? P : y[i][m] + P;
-                } else if (lane == 0) {
-                    part[((int64_t)rs * a.T + t) * (R * MT) + i * MT + m] = P;
-                }
-            }
+            for (int g = 0; g < G; ++g) dst[4 * g + vrow] = red[g];
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) raw[i][0] = nxt[i][0];
     }
 
-    if (a.sw > 1) {
+    if (a.sw_log2 > 0) {
+        __syncthreads();
+        if (sp != 0) return;
+        // lanes 0 .. VP-1: one value each, summed over the segments in order
+        if (lane < VP) {
+            const float* p = part + (int64_t)rs * a.T * VP + lane;
+            float acc = p[0];
+            for (int t = 1; t < a.T; ++t) acc = acc + p[(int64_t)t * VP];
+            const int i = lane / MT, m = lane % MT;
+            if (lane < V && m < a.M && r0 + i < a.rows) a.y[(int64_t)m * a.rows + r0 + i] = acc;
+        }
+        return;
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int vi = 4 * g + vrow;
+            const int i = vi / MT, m = vi % MT;
+            if (vi < V && m < a.M && r0 + i < a.rows) a.y[(int64_t)m * a.rows + r0 + i] = y[g];
+        }
+    }
+}
+
+// Single-row (M = 1) kernel. A wave owns R consecutive rows x TPW segments
+// (R, TPW in {1, 2, 4}): each lane holds R * TPW 16-column chunks in flight,
+// the code is straight-line, and every load of the wave (codes, one block
+// scale per segment -- R <= 4 consecutive rows from a multiple of R never
+// cross a 128-row block --, x) is issued before any arithmetic. The x chunk of
+// a segment is widened once and feeds the R rows. The R * TPW lane partials
+// then go through transposing 64-lane reductions (tree64xV), which yield
+// exactly the per-segment trees of the order above. When a row has more than
+// TPW segments they are split over sw = 2 or 4 waves of the workgroup, which
+// leave their segment sums in LDS; one wave then adds them in order. Lanes
+// whose chunk lies past the last column load a valid chunk and contribute +0.0.
+template <int KIND, int R, int TPW>
+__global__ __launch_bounds__(kThreads) void k_gemv_m1(const GemvArgs a) {
+    constexpr int V = R * TPW;
+    constexpr int VP = V < 4 ? 4 : V;  // reductions run in groups of four values
+    using F = Fetch<KIND>;
+    extern __shared__ float part[];  // [row stream][segment][R], used when sw > 1
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);  // uniform: scalar branches below
+    const int lane = threadIdx.x % kLanes;
+    const int rs = wave >> a.sw_log2, sp = wave & ((1 << a.sw_log2) - 1);
+    const int64_t r0 = (((int64_t)blockIdx.x << (2 - a.sw_log2)) + rs) * R;
+    const int t0 = sp * a.tpw;
+    const int nseg = min(a.tpw, a.T - t0);  // wave-uniform; <= 0 for an idle wave
+    const int last_q = a.K / kChunk - 1;
+
+    // Loads are unconditional and in the order the arithmetic consumes them,
+    // so the compiler can wait for each segment alone (no branch merges the
+    // outstanding-load counts). A segment past this wave's range re-reads
+    // its last one, a chunk past the last column re-reads the last chunk;
+    // both are discarded below.
+    typename F::Raw raw[R][TPW];
+    uint4 xr[TPW][2];
+    const int t_last = max(0, min(t0 + nseg, a.T) - 1);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int q = min(min(t0 + u, t_last) * kLanes + lane, last_q);
+        F::load_rows(a, r0, R, q, raw, u);
+        const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)q * kChunk);
+        xr[u][0] = xp[0];
+        xr[u][1] = xp[1];
+    }
+    // Keep every load ahead of the arithmetic: with one shot of data per wave,
+    // the bytes in flight per CU are what sets the streaming rate.
+    __builtin_amdgcn_sched_barrier(0);
+    float v[VP];
+#pragma unroll
+    for (int k = V; k < VP; ++k) v[k] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const bool live = u < nseg && (t0 + u) * kLanes + lane <= last_q;
+        float xf[kChunk];
+        widen8_bf16(xr[u][0], xf);
+        widen8_bf16(xr[u][1], xf + 8);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            float w[kChunk];
+            F::weights(raw[i][u], w);
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[j], xf[j], s);
+            v[i * TPW + u] = live ? s : 0.0f;
+        }
+    }
+    float red[VP / 4];
+    tree64xV<VP>(v, red);
+    // segment sum of (row i, segment u): value k = i * TPW + u
+#define FP8BLK_P(i, u) lane_value(red[((i) * TPW + (u)) / 4], 16 * kRowOf4[((i) * TPW + (u)) % 4])
+
+    float y[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        y[i] = FP8BLK_P(i, 0);
+#pragma unroll
+        for (int u = 1; u < TPW; ++u)
+            if (u < nseg) y[i] = y[i] + FP8BLK_P(i, u);
+    }
+    if (a.sw_log2 > 0) {
+        if (lane == 0)
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u)
+                    if (u < nseg) part[((int64_t)rs * a.T + t0 + u) * R + i] = FP8BLK_P(i, u);
         __syncthreads();
         if (sp != 0) return;
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float* p = part + (int64_t)rs * a.T * (R * MT) + i * MT + m;
-                float v = p[0];
-                for (int t = 1; t < a.T; ++t) v = v + p[t * (R * MT)];
-                y[i][m] = v;
-            }
+        for (int i = 0; i < R; ++i) {
+            const float* p = part + (int64_t)rs * a.T * R + i;
+            float v = p[0];
+            for (int t = 1; t < a.T; ++t) v = v + p[t * R];
+            y[i] = v;
+        }
     }
-    if (lane == 0) {
+#undef FP8BLK_P
+    if (lane < R && r0 + lane < a.rows) {
+        float out = y[0];
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                if (r0 + i < a.rows && m < a.M) a.y[(int64_t)m * a.rows + r0 + i] = y[i][m];
+        for (int i = 1; i < R; ++i)
+            if (lane == i) out = y[i];
+        a.y[r0 + lane] = out;
     }
 }
 
 struct Plan {
-    int MT, R, sw;
+    int MT, R, sw, tpw;  // tpw: compile-time segments per wave of the M = 1 kernel
+    bool m1;             // the single-row kernel (else the panel kernel)
 };
 
-// Plan: a pure function of (rows, cols, M). Enough waves to fill 256 CUs,
-// splitting the segments of a row over 2 or 4 waves when rows are few.
+// Plan: a pure function of (rows, cols, M); it never changes bits.
+// M = 1 and at most 16 segments: the single-row kernel with four chunks per
+// lane -- TPW segments per wave (the next power of two >= T, at most 4), the
+// rest of a row over sw waves, R = 4 / TPW rows. Measured on the whole-step
+// sweep: more chunks per lane (fewer, longer waves) or fewer (more waves) are
+// both slower. Otherwise the panel kernel with R = 4 rows per wave, splitting
+// the segments of a row over 2 or 4 waves while fewer than 4096 waves would
+// run.
 Plan make_plan(int64_t rows, int64_t K, int64_t M) {
     Plan p;
-    p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
-    p.R = p.MT <= 4 ? 2 : 1;
     const int64_t T = ceil_div(K, kSegCols);
-    const int64_t row_waves = ceil_div(rows, p.R);
+    p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    if (p.MT == 1 && T <= 16) {
+        p.m1 = true;
+        p.tpw = T >= 3 ? 4 : (int)T;
+        p.sw = T <= p.tpw ? 1 : T <= 2 * p.tpw ? 2 : 4;
+        p.R = 4 / p.tpw;
+        return p;
+    }
+    p.m1 = false;
+    p.tpw = 0;
+    p.R = 4;
+    const int64_t groups = ceil_div(rows, p.R);
     p.sw = 1;
-    while (p.sw < 4 && p.sw * 2 <= T && row_waves * p.sw < 4096) p.sw *= 2;
+    while (p.sw < 4 && p.sw * 2 <= T && groups * p.sw < 4096) p.sw *= 2;
     return p;
 }
 
 template <int KIND, int MT, int R>
-void launch(const GemvArgs& a, hipStream_t s) {
+void launch_panel(const GemvArgs& a, hipStream_t s) {
+    constexpr int VP = R * MT < 4 ? 4 : R * MT;
     const int streams = kWaves / a.sw;
     const int64_t blocks = ceil_div(ceil_div(a.rows, R), streams);
-    const size_t lds = a.sw > 1 ? (size_t)streams * a.T * R * MT * sizeof(float) : 0;
-    k_gemv<KIND, MT, R><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(a);
+    const size_t lds = a.sw > 1 ? (size_t)streams * a.T * VP * sizeof(float) : 0;
+    k_panel<KIND, MT, R><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(a);
+}
+
+template <int KIND, int R, int TPW>
+void launch_m1(const GemvArgs& a, hipStream_t s) {
+    const int streams = kWaves / a.sw;
+    const int64_t blocks = ceil_div(ceil_div(a.rows, R), streams);
+    const size_t lds = a.sw > 1 ? (size_t)streams * a.T * R * sizeof(float) : 0;
+    k_gemv_m1<KIND, R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(a);
 }
 
 template <int KIND>
@@ -211,15 +378,23 @@ int run(const void* w, const float* grid, int64_t rows, int64_t cols, const uint
     a.T = (int)ceil_div(cols, kSegCols);
     a.GC = (int)ceil_div(cols, kBlock);
     a.sw = p.sw;
+    a.sw_log2 = p.sw == 4 ? 2 : p.sw == 2 ? 1 : 0;
     a.tpw = (int)ceil_div(a.T, p.sw);
     if (ceil_div(ceil_div(rows, p.R), kWaves / p.sw) > 0x7fffffff) return FP8BLK_ERR_ARG;
     (void)hipGetLastError();
-    switch (p.MT) {
-        case 1: launch<KIND, 1, 2>(a, s); break;
-        case 2: launch<KIND, 2, 2>(a, s); break;
-        case 4: launch<KIND, 4, 2>(a, s); break;
-        case 8: launch<KIND, 8, 1>(a, s); break;
-        default: launch<KIND, 16, 1>(a, s); break;
+    if (p.m1) {
+#define FP8BLK_M1(RR, TT) \
+    if (p.R == RR && p.tpw == TT) launch_m1<KIND, RR, TT>(a, s)
+        FP8BLK_M1(1, 4); else FP8BLK_M1(2, 2); else FP8BLK_M1(4, 1);
+#undef FP8BLK_M1
+    } else {
+        switch (p.MT) {
+            case 1: launch_panel<KIND, 1, 4>(a, s); break;
+            case 2: launch_panel<KIND, 2, 4>(a, s); break;
+            case 4: launch_panel<KIND, 4, 4>(a, s); break;
+            case 8: launch_panel<KIND, 8, 4>(a, s); break;
+            default: launch_panel<KIND, 16, 4>(a, s); break;
+        }
     }
     return launch_status();
 }
