@@ -51,6 +51,14 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the per-config cold-cache table")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--reps", type=int, default=15, help="cold-cache repetitions per config")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (a known-size reference for counter runs)")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
+                   help="CPU only: print a markdown summary of a rocprofv3 --kernel-trace --stats run and exit")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_SIZE_CSV", "WRITE_SIZE_CSV"),
+                   help="CPU only: calibrate two rocprofv3 --pmc runs of --copy-calibration against the 1 GiB "
+                        "copy, print a markdown summary, write profiles/gemv_<arm>_m1_sweep_counters.json, exit")
+    p.add_argument("--command", default="", help="the command line that produced the CSVs (recorded in summaries)")
     return p.parse_args()
 
 
@@ -135,22 +143,65 @@ def time_sweep(torch, fb, sw, steps, warmup, mode):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
-def launch_durations(torch, fb, sw, passes=2):
-    """Per-launch GPU durations: an event pair around every launch, on the
-    launching stream. Returns a list of (spec, seconds)."""
+def per_shape_launches(torch, fb, sw, reps=10):
+    """Average launch duration per distinct shape: a HIP graph of all the
+    sweep's linears of that shape (distinct buffers, so still cold), replayed
+    `reps` times between events on the replaying stream."""
     stream = torch.cuda.current_stream()
-    calls = sw.calls(fb)
+    shapes = {}
+    for l in sw.lins:
+        key = (l["spec"].name.split(".")[-1], l["spec"].rows, l["spec"].cols)
+        shapes.setdefault(key, []).append(l)
     out = []
-    for _ in range(passes):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-        for c, (a, b) in zip(calls, evs):
-            a.record(stream)
-            if c() != 0:
-                raise RuntimeError("GEMV launch failed")
-            b.record(stream)
+    for (name, rows, cols), ls in shapes.items():
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        sub = Sweep.__new__(Sweep)
+        sub.lins, sub.arm = ls, sw.arm
+        with torch.cuda.graph(g, stream=cap):
+            run_calls(sub.calls(fb, stream=cap))
         torch.cuda.synchronize()
-        out = [(l["spec"], a.elapsed_time(b) / 1e3) for l, (a, b) in zip(sw.lins, evs)]  # keep the last pass
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(ls))
+        wb = ls[0]["spec"].weight_bytes()
+        out.append({"shape": f"{name} {rows}x{cols}", "launches_per_step": len(ls), "us": round(us, 3),
+                    "weight_GBps": round(wb / us / 1e3, 1)})
     return out
+
+
+KERNEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(arm):
+    """HBM bytes per launch of the sweep's GEMV launches from the committed
+    rocprofv3 counter summary, or None when absent or taken on other kernel
+    sources (the summary records the source hash it was taken on)."""
+    path = os.path.join(ROOT, "profiles", f"gemv_{arm}_m1_sweep_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def per_config(torch, fb, inputs, dev, reps):
@@ -229,8 +280,89 @@ def cpu_baseline(torch, sw, oracle):
                       f"GEMV over {nthreads} host threads, best of 2 passes of {t:.2f} s each or more"}
 
 
+def _short(name):
+    import re
+    m = re.search(r"\b(k_\w+(?:<[^>]*>)?)", name)
+    return m.group(1) if m else name[:60]
+
+
+def summarize_trace(stats_csv, trace_csv, command):
+    """Markdown: per-kernel stats of the FP8-blk kernels and per-shape medians."""
+    import csv
+    import collections
+    lines = ["# rocprofv3 kernel trace: FP8-blk GEMV, whole-step sweep (M=1)", "",
+             f"Command: `{command}`" if command else "", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        if "fp8blk" in r["Name"]:
+            lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.1f} | {r['MinNs']} | {r['MaxNs']} |")
+    by = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"]:
+            by[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["", "Per launch shape (grid = threads; q/o 262144, kv 65536, gate/up/down 131072, head 8273920):", "",
+              "| kernel | grid | launches | median us | min us |", "|---|---|---|---|---|"]
+    for (k, g), v in sorted(by.items(), key=lambda kv: kv[0][1]):
+        v.sort()
+        lines.append(f"| {k} | {g} | {len(v)} | {v[len(v) // 2] / 1e3:.2f} | {v[0] / 1e3:.2f} |")
+    print("\n".join(lines))
+
+
+def summarize_counters(fetch_csv, write_csv, command, arm="fp8"):
+    """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the 1 GiB
+    copy of --copy-calibration, then average the GEMV dispatches of one sweep
+    step (one launch per linear of the step, taken per launch shape)."""
+    import csv
+    import collections
+
+    def load(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        # the three 1 GiB calibration copies are the last copy dispatches of the run
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
+        gem = collections.defaultdict(list)
+        for r in rows:
+            if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"]:
+                gem[int(r["Grid_Size"])].append(float(r["Counter_Value"]))
+        return copies, {g: sorted(v)[len(v) // 2] for g, v in gem.items()}
+
+    fc, fg = load(fetch_csv)
+    wc, wg = load(write_csv)
+    gib_kib = 1 << 20
+    f_factor = gib_kib / (sorted(fc)[len(fc) // 2])
+    w_factor = gib_kib / (sorted(wc)[len(wc) // 2])
+    # launches per sweep step by grid size (threads): q,o 262144 (86), kv 65536 (43),
+    # gate,up,down 131072 (129), head 8273920 (1)
+    per_step = {262144: 86, 65536: 43, 131072: 129, 8273920: 1}
+    tot = sum(per_step[g] * (fg[g] * f_factor + wg[g] * w_factor) * 1024 for g in per_step)
+    launches = sum(per_step.values())
+    rec = {"source_hash": source_hash(), "arm": arm, "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": int(tot / launches),
+           "per_grid_kib": {str(g): {"fetch": fg[g], "write": wg[g]} for g in per_step},
+           "command": command}
+    with open(os.path.join(ROOT, "profiles", f"gemv_{arm}_m1_sweep_counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# rocprofv3 counters: FP8-blk GEMV, whole-step sweep (M=1)", "",
+             f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
+             f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
+             f"WRITE_SIZE x {w_factor:.3f} give bytes.", "",
+             "| grid (threads) | launches per step | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch |",
+             "|---|---|---|---|---|"]
+    for g in per_step:
+        lines.append(f"| {g} | {per_step[g]} | {fg[g]:.1f} | {wg[g]:.1f} | "
+                     f"{(fg[g] * f_factor + wg[g] * w_factor) * 1024 / 1e6:.3f} |")
+    lines += ["", f"Average HBM bytes per launch over one step: {tot / launches / 1e6:.3f} MB "
+              f"(source hash {rec['source_hash']})."]
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.command, args.arm)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the FP8-blk "
@@ -255,21 +387,33 @@ def main():
     log(f"sweep: {ms_per_step:.4f} ms/step, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak), "
         f"host wall {wall:.3f} s")
 
-    durs = launch_durations(torch, fb, sw)
-    ksum = sum(d for _, d in durs)
-    n = len(durs)
-    bytes_total = sw.read_bytes
-    achieved = bytes_total / ksum / 1e9
-    head = [d for s, d in durs if s.name == "head"]
+    # Roofline of the dominant kernel (the M=1 GEMV, every launch of the step):
+    # the graph replays the launches back to back (the kernel trace shows no
+    # idle gaps), so the timed region / launches is its average duration.
+    n = len(sw.lins)
+    avg_launch = secs / (args.steps * n)
+    achieved = sw.read_bytes / n / avg_launch / 1e9
+    traffic = counted_traffic(args.arm)
+    shapes = per_shape_launches(torch, fb, sw)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_gemv<fp8, M<=1>" if args.arm == "fp8" else "k_gemv<bf16, M<=1>",
-            "launches": n, "avg_launch_us": round(ksum / n * 1e6, 3),
-            "avg_algo_bytes_per_launch": int(bytes_total / n),
-            "sum_kernel_ms_per_step": round(ksum * 1e3, 4),
-            "head_us": round(head[0] * 1e6, 2) if head else None}
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "k_gemv_m1 (fp8)" if args.arm == "fp8" else "k_gemv_m1 (bf16 twin)",
+            "launches_per_step": n, "avg_launch_us": round(avg_launch * 1e6, 3),
+            "avg_algo_bytes_per_launch": int(sw.read_bytes / n), "source_hash": source_hash(),
+            "per_shape": shapes}
     log(f"roofline: avg launch {roof['avg_launch_us']} us, {achieved:.1f} GB/s algorithmic "
-        f"({100 * roof['frac']:.1f}%), sum of kernels {roof['sum_kernel_ms_per_step']} ms/step")
+        f"({100 * roof['frac']:.1f}%)")
+    for r in shapes:
+        log(f"  {r['shape']}: {r['us']} us per launch, {r['weight_GBps']} GB/s")
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+        del src, dst
 
     extra = None
     if not args.no_extra:
