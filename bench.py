@@ -241,14 +241,21 @@ def per_config(torch, fb, inputs, dev, reps):
             y = torch.empty((M, L.rows), dtype=torch.float32, device=dev)
             med, p10, p90 = timed(fb.prepared("fp8blk_gemv", codes, grid, x, y))
             tmed, _, _ = timed(fb.prepared("bf16_gemv_twin", slab, x, y))
+            mmed, _, _ = timed(fb.prepared("fp8blk_gemv_mfma", codes, grid, x, y))
+            mtmed, _, _ = timed(fb.prepared("bf16_gemv_twin_mfma", slab, x, y))
             rows_out.append(dict(linear=name, rows=L.rows, cols=L.cols, M=M, us=round(med * 1e6, 2),
                                  us_p10=round(p10 * 1e6, 2), us_p90=round(p90 * 1e6, 2),
                                  weight_GBps=round(wbytes / med / 1e9, 1),
                                  pct_hbm_peak=round(100 * wbytes / med / 1e9 / HBM_PEAK_GBS, 1),
                                  twin_us=round(tmed * 1e6, 2),
-                                 twin_GBps=round(2 * L.rows * L.cols / tmed / 1e9, 1)))
-            log(f"  {name} M={M}: {rows_out[-1]['us']} us, {rows_out[-1]['weight_GBps']} GB/s "
-                f"({rows_out[-1]['pct_hbm_peak']}%), twin {rows_out[-1]['twin_GBps']} GB/s")
+                                 twin_GBps=round(2 * L.rows * L.cols / tmed / 1e9, 1),
+                                 mfma_us=round(mmed * 1e6, 2), mfma_GBps=round(wbytes / mmed / 1e9, 1),
+                                 mfma_pct_hbm_peak=round(100 * wbytes / mmed / 1e9 / HBM_PEAK_GBS, 1),
+                                 mfma_twin_GBps=round(2 * L.rows * L.cols / mtmed / 1e9, 1)))
+            r = rows_out[-1]
+            log(f"  {name} M={M}: {r['us']} us, {r['weight_GBps']} GB/s ({r['pct_hbm_peak']}%), twin "
+                f"{r['twin_GBps']} GB/s | matrix-core arm {r['mfma_us']} us, {r['mfma_GBps']} GB/s "
+                f"({r['mfma_pct_hbm_peak']}%), twin {r['mfma_twin_GBps']} GB/s")
 
     add("decode_4096x4096", inputs.decode_shape(), [1])
     for L in inputs.projection_pair():
@@ -451,8 +458,11 @@ def main():
                    "weight_bytes_per_step": sw.weight_bytes, "cold_cache": "working set 12x the 256 MB MALL"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "m16_verify_12288x4096": ({"weight_GBps": m16[0]["weight_GBps"], "pct_hbm_peak": m16[0]["pct_hbm_peak"],
-                                   "us": m16[0]["us"]} if m16 else None),
+        "m16_verify_12288x4096": ({"vector_arm": {"weight_GBps": m16[0]["weight_GBps"],
+                                                  "pct_hbm_peak": m16[0]["pct_hbm_peak"], "us": m16[0]["us"]},
+                                   "matrix_core_arm": {"weight_GBps": m16[0]["mfma_GBps"],
+                                                       "pct_hbm_peak": m16[0]["mfma_pct_hbm_peak"],
+                                                       "us": m16[0]["mfma_us"]}} if m16 else None),
         "per_config": extra,
     }
     print(json.dumps(out), flush=True)

@@ -26,7 +26,7 @@ MIN_COLS, MAX_COLS, MAX_M = 16, 65536, 16
 
 # Every symbol include/fp8blk.h declares.
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
-           "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin")
+           "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def load():
     L.fp8blk_gemv.restype = i32
     L.bf16_gemv_twin.argtypes = [vp, i64, i64, vp, i64, vp, vp, sz, vp]
     L.bf16_gemv_twin.restype = i32
+    L.fp8blk_gemv_mfma.argtypes, L.fp8blk_gemv_mfma.restype = [vp, vp, i64, i64, vp, i64, vp, vp], i32
+    L.bf16_gemv_twin_mfma.argtypes, L.bf16_gemv_twin_mfma.restype = [vp, i64, i64, vp, i64, vp, vp], i32
     _lib = L
     return L
 
@@ -162,6 +164,30 @@ def bf16_gemv_twin(w_bf16, x_bf16, y, ws=None, stream=None, check=True):
     return st
 
 
+def fp8blk_gemv_mfma(codes, scales_f32, x_bf16, y, stream=None, check=True):
+    """Matrix-core arm of fp8blk_gemv (bitwise twin of bf16_gemv_twin_mfma)."""
+    import torch
+    rows, cols = codes.shape
+    st = load().fp8blk_gemv_mfma(_dev(codes, (torch.uint8,), "codes"),
+                                 _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
+                                 _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
+                                 _dev(y, (torch.float32,), "y"), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_mfma")
+    return st
+
+
+def bf16_gemv_twin_mfma(w_bf16, x_bf16, y, stream=None, check=True):
+    import torch
+    rows, cols = w_bf16.shape
+    st = load().bf16_gemv_twin_mfma(_dev(w_bf16, _bf16_dtypes(), "w_bf16"), rows, cols,
+                                    _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
+                                    _dev(y, (torch.float32,), "y"), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "bf16_gemv_twin_mfma")
+    return st
+
+
 def raw_call(name: str, *args):
     """Call an exported symbol with raw ctypes arguments (pointers as ints).
     Used by tests that exercise the C ABI's argument checks directly."""
@@ -172,8 +198,9 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
     """Marshal an entry point's arguments once and return a zero-argument
     callable that enqueues it and returns its status. For launch-bound loops
     (benchmarks, graph capture), where per-call tensor inspection would
-    dominate. Supported: "fp8blk_gemv" (codes, scales_f32, x_bf16, y) and
-    "bf16_gemv_twin" (w_bf16, x_bf16, y); no workspace (these need none)."""
+    dominate. Supported: "fp8blk_gemv" and "fp8blk_gemv_mfma" (codes,
+    scales_f32, x_bf16, y), "bf16_gemv_twin" and "bf16_gemv_twin_mfma" (w_bf16,
+    x_bf16, y); no workspace (these need none)."""
     import torch
     fn = getattr(load(), name)
     s = _stream(stream)
@@ -187,6 +214,16 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         rows, cols = w.shape
         args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
                 _dev(y, (torch.float32,), "y"), None, 0, s)
+    elif name == "fp8blk_gemv_mfma":
+        codes, grid, x, y = tensors_and_sizes
+        rows, cols = codes.shape
+        args = (_dev(codes, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows, cols,
+                _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], _dev(y, (torch.float32,), "y"), s)
+    elif name == "bf16_gemv_twin_mfma":
+        w, x, y = tensors_and_sizes
+        rows, cols = w.shape
+        args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
+                _dev(y, (torch.float32,), "y"), s)
     else:
         raise ValueError(f"prepared: unsupported entry point {name!r}")
     return lambda: fn(*args)

@@ -179,6 +179,34 @@ int fp8blk_gemv(const uint8_t *codes, const float *scales_f32, int64_t rows, int
 int bf16_gemv_twin(const uint16_t *w_bf16, int64_t rows, int64_t cols, const uint16_t *x_bf16,
                    int64_t M, float *y, void *ws, size_t ws_bytes, fp8blk_stream_t stream);
 
+/*
+ * Matrix-core arm ("Module dsv4_gpu" page, Fp8Dense; "Struct Dsv4Gpu" page,
+ * dense_fp8 and spec_greedy_batched_with). The same y as fp8blk_gemv, with the
+ * products run on gfx950's matrix cores (v_mfma_f32_16x16x32_bf16): the
+ * weights are decoded in registers to the bf16 values the dequant slab holds
+ * and the activation panel is consumed as bf16, padded to 16 rows, so the
+ * call stays bound by HBM for every M <= 16.
+ *   - fp8blk_gemv_mfma == bf16_gemv_twin_mfma(fp8blk_dequant_bf16(...)) bit for
+ *     bit on load-checked weights (same instruction sequence, same operands);
+ *   - row m of an M-row call == the 1-row call on x[m], bit for bit;
+ *   - the matrix core adds the 32 products of an instruction in an order the
+ *     hardware does not document, so the bits differ from fp8blk_gemv's
+ *     documented order; the result is within 1e-5 * sum_c |w x| of the exact
+ *     sum for inputs in the bf16 normal range (bf16 subnormal operands may be
+ *     flushed by the matrix core).
+ * Column order: blocks of 64 columns in increasing order; in block p, lane
+ * group kg (0..3) feeds columns [64p + 16kg, 64p + 16kg + 8) to one
+ * instruction and the next 8 to the following one, both into the same f32
+ * accumulator; a row's blocks may be split into 2 or 4 contiguous parts, as a
+ * function of (rows, cols) only, whose partial sums are added in part order.
+ * Arguments, limits, alignment, ownership and stream as for fp8blk_gemv /
+ * bf16_gemv_twin; no workspace. Enqueued on `stream`; does not wait.
+ */
+int fp8blk_gemv_mfma(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,
+                     const uint16_t *x_bf16, int64_t M, float *y, fp8blk_stream_t stream);
+int bf16_gemv_twin_mfma(const uint16_t *w_bf16, int64_t rows, int64_t cols, const uint16_t *x_bf16,
+                        int64_t M, float *y, fp8blk_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,8 @@ P = 1 << 12  # a fake, 4096-aligned address: never dereferenced, every call belo
 def test_gemv_refuses_bad_shapes(lib, rows, cols, M):
     assert lib.fp8blk_gemv(P, P, rows, cols, P, M, P, None, 0, None) == fb.ERR_ARG
     assert lib.bf16_gemv_twin(P, rows, cols, P, M, P, None, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_mfma(P, P, rows, cols, P, M, P, None) == fb.ERR_ARG
+    assert lib.bf16_gemv_twin_mfma(P, rows, cols, P, M, P, None) == fb.ERR_ARG
 
 
 def test_refuses_null_and_misaligned_pointers(lib):
@@ -73,6 +75,9 @@ def test_refuses_null_and_misaligned_pointers(lib):
     assert lib.bf16_gemv_twin(P + 4, 4, 16, P, 1, P, None, 0, None) == fb.ERR_ARG
     assert lib.fp8blk_dequant_bf16(P, P, 4, 16, P + 8, None) == fb.ERR_ARG
     assert lib.fp8blk_dequant_bf16(None, P, 4, 16, P, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_mfma(None, P, 4, 16, P, 1, P, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_mfma(P, None, 4, 16, P, 1, P, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_mfma(P + 8, P, 4, 16, P, 1, P, None) == fb.ERR_ARG
 
 
 def test_load_check_refuses_before_device_work(lib):
