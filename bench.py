@@ -16,14 +16,14 @@ Output: one JSON line. Besides the headline it carries
                 duration (HIP events around every launch, instrumented pass),
                 against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle's double-precision GEMV over the same sweep;
-  per_config    cold-cache medians for the single-linear workloads (decode
-                shape, projection pair, verify panel at M=2..16), FP8 arm and
-                bf16 twin.
+  per_config    per-launch times of the single-linear workloads (decode
+                shape, projection pair, verify panel at M=1..16), cold from HBM
+                (graphs over distinct copies), for the vector and matrix-core
+                kernels and their bf16 twins.
 """
 import argparse
 import json
 import os
-import statistics
 import sys
 import time
 
@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--layers", type=int, default=43, help="layers in the sweep (default: the full 43)")
     p.add_argument("--no-extra", action="store_true", help="skip the per-config cold-cache table")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--reps", type=int, default=15, help="cold-cache repetitions per config")
+    p.add_argument("--reps", type=int, default=10, help="graph replays per config measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a known-size reference for counter runs)")
     p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
@@ -205,27 +205,34 @@ def counted_traffic(arm):
 
 
 def per_config(torch, fb, inputs, dev, reps):
-    """Cold-cache medians for the single-linear workloads, FP8 arm and bf16 twin."""
-    # Cold cache without dirty lines: read 1 GiB of other data before each rep
-    # (a write flush would leave write-backs competing with the timed reads).
-    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    """Per-launch times of the single-linear workloads (decode shape,
+    projection pair, verify panel at M = 1..16), both arms of both kernels.
+    Like the sweep: a HIP graph launches the GEMV on enough distinct copies of
+    the linear to exceed 512 MB (twice the Infinity Cache), so every launch
+    reads cold from HBM, and `reps` replays are timed between events."""
     ws = torch.empty(256, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     rows_out = []
 
-    def timed(call):
-        ts = []
-        for r in range(reps):
-            flush.sum()  # 1 GiB read: evicts the 256 MB Infinity Cache and the L2s
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            if call() != 0:
-                raise RuntimeError("launch failed")
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) / 1e3)
-        ts.sort()
-        return statistics.median(ts), ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+    def timed(make_calls):
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            run_calls(make_calls(None))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            calls = make_calls(cap)
+            run_calls(calls)
+        torch.cuda.synchronize()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / (reps * len(calls))
 
     def add(name, L, Ms):
         codes = torch.from_numpy(L.codes).to(dev)
@@ -234,35 +241,42 @@ def per_config(torch, fb, inputs, dev, reps):
         fb.fp8blk_load_check(codes, scales, grid, ws)
         slab = torch.empty((L.rows, L.cols), dtype=torch.int16, device=dev)
         fb.fp8blk_dequant_bf16(codes, grid, slab)
+        copies = max(4, -(-(512 << 20) // (L.rows * L.cols)))
+        cs = [codes] + [codes.clone() for _ in range(copies - 1)]
+        ss = [slab] + [slab.clone() for _ in range(copies - 1)]
         xall = torch.from_numpy(L.x.view("int16")).to(dev)
         wbytes = L.weight_bytes()
         for M in Ms:
             x = xall[:M].contiguous()
             y = torch.empty((M, L.rows), dtype=torch.float32, device=dev)
-            med, p10, p90 = timed(fb.prepared("fp8blk_gemv", codes, grid, x, y))
-            tmed, _, _ = timed(fb.prepared("bf16_gemv_twin", slab, x, y))
-            mmed, _, _ = timed(fb.prepared("fp8blk_gemv_mfma", codes, grid, x, y))
-            mtmed, _, _ = timed(fb.prepared("bf16_gemv_twin_mfma", slab, x, y))
-            rows_out.append(dict(linear=name, rows=L.rows, cols=L.cols, M=M, us=round(med * 1e6, 2),
-                                 us_p10=round(p10 * 1e6, 2), us_p90=round(p90 * 1e6, 2),
-                                 weight_GBps=round(wbytes / med / 1e9, 1),
-                                 pct_hbm_peak=round(100 * wbytes / med / 1e9 / HBM_PEAK_GBS, 1),
-                                 twin_us=round(tmed * 1e6, 2),
-                                 twin_GBps=round(2 * L.rows * L.cols / tmed / 1e9, 1),
-                                 mfma_us=round(mmed * 1e6, 2), mfma_GBps=round(wbytes / mmed / 1e9, 1),
-                                 mfma_pct_hbm_peak=round(100 * wbytes / mmed / 1e9 / HBM_PEAK_GBS, 1),
-                                 mfma_twin_GBps=round(2 * L.rows * L.cols / mtmed / 1e9, 1)))
+            t = {}
+            for arm, fn, ws_ in (("vec", "fp8blk_gemv", cs), ("vec_twin", "bf16_gemv_twin", ss),
+                                 ("mfma", "fp8blk_gemv_mfma", cs), ("mfma_twin", "bf16_gemv_twin_mfma", ss)):
+                if fn.startswith("fp8blk"):
+                    mk = lambda st, fn=fn, ws_=ws_: [fb.prepared(fn, w, grid, x, y, stream=st) for w in ws_]  # noqa: E731
+                else:
+                    mk = lambda st, fn=fn, ws_=ws_: [fb.prepared(fn, w, x, y, stream=st) for w in ws_]  # noqa: E731
+                t[arm] = timed(mk)
+            pct = lambda sec: round(100 * wbytes / sec / 1e9 / HBM_PEAK_GBS, 1)  # noqa: E731
+            rows_out.append(dict(linear=name, rows=L.rows, cols=L.cols, M=M, copies=copies,
+                                 us=round(t["vec"] * 1e6, 2), weight_GBps=round(wbytes / t["vec"] / 1e9, 1),
+                                 pct_hbm_peak=pct(t["vec"]),
+                                 twin_us=round(t["vec_twin"] * 1e6, 2),
+                                 twin_GBps=round(2 * L.rows * L.cols / t["vec_twin"] / 1e9, 1),
+                                 mfma_us=round(t["mfma"] * 1e6, 2), mfma_GBps=round(wbytes / t["mfma"] / 1e9, 1),
+                                 mfma_pct_hbm_peak=pct(t["mfma"]),
+                                 mfma_twin_GBps=round(2 * L.rows * L.cols / t["mfma_twin"] / 1e9, 1)))
             r = rows_out[-1]
-            log(f"  {name} M={M}: {r['us']} us, {r['weight_GBps']} GB/s ({r['pct_hbm_peak']}%), twin "
+            log(f"  {name} M={M}: vector arm {r['us']} us, {r['weight_GBps']} GB/s ({r['pct_hbm_peak']}%), twin "
                 f"{r['twin_GBps']} GB/s | matrix-core arm {r['mfma_us']} us, {r['mfma_GBps']} GB/s "
                 f"({r['mfma_pct_hbm_peak']}%), twin {r['mfma_twin_GBps']} GB/s")
+        del cs, ss
 
     add("decode_4096x4096", inputs.decode_shape(), [1])
     for L in inputs.projection_pair():
         add(L.name, L, [1])
     for L in inputs.verify_panel():
         add(L.name, L, [1] + list(inputs.VERIFY_M))
-    del flush
     return rows_out
 
 

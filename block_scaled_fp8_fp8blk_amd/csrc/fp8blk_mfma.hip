@@ -116,8 +116,13 @@ struct MfFetch<1> {  // bf16 slab
 
 // A wave owns TILES tiles of 16 consecutive rows and one part of the column
 // blocks. Lane l = 16 kg + i: matrix row i of each tile, k-group kg, and, for
-// the activation operand, panel row m = i (rows m >= M are zero).
-template <int KIND, int TILES>
+// the activation operand, panel row m = i (rows m >= M are zero). The blocks
+// are taken U at a time: every load of the U blocks (codes, scales, x) is
+// issued before the matrix instructions that consume them. Loads are
+// unconditional (a block past the part re-reads the part's last block and is
+// skipped; a lane past the last column re-reads the last chunk with a zero
+// activation operand), so the waits stay per block.
+template <int KIND, int TILES, int U>
 __global__ __launch_bounds__(kMfThreads) void k_mfma(const MfArgs a) {
     using F = MfFetch<KIND>;
     __shared__ v4f part[kMfWaves][TILES][kLanes];
@@ -130,46 +135,42 @@ __global__ __launch_bounds__(kMfThreads) void k_mfma(const MfArgs a) {
     const int pb = sp * a.bpp;
     const int pe = min(a.nblk, pb + a.bpp);
     const bool xrow = i < a.M;
+    const int last_col = a.K - 16;
+    const uint16_t* xrow_ptr = a.x + (int64_t)min(i, a.M - 1) * a.K;
 
     v4f acc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    typename F::Raw raw[TILES];
-    uint4 xr[2];
-    auto load_block = [&](int p, typename F::Raw (&dst)[TILES], uint4 (&xd)[2]) {
-        const int col = p * kBlk + kg * 16;
-        const bool live = col < a.K;
+    for (int p0 = pb; p0 < pe; p0 += U) {
+        typename F::Raw raw[U][TILES];
+        uint4 xr[U][2];
 #pragma unroll
-        for (int t = 0; t < TILES; ++t)
-            dst[t] = live ? F::load(a, min(r0 + t * kTile + i, a.rows - 1), col) : F::zero();
-        if (live && xrow) {
-            const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)i * a.K + col);
-            xd[0] = xp[0];
-            xd[1] = xp[1];
-        } else {
-            xd[0] = make_uint4(0, 0, 0, 0);
-            xd[1] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int col = min(min(p0 + u, pe - 1) * kBlk + kg * 16, last_col);
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) raw[u][t] = F::load(a, min(r0 + t * kTile + i, a.rows - 1), col);
+            const uint4* xp = reinterpret_cast<const uint4*>(xrow_ptr + col);
+            xr[u][0] = xp[0];
+            xr[u][1] = xp[1];
         }
-    };
-    if (pb < pe) load_block(pb, raw, xr);
-    for (int p = pb; p < pe; ++p) {
-        typename F::Raw nraw[TILES];
-        uint4 nx[2];
-        if (p + 1 < pe) load_block(p + 1, nraw, nx);
-        const v8bf b0 = __builtin_bit_cast(v8bf, xr[0]);
-        const v8bf b1 = __builtin_bit_cast(v8bf, xr[1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-            v8bf a0, a1;
-            F::operands(raw[t], a0, a1);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            if (p0 + u < pe) {
+                const bool live = xrow && (p0 + u) * kBlk + kg * 16 <= last_col;
+                const uint4 z = make_uint4(0, 0, 0, 0);
+                const v8bf b0 = __builtin_bit_cast(v8bf, live ? xr[u][0] : z);
+                const v8bf b1 = __builtin_bit_cast(v8bf, live ? xr[u][1] : z);
+#pragma unroll
+                for (int t = 0; t < TILES; ++t) {
+                    v8bf a0, a1;
+                    F::operands(raw[u][t], a0, a1);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+                }
+            }
         }
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) raw[t] = nraw[t];
-        xr[0] = nx[0];
-        xr[1] = nx[1];
     }
 
     if (a.sw_log2 > 0) {
@@ -200,16 +201,20 @@ __global__ __launch_bounds__(kMfThreads) void k_mfma(const MfArgs a) {
     }
 }
 
-// Plan, a function of (rows, cols) only: split the column blocks over 2 or 4
-// waves while fewer than 2048 waves would run.
+// Plan, a function of (rows, cols) only: the columns of a row group are split
+// over 2 or 4 waves while fewer than 2048 waves would run; a wave takes TILES
+// = 4, 2 or 1 row tiles -- the most that still leaves >= 768 waves, since the
+// row tiles of a wave share its activation loads -- and U = 8 / TILES blocks
+// per batch of loads. Measured on 12288 x 4096 and 4096 x 4096 at M = 1 and 16.
 struct MfPlan {
     int tiles, sw;
 };
 MfPlan mf_plan(int64_t rows, int64_t K) {
     MfPlan p;
-    p.tiles = 1;
     const int64_t nblk = ceil_div(K, kBlk);
-    const int64_t groups = ceil_div(rows, kTile * p.tiles);
+    p.tiles = 4;
+    while (p.tiles > 1 && ceil_div(rows, (int64_t)kTile * p.tiles) * 4 < 768) p.tiles /= 2;
+    const int64_t groups = ceil_div(rows, (int64_t)kTile * p.tiles);
     p.sw = 1;
     while (p.sw < 4 && p.sw * 2 <= nblk && groups * p.sw < 2048) p.sw *= 2;
     return p;
@@ -235,7 +240,13 @@ int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const u
     const int64_t blocks = ceil_div(ceil_div(rows, (int64_t)kTile * p.tiles), streams);
     if (blocks > 0x7fffffff) return FP8BLK_ERR_ARG;
     (void)hipGetLastError();
-    k_mfma<KIND, 1><<<dim3((unsigned)blocks), dim3(kMfThreads), 0, s>>>(a);
+    const dim3 nb((unsigned)blocks), nt(kMfThreads);
+    if (p.tiles == 4)
+        k_mfma<KIND, 4, 2><<<nb, nt, 0, s>>>(a);
+    else if (p.tiles == 2)
+        k_mfma<KIND, 2, 4><<<nb, nt, 0, s>>>(a);
+    else
+        k_mfma<KIND, 1, 8><<<nb, nt, 0, s>>>(a);
     return launch_status();
 }
 
