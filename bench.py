@@ -103,6 +103,33 @@ class Sweep:
                 out.append(fb.prepared("bf16_gemv_twin", l["w"], l["x"], l["y"], stream=stream))
         return out
 
+    def calls_grouped(self, fb, stream=None):
+        """The same linears with the projections of one input in one launch:
+        per layer [q, kv], o, [gate, up], down; then the head."""
+        out, k = [], 0
+        while k < len(self.lins):
+            l = self.lins[k]
+            kind = l["spec"].name.split(".")[-1]
+            n = 2 if kind in ("q", "gate") else 1
+            ls = self.lins[k:k + n]
+            if n == 1:
+                out += Sweep.calls(_Sub(ls, self.arm), fb, stream)
+            elif self.arm == "fp8":
+                out.append(fb.prepared("fp8blk_gemv_grouped", [(m["w"], m["grid"], m["y"]) for m in ls], l["x"],
+                                       stream=stream))
+            else:
+                out.append(fb.prepared("bf16_gemv_twin_grouped", [(m["w"], m["y"]) for m in ls], l["x"],
+                                       stream=stream))
+            k += n
+        return out
+
+
+class _Sub:
+    """A subset of a sweep's linears (for per-shape graphs and grouping)."""
+
+    def __init__(self, lins, arm):
+        self.lins, self.arm = lins, arm
+
 
 def run_calls(calls):
     for c in calls:
@@ -111,23 +138,24 @@ def run_calls(calls):
             raise RuntimeError(f"GEMV launch returned status {st}")
 
 
-def time_sweep(torch, fb, sw, steps, warmup, mode):
+def time_sweep(torch, fb, sw, steps, warmup, mode, grouped=False):
     """Wall time of `steps` whole sweeps on one stream, events around all of them."""
     stream = torch.cuda.current_stream()
+    make = sw.calls_grouped if grouped else sw.calls
     graph = None
     if mode == "graph":
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
-            run_calls(sw.calls(fb))  # warm the code objects before capture
+            run_calls(make(fb))  # warm the code objects before capture
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap):
-            run_calls(sw.calls(fb, stream=cap))
+            run_calls(make(fb, stream=cap))
         torch.cuda.synchronize()
         step = graph.replay
     else:
-        calls = sw.calls(fb)
+        calls = make(fb)
         step = lambda: run_calls(calls)  # noqa: E731
     for _ in range(warmup):
         step()
@@ -157,10 +185,8 @@ def per_shape_launches(torch, fb, sw, reps=10):
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         g = torch.cuda.CUDAGraph()
-        sub = Sweep.__new__(Sweep)
-        sub.lins, sub.arm = ls, sw.arm
         with torch.cuda.graph(g, stream=cap):
-            run_calls(sub.calls(fb, stream=cap))
+            run_calls(Sweep.calls(_Sub(ls, sw.arm), fb, stream=cap))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -407,6 +433,11 @@ def main():
     value = sw.weight_bytes * args.steps / secs / 1e9
     log(f"sweep: {ms_per_step:.4f} ms/step, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak), "
         f"host wall {wall:.3f} s")
+    gsecs, _ = time_sweep(torch, fb, sw, args.steps, args.warmup, args.mode, grouped=True)
+    gvalue = sw.weight_bytes * args.steps / gsecs / 1e9
+    n_grouped = len(sw.calls_grouped(fb))
+    log(f"sweep, shared-input projections grouped ({n_grouped} launches): {gsecs / args.steps * 1e3:.4f} ms/step, "
+        f"{gvalue:.1f} GB/s ({100 * gvalue / HBM_PEAK_GBS:.1f}% of peak)")
 
     # Roofline of the dominant kernel (the M=1 GEMV, every launch of the step):
     # the graph replays the launches back to back (the kernel trace shows no
@@ -471,6 +502,10 @@ def main():
                    "arm": args.arm, "launch": args.mode, "M": 1, "linears": len(sw.lins),
                    "weight_bytes_per_step": sw.weight_bytes, "cold_cache": "working set 12x the 256 MB MALL"},
         "roofline": roof,
+        "sweep_grouped": {"value": round(gvalue, 1), "unit": "GB/s", "launches_per_step": n_grouped,
+                          "ms_per_step": round(gsecs / args.steps * 1e3, 4),
+                          "pct_hbm_peak": round(100 * gvalue / HBM_PEAK_GBS, 2),
+                          "note": "same 259 linears and bits; q+kv and gate+up each in one launch"},
         "cpu_baseline": cpu,
         "m16_verify_12288x4096": ({"vector_arm": {"weight_GBps": m16[0]["weight_GBps"],
                                                   "pct_hbm_peak": m16[0]["pct_hbm_peak"], "us": m16[0]["us"]},

@@ -26,7 +26,15 @@ MIN_COLS, MAX_COLS, MAX_M = 16, 65536, 16
 
 # Every symbol include/fp8blk.h declares.
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
-           "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma")
+           "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
+           "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma")
+MAX_GROUP = 8
+
+
+class Linear(ctypes.Structure):
+    """fp8blk_linear: one member of a grouped launch."""
+    _fields_ = [("w", ctypes.c_void_p), ("scales_f32", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("y", ctypes.c_void_p)]
 
 _lib = None
 
@@ -60,6 +68,10 @@ def load():
     L.fp8blk_gemv.restype = i32
     L.bf16_gemv_twin.argtypes = [vp, i64, i64, vp, i64, vp, vp, sz, vp]
     L.bf16_gemv_twin.restype = i32
+    L.fp8blk_gemv_grouped.argtypes = [ctypes.POINTER(Linear), i32, i64, vp, i64, vp]
+    L.fp8blk_gemv_grouped.restype = i32
+    L.bf16_gemv_twin_grouped.argtypes = [ctypes.POINTER(Linear), i32, i64, vp, i64, vp]
+    L.bf16_gemv_twin_grouped.restype = i32
     L.fp8blk_gemv_mfma.argtypes, L.fp8blk_gemv_mfma.restype = [vp, vp, i64, i64, vp, i64, vp, vp], i32
     L.bf16_gemv_twin_mfma.argtypes, L.bf16_gemv_twin_mfma.restype = [vp, i64, i64, vp, i64, vp, vp], i32
     _lib = L
@@ -164,6 +176,44 @@ def bf16_gemv_twin(w_bf16, x_bf16, y, ws=None, stream=None, check=True):
     return st
 
 
+def _group(members, fp8):
+    import torch
+    arr = (Linear * len(members))()
+    cols = None
+    for k, mem in enumerate(members):
+        w, grid, y = mem if fp8 else (mem[0], None, mem[1])
+        rows, c = w.shape
+        cols = c if cols is None else cols
+        if c != cols:
+            raise ValueError("grouped linears must share cols")
+        arr[k].w = _dev(w, (torch.uint8,) if fp8 else _bf16_dtypes(), "w")
+        arr[k].scales_f32 = _dev(grid, (torch.float32,), "scales_f32") if fp8 else None
+        arr[k].rows = rows
+        arr[k].y = _dev(y, (torch.float32,), "y")
+    return arr, cols
+
+
+def fp8blk_gemv_grouped(members, x_bf16, stream=None, check=True):
+    """One launch for [(codes, scales_f32, y), ...] sharing x (same bits as
+    separate fp8blk_gemv calls)."""
+    arr, cols = _group(members, True)
+    st = load().fp8blk_gemv_grouped(arr, len(members), cols, _dev(x_bf16, _bf16_dtypes(), "x_bf16"),
+                                    x_bf16.shape[0], _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_grouped")
+    return st
+
+
+def bf16_gemv_twin_grouped(members, x_bf16, stream=None, check=True):
+    """One launch for [(w_bf16, y), ...] sharing x."""
+    arr, cols = _group(members, False)
+    st = load().bf16_gemv_twin_grouped(arr, len(members), cols, _dev(x_bf16, _bf16_dtypes(), "x_bf16"),
+                                       x_bf16.shape[0], _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "bf16_gemv_twin_grouped")
+    return st
+
+
 def fp8blk_gemv_mfma(codes, scales_f32, x_bf16, y, stream=None, check=True):
     """Matrix-core arm of fp8blk_gemv (bitwise twin of bf16_gemv_twin_mfma)."""
     import torch
@@ -224,6 +274,10 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         rows, cols = w.shape
         args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
                 _dev(y, (torch.float32,), "y"), s)
+    elif name in ("fp8blk_gemv_grouped", "bf16_gemv_twin_grouped"):
+        members, x = tensors_and_sizes
+        arr, cols = _group(members, name == "fp8blk_gemv_grouped")
+        args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], s)
     else:
         raise ValueError(f"prepared: unsupported entry point {name!r}")
     return lambda: fn(*args)

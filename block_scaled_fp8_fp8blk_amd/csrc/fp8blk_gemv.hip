@@ -122,7 +122,7 @@ __device__ __forceinline__ int value_in_row(int row) { return row == 1 ? 2 : row
 // and the lanes of a row store their own results. With sw > 1 each segment's
 // sums go to LDS and the first wave of the row stream adds them in order.
 template <int KIND, int MT, int R>
-__global__ __launch_bounds__(kThreads) void k_panel(const GemvArgs a) {
+__device__ __forceinline__ void panel_body(const GemvArgs& a, int64_t block) {
     constexpr int V = R * MT;
     constexpr int VP = V < 4 ? 4 : V;
     constexpr int G = VP / 4;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_panel(const GemvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const int lane = threadIdx.x % kLanes;
     const int rs = wave >> a.sw_log2, sp = wave & ((1 << a.sw_log2) - 1);
-    const int64_t r0 = (((int64_t)blockIdx.x << (2 - a.sw_log2)) + rs) * R;
+    const int64_t r0 = ((block << (2 - a.sw_log2)) + rs) * R;
     const int tb = sp * a.tpw;
     const int te = min(a.T, tb + a.tpw);
     const int last_q = a.K / kChunk - 1;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_panel(const GemvArgs a) {
 // leave their segment sums in LDS; one wave then adds them in order. Lanes
 // whose chunk lies past the last column load a valid chunk and contribute +0.0.
 template <int KIND, int R, int TPW>
-__global__ __launch_bounds__(kThreads) void k_gemv_m1(const GemvArgs a) {
+__device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
     constexpr int V = R * TPW;
     constexpr int VP = V < 4 ? 4 : V;  // reductions run in groups of four values
     using F = Fetch<KIND>;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_m1(const GemvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);  // uniform: scalar branches below
     const int lane = threadIdx.x % kLanes;
     const int rs = wave >> a.sw_log2, sp = wave & ((1 << a.sw_log2) - 1);
-    const int64_t r0 = (((int64_t)blockIdx.x << (2 - a.sw_log2)) + rs) * R;
+    const int64_t r0 = ((block << (2 - a.sw_log2)) + rs) * R;
     const int t0 = sp * a.tpw;
     const int nseg = min(a.tpw, a.T - t0);  // wave-uniform; <= 0 for an idle wave
     const int last_q = a.K / kChunk - 1;
@@ -313,6 +313,58 @@ __global__ __launch_bounds__(kThreads) void k_gemv_m1(const GemvArgs a) {
     }
 }
 
+// Up to kMaxGroup linears that share cols, x and M, in one launch: the
+// workgroups of linear j are [start[j], start[j + 1]). Each output gets the
+// same arithmetic as in a call of its own.
+constexpr int kMaxGroup = 8;
+struct GroupArgs {
+    GemvArgs base;  // w, grid, y and rows are taken per linear
+    const void* w[kMaxGroup];
+    const float* grid[kMaxGroup];
+    float* y[kMaxGroup];
+    int64_t rows[kMaxGroup];
+    int64_t start[kMaxGroup + 1];
+    int n;
+};
+
+__device__ __forceinline__ int group_of(const GroupArgs& g, int64_t block) {
+    int j = 0;
+    for (int k = 1; k < g.n; ++k)
+        if (block >= g.start[k]) j = k;
+    return j;
+}
+
+__host__ __device__ __forceinline__ GemvArgs group_args(const GroupArgs& g, int j) {
+    GemvArgs a = g.base;
+    a.w = g.w[j];
+    a.grid = g.grid[j];
+    a.y = g.y[j];
+    a.rows = g.rows[j];
+    return a;
+}
+
+template <int KIND, int R, int TPW>
+__global__ __launch_bounds__(kThreads) void k_gemv_m1(const GemvArgs a) {
+    m1_body<KIND, R, TPW>(a, blockIdx.x);
+}
+
+template <int KIND, int R, int TPW>
+__global__ __launch_bounds__(kThreads) void k_gemv_m1_group(const GroupArgs g) {
+    const int j = __builtin_amdgcn_readfirstlane(group_of(g, blockIdx.x));
+    m1_body<KIND, R, TPW>(group_args(g, j), (int64_t)blockIdx.x - g.start[j]);
+}
+
+template <int KIND, int MT, int R>
+__global__ __launch_bounds__(kThreads) void k_panel(const GemvArgs a) {
+    panel_body<KIND, MT, R>(a, blockIdx.x);
+}
+
+template <int KIND, int MT, int R>
+__global__ __launch_bounds__(kThreads) void k_panel_group(const GroupArgs g) {
+    const int j = __builtin_amdgcn_readfirstlane(group_of(g, blockIdx.x));
+    panel_body<KIND, MT, R>(group_args(g, j), (int64_t)blockIdx.x - g.start[j]);
+}
+
 struct Plan {
     int MT, R, sw, tpw;  // tpw: compile-time segments per wave of the M = 1 kernel
     bool m1;             // the single-row kernel (else the panel kernel)
@@ -346,33 +398,42 @@ Plan make_plan(int64_t rows, int64_t K, int64_t M) {
     return p;
 }
 
+int64_t blocks_for(const Plan& p, int64_t rows) { return ceil_div(ceil_div(rows, p.R), kWaves / p.sw); }
+
 template <int KIND, int MT, int R>
-void launch_panel(const GemvArgs& a, hipStream_t s) {
+void launch_panel(const GroupArgs& g, int64_t blocks, hipStream_t s) {
     constexpr int VP = R * MT < 4 ? 4 : R * MT;
-    const int streams = kWaves / a.sw;
-    const int64_t blocks = ceil_div(ceil_div(a.rows, R), streams);
-    const size_t lds = a.sw > 1 ? (size_t)streams * a.T * VP * sizeof(float) : 0;
-    k_panel<KIND, MT, R><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(a);
+    const int streams = kWaves / g.base.sw;
+    const size_t lds = g.base.sw > 1 ? (size_t)streams * g.base.T * VP * sizeof(float) : 0;
+    if (g.n == 1)
+        k_panel<KIND, MT, R><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(group_args(g, 0));
+    else
+        k_panel_group<KIND, MT, R><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(g);
 }
 
 template <int KIND, int R, int TPW>
-void launch_m1(const GemvArgs& a, hipStream_t s) {
-    const int streams = kWaves / a.sw;
-    const int64_t blocks = ceil_div(ceil_div(a.rows, R), streams);
-    const size_t lds = a.sw > 1 ? (size_t)streams * a.T * R * sizeof(float) : 0;
-    k_gemv_m1<KIND, R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(a);
+void launch_m1(const GroupArgs& g, int64_t blocks, hipStream_t s) {
+    const int streams = kWaves / g.base.sw;
+    const size_t lds = g.base.sw > 1 ? (size_t)streams * g.base.T * R * sizeof(float) : 0;
+    if (g.n == 1)
+        k_gemv_m1<KIND, R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(group_args(g, 0));
+    else
+        k_gemv_m1_group<KIND, R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(g);
 }
 
+// One launch for g.n linears that share cols, x and M (g.w, g.grid, g.y and
+// g.rows filled in). The plan is that of a single linear with all the rows.
 template <int KIND>
-int run(const void* w, const float* grid, int64_t rows, int64_t cols, const uint16_t* x, int64_t M, float* y,
-        hipStream_t s) {
-    const Plan p = make_plan(rows, cols, M);
-    GemvArgs a;
-    a.w = w;
-    a.grid = grid;
+int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s) {
+    int64_t all_rows = 0;
+    for (int j = 0; j < g.n; ++j) all_rows += g.rows[j];
+    const Plan p = make_plan(all_rows, cols, M);
+    GemvArgs& a = g.base;
+    a.w = nullptr;
+    a.grid = nullptr;
+    a.y = nullptr;
+    a.rows = 0;
     a.x = x;
-    a.y = y;
-    a.rows = rows;
     a.K = (int)cols;
     a.M = (int)M;
     a.T = (int)ceil_div(cols, kSegCols);
@@ -380,20 +441,23 @@ int run(const void* w, const float* grid, int64_t rows, int64_t cols, const uint
     a.sw = p.sw;
     a.sw_log2 = p.sw == 4 ? 2 : p.sw == 2 ? 1 : 0;
     a.tpw = (int)ceil_div(a.T, p.sw);
-    if (ceil_div(ceil_div(rows, p.R), kWaves / p.sw) > 0x7fffffff) return FP8BLK_ERR_ARG;
+    g.start[0] = 0;
+    for (int j = 0; j < g.n; ++j) g.start[j + 1] = g.start[j] + blocks_for(p, g.rows[j]);
+    const int64_t blocks = g.start[g.n];
+    if (blocks > 0x7fffffff) return FP8BLK_ERR_ARG;
     (void)hipGetLastError();
     if (p.m1) {
 #define FP8BLK_M1(RR, TT) \
-    if (p.R == RR && p.tpw == TT) launch_m1<KIND, RR, TT>(a, s)
+    if (p.R == RR && p.tpw == TT) launch_m1<KIND, RR, TT>(g, blocks, s)
         FP8BLK_M1(1, 4); else FP8BLK_M1(2, 2); else FP8BLK_M1(4, 1);
 #undef FP8BLK_M1
     } else {
         switch (p.MT) {
-            case 1: launch_panel<KIND, 1, 4>(a, s); break;
-            case 2: launch_panel<KIND, 2, 4>(a, s); break;
-            case 4: launch_panel<KIND, 4, 4>(a, s); break;
-            case 8: launch_panel<KIND, 8, 4>(a, s); break;
-            default: launch_panel<KIND, 16, 4>(a, s); break;
+            case 1: launch_panel<KIND, 1, 4>(g, blocks, s); break;
+            case 2: launch_panel<KIND, 2, 4>(g, blocks, s); break;
+            case 4: launch_panel<KIND, 4, 4>(g, blocks, s); break;
+            case 8: launch_panel<KIND, 8, 4>(g, blocks, s); break;
+            default: launch_panel<KIND, 16, 4>(g, blocks, s); break;
         }
     }
     return launch_status();
@@ -408,6 +472,37 @@ int check_common(const void* w, int64_t rows, int64_t cols, const uint16_t* x, i
     return FP8BLK_OK;
 }
 
+template <int KIND>
+int run_single(const void* w, const float* grid, int64_t rows, int64_t cols, const uint16_t* x, int64_t M,
+               float* y, hipStream_t s) {
+    GroupArgs g;
+    g.n = 1;
+    g.w[0] = w;
+    g.grid[0] = grid;
+    g.y[0] = y;
+    g.rows[0] = rows;
+    return run<KIND>(g, cols, x, M, s);
+}
+
+template <int KIND>
+int run_grouped(const fp8blk_linear* lin, int n, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s) {
+    if (!lin || n < 1 || n > FP8BLK_MAX_GROUP) return FP8BLK_ERR_ARG;
+    GroupArgs g;
+    g.n = n;
+    for (int j = 0; j < n; ++j) {
+        const int st = check_common(lin[j].w, lin[j].rows, cols, x, M, lin[j].y, 0, nullptr, 0);
+        if (st != FP8BLK_OK) return st;
+        if (KIND == kFp8 && (!lin[j].scales_f32 || !aligned(lin[j].scales_f32, 4))) return FP8BLK_ERR_ARG;
+        g.w[j] = lin[j].w;
+        g.grid[j] = KIND == kFp8 ? lin[j].scales_f32 : nullptr;
+        g.y[j] = lin[j].y;
+        g.rows[j] = lin[j].rows;
+    }
+    return run<KIND>(g, cols, x, M, s);
+}
+
+static_assert(kMaxGroup == FP8BLK_MAX_GROUP, "group size of the ABI");
+
 }  // namespace
 }  // namespace fp8blk
 
@@ -420,7 +515,7 @@ extern "C" int fp8blk_gemv(const uint8_t* codes, const float* scales_f32, int64_
                                 fp8blk_workspace_bytes(FP8BLK_OP_GEMV, rows, cols, M), ws, ws_bytes);
     if (st != FP8BLK_OK) return st;
     if (!scales_f32 || !aligned(scales_f32, 4)) return FP8BLK_ERR_ARG;
-    return run<kFp8>(codes, scales_f32, rows, cols, x_bf16, M, y, reinterpret_cast<hipStream_t>(stream));
+    return run_single<kFp8>(codes, scales_f32, rows, cols, x_bf16, M, y, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int bf16_gemv_twin(const uint16_t* w_bf16, int64_t rows, int64_t cols, const uint16_t* x_bf16,
@@ -428,5 +523,15 @@ extern "C" int bf16_gemv_twin(const uint16_t* w_bf16, int64_t rows, int64_t cols
     const int st = check_common(w_bf16, rows, cols, x_bf16, M, y,
                                 fp8blk_workspace_bytes(FP8BLK_OP_BF16_TWIN, rows, cols, M), ws, ws_bytes);
     if (st != FP8BLK_OK) return st;
-    return run<kBf16>(w_bf16, nullptr, rows, cols, x_bf16, M, y, reinterpret_cast<hipStream_t>(stream));
+    return run_single<kBf16>(w_bf16, nullptr, rows, cols, x_bf16, M, y, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8blk_gemv_grouped(const fp8blk_linear* linears, int n, int64_t cols, const uint16_t* x_bf16,
+                                   int64_t M, fp8blk_stream_t stream) {
+    return run_grouped<kFp8>(linears, n, cols, x_bf16, M, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int bf16_gemv_twin_grouped(const fp8blk_linear* linears, int n, int64_t cols, const uint16_t* x_bf16,
+                                      int64_t M, fp8blk_stream_t stream) {
+    return run_grouped<kBf16>(linears, n, cols, x_bf16, M, reinterpret_cast<hipStream_t>(stream));
 }

@@ -180,6 +180,34 @@ int bf16_gemv_twin(const uint16_t *w_bf16, int64_t rows, int64_t cols, const uin
                    int64_t M, float *y, void *ws, size_t ws_bytes, fp8blk_stream_t stream);
 
 /*
+ * Grouped launch: several linears that read the same activation panel (the
+ * projections of one input, such as q and kv, or gate and up) in one kernel
+ * launch. Each output gets exactly the arithmetic of a call of its own, so
+ * fp8blk_gemv_grouped({L1, L2}, x) == fp8blk_gemv(L1, x), fp8blk_gemv(L2, x)
+ * bit for bit, and likewise for the twin. One launch instead of n removes the
+ * fixed per-launch cost; the same idea as the single launch per projection
+ * that the device decode path uses for its routed experts ("Module dsv4_gpu",
+ * DecodePath).
+ *   linears: HOST array of n descriptors, 1 <= n <= FP8BLK_MAX_GROUP; for each,
+ *     w = codes (fp8blk_gemv_grouped) or bf16 slab (bf16_gemv_twin_grouped),
+ *     scales_f32 = the f32 grid (ignored by the twin), rows >= 1, y = [M, rows].
+ *   cols, x_bf16, M: shared by all the linears; limits and alignment as for
+ *     fp8blk_gemv. No workspace. Enqueued on `stream`; does not wait.
+ */
+#define FP8BLK_MAX_GROUP 8
+typedef struct fp8blk_linear {
+    const void *w;
+    const float *scales_f32;
+    int64_t rows;
+    float *y;
+} fp8blk_linear;
+
+int fp8blk_gemv_grouped(const fp8blk_linear *linears, int n, int64_t cols, const uint16_t *x_bf16,
+                        int64_t M, fp8blk_stream_t stream);
+int bf16_gemv_twin_grouped(const fp8blk_linear *linears, int n, int64_t cols, const uint16_t *x_bf16,
+                           int64_t M, fp8blk_stream_t stream);
+
+/*
  * Matrix-core arm ("Module dsv4_gpu" page, Fp8Dense; "Struct Dsv4Gpu" page,
  * dense_fp8 and spec_greedy_batched_with). The same y as fp8blk_gemv, with the
  * products run on gfx950's matrix cores (v_mfma_f32_16x16x32_bf16): the

@@ -94,3 +94,22 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fb, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         fb.load()
+
+
+def test_grouped_refusals(lib):
+    L = fb.Linear
+    good = (L * 2)(L(P, P, 4, P), L(P, P, 4, P))
+    assert lib.fp8blk_gemv_grouped(good, 0, 16, P, 1, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_grouped(good, 9, 16, P, 1, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_grouped(None, 1, 16, P, 1, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_grouped(good, 2, 24, P, 1, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_grouped(good, 2, 16, P, 0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_grouped(good, 2, 16, P + 2, 1, None) == fb.ERR_ARG
+    bad = (L * 2)(L(P, P, 4, P), L(P + 8, P, 4, P))
+    assert lib.fp8blk_gemv_grouped(bad, 2, 16, P, 1, None) == fb.ERR_ARG
+    bad = (L * 2)(L(P, P, 4, P), L(P, None, 4, P))
+    assert lib.fp8blk_gemv_grouped(bad, 2, 16, P, 1, None) == fb.ERR_ARG
+    bad = (L * 2)(L(P, P, 0, P), L(P, P, 4, P))
+    assert lib.bf16_gemv_twin_grouped(bad, 2, 16, P, 1, None) == fb.ERR_ARG
+    bad = (L * 1)(L(P, P, 4, None))
+    assert lib.bf16_gemv_twin_grouped(bad, 1, 16, P, 1, None) == fb.ERR_ARG
