@@ -67,6 +67,14 @@ struct Fetch<kFp8> {
         return raw;
     }
     __device__ __forceinline__ static void weights(const Raw& raw, float* w) { decode16_fp8_scaled(raw.c, raw.s, w); }
+    // Codes only of rows r0 .. r0 + n - 1 (clamped to the last row) of chunk
+    // q; the scales are filled in by the caller.
+    template <int N, int TPW>
+    __device__ __forceinline__ static void load_codes(const GemvArgs& a, int64_t r0, int q, Raw (&raw)[N][TPW], int u) {
+        const uint8_t* base = static_cast<const uint8_t*>(a.w) + (int64_t)q * kChunk;
+#pragma unroll
+        for (int i = 0; i < N; ++i) raw[i][u].c = load_stream16(base + min(r0 + i, a.rows - 1) * a.K);
+    }
     // Rows r0 .. r0 + n - 1 (clamped to the last row) of chunk q, into
     // raw[i][u]. n <= 4 rows starting at a multiple of n share one 128-row
     // block, hence one scale load.
@@ -104,6 +112,10 @@ struct Fetch<kBf16> {
                                                      int u) {
 #pragma unroll
         for (int i = 0; i < N; ++i) raw[i][u] = load(a, min(r0 + i, a.rows - 1), q);
+    }
+    template <int N, int TPW>
+    __device__ __forceinline__ static void load_codes(const GemvArgs& a, int64_t r0, int q, Raw (&raw)[N][TPW], int u) {
+        load_rows(a, r0, N, q, raw, u);
     }
 };
 
@@ -243,10 +255,18 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
     typename F::Raw raw[R][TPW];
     uint4 xr[TPW][2];
     const int t_last = max(0, min(t0 + nseg, a.T) - 1);
+    // FP8: the wave's rows share one 128-row block, and its TPW segments need
+    // 8 * TPW consecutive block scales: lanes load one each (one instruction
+    // for the wave) and every chunk takes its scale from lane 8 u + lane / 8.
+    // An index past the grid is clamped; only chunks past the last column,
+    // whose results are discarded, would read it.
+    float svec = 0.0f;
+    if constexpr (KIND == kFp8)
+        svec = a.grid[(min(r0, a.rows - 1) >> 7) * a.GC + min(t0 * 8 + lane, a.GC - 1)];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int q = min(min(t0 + u, t_last) * kLanes + lane, last_q);
-        F::load_rows(a, r0, R, q, raw, u);
+        F::load_codes(a, r0, q, raw, u);
         const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)q * kChunk);
         xr[u][0] = xp[0];
         xr[u][1] = xp[1];
@@ -254,6 +274,14 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
     // Keep every load ahead of the arithmetic: with one shot of data per wave,
     // the bytes in flight per CU are what sets the streaming rate.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KIND == kFp8) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const float su = __shfl(svec, 8 * u + (lane >> 3));
+#pragma unroll
+            for (int i = 0; i < R; ++i) raw[i][u].s = su;
+        }
+    }
     float v[VP];
 #pragma unroll
     for (int k = V; k < VP; ++k) v[k] = 0.0f;
