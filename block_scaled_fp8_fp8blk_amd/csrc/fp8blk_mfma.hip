@@ -13,22 +13,24 @@
 // instruction sequence from the slab, so the two arms of this kernel give
 // identical bits ("Module dsv4_gpu", Fp8Dense). A batched call gives the same
 // bits as a single-row call ("Struct Dsv4Gpu", spec_greedy_batched_with): the
-// activation panel is always padded to 16 rows, and an output never depends
-// on another row of the panel.
+// matrix core always sees a 16-row panel (rows past M are filler whose outputs
+// are dropped), and an output never depends on another row of the panel.
 //
 // What differs from fp8blk_gemv: the matrix core sums the 32 products of an
 // instruction internally in an order the hardware does not document, so the
 // result is not the documented f32 order of fp8blk_gemv and is checked against
 // the exact sum by tolerance only.
 //
-// Order of operations for output (m, r), with T64 = ceil(cols / 64) blocks of
-// 64 columns: within block p, lane group kg (0..3) owns columns
-// [64 p + 16 kg, 64 p + 16 kg + 16); the first 8 of them form the k-slice of
-// one matrix instruction, the last 8 of the next, and both instructions
-// accumulate into the same f32 tile. Blocks are visited in increasing order
-// inside each of the sw parts the columns are split into (part s covers blocks
-// [s * bpp, (s + 1) * bpp)); the sw partial tiles are added in part order.
-// The split sw is a function of (rows, cols) only, never of M.
+// Order of operations for output (m, r): the columns are taken in windows of
+// 128 (one scale-block column). Within window w, lane group kg (0..3) of the
+// matrix instruction owns four 8-column groups; the window is four matrix
+// instructions, (c0w, h) = (0,0), (0,1), (1,0), (1,1), where instruction
+// (c0w, h) takes from lane group kg the columns [128 w + 8 G, 128 w + 8 G + 8),
+// G = 8 c0w + 4 (kg >> 1) + 2 (kg & 1) + h; all accumulate into the same f32
+// tile. Windows are visited in increasing order inside each of the sw parts
+// the windows are split into (part s covers windows [s * bpp, (s + 1) * bpp));
+// the sw partial tiles are added in part order. The split sw is a function of
+// (rows, cols) only, never of M.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,10 +45,10 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kMfWaves = 4;
-constexpr int kMfThreads = kMfWaves * kLanes;
+constexpr int kMfMinWaves = 4;   // waves of a workgroup: max(4, sw)
+constexpr int kMfMaxWaves = 8;
+constexpr int kMfMaxThreads = kMfMaxWaves * kLanes;
 constexpr int kTile = 16;    // rows per matrix tile, and the padded panel
-constexpr int kBlk = 64;     // columns per block (two matrix instructions)
 
 struct MfArgs {
     const void* w;        // uint8 codes or uint16 bf16 slab, [rows, K]
@@ -55,120 +57,208 @@ struct MfArgs {
     float* y;             // f32 [M, rows]
     int64_t rows;
     int K, M, GC;
-    int nblk;             // ceil(K / 64)
-    int sw_log2;          // waves splitting the columns of a tile: 1, 2, 4
-    int bpp;              // blocks per part, ceil(nblk / sw)
+    int nwin;             // ceil(K / 128) column windows
+    int sw_log2;          // waves splitting the windows of a row group: 1, 2, 4, 8
+    int streams_log2;     // row groups per workgroup: log2(max(4, sw) / sw)
+    int bpp;              // windows per part, ceil(nwin / sw)
 };
 
-// 16 consecutive weights of one lane as two 8-wide bf16 operands.
+// Window layout. The columns are taken in windows of 128 (one scale-block
+// column). For a 16-row tile, lane l = 8 c + r (r = l & 7, c = l >> 3 with
+// bits c2 c1 c0) loads, from tile rows r and 8 + r, the 16 codes of chunk
+// C = 4 c0 + 2 c2 + c1 of the window (columns [16 C, 16 C + 16)), so each load
+// instruction covers 8 rows x 128 contiguous bytes. One exchange of lane bit 3
+// with the row-half register (swap8) then leaves tile row i = l & 15 on lane
+// bits 0..3, as the matrix instruction wants; the register index becomes c0.
+// The activation rows are loaded the same way: lane l, register (q, g) holds
+// panel row 8 q + r, columns [8 G, 8 G + 8) with G = 8 g + 4 c2 + 2 c1 + c0,
+// and the same exchange puts panel row n = l & 15 on lane bits 0..3. After it,
+// weight register c0w, half h and activation register (c0 = h, g = c0w) hold
+// the same 8 columns, 8 G with G = 8 c0w + 4 c2 + 2 c1 + h, on every lane.
+
+// Exchange lane bit 3 with the register index of the pair (p, q):
+// p'[l] = l & 8 ? q[l ^ 8] : p[l], q'[l] = l & 8 ? q[l] : p[l ^ 8].
+// row_ror:8 inside a row of 16 lanes is lane ^ 8.
+__device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kRowRor8, 0xF, 0xF, true);
+}
+__device__ __forceinline__ void swap8(uint4& p, uint4& q, bool hi) {
+    uint32_t* pp = reinterpret_cast<uint32_t*>(&p);
+    uint32_t* qq = reinterpret_cast<uint32_t*>(&q);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t px = lane_xor8(pp[d]), qx = lane_xor8(qq[d]);
+        const uint32_t np = hi ? qx : pp[d];
+        const uint32_t nq = hi ? qq[d] : px;
+        pp[d] = np;
+        qq[d] = nq;
+    }
+}
+
+// The weights of one 16-row tile in one window, as loaded.
 template <int KIND>
 struct MfFetch;
 
 template <>
-struct MfFetch<0> {  // FP8: codes + f32 block scale, decoded in registers
+struct MfFetch<0> {  // FP8: 16 codes per row half, decoded in registers
     struct Raw {
-        uint4 c;
-        float s;
+        uint4 c[2];  // [row half q]
     };
-    __device__ __forceinline__ static Raw load(const MfArgs& a, int64_t r, int col) {
-        Raw raw;
-        raw.c = load_stream16(static_cast<const uint8_t*>(a.w) + r * a.K + col);
-        raw.s = a.grid[(r >> 7) * a.GC + (col >> 7)];
-        return raw;
+    // col: first column of the lane's chunk (already clamped into the row)
+    __device__ __forceinline__ static void load(Raw& raw, const MfArgs& a, int64_t r_lo, int64_t r_hi, int col) {
+        const uint8_t* w = static_cast<const uint8_t*>(a.w);
+        raw.c[0] = load_stream16(w + r_lo * a.K + col);
+        raw.c[1] = load_stream16(w + r_hi * a.K + col);
     }
-    __device__ __forceinline__ static void operands(const Raw& raw, v8bf& lo, v8bf& hi) {
-        const uint32_t d[4] = {raw.c.x, raw.c.y, raw.c.z, raw.c.w};
-        v2bf p[8];
+    // The four 8-wide operands, [c0w][h], after the exchange.
+    __device__ __forceinline__ static void operands(Raw raw, float sc, bool hi, v8bf op[2][2]) {
+        swap8(raw.c[0], raw.c[1], hi);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            p[2 * k] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[k], raw.s, false);     // bytes 0, 1
-            p[2 * k + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[k], raw.s, true);  // bytes 2, 3
-        }
+        for (int c = 0; c < 2; ++c) {
+            const uint32_t d[4] = {raw.c[c].x, raw.c[c].y, raw.c[c].z, raw.c[c].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            lo[2 * e] = p[e][0];
-            lo[2 * e + 1] = p[e][1];
-            hi[2 * e] = p[4 + e][0];
-            hi[2 * e + 1] = p[4 + e][1];
+            for (int k = 0; k < 4; ++k) {
+                const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[k], sc, false);  // bytes 0, 1
+                const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[k], sc, true);   // bytes 2, 3
+                v8bf& o = op[c][k >> 1];
+                o[4 * (k & 1) + 0] = p0[0];
+                o[4 * (k & 1) + 1] = p0[1];
+                o[4 * (k & 1) + 2] = p1[0];
+                o[4 * (k & 1) + 3] = p1[1];
+            }
         }
     }
-    __device__ __forceinline__ static Raw zero() { return Raw{make_uint4(0, 0, 0, 0), 1.0f}; }
 };
 
 template <>
-struct MfFetch<1> {  // bf16 slab
+struct MfFetch<1> {  // bf16 slab: the same 16 columns are 32 bytes, two loads per row half
     struct Raw {
-        uint4 lo, hi;
+        uint4 c[2][2];  // [h][row half q]
     };
-    __device__ __forceinline__ static Raw load(const MfArgs& a, int64_t r, int col) {
-        const uint16_t* p = static_cast<const uint16_t*>(a.w) + r * a.K + col;
-        Raw raw;
-        raw.lo = load_stream16(p);
-        raw.hi = load_stream16(p + 8);
-        return raw;
+    __device__ __forceinline__ static void load(Raw& raw, const MfArgs& a, int64_t r_lo, int64_t r_hi, int col) {
+        const uint16_t* w = static_cast<const uint16_t*>(a.w);
+        raw.c[0][0] = load_stream16(w + r_lo * a.K + col);
+        raw.c[1][0] = load_stream16(w + r_lo * a.K + col + 8);
+        raw.c[0][1] = load_stream16(w + r_hi * a.K + col);
+        raw.c[1][1] = load_stream16(w + r_hi * a.K + col + 8);
     }
-    __device__ __forceinline__ static void operands(const Raw& raw, v8bf& lo, v8bf& hi) {
-        lo = __builtin_bit_cast(v8bf, raw.lo);
-        hi = __builtin_bit_cast(v8bf, raw.hi);
+    __device__ __forceinline__ static void operands(Raw raw, float, bool hi, v8bf op[2][2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            swap8(raw.c[h][0], raw.c[h][1], hi);
+            op[0][h] = __builtin_bit_cast(v8bf, raw.c[h][0]);
+            op[1][h] = __builtin_bit_cast(v8bf, raw.c[h][1]);
+        }
     }
-    __device__ __forceinline__ static Raw zero() { return Raw{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)}; }
 };
 
-// A wave owns TILES tiles of 16 consecutive rows and one part of the column
-// blocks. Lane l = 16 kg + i: matrix row i of each tile, k-group kg, and, for
-// the activation operand, panel row m = i (rows m >= M are zero). The blocks
-// are taken U at a time: every load of the U blocks (codes, scales, x) is
-// issued before the matrix instructions that consume them. Loads are
-// unconditional (a block past the part re-reads the part's last block and is
-// skipped; a lane past the last column re-reads the last chunk with a zero
-// activation operand), so the waits stay per block.
-template <int KIND, int TILES, int U>
-__global__ __launch_bounds__(kMfThreads) void k_mfma(const MfArgs a) {
-    using F = MfFetch<KIND>;
-    __shared__ v4f part[kMfWaves][TILES][kLanes];
+// Everything one window needs, loaded ahead of the matrix work that uses it.
+template <int KIND, int TILES, bool BIGM>
+struct MfWindow {
+    typename MfFetch<KIND>::Raw w[TILES];
+    uint4 x[2][2];  // [row half q][g]
+    float sc;
+};
+
+// Per-lane constants of the layout.
+struct MfLane {
+    int64_t r0;             // first row of the wave
+    int r;                  // l & 7
+    int wchunk;             // 16 C
+    int xcol[2];            // 8 G for g = 0, 1 (before the exchange)
+    const uint16_t* xrow[2];  // panel rows 8 q + r, clamped to M - 1
+    bool hi;                // lane bit 3
+};
+
+template <int KIND, int TILES, bool BIGM>
+__device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, BIGM>& b, const MfArgs& a, const MfLane& L, int win) {
+    const int base = win * kBlock;
+    const int wcol = min(base + L.wchunk, a.K - 16);  // a chunk past the last column re-reads the last one
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        const int64_t lo = min(L.r0 + t * kTile + L.r, a.rows - 1);
+        const int64_t hi = min(L.r0 + t * kTile + 8 + L.r, a.rows - 1);
+        MfFetch<KIND>::load(b.w[t], a, lo, hi, wcol);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int xc = min(base + L.xcol[g], a.K - 8);
+        b.x[0][g] = *reinterpret_cast<const uint4*>(L.xrow[0] + xc);
+        if constexpr (BIGM) b.x[1][g] = *reinterpret_cast<const uint4*>(L.xrow[1] + xc);
+    }
+    b.sc = 1.0f;
+    if constexpr (KIND == 0) b.sc = a.grid[(min(L.r0, a.rows - 1) >> 7) * a.GC + win];
+}
+
+template <int KIND, int TILES, bool BIGM>
+__device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, BIGM> b, const MfArgs& a, const MfLane& L, int win,
+                                           v4f* acc) {
+    const int base = win * kBlock;
+    if (base + kBlock > a.K) {  // ragged last window: activation columns past the end feed zeros
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            if (base + L.xcol[g] + 8 > a.K) b.x[0][g] = b.x[1][g] = make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (!BIGM) {
+        // panel rows 8..15 are beyond M: any values serve, their outputs are not stored
+        b.x[1][0] = b.x[0][0];
+        b.x[1][1] = b.x[0][1];
+    }
+    swap8(b.x[0][0], b.x[1][0], L.hi);
+    swap8(b.x[0][1], b.x[1][1], L.hi);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        v8bf op[2][2];
+        MfFetch<KIND>::operands(b.w[t], b.sc, L.hi, op);
+#pragma unroll
+        for (int c0w = 0; c0w < 2; ++c0w)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[c0w][h], __builtin_bit_cast(v8bf, b.x[h][c0w]),
+                                                                 acc[t], 0, 0, 0);
+    }
+}
+
+// A wave owns TILES tiles of 16 consecutive rows (inside one 128-row scale
+// block) and one part of the windows; the loads of the next DEPTH - 1 windows
+// are in flight while a window is multiplied. Loads are unconditional: past
+// the end of the part they re-read its last window, which is then not used.
+template <int KIND, int TILES, bool BIGM, int DEPTH>
+__global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
+    using Win = MfWindow<KIND, TILES, BIGM>;
+    __shared__ v4f part[kMfMaxWaves][TILES][kLanes];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const int lane = threadIdx.x % kLanes;
-    const int i = lane % kTile, kg = lane / kTile;
     const int rs = wave >> a.sw_log2, sp = wave & ((1 << a.sw_log2) - 1);
-    const int64_t r0 = (((int64_t)blockIdx.x << (2 - a.sw_log2)) + rs) * (TILES * kTile);
-    const int pb = sp * a.bpp;
-    const int pe = min(a.nblk, pb + a.bpp);
-    const bool xrow = i < a.M;
-    const int last_col = a.K - 16;
-    const uint16_t* xrow_ptr = a.x + (int64_t)min(i, a.M - 1) * a.K;
+    MfLane L;
+    L.r0 = (((int64_t)blockIdx.x << a.streams_log2) + rs) * (TILES * kTile);
+    L.r = lane & 7;
+    const int c0 = (lane >> 3) & 1, c1 = (lane >> 4) & 1, c2 = (lane >> 5) & 1;
+    L.hi = c0 != 0;
+    L.wchunk = 16 * (4 * c0 + 2 * c2 + c1);
+    L.xcol[0] = 8 * (4 * c2 + 2 * c1 + c0);
+    L.xcol[1] = 8 * (8 + 4 * c2 + 2 * c1 + c0);
+    L.xrow[0] = a.x + (int64_t)min(L.r, a.M - 1) * a.K;
+    L.xrow[1] = a.x + (int64_t)min(8 + L.r, a.M - 1) * a.K;
+    const int wb = sp * a.bpp;
+    const int we = min(a.nwin, wb + a.bpp);
 
     v4f acc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int p0 = pb; p0 < pe; p0 += U) {
-        typename F::Raw raw[U][TILES];
-        uint4 xr[U][2];
+    if (wb < we) {
+        Win buf[DEPTH];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int col = min(min(p0 + u, pe - 1) * kBlk + kg * 16, last_col);
+        for (int d = 0; d + 1 < DEPTH; ++d) mf_issue(buf[d], a, L, min(wb + d, we - 1));
+        for (int w = wb; w < we; w += DEPTH) {
 #pragma unroll
-            for (int t = 0; t < TILES; ++t) raw[u][t] = F::load(a, min(r0 + t * kTile + i, a.rows - 1), col);
-            const uint4* xp = reinterpret_cast<const uint4*>(xrow_ptr + col);
-            xr[u][0] = xp[0];
-            xr[u][1] = xp[1];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (p0 + u < pe) {
-                const bool live = xrow && (p0 + u) * kBlk + kg * 16 <= last_col;
-                const uint4 z = make_uint4(0, 0, 0, 0);
-                const v8bf b0 = __builtin_bit_cast(v8bf, live ? xr[u][0] : z);
-                const v8bf b1 = __builtin_bit_cast(v8bf, live ? xr[u][1] : z);
-#pragma unroll
-                for (int t = 0; t < TILES; ++t) {
-                    v8bf a0, a1;
-                    F::operands(raw[u][t], a0, a1);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
-                }
+            for (int d = 0; d < DEPTH; ++d) {
+                mf_issue(buf[(d + DEPTH - 1) % DEPTH], a, L, min(w + d + DEPTH - 1, we - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                if (w + d < we) mf_compute(buf[d], a, L, w + d, acc);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -189,41 +279,54 @@ __global__ __launch_bounds__(kMfThreads) void k_mfma(const MfArgs a) {
             acc[t] = s;
         }
     }
-    // lane l holds D[4 (l / 16) + e][l % 16]: row 4 kg + e of the tile, panel row i
-    if (i < a.M) {
+    // lane l holds D[4 (l / 16) + e][l % 16]: row 4 (l / 16) + e of the tile, panel row l % 16
+    const int n = lane & 15, kg = lane >> 4;
+    if (n < a.M) {
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t r = r0 + t * kTile + 4 * kg + e;
-                if (r < a.rows) a.y[(int64_t)i * a.rows + r] = acc[t][e];
+                const int64_t r = L.r0 + t * kTile + 4 * kg + e;
+                if (r < a.rows) a.y[(int64_t)n * a.rows + r] = acc[t][e];
             }
     }
 }
 
-// Plan, a function of (rows, cols) only: the columns of a row group are split
-// over 2 or 4 waves while fewer than 2048 waves would run; a wave takes TILES
-// = 4, 2 or 1 row tiles -- the most that still leaves >= 768 waves, since the
-// row tiles of a wave share its activation loads -- and U = 8 / TILES blocks
-// per batch of loads. Measured on 12288 x 4096 and 4096 x 4096 at M = 1 and 16.
+// Plan. The split sw is a function of (rows, cols) only -- it fixes the
+// order of the sums -- : the largest of 1, 2, 4, 8 that leaves >= 8 windows
+// per part, or >= 4 windows while fewer than 1024 single-tile waves would run.
+// TILES only changes which wave computes an output, not its order, so it may
+// follow M: from M = 8 on, a wave takes 4 row tiles, which share its
+// activation loads, as long as >= 768 waves remain; else 1 tile, for the most
+// waves in flight. Measured on 12288 x 4096, 4096 x 4096, 4096 x 16384 and
+// 16384 x 4096 at M = 1, 8, 16.
 struct MfPlan {
-    int tiles, sw;
+    int tiles, sw, depth;
 };
-MfPlan mf_plan(int64_t rows, int64_t K) {
+MfPlan mf_plan(int64_t rows, int64_t K, int64_t M) {
     MfPlan p;
-    const int64_t nblk = ceil_div(K, kBlk);
-    p.tiles = 4;
-    while (p.tiles > 1 && ceil_div(rows, (int64_t)kTile * p.tiles) * 4 < 768) p.tiles /= 2;
-    const int64_t groups = ceil_div(rows, (int64_t)kTile * p.tiles);
+    const int64_t nwin = ceil_div(K, (int64_t)kBlock);
+    const int64_t groups1 = ceil_div(rows, (int64_t)kTile);
     p.sw = 1;
-    while (p.sw < 4 && p.sw * 2 <= nblk && groups * p.sw < 2048) p.sw *= 2;
+    while (p.sw < kMfMaxWaves && (nwin >= 16 * p.sw || (nwin >= 8 * p.sw && groups1 * p.sw < 1024))) p.sw *= 2;
+    p.tiles = 1;
+    if (M >= 8 && ceil_div(rows, (int64_t)kTile * 4) * p.sw >= 768) p.tiles = 4;
+    p.depth = 2;
     return p;
+}
+
+template <int KIND, bool BIGM>
+void mf_launch(const MfPlan& p, dim3 nb, dim3 nt, hipStream_t s, const MfArgs& a) {
+    if (p.tiles == 4)
+        k_mfma<KIND, 4, BIGM, 2><<<nb, nt, 0, s>>>(a);
+    else
+        k_mfma<KIND, 1, BIGM, 2><<<nb, nt, 0, s>>>(a);
 }
 
 template <int KIND>
 int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const uint16_t* x, int64_t M, float* y,
            hipStream_t s) {
-    const MfPlan p = mf_plan(rows, cols);
+    const MfPlan p = mf_plan(rows, cols, M);
     MfArgs a;
     a.w = w;
     a.grid = grid;
@@ -233,20 +336,20 @@ int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const u
     a.K = (int)cols;
     a.M = (int)M;
     a.GC = (int)ceil_div(cols, kBlock);
-    a.nblk = (int)ceil_div(cols, kBlk);
-    a.sw_log2 = p.sw == 4 ? 2 : p.sw == 2 ? 1 : 0;
-    a.bpp = (int)ceil_div(a.nblk, p.sw);
-    const int streams = kMfWaves / p.sw;
+    a.nwin = a.GC;
+    a.sw_log2 = p.sw == 8 ? 3 : p.sw == 4 ? 2 : p.sw == 2 ? 1 : 0;
+    const int waves = p.sw > kMfMinWaves ? p.sw : kMfMinWaves;
+    a.streams_log2 = p.sw >= kMfMinWaves ? 0 : a.sw_log2 == 1 ? 1 : 2;
+    a.bpp = (int)ceil_div(a.nwin, p.sw);
+    const int streams = waves / p.sw;
     const int64_t blocks = ceil_div(ceil_div(rows, (int64_t)kTile * p.tiles), streams);
     if (blocks > 0x7fffffff) return FP8BLK_ERR_ARG;
     (void)hipGetLastError();
-    const dim3 nb((unsigned)blocks), nt(kMfThreads);
-    if (p.tiles == 4)
-        k_mfma<KIND, 4, 2><<<nb, nt, 0, s>>>(a);
-    else if (p.tiles == 2)
-        k_mfma<KIND, 2, 4><<<nb, nt, 0, s>>>(a);
+    const dim3 nb((unsigned)blocks), nt(waves * kLanes);
+    if (M > 8)
+        mf_launch<KIND, true>(p, nb, nt, s, a);
     else
-        k_mfma<KIND, 1, 8><<<nb, nt, 0, s>>>(a);
+        mf_launch<KIND, false>(p, nb, nt, s, a);
     return launch_status();
 }
 
