@@ -22,15 +22,13 @@
 // the exact sum by tolerance only.
 //
 // Order of operations for output (m, r): the columns are taken in windows of
-// 128 (one scale-block column). Within window w, lane group kg (0..3) of the
-// matrix instruction owns four 8-column groups; the window is four matrix
-// instructions, (c0w, h) = (0,0), (0,1), (1,0), (1,1), where instruction
-// (c0w, h) takes from lane group kg the columns [128 w + 8 G, 128 w + 8 G + 8),
-// G = 8 c0w + 4 (kg >> 1) + 2 (kg & 1) + h; all accumulate into the same f32
-// tile. Windows are visited in increasing order inside each of the sw parts
-// the windows are split into (part s covers windows [s * bpp, (s + 1) * bpp));
-// the sw partial tiles are added in part order. The split sw is a function of
-// (rows, cols) only, never of M.
+// 128 (one scale-block column). Window w is four matrix instructions, (u, v) =
+// (0,0), (0,1), (1,0), (1,1); instruction (u, v) takes from lane group kg
+// (0..3) the 8 columns starting at 128 w + 32 kg + 16 u + 8 v, and all four
+// accumulate into the same f32 tile. Windows are visited in increasing order
+// inside each of the sw parts the windows are split into (part s covers
+// windows [s * bpp, (s + 1) * bpp)); the sw partial tiles are added in part
+// order. The split sw is a function of (rows, cols) only, never of M.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,30 +62,40 @@ struct MfArgs {
 };
 
 // Window layout. The columns are taken in windows of 128 (one scale-block
-// column). For a 16-row tile, lane l = 8 c + r (r = l & 7, c = l >> 3 with
-// bits c2 c1 c0) loads, from tile rows r and 8 + r, the 16 codes of chunk
-// C = 4 c0 + 2 c2 + c1 of the window (columns [16 C, 16 C + 16)), so each load
-// instruction covers 8 rows x 128 contiguous bytes. One exchange of lane bit 3
-// with the row-half register (swap8) then leaves tile row i = l & 15 on lane
-// bits 0..3, as the matrix instruction wants; the register index becomes c0.
-// The activation rows are loaded the same way: lane l, register (q, g) holds
-// panel row 8 q + r, columns [8 G, 8 G + 8) with G = 8 g + 4 c2 + 2 c1 + c0,
-// and the same exchange puts panel row n = l & 15 on lane bits 0..3. After it,
-// weight register c0w, half h and activation register (c0 = h, g = c0w) hold
-// the same 8 columns, 8 G with G = 8 c0w + 4 c2 + 2 c1 + h, on every lane.
+// column); the matrix instruction wants tile row i (weights) and panel row n
+// (activations) on lane bits 0..3 and a lane group kg = l >> 4 that is the
+// same set of columns in both operands.
+//
+// Weights: for a 16-row tile, lane l loads from tile rows (l & 7) and 8 +
+// (l & 7) the 16 codes of chunk l >> 3 of the window (columns [16 (l >> 3),
+// +16)), so one load instruction covers 8 rows x 128 contiguous bytes. One
+// exchange of lane bit 3 with the row-half register leaves tile row i = l & 15
+// on lane bits 0..3: register u then holds, on lane (i, kg), row i, columns
+// [32 kg + 16 u, +16).
+//
+// Activations: register (n1, n0) of lane l holds panel row 8 l3 + 4 l2 + 2 n1
+// + n0 (lj = bit j of l), columns [8 G, 8 G + 8) with G = 8 l5 + 4 l4 + 2 l1 +
+// l0: each group of four consecutive lanes reads 64 contiguous bytes of one
+// row, and an instruction covers 4 rows x 256 bytes. Exchanging lane bit 0
+// with n0 and lane bit 1 with n1 puts panel row n = l & 15 on lane bits 0..3;
+// register (u, v) then holds, on lane (n, kg), row n, columns [32 kg + 16 u +
+// 8 v, +8) -- the columns of half v of weight register u.
 
-// Exchange lane bit 3 with the register index of the pair (p, q):
-// p'[l] = l & 8 ? q[l ^ 8] : p[l], q'[l] = l & 8 ? q[l] : p[l ^ 8].
-// row_ror:8 inside a row of 16 lanes is lane ^ 8.
-__device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kRowRor8, 0xF, 0xF, true);
+// Exchange lane bit B (B = 0, 1 or 3) with the register index of the pair
+// (p, q): p'[l] = bit B of l ? q[l ^ 2^B] : p[l],
+//         q'[l] = bit B of l ? q[l] : p[l ^ 2^B].
+template <int B>
+__device__ __forceinline__ uint32_t lane_flip(uint32_t v) {
+    constexpr int ctrl = B == 0 ? kQuadXor1 : B == 1 ? kQuadXor2 : kRowRor8;  // lane ^ 2^B
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, true);
 }
-__device__ __forceinline__ void swap8(uint4& p, uint4& q, bool hi) {
+template <int B>
+__device__ __forceinline__ void exchange(uint4& p, uint4& q, bool hi) {
     uint32_t* pp = reinterpret_cast<uint32_t*>(&p);
     uint32_t* qq = reinterpret_cast<uint32_t*>(&q);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t px = lane_xor8(pp[d]), qx = lane_xor8(qq[d]);
+        const uint32_t px = lane_flip<B>(pp[d]), qx = lane_flip<B>(qq[d]);
         const uint32_t np = hi ? qx : pp[d];
         const uint32_t nq = hi ? qq[d] : px;
         pp[d] = np;
@@ -110,9 +118,9 @@ struct MfFetch<0> {  // FP8: 16 codes per row half, decoded in registers
         raw.c[0] = load_stream16(w + r_lo * a.K + col);
         raw.c[1] = load_stream16(w + r_hi * a.K + col);
     }
-    // The four 8-wide operands, [c0w][h], after the exchange.
+    // The four 8-wide operands, [u][v], after the exchange.
     __device__ __forceinline__ static void operands(Raw raw, float sc, bool hi, v8bf op[2][2]) {
-        swap8(raw.c[0], raw.c[1], hi);
+        exchange<3>(raw.c[0], raw.c[1], hi);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const uint32_t d[4] = {raw.c[c].x, raw.c[c].y, raw.c[c].z, raw.c[c].w};
@@ -145,7 +153,7 @@ struct MfFetch<1> {  // bf16 slab: the same 16 columns are 32 bytes, two loads p
     __device__ __forceinline__ static void operands(Raw raw, float, bool hi, v8bf op[2][2]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            swap8(raw.c[h][0], raw.c[h][1], hi);
+            exchange<3>(raw.c[h][0], raw.c[h][1], hi);
             op[0][h] = __builtin_bit_cast(v8bf, raw.c[h][0]);
             op[1][h] = __builtin_bit_cast(v8bf, raw.c[h][1]);
         }
@@ -153,25 +161,27 @@ struct MfFetch<1> {  // bf16 slab: the same 16 columns are 32 bytes, two loads p
 };
 
 // Everything one window needs, loaded ahead of the matrix work that uses it.
-template <int KIND, int TILES, bool BIGM>
+// XR activation registers are loaded: 1 for M = 1, 2 for M = 2, else 4 (the
+// others would hold only panel rows >= M).
+template <int KIND, int TILES, int XR>
 struct MfWindow {
     typename MfFetch<KIND>::Raw w[TILES];
-    uint4 x[2][2];  // [row half q][g]
+    uint4 x[4];  // [2 n1 + n0] as loaded, [2 u + v] after the exchanges
     float sc;
 };
 
 // Per-lane constants of the layout.
 struct MfLane {
-    int64_t r0;             // first row of the wave
-    int r;                  // l & 7
-    int wchunk;             // 16 C
-    int xcol[2];            // 8 G for g = 0, 1 (before the exchange)
-    const uint16_t* xrow[2];  // panel rows 8 q + r, clamped to M - 1
-    bool hi;                // lane bit 3
+    int64_t r0;               // first row of the wave
+    int r;                    // l & 7
+    int wchunk;               // 16 (l >> 3)
+    int xcol;                 // 8 G
+    const uint16_t* xrow[4];  // panel rows 8 l3 + 4 l2 + 2 n1 + n0, clamped to M - 1
+    bool b0, b1, b3;          // lane bits 0, 1, 3
 };
 
-template <int KIND, int TILES, bool BIGM>
-__device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, BIGM>& b, const MfArgs& a, const MfLane& L, int win) {
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, XR>& b, const MfArgs& a, const MfLane& L, int win) {
     const int base = win * kBlock;
     const int wcol = min(base + L.wchunk, a.K - 16);  // a chunk past the last column re-reads the last one
 #pragma unroll
@@ -180,41 +190,38 @@ __device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, BIGM>& b, const M
         const int64_t hi = min(L.r0 + t * kTile + 8 + L.r, a.rows - 1);
         MfFetch<KIND>::load(b.w[t], a, lo, hi, wcol);
     }
+    const int xc = min(base + L.xcol, a.K - 8);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int xc = min(base + L.xcol[g], a.K - 8);
-        b.x[0][g] = *reinterpret_cast<const uint4*>(L.xrow[0] + xc);
-        if constexpr (BIGM) b.x[1][g] = *reinterpret_cast<const uint4*>(L.xrow[1] + xc);
-    }
+    for (int k = 0; k < XR; ++k) b.x[k] = *reinterpret_cast<const uint4*>(L.xrow[k] + xc);
     b.sc = 1.0f;
     if constexpr (KIND == 0) b.sc = a.grid[(min(L.r0, a.rows - 1) >> 7) * a.GC + win];
 }
 
-template <int KIND, int TILES, bool BIGM>
-__device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, BIGM> b, const MfArgs& a, const MfLane& L, int win,
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, XR> b, const MfArgs& a, const MfLane& L, int win,
                                            v4f* acc) {
     const int base = win * kBlock;
-    if (base + kBlock > a.K) {  // ragged last window: activation columns past the end feed zeros
+    if (base + kBlock > a.K && base + L.xcol + 8 > a.K) {
+        // ragged last window: activation columns past the end feed zeros
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-            if (base + L.xcol[g] + 8 > a.K) b.x[0][g] = b.x[1][g] = make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < XR; ++k) b.x[k] = make_uint4(0, 0, 0, 0);
     }
-    if constexpr (!BIGM) {
-        // panel rows 8..15 are beyond M: any values serve, their outputs are not stored
-        b.x[1][0] = b.x[0][0];
-        b.x[1][1] = b.x[0][1];
-    }
-    swap8(b.x[0][0], b.x[1][0], L.hi);
-    swap8(b.x[0][1], b.x[1][1], L.hi);
+    // registers not loaded hold only panel rows >= M: any values serve, their outputs are not stored
+#pragma unroll
+    for (int k = XR; k < 4; ++k) b.x[k] = b.x[0];
+    exchange<0>(b.x[0], b.x[1], L.b0);
+    exchange<0>(b.x[2], b.x[3], L.b0);
+    exchange<1>(b.x[0], b.x[2], L.b1);
+    exchange<1>(b.x[1], b.x[3], L.b1);
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
         v8bf op[2][2];
-        MfFetch<KIND>::operands(b.w[t], b.sc, L.hi, op);
+        MfFetch<KIND>::operands(b.w[t], b.sc, L.b3, op);
 #pragma unroll
-        for (int c0w = 0; c0w < 2; ++c0w)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[c0w][h], __builtin_bit_cast(v8bf, b.x[h][c0w]),
+            for (int v = 0; v < 2; ++v)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[u][v], __builtin_bit_cast(v8bf, b.x[2 * u + v]),
                                                                  acc[t], 0, 0, 0);
     }
 }
@@ -223,9 +230,9 @@ __device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, BIGM> b, const 
 // block) and one part of the windows; the loads of the next DEPTH - 1 windows
 // are in flight while a window is multiplied. Loads are unconditional: past
 // the end of the part they re-read its last window, which is then not used.
-template <int KIND, int TILES, bool BIGM, int DEPTH>
+template <int KIND, int TILES, int XR, int DEPTH>
 __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
-    using Win = MfWindow<KIND, TILES, BIGM>;
+    using Win = MfWindow<KIND, TILES, XR>;
     __shared__ v4f part[kMfMaxWaves][TILES][kLanes];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
@@ -234,13 +241,14 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
     MfLane L;
     L.r0 = (((int64_t)blockIdx.x << a.streams_log2) + rs) * (TILES * kTile);
     L.r = lane & 7;
-    const int c0 = (lane >> 3) & 1, c1 = (lane >> 4) & 1, c2 = (lane >> 5) & 1;
-    L.hi = c0 != 0;
-    L.wchunk = 16 * (4 * c0 + 2 * c2 + c1);
-    L.xcol[0] = 8 * (4 * c2 + 2 * c1 + c0);
-    L.xcol[1] = 8 * (8 + 4 * c2 + 2 * c1 + c0);
-    L.xrow[0] = a.x + (int64_t)min(L.r, a.M - 1) * a.K;
-    L.xrow[1] = a.x + (int64_t)min(8 + L.r, a.M - 1) * a.K;
+    L.wchunk = 16 * (lane >> 3);
+    L.xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
+    const int xr_base = 8 * ((lane >> 3) & 1) + 4 * ((lane >> 2) & 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) L.xrow[k] = a.x + (int64_t)min(xr_base + k, a.M - 1) * a.K;
+    L.b0 = (lane & 1) != 0;
+    L.b1 = (lane & 2) != 0;
+    L.b3 = (lane & 8) != 0;
     const int wb = sp * a.bpp;
     const int we = min(a.nwin, wb + a.bpp);
 
@@ -315,12 +323,12 @@ MfPlan mf_plan(int64_t rows, int64_t K, int64_t M) {
     return p;
 }
 
-template <int KIND, bool BIGM>
+template <int KIND, int XR>
 void mf_launch(const MfPlan& p, dim3 nb, dim3 nt, hipStream_t s, const MfArgs& a) {
     if (p.tiles == 4)
-        k_mfma<KIND, 4, BIGM, 2><<<nb, nt, 0, s>>>(a);
+        k_mfma<KIND, 4, XR, 2><<<nb, nt, 0, s>>>(a);
     else
-        k_mfma<KIND, 1, BIGM, 2><<<nb, nt, 0, s>>>(a);
+        k_mfma<KIND, 1, XR, 2><<<nb, nt, 0, s>>>(a);
 }
 
 template <int KIND>
@@ -346,10 +354,12 @@ int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const u
     if (blocks > 0x7fffffff) return FP8BLK_ERR_ARG;
     (void)hipGetLastError();
     const dim3 nb((unsigned)blocks), nt(waves * kLanes);
-    if (M > 8)
-        mf_launch<KIND, true>(p, nb, nt, s, a);
+    if (M > 2)
+        mf_launch<KIND, 4>(p, nb, nt, s, a);
+    else if (M == 2)
+        mf_launch<KIND, 2>(p, nb, nt, s, a);
     else
-        mf_launch<KIND, false>(p, nb, nt, s, a);
+        mf_launch<KIND, 1>(p, nb, nt, s, a);
     return launch_status();
 }
 
