@@ -27,14 +27,32 @@ MIN_COLS, MAX_COLS, MAX_M = 16, 65536, 16
 # Every symbol include/fp8blk.h declares.
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
-           "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma")
+           "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
+           "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence")
 MAX_GROUP = 8
+MAX_SEQ = 65536
+ARM_FP8, ARM_BF16 = 0, 1
 
 
 class Linear(ctypes.Structure):
     """fp8blk_linear: one member of a grouped launch."""
     _fields_ = [("w", ctypes.c_void_p), ("scales_f32", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("y", ctypes.c_void_p)]
+
+
+
+class SeqLinear(ctypes.Structure):
+    """fp8blk_seq_linear: one member of a sequence launch."""
+    _fields_ = [("w", ctypes.c_void_p), ("scales_f32", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("x_bf16", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class SequenceHandle(ctypes.Structure):
+    """fp8blk_sequence: the host-side record of a planned sequence."""
+    _fields_ = [("plan", ctypes.c_void_p), ("units_dense", ctypes.c_int64), ("units_general", ctypes.c_int64),
+                ("n", ctypes.c_int32), ("arm", ctypes.c_int32), ("grid_dense", ctypes.c_int32),
+                ("grid_general", ctypes.c_int32)]
+
 
 _lib = None
 
@@ -74,6 +92,14 @@ def load():
     L.bf16_gemv_twin_grouped.restype = i32
     L.fp8blk_gemv_mfma.argtypes, L.fp8blk_gemv_mfma.restype = [vp, vp, i64, i64, vp, i64, vp, vp], i32
     L.bf16_gemv_twin_mfma.argtypes, L.bf16_gemv_twin_mfma.restype = [vp, i64, i64, vp, i64, vp, vp], i32
+    L.fp8blk_sequence_bytes.argtypes, L.fp8blk_sequence_bytes.restype = [i32], sz
+    L.fp8blk_sequence_init.argtypes = [ctypes.POINTER(SequenceHandle), i32, ctypes.POINTER(SeqLinear), i32, vp, sz,
+                                       vp]
+    L.fp8blk_sequence_init.restype = i32
+    L.fp8blk_gemv_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
+    L.fp8blk_gemv_sequence.restype = i32
+    L.bf16_gemv_twin_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
+    L.bf16_gemv_twin_sequence.restype = i32
     _lib = L
     return L
 
@@ -238,6 +264,77 @@ def bf16_gemv_twin_mfma(w_bf16, x_bf16, y, stream=None, check=True):
     return st
 
 
+def fp8blk_sequence_bytes(n: int) -> int:
+    return load().fp8blk_sequence_bytes(n)
+
+
+class Sequence:
+    """A planned sequence launch (fp8blk_sequence_init): the plan lives in
+    `ws` (a device byte tensor this object keeps alive) and `handle` is the
+    host record the launch entry points take. `keep` holds the tensors whose
+    addresses the plan records."""
+
+    def __init__(self, handle, ws, keep):
+        self.handle = handle
+        self.ws = ws
+        self.keep = keep
+
+
+def fp8blk_sequence_init(arm: int, linears, ws=None, stream=None, check=True):
+    """Plan a sequence launch over independent M = 1 linears.
+    linears: [(codes, scales_f32, x_bf16, y), ...] for ARM_FP8, or
+             [(w_bf16, x_bf16, y), ...] for ARM_BF16; x_bf16 is [1, cols] (or
+             [cols]), y is [1, rows] (or [rows]).
+    ws: a device uint8 tensor of at least fp8blk_sequence_bytes(n) bytes, or
+        None to allocate one here. Waits for the plan's copy to the device."""
+    import torch
+    n = len(linears)
+    arr = (SeqLinear * max(n, 1))()
+    keep = []
+    for k, lin in enumerate(linears):
+        if arm == ARM_FP8:
+            w, grid, x, y = lin
+            arr[k].w = _dev(w, (torch.uint8,), "codes")
+            arr[k].scales_f32 = _dev(grid, (torch.float32,), "scales_f32")
+        else:
+            w, x, y = lin
+            grid = None
+            arr[k].w = _dev(w, _bf16_dtypes(), "w_bf16")
+            arr[k].scales_f32 = None
+        rows, cols = w.shape
+        if x.numel() != cols or y.numel() != rows:
+            raise ValueError(f"linear {k}: x must hold cols={cols} and y rows={rows} elements (M = 1)")
+        arr[k].rows, arr[k].cols = rows, cols
+        arr[k].x_bf16 = _dev(x, _bf16_dtypes(), "x_bf16")
+        arr[k].y = _dev(y, (torch.float32,), "y")
+        keep.append((w, grid, x, y))
+    if ws is None:
+        nb = fp8blk_sequence_bytes(n) if 1 <= n <= MAX_SEQ else 64
+        ws = torch.empty(max(nb, 64), dtype=torch.uint8, device=(linears[0][0].device if n else "cuda"))
+    wsp, wsb = _ws(ws)
+    h = SequenceHandle()
+    st = load().fp8blk_sequence_init(ctypes.byref(h), arm, arr, n, wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_sequence_init")
+    return Sequence(h, ws, keep) if st == OK else st
+
+
+def fp8blk_gemv_sequence(seq, stream=None, check=True):
+    """One persistent launch of every linear of an ARM_FP8 sequence."""
+    st = load().fp8blk_gemv_sequence(ctypes.byref(seq.handle), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_sequence")
+    return st
+
+
+def bf16_gemv_twin_sequence(seq, stream=None, check=True):
+    """One persistent launch of every linear of an ARM_BF16 sequence."""
+    st = load().bf16_gemv_twin_sequence(ctypes.byref(seq.handle), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "bf16_gemv_twin_sequence")
+    return st
+
+
 def raw_call(name: str, *args):
     """Call an exported symbol with raw ctypes arguments (pointers as ints).
     Used by tests that exercise the C ABI's argument checks directly."""
@@ -278,6 +375,9 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         members, x = tensors_and_sizes
         arr, cols = _group(members, name == "fp8blk_gemv_grouped")
         args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], s)
+    elif name in ("fp8blk_gemv_sequence", "bf16_gemv_twin_sequence"):
+        (seq,) = tensors_and_sizes
+        args = (ctypes.byref(seq.handle), s)
     else:
         raise ValueError(f"prepared: unsupported entry point {name!r}")
     return lambda: fn(*args)

@@ -59,11 +59,24 @@ __device__ __forceinline__ void decode16_fp8_scaled(const uint4& c, float s, flo
 
 // 16-byte load that streams past the caches' retention (the weights are read
 // once per call): global_load_dwordx4 with the nontemporal hint.
+// The pointer is taken as a global-memory address (every buffer of this
+// library is device global memory), so the load is a global_load and not a
+// flat one, which would also hold the scalar-load counter.
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u global_v4u;
+typedef __attribute__((address_space(1))) const float global_f32;
+typedef __attribute__((address_space(1))) float global_f32_out;
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
-    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    const v4u v = __builtin_nontemporal_load((global_v4u*)p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Plain (cached) global loads and stores of the same kind.
+__device__ __forceinline__ uint4 load_global16(const void* p) {
+    const v4u v = *(global_v4u*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float load_global_f32(const float* p) { return *(global_f32*)p; }
+__device__ __forceinline__ void store_global_f32(float* p, float v) { *(global_f32_out*)p = v; }
 
 // Two bf16 patterns packed in a dword (lower column in the low half) widened
 // to f32: a bf16 pattern is the high half of the f32.

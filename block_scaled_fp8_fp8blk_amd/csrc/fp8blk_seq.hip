@@ -1,0 +1,436 @@
+// Sequence launch: many independent M = 1 linears streamed by one persistent
+// kernel, each output computed exactly as a call of its own.
+//
+// "Struct Dsv4Gpu" page, field dense_fp8: a decode step reads its dense
+// linears as stored, and their weights are most of the step's bytes. Small
+// linears launched one at a time leave HBM idle while each launch ramps up
+// and drains; here the whole list is one stream of 4-chunk steps that every
+// wave walks in list order, so the loads of the next linear are in flight
+// while the current one finishes, and there is one launch for the list.
+//
+// Work: linear j is cut into units of R = 8 >> tl consecutive rows, tl =
+// log2 of the segments of a row that one step covers (2 rows x 4 segments,
+// 4 x 2 or 8 x 1: eight 16-byte chunk loads per lane per step). A unit of a
+// linear with T <= 4 segments is one step; with T > 4 it is ceil(T / 4) steps
+// of 4 segments of its two rows, walked in segment order. Units are numbered
+// across the list in order, and wave w of the W waves in the grid takes units
+// w, w + W, w + 2W, ...: the waves move through the list together. Each wave
+// issues the next step's loads (codes, x chunks, block scales) before it
+// computes the current step.
+//
+// Arithmetic per output (the order the library header documents):
+//   lane partial = FMA chain over the chunk's 16 columns from +0.0;
+//   segment sum  = tree64 over the lanes (tree64xV below);
+//   y = P[0] + P[1] + ... + P[T-1] left to right (a running sum carried
+//       across the steps of a unit when T > 4).
+// This is the arithmetic of fp8blk_gemv / bf16_gemv_twin at M = 1, so each y
+// is bitwise the same as from a call of its own.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "fp8blk.h"
+#include "fp8blk_device.hpp"
+#include "fp8blk_host.hpp"
+
+namespace fp8blk {
+namespace {
+
+constexpr int kSeqWaves = 4;                  // waves per workgroup
+constexpr int kSeqThreads = kSeqWaves * kLanes;
+constexpr int kSeqSlots = 8;                  // chunk slots per lane per step
+constexpr int kSeqBlocksPerCU = 2;            // workgroups per compute unit
+// Each workgroup reserves this much LDS (it uses none), so that no compute
+// unit can hold more than kSeqBlocksPerCU of them (160 KB of LDS per CU): the
+// units are dealt to the waves in a fixed rotation, which assumes every wave
+// progresses at the same rate, and a CU holding one workgroup more than
+// another would finish last.
+constexpr int kSeqLdsBytes = 160 * 1024 / (kSeqBlocksPerCU + 1) + 1024;
+
+// Device descriptor of one linear: 64 bytes of 32- and 64-bit fields, one
+// scalar load.
+struct alignas(64) SeqLin {
+    const void* w;        // codes [rows, K] (FP8) or bf16 slab [rows, K] (twin)
+    const float* grid;    // f32 block scales [ceil(rows/128), ceil(K/128)] (FP8 arm)
+    const uint16_t* x;    // bf16 [K]
+    float* y;             // f32 [rows]
+    int64_t rows;
+    int64_t dense_units;  // units on the dense path: 0 .. dense_units - 1
+    int32_t K;            // cols
+    int32_t T;            // segments, ceil(K / 1024)
+    int32_t tl;           // log2 of segments of a row per step: 2 (T >= 3), 1 (T = 2), 0 (T = 1)
+    int32_t Q;            // steps per unit: ceil(T / 4)
+};
+static_assert(sizeof(SeqLin) == 64, "one scalar load per descriptor");
+
+// The plan in the caller's workspace: n descriptors, then two arrays of n + 1
+// prefix sums (int64): of the dense unit counts, and of the general ones.
+size_t plan_bytes(int n) { return (size_t)n * sizeof(SeqLin) + (size_t)(n + 1) * 2 * sizeof(int64_t); }
+
+enum Kind { kFp8 = 0, kBf16 = 1 };
+
+// A step: chunk slot s (0..7) holds row r0 + (s >> tl) and segment
+// 4k + (s & (tpw - 1)); x position p (0..3) holds the x chunk of segment
+// 4k + (p & (tpw - 1)). Slot s then always meets the x chunk of position s & 3,
+// whatever tl is. With R = 8 >> tl rows per unit:
+//   tl = 2: 2 rows x 4 segments, tl = 1: 4 rows x 2 segments, tl = 0: 8 rows x 1.
+// Scale position p holds, in lane l, the block scale of column block
+// 8 (4k + (p & (tpw - 1))) + l / 8 of the unit's row block (R <= 8 rows that
+// start at a multiple of R never cross a 128-row block): the scale of the
+// lane's chunk in the segments of position p.
+template <int KIND>
+struct SeqRaw;
+
+template <>
+struct SeqRaw<kFp8> {
+    uint4 c[kSeqSlots];
+    uint4 x[4][2];
+    float s[4];
+};
+
+template <>
+struct SeqRaw<kBf16> {
+    uint4 c[kSeqSlots][2];
+    uint4 x[4][2];
+};
+
+constexpr int el_bytes(int kind) { return kind == kFp8 ? 1 : 2; }
+__device__ __forceinline__ int grid_cols(const SeqLin& L) { return (L.K + kBlock - 1) / kBlock; }
+
+// The dense path: a unit whose R rows all exist, of a linear with K = 1024,
+// K = 2048 or K a multiple of 4096. The step's slots then lie at
+//   row block base + (s >> 2) * H + (s & 3) * 1024 weights,
+// H = K for tl = 2 (the unit's second row) and H = 4096 otherwise (slots 4..7
+// continue the same contiguous run of rows), and every chunk and scale index
+// is in range with no clamping: each load is a wave-uniform base plus the
+// lane's fixed offset.
+template <int KIND>
+__device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
+    constexpr int E = el_bytes(KIND);
+    const int tl = L.tl;
+    const int64_t r0 = v << (3 - tl);
+    const char* b0 = static_cast<const char*>(L.w) + (r0 * L.K + (int64_t)k * 4 * kSegCols) * E;
+    const int64_t H = tl == 2 ? L.K : 4 * kSegCols;
+    const char* b1 = b0 + H * E;
+    const uint32_t lo = (uint32_t)lane * (kChunk * E);
+#pragma unroll
+    for (int s = 0; s < kSeqSlots; ++s) {
+        const char* p = (s < 4 ? b0 : b1) + (s & 3) * kSegCols * E + lo;
+        if constexpr (KIND == kFp8) {
+            raw.c[s] = load_stream16(p);
+        } else {
+            raw.c[s][0] = load_stream16(p);
+            raw.c[s][1] = load_stream16(p + 16);
+        }
+    }
+    const int tm = (1 << tl) - 1;
+    const char* xb = reinterpret_cast<const char*>(L.x) + (int64_t)k * 4 * kSegCols * 2 + (uint32_t)lane * 32;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const char* xp = xb + (p & tm) * kSegCols * 2;
+        raw.x[p][0] = load_global16(xp);
+        raw.x[p][1] = load_global16(xp + 16);
+    }
+    if constexpr (KIND == kFp8) {
+        const float* g = L.grid + (r0 >> 7) * grid_cols(L) + 32 * k + (lane >> 3);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) raw.s[p] = load_global_f32(g + 8 * (p & tm));
+    }
+}
+
+// The general path: any K (a multiple of 16) and a last unit with fewer than
+// R rows. Rows past the end re-read the last row and chunks past the last
+// column re-read the last chunk; both are discarded by compute_step.
+template <int KIND>
+__device__ __forceinline__ void load_general(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
+    constexpr int E = el_bytes(KIND);
+    const int tl = L.tl, tm = (1 << tl) - 1;
+    const int64_t r0 = v << (3 - tl);
+    const char* wb = static_cast<const char*>(L.w) + (int64_t)k * 4 * kSegCols * E;
+    const char* xb = reinterpret_cast<const char*>(L.x) + (int64_t)k * 4 * kSegCols * 2;
+    const int qmax = L.K / kChunk - 1 - 4 * k * kLanes;  // last chunk, relative to the step
+#pragma unroll
+    for (int s = 0; s < kSeqSlots; ++s) {
+        const int64_t row = min(r0 + (s >> tl), L.rows - 1);
+        const uint32_t off = (uint32_t)min((s & tm) * kLanes + lane, qmax) * (kChunk * E);
+        const char* p = wb + row * L.K * E + off;
+        if constexpr (KIND == kFp8) {
+            raw.c[s] = load_stream16(p);
+        } else {
+            raw.c[s][0] = load_stream16(p);
+            raw.c[s][1] = load_stream16(p + 16);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const char* xp = xb + (uint32_t)min((p & tm) * kLanes + lane, qmax) * (kChunk * 2);
+        raw.x[p][0] = load_global16(xp);
+        raw.x[p][1] = load_global16(xp + 16);
+    }
+    if constexpr (KIND == kFp8) {
+        const int gc = grid_cols(L);
+        const float* g = L.grid + (min(r0, L.rows - 1) >> 7) * gc;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) raw.s[p] = load_global_f32(g + min(32 * k + 8 * (p & tm) + (lane >> 3), gc - 1));
+    }
+}
+
+template <int KIND, bool DENSE>
+__device__ __forceinline__ void load_step(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
+    if constexpr (DENSE)
+        load_dense<KIND>(L, v, k, lane, raw);
+    else
+        load_general<KIND>(L, v, k, lane, raw);
+}
+
+// Arithmetic of step k of unit v; yacc carries the running sums of the two
+// rows of a unit across its steps (tl = 2). Stores after the unit's last step.
+template <int KIND, bool DENSE>
+__device__ __forceinline__ void compute_step(const SeqLin& L, int64_t v, int k, int lane, const SeqRaw<KIND>& raw,
+                                             float (&yacc)[2]) {
+    const int tl = L.tl;
+    const int tpw = 1 << tl;
+    const int nseg = min(tpw, L.T - 4 * k);  // live segments of a row in this step
+    const int qmax = L.K / kChunk - 1 - 4 * k * kLanes;
+    float part[kSeqSlots];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float xf[kChunk];
+        widen8_bf16(raw.x[p][0], xf);
+        widen8_bf16(raw.x[p][1], xf + 8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s = p + 4 * h;
+            const int us = s & (tpw - 1);
+            float w[kChunk];
+            if constexpr (KIND == kFp8) {
+                decode16_fp8_scaled(raw.c[s], raw.s[p], w);
+            } else {
+                widen8_bf16(raw.c[s][0], w);
+                widen8_bf16(raw.c[s][1], w + 8);
+            }
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) acc = __builtin_fmaf(w[j], xf[j], acc);
+            if constexpr (DENSE) {
+                part[s] = acc;  // every chunk of a dense step exists
+            } else {
+                const bool live = us < nseg && us * kLanes + lane <= qmax;
+                part[s] = live ? acc : 0.0f;
+            }
+        }
+    }
+    float red[2];
+    tree64xV<kSeqSlots>(part, red);
+    // segment sum of slot s, uniform across the wave
+    float P[kSeqSlots];
+#pragma unroll
+    for (int s = 0; s < kSeqSlots; ++s) P[s] = lane_value(red[s >> 2], 16 * kRowOf4[s & 3]);
+
+    const int64_t r0 = v << (3 - tl);
+    float out;
+    if (tl == 2) {  // two rows, four segments of each
+        float y[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            y[h] = (k == 0) ? P[4 * h] : yacc[h] + P[4 * h];
+#pragma unroll
+            for (int us = 1; us < 4; ++us)
+                if (us < nseg) y[h] = y[h] + P[4 * h + us];
+            yacc[h] = y[h];
+        }
+        if (k + 1 < L.Q) return;
+        out = lane == 0 ? y[0] : y[1];
+    } else if (tl == 1) {  // four rows, two segments each
+        out = P[6] + P[7];
+#pragma unroll
+        for (int i = 2; i >= 0; --i)
+            if (lane == i) out = P[2 * i] + P[2 * i + 1];
+    } else {  // eight rows, one segment each
+        out = P[7];
+#pragma unroll
+        for (int i = 6; i >= 0; --i)
+            if (lane == i) out = P[i];
+    }
+    const int R = kSeqSlots >> tl;
+    if (lane < R && r0 + lane < L.rows) store_global_f32(L.y + r0 + lane, out);
+}
+
+// Where a wave is in the list: unit u (global numbering within the path),
+// v = the unit's index within its linear, step k of it, its linear j and that
+// linear's descriptor.
+struct SeqPos {
+    int64_t u, v;
+    int k, j;
+    bool more;  // false: past the wave's last step (the position is the last step again)
+    SeqLin L;
+};
+
+// The step after p: the next step of the unit, else the wave's next unit.
+// Past the wave's last step the last step is repeated (its loads are issued
+// and discarded), so every stage of the loop below issues the same loads.
+// `first` maps a path-local unit index to the unit index within the linear:
+// 0 on the dense path, the linear's dense_units on the general one.
+template <bool DENSE>
+__device__ __forceinline__ SeqPos next_pos(const SeqPos& p, const SeqLin* lin, const int64_t* pre, int64_t W,
+                                           int64_t total) {
+    SeqPos n = p;
+    if (!p.more) return n;
+    if (p.k + 1 < p.L.Q) {
+        n.k = p.k + 1;
+    } else if (p.u + W < total) {
+        n.u = p.u + W;
+        n.v = p.v + W;
+        n.k = 0;
+        if (n.u >= pre[n.j + 1]) {
+            do ++n.j;
+            while (n.u >= pre[n.j + 1]);
+            n.L = lin[n.j];
+            n.v = n.u - pre[n.j] + (DENSE ? 0 : n.L.dense_units);
+        }
+    } else {
+        n.more = false;
+    }
+    return n;
+}
+
+template <int KIND, bool DENSE>
+__device__ __forceinline__ void stage(const SeqPos& nxt, SeqRaw<KIND>& into, const SeqPos& cur,
+                                      const SeqRaw<KIND>& have, int lane, float (&yacc)[2]) {
+    load_step<KIND, DENSE>(nxt.L, nxt.v, nxt.k, lane, into);
+    __builtin_amdgcn_sched_barrier(0);  // keep the later step's loads ahead of this step's arithmetic
+    compute_step<KIND, DENSE>(cur.L, cur.v, cur.k, lane, have, yacc);
+}
+
+// One path (dense or general) of a sequence: `total` units, linear j owning
+// path units [pre[j], pre[j + 1]). Two register sets in turn: the loads of
+// the next step are issued before the arithmetic of the current one, and no
+// register copy makes the wave wait for loads it does not need yet.
+template <int KIND, bool DENSE>
+__global__ __launch_bounds__(kSeqThreads) void k_seq(const SeqLin* __restrict__ lin, const int64_t* __restrict__ pre,
+                                                     int64_t total) {
+    const int lane = threadIdx.x % kLanes;
+    const int64_t W = (int64_t)gridDim.x * kSeqWaves;
+    SeqPos p0;
+    p0.u = (int64_t)blockIdx.x * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    if (p0.u >= total) return;
+    p0.k = 0;
+    p0.j = 0;
+    p0.more = true;
+    while (p0.u >= pre[p0.j + 1]) ++p0.j;
+    p0.L = lin[p0.j];
+    p0.v = p0.u - pre[p0.j] + (DENSE ? 0 : p0.L.dense_units);
+    float yacc[2] = {0.0f, 0.0f};
+    SeqRaw<KIND> a, b;
+    load_step<KIND, DENSE>(p0.L, p0.v, p0.k, lane, a);
+    for (;;) {
+        const SeqPos p1 = next_pos<DENSE>(p0, lin, pre, W, total);
+        stage<KIND, DENSE>(p1, b, p0, a, lane, yacc);
+        if (!p1.more) break;
+        p0 = next_pos<DENSE>(p1, lin, pre, W, total);
+        stage<KIND, DENSE>(p0, a, p1, b, lane, yacc);
+        if (!p0.more) break;
+    }
+}
+
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return cus;
+}
+
+}  // namespace
+}  // namespace fp8blk
+
+using namespace fp8blk;
+
+extern "C" size_t fp8blk_sequence_bytes(int n) {
+    if (n < 1 || n > FP8BLK_MAX_SEQ) return 0;
+    return plan_bytes(n);
+}
+
+extern "C" int fp8blk_sequence_init(fp8blk_sequence* seq, int arm, const fp8blk_seq_linear* linears, int n,
+                                    void* ws, size_t ws_bytes, fp8blk_stream_t stream) {
+    if (!seq || !linears || n < 1 || n > FP8BLK_MAX_SEQ || (arm != FP8BLK_ARM_FP8 && arm != FP8BLK_ARM_BF16))
+        return FP8BLK_ERR_ARG;
+    if (!ws || !aligned(ws, 64) || ws_bytes < plan_bytes(n)) return FP8BLK_ERR_WORKSPACE;
+    std::vector<unsigned char> host(plan_bytes(n));
+    SeqLin* d = reinterpret_cast<SeqLin*>(host.data());
+    int64_t* pre_d = reinterpret_cast<int64_t*>(host.data() + (size_t)n * sizeof(SeqLin));
+    int64_t* pre_g = pre_d + (n + 1);
+    pre_d[0] = pre_g[0] = 0;
+    for (int j = 0; j < n; ++j) {
+        const fp8blk_seq_linear& l = linears[j];
+        if (!l.w || !l.x_bf16 || !l.y || !shape_ok(l.rows, l.cols) || !aligned(l.w, 16) || !aligned(l.x_bf16, 16) ||
+            !aligned(l.y, 4))
+            return FP8BLK_ERR_ARG;
+        if (arm == FP8BLK_ARM_FP8 && (!l.scales_f32 || !aligned(l.scales_f32, 4))) return FP8BLK_ERR_ARG;
+        SeqLin& s = d[j];
+        s.w = l.w;
+        s.grid = arm == FP8BLK_ARM_FP8 ? l.scales_f32 : nullptr;
+        s.x = l.x_bf16;
+        s.y = l.y;
+        s.rows = l.rows;
+        s.K = (int32_t)l.cols;
+        s.T = (int32_t)ceil_div(l.cols, kSegCols);
+        s.tl = s.T >= 3 ? 2 : s.T == 2 ? 1 : 0;
+        s.Q = (int32_t)ceil_div(s.T, 4);
+        // Dense: every chunk slot of a step is a whole chunk of the row it
+        // names (K = 1024, 2048 or a multiple of 4096) and the unit has all
+        // its R rows; a last unit with fewer rows, and every unit of another
+        // K, take the general path.
+        const int64_t R = kSeqSlots >> s.tl;
+        const bool dense = l.cols == kSegCols || l.cols == 2 * kSegCols || l.cols % (4 * kSegCols) == 0;
+        s.dense_units = dense ? l.rows / R : 0;
+        pre_d[j + 1] = pre_d[j] + s.dense_units;
+        pre_g[j + 1] = pre_g[j] + (ceil_div(l.rows, R) - s.dense_units);
+    }
+    const int cus = device_cus();
+    if (cus < 1) return FP8BLK_ERR_HIP;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess) return FP8BLK_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return FP8BLK_ERR_HIP;
+    const int64_t waves = (int64_t)cus * kSeqBlocksPerCU * kSeqWaves;
+    seq->plan = ws;
+    seq->units_dense = pre_d[n];
+    seq->units_general = pre_g[n];
+    seq->n = n;
+    seq->arm = arm;
+    seq->grid_dense = (int32_t)ceil_div(std::min<int64_t>(waves, pre_d[n]), kSeqWaves);
+    seq->grid_general = (int32_t)ceil_div(std::min<int64_t>(waves, pre_g[n]), kSeqWaves);
+    return FP8BLK_OK;
+}
+
+namespace {
+template <int KIND>
+int launch_seq(const fp8blk_sequence* seq, int arm, fp8blk_stream_t stream) {
+    if (!seq || !seq->plan || seq->arm != arm || seq->n < 1 || seq->units_dense < 0 || seq->units_general < 0 ||
+        seq->units_dense + seq->units_general < 1 || (seq->units_dense > 0 && seq->grid_dense < 1) ||
+        (seq->units_general > 0 && seq->grid_general < 1))
+        return FP8BLK_ERR_ARG;
+    const SeqLin* lin = static_cast<const SeqLin*>(seq->plan);
+    const int64_t* pre_d = reinterpret_cast<const int64_t*>(static_cast<const unsigned char*>(seq->plan) +
+                                                            (size_t)seq->n * sizeof(SeqLin));
+    const int64_t* pre_g = pre_d + (seq->n + 1);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (seq->units_dense > 0)
+        k_seq<KIND, true><<<dim3((unsigned)seq->grid_dense), dim3(kSeqThreads), kSeqLdsBytes, st>>>(lin, pre_d,
+                                                                                                 seq->units_dense);
+    if (seq->units_general > 0)
+        k_seq<KIND, false><<<dim3((unsigned)seq->grid_general), dim3(kSeqThreads), kSeqLdsBytes, st>>>(
+            lin, pre_g, seq->units_general);
+    return launch_status();
+}
+}  // namespace
+
+extern "C" int fp8blk_gemv_sequence(const fp8blk_sequence* seq, fp8blk_stream_t stream) {
+    return launch_seq<kFp8>(seq, FP8BLK_ARM_FP8, stream);
+}
+
+extern "C" int bf16_gemv_twin_sequence(const fp8blk_sequence* seq, fp8blk_stream_t stream) {
+    return launch_seq<kBf16>(seq, FP8BLK_ARM_BF16, stream);
+}

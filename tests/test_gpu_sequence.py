@@ -1,0 +1,127 @@
+"""GPU: a sequence launch (one persistent kernel over a list of independent
+M = 1 linears) gives every linear the same bits as a call of its own, for the
+FP8 arm and the bf16 twin, over every plan shape: 1, 2 and 4 rows per step
+(1, 2 and 3-4 segments), rows and columns past the last full step, and rows
+of more than 4 segments walked over several steps."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_fp8blk_amd as fb
+import oracle
+from block_scaled_fp8_fp8blk_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+# (rows, cols): one segment (4 rows per step, also fewer columns than a
+# segment), two (2 rows per step), three and four (one row), more than four
+# (several steps per row, a partial last step), ragged rows everywhere.
+SHAPES = [(256, 512), (13, 1024), (130, 16), (257, 2048), (3, 1040), (129, 2064), (64, 3072), (300, 4096),
+          (77, 4112), (40, 8192), (33, 16400), (5, 65536), (1, 16)]
+
+
+def _members(shapes, seed0):
+    from gpu_util import DevLinear, DEV
+    out = []
+    for k, (rows, cols) in enumerate(shapes):
+        L = inputs.host_linear(rows, cols, 1, seed0 + 7 * k)
+        D = DevLinear(L.codes, L.scales, L.x)
+        assert D.check(check=False) == (0, -1)
+        out.append((L, D, D.slab()))
+    return out
+
+
+def _run_sequence(members):
+    from gpu_util import DEV
+    y8 = [torch.full((1, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    yt = [torch.full((1, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    s8 = fb.fp8blk_sequence_init(fb.ARM_FP8, [(D.codes, D.grid, D.x, y) for (_, D, _), y in zip(members, y8)])
+    st = fb.fp8blk_sequence_init(fb.ARM_BF16, [(s, D.x, y) for (_, D, s), y in zip(members, yt)])
+    fb.fp8blk_gemv_sequence(s8)
+    fb.bf16_gemv_twin_sequence(st)
+    torch.cuda.synchronize()
+    return s8, st, y8, yt
+
+
+def test_sequence_equals_separate_calls(gpu):
+    from gpu_util import say, u32
+    members = _members(SHAPES, 500)
+    _, _, y8, yt = _run_sequence(members)
+    for (L, D, slab), a, b in zip(members, y8, yt):
+        say(f"  {D.rows}x{D.cols}")
+        ref = D.gemv()
+        assert np.array_equal(u32(a), u32(ref)), (D.rows, D.cols)
+        assert np.array_equal(u32(b), u32(ref)), (D.rows, D.cols)
+
+
+def test_sequence_matches_oracle(gpu):
+    """Against the oracle directly: the documented order bitwise (O7) and the
+    double GEMV within 1e-5 * sum|w x| (O6)."""
+    from gpu_util import assert_within_tolerance, u32
+    members = _members([(256, 512), (257, 2048), (129, 2064), (33, 16400), (300, 4096)], 900)
+    _, _, y8, yt = _run_sequence(members)
+    for (L, D, _), a, b in zip(members, y8, yt):
+        ya = a.cpu().numpy()
+        assert np.array_equal(u32(ya), u32(b))
+        y7 = oracle.gemv_f32_order(L.x, codes=L.codes, scales=L.scales, nthreads=8)
+        assert np.array_equal(u32(ya), y7.view(np.uint32)), (D.rows, D.cols)
+        y64, yabs = oracle.gemv_f64(L.codes, L.scales, L.x, nthreads=8)
+        assert_within_tolerance(ya, y64, yabs, what=f"{D.rows}x{D.cols}")
+
+
+def test_sequence_relaunch_and_single_member(gpu):
+    """The plan keeps pointers, not values: a second launch after x changes
+    gives the new result; a launch is deterministic; a list of one works, and
+    a list with fewer units than the grid's waves leaves the idle waves out."""
+    from gpu_util import DEV, u32
+    members = _members([(5, 4096), (2, 1024)], 77)
+    s8, _, y8, _ = _run_sequence(members)
+    first = [y.clone() for y in y8]
+    fb.fp8blk_gemv_sequence(s8)
+    torch.cuda.synchronize()
+    for a, b in zip(first, y8):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    for _, D, _ in members:
+        D.x.copy_(torch.flip(D.x, dims=[1]))
+    fb.fp8blk_gemv_sequence(s8)
+    torch.cuda.synchronize()
+    for (_, D, _), y in zip(members, y8):
+        assert np.array_equal(u32(y), u32(D.gemv()))
+    one = _members([(1, 16)], 3)
+    _, _, y1, t1 = _run_sequence(one)
+    assert np.array_equal(u32(y1[0]), u32(one[0][1].gemv()))
+    assert np.array_equal(u32(t1[0]), u32(y1[0]))
+
+
+def test_sequence_whole_step_sweep(gpu):
+    """The benchmark's launch: the 259 linears of the whole-step sweep in one
+    sequence. Every output equals the per-linear call bitwise (on the GPU);
+    128-row windows of a few linears are checked against the oracle."""
+    from gpu_util import DEV, DevLinear, assert_within_tolerance, say, u32
+    sw = inputs.sweep_plan()
+    xs = {c: inputs.device_x(c, 1, 7 + c, DEV) for c in {l.cols for l in sw.linears}}
+    lins, ys = [], []
+    for spec in sw.linears:
+        codes, scales = inputs.device_linear(spec.rows, spec.cols, spec.seed, DEV)
+        D = DevLinear(codes, scales, xs[spec.cols])
+        assert D.check(check=False) == (0, -1), spec.name
+        lins.append((spec, D))
+        ys.append(torch.full((1, spec.rows), float("nan"), device=DEV))
+    seq = fb.fp8blk_sequence_init(fb.ARM_FP8, [(D.codes, D.grid, D.x, y) for (_, D), y in zip(lins, ys)])
+    fb.fp8blk_gemv_sequence(seq)
+    torch.cuda.synchronize()
+    say("  sweep sequence launched")
+    for i, ((spec, D), y) in enumerate(zip(lins, ys)):
+        ref = D.gemv()
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), (i, spec.name)
+        if i in (0, 1, 2, 3, 4, 5, len(lins) - 1):
+            r0 = 128 * (spec.rows // 256)
+            ch = D.codes[r0:r0 + 128].cpu().numpy()
+            sh = D.scales[r0 // 128:r0 // 128 + 1].cpu().numpy()
+            xh = D.x.cpu().numpy().view(np.uint16)
+            yw = y[:, r0:r0 + 128].cpu().numpy()
+            y7 = oracle.gemv_f32_order(xh, codes=ch, scales=sh, nthreads=8)
+            assert np.array_equal(u32(yw), y7.view(np.uint32)), (spec.name, r0)
+            y64, yabs = oracle.gemv_f64(ch, sh, xh, nthreads=8)
+            assert_within_tolerance(yw, y64, yabs, what=f"{spec.name} rows {r0}..")
+    say(f"  {len(lins)} sweep linears equal their single calls")
