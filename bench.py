@@ -8,13 +8,19 @@ Default workload (one "step"): the whole-step dense sweep -- 43 layers x
 [q 4096x4096, kv 1024x4096, o 4096x4096, gate 2048x4096, up 2048x4096,
 down 4096x2048] plus the 129280x4096 head: 259 distinct FP8-blk linears
 (~3.2 GB of codes, far above the 256 MB Infinity Cache, so every step reads
-cold from HBM), M=1, launched back to back on one stream. Inputs are drawn
-on the device with seeded generators and are resident in HBM before timing.
+cold from HBM), M=1, back to back on one stream. Inputs are drawn on the
+device with seeded generators and are resident in HBM before timing.
+
+Launch modes (--mode): "sequence" (default) runs the 259 linears as one
+sequence launch -- one persistent kernel that streams them in list order;
+"graph" replays one launch per linear from a captured HIP graph; "stream"
+enqueues those launches one by one. Every mode computes the same outputs bit
+for bit; the JSON line reports the other modes beside the headline.
 
 Output: one JSON line. Besides the headline it carries
-  roofline      the GEMV kernel's algorithmic bytes / its average launch
-                duration (HIP events around every launch, instrumented pass),
-                against the 8 TB/s HBM peak;
+  roofline      the dominant kernel's algorithmic bytes per launch / its
+                average launch duration (HIP events on the launching stream
+                around the timed launches), against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle's double-precision GEMV over the same sweep;
   per_config    per-launch times of the single-linear workloads (decode
                 shape, projection pair, verify panel at M=1..16), cold from HBM
@@ -44,8 +50,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--mode", choices=("graph", "stream"), default="graph",
-                   help="replay the sweep's 259 launches from a captured HIP graph, or enqueue them one by one")
+    p.add_argument("--mode", choices=("sequence", "graph", "stream"), default="sequence",
+                   help="one sequence launch per step (default), or one launch per linear replayed from a captured "
+                        "HIP graph, or enqueued one by one")
     p.add_argument("--arm", choices=("fp8", "bf16"), default="fp8", help="time the FP8 arm or the bf16 twin")
     p.add_argument("--layers", type=int, default=43, help="layers in the sweep (default: the full 43)")
     p.add_argument("--no-extra", action="store_true", help="skip the per-config cold-cache table")
@@ -93,6 +100,14 @@ class Sweep:
         gr, gc = -(-spec.rows // 128), -(-spec.cols // 128)
         wb = spec.rows * spec.cols * (1 if self.arm == "fp8" else 2)
         return wb + (4 * gr * gc if self.arm == "fp8" else 0) + 2 * spec.cols + 4 * spec.rows
+
+    def sequence(self, fb):
+        """The sweep's linears as one planned sequence launch (same bits)."""
+        if self.arm == "fp8":
+            seq = fb.fp8blk_sequence_init(fb.ARM_FP8, [(l["w"], l["grid"], l["x"], l["y"]) for l in self.lins])
+            return seq, fb.prepared("fp8blk_gemv_sequence", seq)
+        seq = fb.fp8blk_sequence_init(fb.ARM_BF16, [(l["w"], l["x"], l["y"]) for l in self.lins])
+        return seq, fb.prepared("bf16_gemv_twin_sequence", seq)
 
     def calls(self, fb, stream=None):
         out = []
@@ -171,6 +186,26 @@ def time_sweep(torch, fb, sw, steps, warmup, mode, grouped=False):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
+def time_sequence(torch, fb, sw, steps, warmup):
+    """Time `steps` sequence launches back to back on the current stream,
+    HIP events around all of them (on that stream)."""
+    seq, call = sw.sequence(fb)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run_calls([call])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        run_calls([call])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del seq
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
 def per_shape_launches(torch, fb, sw, reps=10):
     """Average launch duration per distinct shape: a HIP graph of all the
     sweep's linears of that shape (distinct buffers, so still cold), replayed
@@ -203,7 +238,8 @@ def per_shape_launches(torch, fb, sw, reps=10):
     return out
 
 
-KERNEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+KERNEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_seq.hip",
+                  "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
 
 
 def source_hash():
@@ -215,11 +251,16 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def counted_traffic(arm):
-    """HBM bytes per launch of the sweep's GEMV launches from the committed
-    rocprofv3 counter summary, or None when absent or taken on other kernel
-    sources (the summary records the source hash it was taken on)."""
-    path = os.path.join(ROOT, "profiles", f"gemv_{arm}_m1_sweep_counters.json")
+def counters_path(arm, mode):
+    kind = "sequence" if mode == "sequence" else "per_linear"
+    return os.path.join(ROOT, "profiles", f"gemv_{arm}_m1_sweep_{kind}_counters.json")
+
+
+def counted_traffic(arm, mode):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when absent or taken on other kernel sources (the
+    summary records the source hash it was taken on)."""
+    path = counters_path(arm, mode)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -333,11 +374,12 @@ def _short(name):
     return m.group(1) if m else name[:60]
 
 
-def summarize_trace(stats_csv, trace_csv, command):
+def summarize_trace(stats_csv, trace_csv, command, mode="sequence"):
     """Markdown: per-kernel stats of the FP8-blk kernels and per-shape medians."""
     import csv
     import collections
-    lines = ["# rocprofv3 kernel trace: FP8-blk GEMV, whole-step sweep (M=1)", "",
+    title = "one sequence launch per step" if mode == "sequence" else "one launch per linear"
+    lines = [f"# rocprofv3 kernel trace: FP8-blk GEMV, whole-step sweep (M=1), {title}", "",
              f"Command: `{command}`" if command else "", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(stats_csv)):
@@ -345,9 +387,10 @@ def summarize_trace(stats_csv, trace_csv, command):
             lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.1f} | {r['MinNs']} | {r['MaxNs']} |")
     by = collections.defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
-        if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"]:
+        if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"] or "k_seq" in r["Kernel_Name"]:
             by[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines += ["", "Per launch shape (grid = threads; q/o 262144, kv 65536, gate/up/down 131072, head 8273920):", "",
+    lines += ["", "Per launch shape (grid = threads; one launch per linear: q/o 262144, kv 65536, gate/up/down "
+              "131072, head 8273920; the sequence kernel: its persistent grid):", "",
               "| kernel | grid | launches | median us | min us |", "|---|---|---|---|---|"]
     for (k, g), v in sorted(by.items(), key=lambda kv: kv[0][1]):
         v.sort()
@@ -355,10 +398,11 @@ def summarize_trace(stats_csv, trace_csv, command):
     print("\n".join(lines))
 
 
-def summarize_counters(fetch_csv, write_csv, command, arm="fp8"):
+def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"):
     """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the 1 GiB
-    copy of --copy-calibration, then average the GEMV dispatches of one sweep
-    step (one launch per linear of the step, taken per launch shape)."""
+    copies of --copy-calibration, then give the HBM bytes per launch of the
+    dominant kernel: the sequence kernel (one dispatch per step), or the mean
+    over one step's per-linear launches (taken per launch shape)."""
     import csv
     import collections
 
@@ -368,7 +412,10 @@ def summarize_counters(fetch_csv, write_csv, command, arm="fp8"):
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
         gem = collections.defaultdict(list)
         for r in rows:
-            if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            if mode == "sequence" and "k_seq" in name:
+                gem["seq"].append(float(r["Counter_Value"]))
+            elif mode != "sequence" and ("k_gemv_m1" in name or "k_panel" in name):
                 gem[int(r["Grid_Size"])].append(float(r["Counter_Value"]))
         return copies, {g: sorted(v)[len(v) // 2] for g, v in gem.items()}
 
@@ -377,25 +424,29 @@ def summarize_counters(fetch_csv, write_csv, command, arm="fp8"):
     gib_kib = 1 << 20
     f_factor = gib_kib / (sorted(fc)[len(fc) // 2])
     w_factor = gib_kib / (sorted(wc)[len(wc) // 2])
-    # launches per sweep step by grid size (threads): q,o 262144 (86), kv 65536 (43),
-    # gate,up,down 131072 (129), head 8273920 (1)
-    per_step = {262144: 86, 65536: 43, 131072: 129, 8273920: 1}
+    if mode == "sequence":
+        per_step = {"seq": 1}
+    else:
+        # launches per sweep step by grid size (threads): q,o 262144 (86), kv 65536 (43),
+        # gate,up,down 131072 (129), head 8273920 (1)
+        per_step = {262144: 86, 65536: 43, 131072: 129, 8273920: 1}
     tot = sum(per_step[g] * (fg[g] * f_factor + wg[g] * w_factor) * 1024 for g in per_step)
     launches = sum(per_step.values())
-    rec = {"source_hash": source_hash(), "arm": arm, "fetch_factor": round(f_factor, 4),
+    rec = {"source_hash": source_hash(), "arm": arm, "mode": mode, "fetch_factor": round(f_factor, 4),
            "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": int(tot / launches),
            "per_grid_kib": {str(g): {"fetch": fg[g], "write": wg[g]} for g in per_step},
            "command": command}
-    with open(os.path.join(ROOT, "profiles", f"gemv_{arm}_m1_sweep_counters.json"), "w") as f:
+    with open(counters_path(arm, mode), "w") as f:
         json.dump(rec, f, indent=1)
-    lines = ["# rocprofv3 counters: FP8-blk GEMV, whole-step sweep (M=1)", "",
+    title = "one sequence launch per step" if mode == "sequence" else "one launch per linear"
+    lines = [f"# rocprofv3 counters: FP8-blk GEMV ({arm} arm), whole-step sweep (M=1), {title}", "",
              f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
              f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
              f"WRITE_SIZE x {w_factor:.3f} give bytes.", "",
-             "| grid (threads) | launches per step | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch |",
+             "| dispatch | launches per step | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch |",
              "|---|---|---|---|---|"]
     for g in per_step:
-        lines.append(f"| {g} | {per_step[g]} | {fg[g]:.1f} | {wg[g]:.1f} | "
+        lines.append(f"| {'k_seq' if g == 'seq' else f'grid {g}'} | {per_step[g]} | {fg[g]:.1f} | {wg[g]:.1f} | "
                      f"{(fg[g] * f_factor + wg[g] * w_factor) * 1024 / 1e6:.3f} |")
     lines += ["", f"Average HBM bytes per launch over one step: {tot / launches / 1e6:.3f} MB "
               f"(source hash {rec['source_hash']})."]
@@ -405,10 +456,10 @@ def summarize_counters(fetch_csv, write_csv, command, arm="fp8"):
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, args.command)
+        summarize_trace(*args.summarize_trace, args.command, args.mode)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.command, args.arm)
+        summarize_counters(*args.summarize_counters, args.command, args.arm, args.mode)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
@@ -428,35 +479,62 @@ def main():
     sw = Sweep(torch, fb, inputs, dev, args.layers, args.arm)
     log(f"  {len(sw.lins)} linears, {sw.weight_bytes / 1e9:.3f} GB weights, set up in {time.perf_counter() - t0:.1f} s")
 
-    secs, wall = time_sweep(torch, fb, sw, args.steps, args.warmup, args.mode)
-    ms_per_step = secs / args.steps * 1e3
-    value = sw.weight_bytes * args.steps / secs / 1e9
-    log(f"sweep: {ms_per_step:.4f} ms/step, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak), "
-        f"host wall {wall:.3f} s")
-    gsecs, _ = time_sweep(torch, fb, sw, args.steps, args.warmup, args.mode, grouped=True)
+    # The three launch modes over the same linears (same output bits).
+    modes = {}
+    ssecs, swall = time_sequence(torch, fb, sw, args.steps, args.warmup)
+    modes["sequence"] = (ssecs, swall, 1)
+    log(f"sweep, one sequence launch: {ssecs / args.steps * 1e3:.4f} ms/step, "
+        f"{sw.weight_bytes * args.steps / ssecs / 1e9:.1f} GB/s "
+        f"({100 * sw.weight_bytes * args.steps / ssecs / 1e9 / HBM_PEAK_GBS:.1f}% of peak)")
+    for m in ("graph", "stream"):
+        if m != args.mode and m != "graph":
+            continue
+        psecs, pwall = time_sweep(torch, fb, sw, args.steps, args.warmup, m)
+        modes[m] = (psecs, pwall, len(sw.lins))
+        log(f"sweep, one launch per linear ({m}): {psecs / args.steps * 1e3:.4f} ms/step, "
+            f"{sw.weight_bytes * args.steps / psecs / 1e9:.1f} GB/s "
+            f"({100 * sw.weight_bytes * args.steps / psecs / 1e9 / HBM_PEAK_GBS:.1f}% of peak)")
+    gsecs, _ = time_sweep(torch, fb, sw, args.steps, args.warmup, "graph", grouped=True)
     gvalue = sw.weight_bytes * args.steps / gsecs / 1e9
     n_grouped = len(sw.calls_grouped(fb))
-    log(f"sweep, shared-input projections grouped ({n_grouped} launches): {gsecs / args.steps * 1e3:.4f} ms/step, "
-        f"{gvalue:.1f} GB/s ({100 * gvalue / HBM_PEAK_GBS:.1f}% of peak)")
+    log(f"sweep, shared-input projections grouped ({n_grouped} launches, graph): {gsecs / args.steps * 1e3:.4f} "
+        f"ms/step, {gvalue:.1f} GB/s ({100 * gvalue / HBM_PEAK_GBS:.1f}% of peak)")
 
-    # Roofline of the dominant kernel (the M=1 GEMV, every launch of the step):
-    # the graph replays the launches back to back (the kernel trace shows no
-    # idle gaps), so the timed region / launches is its average duration.
-    n = len(sw.lins)
-    avg_launch = secs / (args.steps * n)
-    achieved = sw.read_bytes / n / avg_launch / 1e9
-    traffic = counted_traffic(args.arm)
-    shapes = per_shape_launches(torch, fb, sw)
+    secs, wall, launches = modes[args.mode]
+    ms_per_step = secs / args.steps * 1e3
+    value = sw.weight_bytes * args.steps / secs / 1e9
+    log(f"headline ({args.mode}): {ms_per_step:.4f} ms/step, {value:.1f} GB/s "
+        f"({100 * value / HBM_PEAK_GBS:.1f}% of peak), host wall {wall:.3f} s")
+
+    # Roofline of the dominant kernel. Sequence mode: one launch per step, the
+    # persistent kernel, so the timed region / steps is its average duration.
+    # Per-linear modes: the launches run back to back (the kernel trace shows
+    # no idle gaps), so the timed region / launches is their average duration.
+    avg_launch = secs / (args.steps * launches)
+    algo_per_launch = sw.read_bytes / launches
+    achieved = algo_per_launch / avg_launch / 1e9
+    traffic = counted_traffic(args.arm, args.mode)
+    kname = ("k_seq (fp8, 16-slot steps)" if args.arm == "fp8" else "k_seq (bf16 twin, 8-slot steps)") \
+        if args.mode == "sequence" else ("k_gemv_m1 (fp8)" if args.arm == "fp8" else "k_gemv_m1 (bf16 twin)")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "k_gemv_m1 (fp8)" if args.arm == "fp8" else "k_gemv_m1 (bf16 twin)",
-            "launches_per_step": n, "avg_launch_us": round(avg_launch * 1e6, 3),
-            "avg_algo_bytes_per_launch": int(sw.read_bytes / n), "source_hash": source_hash(),
-            "per_shape": shapes}
-    log(f"roofline: avg launch {roof['avg_launch_us']} us, {achieved:.1f} GB/s algorithmic "
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
+            "launches_per_step": launches, "avg_launch_us": round(avg_launch * 1e6, 3),
+            "avg_algo_bytes_per_launch": int(algo_per_launch), "source_hash": source_hash()}
+    log(f"roofline: {kname}, avg launch {roof['avg_launch_us']} us, {achieved:.1f} GB/s algorithmic "
         f"({100 * roof['frac']:.1f}%)")
+    shapes = per_shape_launches(torch, fb, sw)
     for r in shapes:
-        log(f"  {r['shape']}: {r['us']} us per launch, {r['weight_GBps']} GB/s")
+        log(f"  one launch per linear, {r['shape']}: {r['us']} us per launch, {r['weight_GBps']} GB/s")
+    launch_modes = {}
+    for m, (t, _, nl) in modes.items():
+        v = sw.weight_bytes * args.steps / t / 1e9
+        launch_modes[m] = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                           "launches_per_step": nl, "ms_per_step": round(t / args.steps * 1e3, 4)}
+    launch_modes["graph_grouped"] = {"value": round(gvalue, 1), "unit": "GB/s", "launches_per_step": n_grouped,
+                                     "ms_per_step": round(gsecs / args.steps * 1e3, 4),
+                                     "pct_hbm_peak": round(100 * gvalue / HBM_PEAK_GBS, 2),
+                                     "note": "q+kv and gate+up each in one launch, graph-replayed"}
+    launch_modes["per_linear_shapes"] = shapes
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -499,13 +577,11 @@ def main():
         "config": {"workload": f"whole-step dense sweep: {args.layers} x [q 4096x4096, kv 1024x4096, o 4096x4096, "
                                f"gate 2048x4096, up 2048x4096, down 4096x2048] + head 129280x4096; "
                                f"{len(sw.lins)} distinct FP8-blk linears, M=1, back to back on one stream",
-                   "arm": args.arm, "launch": args.mode, "M": 1, "linears": len(sw.lins),
+                   "launch": args.mode,
+                   "arm": args.arm, "M": 1, "linears": len(sw.lins),
                    "weight_bytes_per_step": sw.weight_bytes, "cold_cache": "working set 12x the 256 MB MALL"},
         "roofline": roof,
-        "sweep_grouped": {"value": round(gvalue, 1), "unit": "GB/s", "launches_per_step": n_grouped,
-                          "ms_per_step": round(gsecs / args.steps * 1e3, 4),
-                          "pct_hbm_peak": round(100 * gvalue / HBM_PEAK_GBS, 2),
-                          "note": "same 259 linears and bits; q+kv and gate+up each in one launch"},
+        "launch_modes": launch_modes,
         "cpu_baseline": cpu,
         "m16_verify_12288x4096": ({"vector_arm": {"weight_GBps": m16[0]["weight_GBps"],
                                                   "pct_hbm_peak": m16[0]["pct_hbm_peak"], "us": m16[0]["us"]},

@@ -8,15 +8,16 @@
 // wave walks in list order, so the loads of the next linear are in flight
 // while the current one finishes, and there is one launch for the list.
 //
-// Work: linear j is cut into units of R = 8 >> tl consecutive rows, tl =
-// log2 of the segments of a row that one step covers (2 rows x 4 segments,
-// 4 x 2 or 8 x 1: eight 16-byte chunk loads per lane per step). A unit of a
-// linear with T <= 4 segments is one step; with T > 4 it is ceil(T / 4) steps
-// of 4 segments of its two rows, walked in segment order. Units are numbered
-// across the list in order, and wave w of the W waves in the grid takes units
-// w, w + W, w + 2W, ...: the waves move through the list together. Each wave
-// issues the next step's loads (codes, x chunks, block scales) before it
-// computes the current step.
+// Work: a step is S chunk slots per lane (S = 16 on the FP8 arm, 8 on the
+// twin; 16 KB of weights per wave either way). Linear j is cut into units of
+// R = S >> tl consecutive rows, tl = log2 of the segments of a row that one
+// step covers: S/4 rows x 4 segments (T >= 3), S/2 rows x 2 segments (T = 2),
+// S rows x 1 segment (T = 1). A unit of a linear with T <= 4 segments is one
+// step; with T > 4 it is ceil(T / 4) steps of 4 segments of its rows, walked
+// in segment order. Units are numbered across the list in order, and wave w
+// of the W waves in the grid takes units w, w + W, w + 2W, ...: the waves
+// move through the list together. Each wave issues the next step's loads
+// (codes, x chunks, block scales) before it computes the current step.
 //
 // Arithmetic per output (the order the library header documents):
 //   lane partial = FMA chain over the chunk's 16 columns from +0.0;
@@ -40,7 +41,6 @@ namespace {
 
 constexpr int kSeqWaves = 4;                  // waves per workgroup
 constexpr int kSeqThreads = kSeqWaves * kLanes;
-constexpr int kSeqSlots = 8;                  // chunk slots per lane per step
 constexpr int kSeqBlocksPerCU = 2;            // workgroups per compute unit
 // Each workgroup reserves this much LDS (it uses none), so that no compute
 // unit can hold more than kSeqBlocksPerCU of them (160 KB of LDS per CU): the
@@ -71,28 +71,32 @@ size_t plan_bytes(int n) { return (size_t)n * sizeof(SeqLin) + (size_t)(n + 1) *
 
 enum Kind { kFp8 = 0, kBf16 = 1 };
 
-// A step: chunk slot s (0..7) holds row r0 + (s >> tl) and segment
+// Chunk slots per lane per step: 16 for the FP8 arm (16 KB of codes per wave
+// step), 8 for the bf16 twin (the same bytes per step at 2 bytes a weight).
+// Measured on the whole-step sweep: 8 FP8 slots run ~4% slower; 16 bf16 slots
+// need more registers than two waves per SIMD allow.
+constexpr int seq_slots(int kind) { return kind == kFp8 ? 16 : 8; }
+
+// A step: chunk slot s (0 .. S-1) holds row r0 + (s >> tl) and segment
 // 4k + (s & (tpw - 1)); x position p (0..3) holds the x chunk of segment
 // 4k + (p & (tpw - 1)). Slot s then always meets the x chunk of position s & 3,
-// whatever tl is. With R = 8 >> tl rows per unit:
-//   tl = 2: 2 rows x 4 segments, tl = 1: 4 rows x 2 segments, tl = 0: 8 rows x 1.
-// Scale position p holds, in lane l, the block scale of column block
-// 8 (4k + (p & (tpw - 1))) + l / 8 of the unit's row block (R <= 8 rows that
-// start at a multiple of R never cross a 128-row block): the scale of the
+// whatever tl is. Scale position p holds, in lane l, the block scale of column
+// block 8 (4k + (p & (tpw - 1))) + l / 8 of the unit's row block (R <= 16 rows
+// that start at a multiple of R never cross a 128-row block): the scale of the
 // lane's chunk in the segments of position p.
 template <int KIND>
 struct SeqRaw;
 
 template <>
 struct SeqRaw<kFp8> {
-    uint4 c[kSeqSlots];
+    uint4 c[seq_slots(kFp8)];
     uint4 x[4][2];
     float s[4];
 };
 
 template <>
 struct SeqRaw<kBf16> {
-    uint4 c[kSeqSlots][2];
+    uint4 c[seq_slots(kBf16)][2];
     uint4 x[4][2];
 };
 
@@ -101,23 +105,23 @@ __device__ __forceinline__ int grid_cols(const SeqLin& L) { return (L.K + kBlock
 
 // The dense path: a unit whose R rows all exist, of a linear with K = 1024,
 // K = 2048 or K a multiple of 4096. The step's slots then lie at
-//   row block base + (s >> 2) * H + (s & 3) * 1024 weights,
-// H = K for tl = 2 (the unit's second row) and H = 4096 otherwise (slots 4..7
-// continue the same contiguous run of rows), and every chunk and scale index
-// is in range with no clamping: each load is a wave-uniform base plus the
-// lane's fixed offset.
+//   unit base + (s >> 2) * H + (s & 3) * 1024 weights,
+// H = K for tl = 2 (the unit's next row) and H = 4096 otherwise (the slots
+// continue one contiguous run of rows), and every chunk and scale index is
+// in range with no clamping: each load is a wave-uniform base plus the lane's
+// fixed offset.
 template <int KIND>
 __device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
     constexpr int E = el_bytes(KIND);
+    constexpr int S = seq_slots(KIND);
     const int tl = L.tl;
-    const int64_t r0 = v << (3 - tl);
+    const int64_t r0 = v * (S >> tl);
     const char* b0 = static_cast<const char*>(L.w) + (r0 * L.K + (int64_t)k * 4 * kSegCols) * E;
-    const int64_t H = tl == 2 ? L.K : 4 * kSegCols;
-    const char* b1 = b0 + H * E;
+    const int64_t H = (tl == 2 ? L.K : 4 * kSegCols) * E;
     const uint32_t lo = (uint32_t)lane * (kChunk * E);
 #pragma unroll
-    for (int s = 0; s < kSeqSlots; ++s) {
-        const char* p = (s < 4 ? b0 : b1) + (s & 3) * kSegCols * E + lo;
+    for (int s = 0; s < S; ++s) {
+        const char* p = b0 + (s >> 2) * H + (s & 3) * kSegCols * E + lo;
         if constexpr (KIND == kFp8) {
             raw.c[s] = load_stream16(p);
         } else {
@@ -146,13 +150,14 @@ __device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, in
 template <int KIND>
 __device__ __forceinline__ void load_general(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
     constexpr int E = el_bytes(KIND);
+    constexpr int S = seq_slots(KIND);
     const int tl = L.tl, tm = (1 << tl) - 1;
-    const int64_t r0 = v << (3 - tl);
+    const int64_t r0 = v * (S >> tl);
     const char* wb = static_cast<const char*>(L.w) + (int64_t)k * 4 * kSegCols * E;
     const char* xb = reinterpret_cast<const char*>(L.x) + (int64_t)k * 4 * kSegCols * 2;
     const int qmax = L.K / kChunk - 1 - 4 * k * kLanes;  // last chunk, relative to the step
 #pragma unroll
-    for (int s = 0; s < kSeqSlots; ++s) {
+    for (int s = 0; s < S; ++s) {
         const int64_t row = min(r0 + (s >> tl), L.rows - 1);
         const uint32_t off = (uint32_t)min((s & tm) * kLanes + lane, qmax) * (kChunk * E);
         const char* p = wb + row * L.K * E + off;
@@ -185,23 +190,24 @@ __device__ __forceinline__ void load_step(const SeqLin& L, int64_t v, int k, int
         load_general<KIND>(L, v, k, lane, raw);
 }
 
-// Arithmetic of step k of unit v; yacc carries the running sums of the two
-// rows of a unit across its steps (tl = 2). Stores after the unit's last step.
+// Arithmetic of step k of unit v; yacc carries the running sums of the rows
+// of a unit across its steps (tl = 2). Stores after the unit's last step.
 template <int KIND, bool DENSE>
 __device__ __forceinline__ void compute_step(const SeqLin& L, int64_t v, int k, int lane, const SeqRaw<KIND>& raw,
-                                             float (&yacc)[2]) {
+                                             float (&yacc)[seq_slots(KIND) / 4]) {
+    constexpr int S = seq_slots(KIND), NR = S / 4;
     const int tl = L.tl;
     const int tpw = 1 << tl;
     const int nseg = min(tpw, L.T - 4 * k);  // live segments of a row in this step
     const int qmax = L.K / kChunk - 1 - 4 * k * kLanes;
-    float part[kSeqSlots];
+    float part[S];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         float xf[kChunk];
         widen8_bf16(raw.x[p][0], xf);
         widen8_bf16(raw.x[p][1], xf + 8);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NR; ++h) {
             const int s = p + 4 * h;
             const int us = s & (tpw - 1);
             float w[kChunk];
@@ -222,39 +228,42 @@ __device__ __forceinline__ void compute_step(const SeqLin& L, int64_t v, int k, 
             }
         }
     }
-    float red[2];
-    tree64xV<kSeqSlots>(part, red);
+    float red[NR];
+    tree64xV<S>(part, red);
     // segment sum of slot s, uniform across the wave
-    float P[kSeqSlots];
+    float P[S];
 #pragma unroll
-    for (int s = 0; s < kSeqSlots; ++s) P[s] = lane_value(red[s >> 2], 16 * kRowOf4[s & 3]);
+    for (int s = 0; s < S; ++s) P[s] = lane_value(red[s >> 2], 16 * kRowOf4[s & 3]);
 
-    const int64_t r0 = v << (3 - tl);
+    const int64_t r0 = v * (S >> tl);
     float out;
-    if (tl == 2) {  // two rows, four segments of each
-        float y[2];
+    if (tl == 2) {  // NR rows, four segments of each
+        float y[NR];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NR; ++h) {
             y[h] = (k == 0) ? P[4 * h] : yacc[h] + P[4 * h];
 #pragma unroll
             for (int us = 1; us < 4; ++us)
-                if (us < nseg) y[h] = y[h] + P[4 * h + us];
+                if (DENSE || us < nseg) y[h] = y[h] + P[4 * h + us];
             yacc[h] = y[h];
         }
         if (k + 1 < L.Q) return;
-        out = lane == 0 ? y[0] : y[1];
-    } else if (tl == 1) {  // four rows, two segments each
-        out = P[6] + P[7];
+        out = y[NR - 1];
 #pragma unroll
-        for (int i = 2; i >= 0; --i)
+        for (int h = NR - 2; h >= 0; --h)
+            if (lane == h) out = y[h];
+    } else if (tl == 1) {  // 2 * NR rows, two segments each
+        out = P[S - 2] + P[S - 1];
+#pragma unroll
+        for (int i = S / 2 - 2; i >= 0; --i)
             if (lane == i) out = P[2 * i] + P[2 * i + 1];
-    } else {  // eight rows, one segment each
-        out = P[7];
+    } else {  // 4 * NR rows, one segment each
+        out = P[S - 1];
 #pragma unroll
-        for (int i = 6; i >= 0; --i)
+        for (int i = S - 2; i >= 0; --i)
             if (lane == i) out = P[i];
     }
-    const int R = kSeqSlots >> tl;
+    const int R = S >> tl;
     if (lane < R && r0 + lane < L.rows) store_global_f32(L.y + r0 + lane, out);
 }
 
@@ -298,7 +307,7 @@ __device__ __forceinline__ SeqPos next_pos(const SeqPos& p, const SeqLin* lin, c
 
 template <int KIND, bool DENSE>
 __device__ __forceinline__ void stage(const SeqPos& nxt, SeqRaw<KIND>& into, const SeqPos& cur,
-                                      const SeqRaw<KIND>& have, int lane, float (&yacc)[2]) {
+                                      const SeqRaw<KIND>& have, int lane, float (&yacc)[seq_slots(KIND) / 4]) {
     load_step<KIND, DENSE>(nxt.L, nxt.v, nxt.k, lane, into);
     __builtin_amdgcn_sched_barrier(0);  // keep the later step's loads ahead of this step's arithmetic
     compute_step<KIND, DENSE>(cur.L, cur.v, cur.k, lane, have, yacc);
@@ -322,7 +331,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const SeqLin* __restrict__ 
     while (p0.u >= pre[p0.j + 1]) ++p0.j;
     p0.L = lin[p0.j];
     p0.v = p0.u - pre[p0.j] + (DENSE ? 0 : p0.L.dense_units);
-    float yacc[2] = {0.0f, 0.0f};
+    float yacc[seq_slots(KIND) / 4] = {};
     SeqRaw<KIND> a, b;
     load_step<KIND, DENSE>(p0.L, p0.v, p0.k, lane, a);
     for (;;) {
@@ -382,7 +391,7 @@ extern "C" int fp8blk_sequence_init(fp8blk_sequence* seq, int arm, const fp8blk_
         // names (K = 1024, 2048 or a multiple of 4096) and the unit has all
         // its R rows; a last unit with fewer rows, and every unit of another
         // K, take the general path.
-        const int64_t R = kSeqSlots >> s.tl;
+        const int64_t R = (arm == FP8BLK_ARM_FP8 ? seq_slots(kFp8) : seq_slots(kBf16)) >> s.tl;
         const bool dense = l.cols == kSegCols || l.cols == 2 * kSegCols || l.cols % (4 * kSegCols) == 0;
         s.dense_units = dense ? l.rows / R : 0;
         pre_d[j + 1] = pre_d[j] + s.dense_units;
