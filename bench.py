@@ -48,8 +48,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--mode", choices=("sequence", "graph", "stream"), default="sequence",
                    help="one sequence launch per step (default), or one launch per linear replayed from a captured "
                         "HIP graph, or enqueued one by one")

@@ -103,6 +103,13 @@ struct SeqRaw<kBf16> {
 constexpr int el_bytes(int kind) { return kind == kFp8 ? 1 : 2; }
 __device__ __forceinline__ int grid_cols(const SeqLin& L) { return (L.K + kBlock - 1) / kBlock; }
 
+// The loads of a step come in four phases, one per x position p: the code
+// chunks of slots p, p + 4, p + 8, ... (segment p of every row of the step),
+// the x chunk of position p and, on the FP8 arm, the block scales of position
+// p. The arithmetic takes the same phases in the same order, so a wave can
+// issue the next step's phase p just before it computes this step's phase p
+// and keep one step of loads in flight at an even rate.
+//
 // The dense path: a unit whose R rows all exist, of a linear with K = 1024,
 // K = 2048 or K a multiple of 4096. The step's slots then lie at
 //   unit base + (s >> 2) * H + (s & 3) * 1024 weights,
@@ -111,123 +118,122 @@ __device__ __forceinline__ int grid_cols(const SeqLin& L) { return (L.K + kBlock
 // in range with no clamping: each load is a wave-uniform base plus the lane's
 // fixed offset.
 template <int KIND>
-__device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
+__device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, int lane, int p, SeqRaw<KIND>& raw) {
     constexpr int E = el_bytes(KIND);
     constexpr int S = seq_slots(KIND);
-    const int tl = L.tl;
+    const int tl = L.tl, tm = (1 << tl) - 1;
     const int64_t r0 = v * (S >> tl);
     const char* b0 = static_cast<const char*>(L.w) + (r0 * L.K + (int64_t)k * 4 * kSegCols) * E;
     const int64_t H = (tl == 2 ? L.K : 4 * kSegCols) * E;
     const uint32_t lo = (uint32_t)lane * (kChunk * E);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const char* p = b0 + (s >> 2) * H + (s & 3) * kSegCols * E + lo;
+    for (int s = p; s < S; s += 4) {
+        const char* a = b0 + (s >> 2) * H + p * kSegCols * E + lo;
         if constexpr (KIND == kFp8) {
-            raw.c[s] = load_stream16(p);
+            raw.c[s] = load_stream16(a);
         } else {
-            raw.c[s][0] = load_stream16(p);
-            raw.c[s][1] = load_stream16(p + 16);
+            raw.c[s][0] = load_stream16(a);
+            raw.c[s][1] = load_stream16(a + 16);
         }
     }
-    const int tm = (1 << tl) - 1;
-    const char* xb = reinterpret_cast<const char*>(L.x) + (int64_t)k * 4 * kSegCols * 2 + (uint32_t)lane * 32;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const char* xp = xb + (p & tm) * kSegCols * 2;
-        raw.x[p][0] = load_global16(xp);
-        raw.x[p][1] = load_global16(xp + 16);
-    }
-    if constexpr (KIND == kFp8) {
-        const float* g = L.grid + (r0 >> 7) * grid_cols(L) + 32 * k + (lane >> 3);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) raw.s[p] = load_global_f32(g + 8 * (p & tm));
-    }
+    const char* xp = reinterpret_cast<const char*>(L.x) + ((int64_t)k * 4 + (p & tm)) * kSegCols * 2 + (uint32_t)lane * 32;
+    raw.x[p][0] = load_global16(xp);
+    raw.x[p][1] = load_global16(xp + 16);
+    if constexpr (KIND == kFp8)
+        raw.s[p] = load_global_f32(L.grid + (r0 >> 7) * grid_cols(L) + 32 * k + 8 * (p & tm) + (lane >> 3));
 }
 
 // The general path: any K (a multiple of 16) and a last unit with fewer than
 // R rows. Rows past the end re-read the last row and chunks past the last
-// column re-read the last chunk; both are discarded by compute_step.
+// column re-read the last chunk; both are discarded by compute_phase.
 template <int KIND>
-__device__ __forceinline__ void load_general(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
+__device__ __forceinline__ void load_general(const SeqLin& L, int64_t v, int k, int lane, int p, SeqRaw<KIND>& raw) {
     constexpr int E = el_bytes(KIND);
     constexpr int S = seq_slots(KIND);
     const int tl = L.tl, tm = (1 << tl) - 1;
     const int64_t r0 = v * (S >> tl);
     const char* wb = static_cast<const char*>(L.w) + (int64_t)k * 4 * kSegCols * E;
-    const char* xb = reinterpret_cast<const char*>(L.x) + (int64_t)k * 4 * kSegCols * 2;
     const int qmax = L.K / kChunk - 1 - 4 * k * kLanes;  // last chunk, relative to the step
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+    for (int s = p; s < S; s += 4) {
         const int64_t row = min(r0 + (s >> tl), L.rows - 1);
         const uint32_t off = (uint32_t)min((s & tm) * kLanes + lane, qmax) * (kChunk * E);
-        const char* p = wb + row * L.K * E + off;
+        const char* a = wb + row * L.K * E + off;
         if constexpr (KIND == kFp8) {
-            raw.c[s] = load_stream16(p);
+            raw.c[s] = load_stream16(a);
         } else {
-            raw.c[s][0] = load_stream16(p);
-            raw.c[s][1] = load_stream16(p + 16);
+            raw.c[s][0] = load_stream16(a);
+            raw.c[s][1] = load_stream16(a + 16);
         }
     }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const char* xp = xb + (uint32_t)min((p & tm) * kLanes + lane, qmax) * (kChunk * 2);
-        raw.x[p][0] = load_global16(xp);
-        raw.x[p][1] = load_global16(xp + 16);
-    }
+    const char* xp = reinterpret_cast<const char*>(L.x) + (int64_t)k * 4 * kSegCols * 2 +
+                     (uint32_t)min((p & tm) * kLanes + lane, qmax) * (kChunk * 2);
+    raw.x[p][0] = load_global16(xp);
+    raw.x[p][1] = load_global16(xp + 16);
     if constexpr (KIND == kFp8) {
         const int gc = grid_cols(L);
-        const float* g = L.grid + (min(r0, L.rows - 1) >> 7) * gc;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) raw.s[p] = load_global_f32(g + min(32 * k + 8 * (p & tm) + (lane >> 3), gc - 1));
+        raw.s[p] = load_global_f32(L.grid + (min(r0, L.rows - 1) >> 7) * gc +
+                                   min(32 * k + 8 * (p & tm) + (lane >> 3), gc - 1));
     }
+}
+
+template <int KIND, bool DENSE>
+__device__ __forceinline__ void load_phase(const SeqLin& L, int64_t v, int k, int lane, int p, SeqRaw<KIND>& raw) {
+    if constexpr (DENSE)
+        load_dense<KIND>(L, v, k, lane, p, raw);
+    else
+        load_general<KIND>(L, v, k, lane, p, raw);
 }
 
 template <int KIND, bool DENSE>
 __device__ __forceinline__ void load_step(const SeqLin& L, int64_t v, int k, int lane, SeqRaw<KIND>& raw) {
-    if constexpr (DENSE)
-        load_dense<KIND>(L, v, k, lane, raw);
-    else
-        load_general<KIND>(L, v, k, lane, raw);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) load_phase<KIND, DENSE>(L, v, k, lane, p, raw);
 }
 
-// Arithmetic of step k of unit v; yacc carries the running sums of the rows
-// of a unit across its steps (tl = 2). Stores after the unit's last step.
+// Phase p of the arithmetic of step k: the lane partials of slots p, p + 4,
+// ... (one FMA chain over each chunk's 16 columns, from +0.0), into part.
 template <int KIND, bool DENSE>
-__device__ __forceinline__ void compute_step(const SeqLin& L, int64_t v, int k, int lane, const SeqRaw<KIND>& raw,
-                                             float (&yacc)[seq_slots(KIND) / 4]) {
-    constexpr int S = seq_slots(KIND), NR = S / 4;
+__device__ __forceinline__ void compute_phase(const SeqLin& L, int k, int lane, int p, const SeqRaw<KIND>& raw,
+                                              float (&part)[seq_slots(KIND)]) {
+    constexpr int S = seq_slots(KIND);
     const int tl = L.tl;
     const int tpw = 1 << tl;
-    const int nseg = min(tpw, L.T - 4 * k);  // live segments of a row in this step
-    const int qmax = L.K / kChunk - 1 - 4 * k * kLanes;
-    float part[S];
+    float xf[kChunk];
+    widen8_bf16(raw.x[p][0], xf);
+    widen8_bf16(raw.x[p][1], xf + 8);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        float xf[kChunk];
-        widen8_bf16(raw.x[p][0], xf);
-        widen8_bf16(raw.x[p][1], xf + 8);
+    for (int s = p; s < S; s += 4) {
+        float w[kChunk];
+        if constexpr (KIND == kFp8) {
+            decode16_fp8_scaled(raw.c[s], raw.s[p], w);
+        } else {
+            widen8_bf16(raw.c[s][0], w);
+            widen8_bf16(raw.c[s][1], w + 8);
+        }
+        float acc = 0.0f;
 #pragma unroll
-        for (int h = 0; h < NR; ++h) {
-            const int s = p + 4 * h;
+        for (int j = 0; j < kChunk; ++j) acc = __builtin_fmaf(w[j], xf[j], acc);
+        if constexpr (DENSE) {
+            part[s] = acc;  // every chunk of a dense step exists
+        } else {
             const int us = s & (tpw - 1);
-            float w[kChunk];
-            if constexpr (KIND == kFp8) {
-                decode16_fp8_scaled(raw.c[s], raw.s[p], w);
-            } else {
-                widen8_bf16(raw.c[s][0], w);
-                widen8_bf16(raw.c[s][1], w + 8);
-            }
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kChunk; ++j) acc = __builtin_fmaf(w[j], xf[j], acc);
-            if constexpr (DENSE) {
-                part[s] = acc;  // every chunk of a dense step exists
-            } else {
-                const bool live = us < nseg && us * kLanes + lane <= qmax;
-                part[s] = live ? acc : 0.0f;
-            }
+            const int nseg = min(tpw, L.T - 4 * k);  // live segments of a row in this step
+            const bool live = us < nseg && us * kLanes + lane <= L.K / kChunk - 1 - 4 * k * kLanes;
+            part[s] = live ? acc : 0.0f;
         }
     }
+}
+
+// The end of step k of unit v: segment sums (tree64xV) and the row sums in
+// segment order; yacc carries the running sums of the rows of a unit across
+// its steps (tl = 2). Stores after the unit's last step.
+template <int KIND, bool DENSE>
+__device__ __forceinline__ void finish_step(const SeqLin& L, int64_t v, int k, int lane,
+                                            float (&part)[seq_slots(KIND)], float (&yacc)[seq_slots(KIND) / 4]) {
+    constexpr int S = seq_slots(KIND), NR = S / 4;
+    const int tl = L.tl;
+    const int nseg = min(1 << tl, L.T - 4 * k);
     float red[NR];
     tree64xV<S>(part, red);
     // segment sum of slot s, uniform across the wave
@@ -305,12 +311,20 @@ __device__ __forceinline__ SeqPos next_pos(const SeqPos& p, const SeqLin* lin, c
     return n;
 }
 
+// Issue the loads of step `nxt` phase by phase, each just before the same
+// phase of the arithmetic of step `cur`; then finish `cur`.
 template <int KIND, bool DENSE>
 __device__ __forceinline__ void stage(const SeqPos& nxt, SeqRaw<KIND>& into, const SeqPos& cur,
                                       const SeqRaw<KIND>& have, int lane, float (&yacc)[seq_slots(KIND) / 4]) {
-    load_step<KIND, DENSE>(nxt.L, nxt.v, nxt.k, lane, into);
-    __builtin_amdgcn_sched_barrier(0);  // keep the later step's loads ahead of this step's arithmetic
-    compute_step<KIND, DENSE>(cur.L, cur.v, cur.k, lane, have, yacc);
+    float part[seq_slots(KIND)];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        load_phase<KIND, DENSE>(nxt.L, nxt.v, nxt.k, lane, p, into);
+        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the phase's arithmetic
+        compute_phase<KIND, DENSE>(cur.L, cur.k, lane, p, have, part);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    finish_step<KIND, DENSE>(cur.L, cur.v, cur.k, lane, part, yacc);
 }
 
 // One path (dense or general) of a sequence: `total` units, linear j owning
@@ -323,7 +337,13 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const SeqLin* __restrict__ 
     const int lane = threadIdx.x % kLanes;
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     SeqPos p0;
-    p0.u = (int64_t)blockIdx.x * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
+    // b % 8); renumber them so that each XCD holds a contiguous range of wave
+    // numbers, and so takes contiguous runs of units: each XCD's L2 then
+    // serves the x chunks and scale rows of fewer linears at a time.
+    const int G = gridDim.x, wg = blockIdx.x, xcd = wg % 8, q = G / 8, r = G % 8;
+    const int bx = xcd * q + min(xcd, r) + wg / 8;
+    p0.u = (int64_t)bx * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     if (p0.u >= total) return;
     p0.k = 0;
     p0.j = 0;
