@@ -28,10 +28,11 @@ MIN_COLS, MAX_COLS, MAX_M = 16, 65536, 16
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
            "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
-           "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence")
+           "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
+           "bf16_gemv_twin_mfma_sequence")
 MAX_GROUP = 8
 MAX_SEQ = 65536
-ARM_FP8, ARM_BF16 = 0, 1
+ARM_FP8, ARM_BF16, ARM_FP8_MFMA, ARM_BF16_MFMA = 0, 1, 2, 3
 
 
 class Linear(ctypes.Structure):
@@ -44,14 +45,14 @@ class Linear(ctypes.Structure):
 class SeqLinear(ctypes.Structure):
     """fp8blk_seq_linear: one member of a sequence launch."""
     _fields_ = [("w", ctypes.c_void_p), ("scales_f32", ctypes.c_void_p), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64), ("x_bf16", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+                ("cols", ctypes.c_int64), ("M", ctypes.c_int64), ("x_bf16", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class SequenceHandle(ctypes.Structure):
     """fp8blk_sequence: the host-side record of a planned sequence."""
     _fields_ = [("plan", ctypes.c_void_p), ("units_dense", ctypes.c_int64), ("units_general", ctypes.c_int64),
                 ("n", ctypes.c_int32), ("arm", ctypes.c_int32), ("grid_dense", ctypes.c_int32),
-                ("grid_general", ctypes.c_int32)]
+                ("grid_general", ctypes.c_int32), ("M", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -100,6 +101,10 @@ def load():
     L.fp8blk_gemv_sequence.restype = i32
     L.bf16_gemv_twin_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
     L.bf16_gemv_twin_sequence.restype = i32
+    L.fp8blk_gemv_mfma_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
+    L.fp8blk_gemv_mfma_sequence.restype = i32
+    L.bf16_gemv_twin_mfma_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
+    L.bf16_gemv_twin_mfma_sequence.restype = i32
     _lib = L
     return L
 
@@ -281,18 +286,20 @@ class Sequence:
 
 
 def fp8blk_sequence_init(arm: int, linears, ws=None, stream=None, check=True):
-    """Plan a sequence launch over independent M = 1 linears.
-    linears: [(codes, scales_f32, x_bf16, y), ...] for ARM_FP8, or
-             [(w_bf16, x_bf16, y), ...] for ARM_BF16; x_bf16 is [1, cols] (or
-             [cols]), y is [1, rows] (or [rows]).
+    """Plan a sequence launch over independent linears.
+    linears: [(codes, scales_f32, x_bf16, y), ...] for ARM_FP8 / ARM_FP8_MFMA,
+             [(w_bf16, x_bf16, y), ...] for ARM_BF16 / ARM_BF16_MFMA;
+             x_bf16 is [M, cols] and y is [M, rows] (M = 1 on the vector arms,
+             and the same M for every linear).
     ws: a device uint8 tensor of at least fp8blk_sequence_bytes(n) bytes, or
         None to allocate one here. Waits for the plan's copy to the device."""
     import torch
     n = len(linears)
     arr = (SeqLinear * max(n, 1))()
     keep = []
+    fp8 = arm in (ARM_FP8, ARM_FP8_MFMA)
     for k, lin in enumerate(linears):
-        if arm == ARM_FP8:
+        if fp8:
             w, grid, x, y = lin
             arr[k].w = _dev(w, (torch.uint8,), "codes")
             arr[k].scales_f32 = _dev(grid, (torch.float32,), "scales_f32")
@@ -302,9 +309,10 @@ def fp8blk_sequence_init(arm: int, linears, ws=None, stream=None, check=True):
             arr[k].w = _dev(w, _bf16_dtypes(), "w_bf16")
             arr[k].scales_f32 = None
         rows, cols = w.shape
-        if x.numel() != cols or y.numel() != rows:
-            raise ValueError(f"linear {k}: x must hold cols={cols} and y rows={rows} elements (M = 1)")
-        arr[k].rows, arr[k].cols = rows, cols
+        M = x.shape[0] if x.dim() == 2 else 1
+        if x.numel() != M * cols or y.numel() != M * rows:
+            raise ValueError(f"linear {k}: x must be [M, cols={cols}] and y [M, rows={rows}]")
+        arr[k].rows, arr[k].cols, arr[k].M = rows, cols, M
         arr[k].x_bf16 = _dev(x, _bf16_dtypes(), "x_bf16")
         arr[k].y = _dev(y, (torch.float32,), "y")
         keep.append((w, grid, x, y))
@@ -332,6 +340,22 @@ def bf16_gemv_twin_sequence(seq, stream=None, check=True):
     st = load().bf16_gemv_twin_sequence(ctypes.byref(seq.handle), _stream(stream))
     if check and st != OK:
         raise Fp8BlkError(st, "bf16_gemv_twin_sequence")
+    return st
+
+
+def fp8blk_gemv_mfma_sequence(seq, stream=None, check=True):
+    """One persistent launch of every linear of an ARM_FP8_MFMA sequence."""
+    st = load().fp8blk_gemv_mfma_sequence(ctypes.byref(seq.handle), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_mfma_sequence")
+    return st
+
+
+def bf16_gemv_twin_mfma_sequence(seq, stream=None, check=True):
+    """One persistent launch of every linear of an ARM_BF16_MFMA sequence."""
+    st = load().bf16_gemv_twin_mfma_sequence(ctypes.byref(seq.handle), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "bf16_gemv_twin_mfma_sequence")
     return st
 
 
@@ -375,7 +399,8 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         members, x = tensors_and_sizes
         arr, cols = _group(members, name == "fp8blk_gemv_grouped")
         args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], s)
-    elif name in ("fp8blk_gemv_sequence", "bf16_gemv_twin_sequence"):
+    elif name in ("fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
+                  "bf16_gemv_twin_mfma_sequence"):
         (seq,) = tensors_and_sizes
         args = (ctypes.byref(seq.handle), s)
     else:

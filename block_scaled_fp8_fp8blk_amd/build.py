@@ -15,10 +15,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly, nothing else may be contracted. Packed FP32 instructions are
 # disabled. f32 subnormals are kept (the default; stated for the reader).
+# Matrix-core accumulators live in ordinary VGPRs (-amdgpu-mfma-vgpr-form):
+# with AGPR accumulators the compiler copies them between the two register
+# files around every loop iteration of the sequence kernel.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -163,4 +163,15 @@ __device__ __forceinline__ float tree64(float v) {
     return v;
 }
 
+// Workgroups are dealt to the 8 XCDs of the chip in turn (workgroup b runs
+// on XCD b % 8). This renumbering gives each XCD a contiguous range of
+// numbers, so that a persistent kernel whose waves take consecutive work
+// units by number keeps each XCD on contiguous runs of units (its L2 then
+// serves the activations and scale rows of fewer linears at a time). A
+// bijection on [0, gridDim.x) for every grid size.
+__device__ __forceinline__ int xcd_contiguous_block() {
+    const int G = gridDim.x, wg = blockIdx.x, xcd = wg % 8, q = G / 8, r = G % 8;
+    return xcd * q + min(xcd, r) + wg / 8;
+}
+
 }  // namespace fp8blk

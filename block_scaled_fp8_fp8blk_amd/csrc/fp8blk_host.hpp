@@ -25,4 +25,29 @@ inline int launch_status() {
     return hipGetLastError() == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_HIP;
 }
 
+// Sequence launches (fp8blk_seq.hip, fp8blk_mfma.hip). A plan in the
+// caller's workspace: n descriptors of kSeqDescBytes, then two arrays of
+// n + 1 int64 prefix sums of work units.
+constexpr int kSeqWaves = 4;         // waves per workgroup of the persistent kernels
+constexpr int kSeqDescBytes = 64;    // one descriptor: one scalar load
+constexpr int kMfSeqBlocksPerCU = 2; // workgroups per compute unit, matrix-core sequence
+inline size_t plan_bytes(int n) { return (size_t)n * kSeqDescBytes + (size_t)(n + 1) * 2 * sizeof(int64_t); }
+
+// LDS bytes a workgroup reserves (and leaves unused) so that no compute unit
+// (160 KB of LDS) holds more than `per_cu` of them: a persistent kernel that
+// deals its units to the waves in a fixed rotation assumes every wave
+// progresses at the same rate.
+constexpr int lds_cap_bytes(int per_cu) { return 160 * 1024 / (per_cu + 1) + 1024; }
+
+inline int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return cus;
+}
+
+// Writes the matrix-core sequence plan of n validated linears (panel rows M,
+// the same for all) into host (plan_bytes(n) bytes); returns its work units.
+int64_t mf_sequence_plan(unsigned char* host, bool fp8, const fp8blk_seq_linear* linears, int n);
+
 }  // namespace fp8blk

@@ -192,9 +192,9 @@ __device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, XR>& b, const MfA
     }
     const int xc = min(base + L.xcol, a.K - 8);
 #pragma unroll
-    for (int k = 0; k < XR; ++k) b.x[k] = *reinterpret_cast<const uint4*>(L.xrow[k] + xc);
+    for (int k = 0; k < XR; ++k) b.x[k] = load_global16(L.xrow[k] + xc);
     b.sc = 1.0f;
-    if constexpr (KIND == 0) b.sc = a.grid[(min(L.r0, a.rows - 1) >> 7) * a.GC + win];
+    if constexpr (KIND == 0) b.sc = load_global_f32(a.grid + (min(L.r0, a.rows - 1) >> 7) * a.GC + win);
 }
 
 template <int KIND, int TILES, int XR>
@@ -363,6 +363,258 @@ int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const u
     return launch_status();
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core sequence: a list of independent linears with a panel of M rows
+// each, run by one persistent kernel. A unit is TILES 16-row tiles of one
+// linear (inside one 128-row scale block) across all its column windows, in
+// increasing window order into one accumulator per tile (the order of
+// k_mfma with one part). Units are numbered over the list in order; wave w of
+// W takes units w, w + W, ...; each wave loads the next window (of this unit
+// or of its next one) before it multiplies the current one.
+
+struct alignas(64) MfSeqLin {
+    const void* w;       // codes or bf16 slab [rows, K]
+    const float* grid;   // f32 block scales (FP8 arm)
+    const uint16_t* x;   // bf16 [M, K]
+    float* y;            // f32 [M, rows]
+    int64_t rows;
+    int32_t K, M, GC, nwin;
+    int64_t pad;
+};
+static_assert(sizeof(MfSeqLin) == kSeqDescBytes, "descriptor size of the plan");
+
+// Row tiles per unit: 4 for panels of 8 rows or more (the tiles share a
+// wave's activation loads), else 2. Measured on the whole-step sweep.
+constexpr int mf_seq_tiles(int M) { return M >= 8 ? 4 : 2; }
+constexpr int kMfSeqDepth = 2;  // register sets: windows loaded ahead + 1
+
+// Per-unit addressing, computed once when a wave starts a unit: wave-uniform
+// bases plus 32-bit lane offsets, so that a window's loads need no vector
+// arithmetic (the row clamps of the last, partial tile group are folded into
+// the offsets).
+template <int TILES, int XR>
+struct MfUnit {
+    const char* w;              // weights of the unit's first row
+    const char* x;              // the linear's activation panel
+    const float* g;             // the unit's row of block scales (FP8 arm)
+    uint32_t roff[TILES][2];    // lane: byte offset of its rows (lo, hi) + its chunk's first column
+    uint32_t xoff[XR];          // lane: byte offset of its panel rows + its column group
+};
+
+struct MfPos {
+    int64_t u, v;  // unit (list numbering) and unit within its linear
+    int win, j;
+    bool more;     // false: past the wave's last window (the position repeats the last one)
+    MfSeqLin d;
+};
+
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_unit(MfUnit<TILES, XR>& U, const MfSeqLin& d, int64_t v, int lane) {
+    constexpr int E = KIND == 0 ? 1 : 2;
+    const int64_t r0 = v * (TILES * kTile);
+    U.w = static_cast<const char*>(d.w) + r0 * d.K * E;
+    U.x = reinterpret_cast<const char*>(d.x);
+    U.g = d.grid + (r0 >> 7) * d.GC;
+    const int r = lane & 7, wchunk = 16 * (lane >> 3);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t row = min(r0 + t * kTile + 8 * h + r, d.rows - 1) - r0;
+            U.roff[t][h] = (uint32_t)((row * d.K + wchunk) * E);
+        }
+    const int xr_base = 8 * ((lane >> 3) & 1) + 4 * ((lane >> 2) & 1);
+    const int xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
+#pragma unroll
+    for (int k = 0; k < XR; ++k) U.xoff[k] = (uint32_t)((min(xr_base + k, d.M - 1) * d.K + xcol) * 2);
+}
+
+__device__ __forceinline__ MfPos mf_next(const MfPos& p, const MfSeqLin* lin, const int64_t* pre, int64_t W,
+                                         int64_t total) {
+    MfPos n = p;
+    if (!p.more) return n;
+    if (p.win + 1 < p.d.nwin) {
+        n.win = p.win + 1;
+    } else if (p.u + W < total) {
+        n.u = p.u + W;
+        n.v = p.v + W;
+        n.win = 0;
+        if (n.u >= pre[n.j + 1]) {
+            do ++n.j;
+            while (n.u >= pre[n.j + 1]);
+            n.d = lin[n.j];
+            n.v = n.u - pre[n.j];
+        }
+    } else {
+        n.more = false;
+    }
+    return n;
+}
+
+typedef __attribute__((address_space(4))) const float constant_f32;
+
+// The loads of window `win` of a unit: the unit's bases plus the lane
+// offsets. In the last window of a row whose cols is not a multiple of 128,
+// a lane whose chunk lies past the last column moves back to the last chunk
+// (its products are then multiplied by the zeroed activations, see
+// mf_seq_compute); elsewhere the shift is 0. No branch: every window issues
+// the same loads, so the waits for a window never cover the next one's. The
+// block scale is the same for every lane: one scalar load.
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_seq_issue(MfWindow<KIND, TILES, XR>& b, const MfUnit<TILES, XR>& U, int K, int win,
+                                             int lane) {
+    constexpr int E = KIND == 0 ? 1 : 2;
+    const int base = win * kBlock;
+    const char* wsrc = U.w + base * E;
+    const char* xsrc = U.x + base * 2;
+    const int wchunk = 16 * (lane >> 3), xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
+    const uint32_t wshift = (uint32_t)((min(base + wchunk, K - 16) - base - wchunk) * E);  // 0, or minus the overrun
+    const uint32_t xshift = (uint32_t)((min(base + xcol, K - 8) - base - xcol) * 2);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        const uint32_t lo = U.roff[t][0] + wshift, hi = U.roff[t][1] + wshift;
+        if constexpr (KIND == 0) {
+            b.w[t].c[0] = load_stream16(wsrc + lo);
+            b.w[t].c[1] = load_stream16(wsrc + hi);
+        } else {
+            b.w[t].c[0][0] = load_stream16(wsrc + lo);
+            b.w[t].c[1][0] = load_stream16(wsrc + lo + 16);
+            b.w[t].c[0][1] = load_stream16(wsrc + hi);
+            b.w[t].c[1][1] = load_stream16(wsrc + hi + 16);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < XR; ++k) b.x[k] = load_global16(xsrc + (uint32_t)(U.xoff[k] + xshift));
+    b.sc = 1.0f;
+    if constexpr (KIND == 0) b.sc = *(constant_f32*)(U.g + win);
+}
+
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_seq_compute(MfWindow<KIND, TILES, XR> b, int K, int win, int lane, v4f* acc) {
+    const int base = win * kBlock;
+    const int xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
+    if (base + kBlock > K && base + xcol + 8 > K) {
+        // ragged last window: activation columns past the end feed zeros
+#pragma unroll
+        for (int k = 0; k < XR; ++k) b.x[k] = make_uint4(0, 0, 0, 0);
+    }
+    // registers not loaded hold only panel rows >= M: any values serve, their outputs are not stored
+#pragma unroll
+    for (int k = XR; k < 4; ++k) b.x[k] = b.x[0];
+    const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0, b3 = (lane & 8) != 0;
+    exchange<0>(b.x[0], b.x[1], b0);
+    exchange<0>(b.x[2], b.x[3], b0);
+    exchange<1>(b.x[0], b.x[2], b1);
+    exchange<1>(b.x[1], b.x[3], b1);
+    // Every tile's operands first, then the matrix instructions with the tile
+    // innermost: the TILES accumulator chains are independent, so each
+    // instruction waits on one issued TILES instructions earlier. Each tile
+    // still takes (u, v) = (0,0), (0,1), (1,0), (1,1) in that order.
+    v8bf op[TILES][2][2];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) MfFetch<KIND>::operands(b.w[t], b.sc, b3, op[t]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int t = 0; t < TILES; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[t][u][v], __builtin_bit_cast(v8bf, b.x[2 * u + v]),
+                                                                 acc[t], 0, 0, 0);
+}
+
+template <int TILES>
+__device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int lane, v4f* acc) {
+    // lane l holds D[4 (l / 16) + e][l % 16]: row 4 (l / 16) + e of the tile, panel row l % 16
+    const int n = lane & 15, kg = lane >> 4;
+    const int64_t r0 = v * (TILES * kTile);
+    if (n < d.M) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t r = r0 + t * kTile + 4 * kg + e;
+                if (r < d.rows) store_global_f32(d.y + (int64_t)n * d.rows + r, acc[t][e]);
+            }
+    }
+}
+
+// DEPTH register sets in turn: the loads of the window DEPTH - 1 ahead are
+// issued before the matrix work of the current one.
+template <int KIND, int TILES, int XR, int DEPTH>
+__global__ __launch_bounds__(kSeqWaves * kLanes) void k_mfseq(const MfSeqLin* __restrict__ lin,
+                                                               const int64_t* __restrict__ pre, int64_t total) {
+    using Win = MfWindow<KIND, TILES, XR>;
+    using Unit = MfUnit<TILES, XR>;
+    const int lane = threadIdx.x % kLanes;
+    const int64_t W = (int64_t)gridDim.x * kSeqWaves;
+    MfPos pos[DEPTH];
+    Unit unit[DEPTH];
+    pos[0].u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    if (pos[0].u >= total) return;
+    pos[0].win = 0;
+    pos[0].j = 0;
+    pos[0].more = true;
+    while (pos[0].u >= pre[pos[0].j + 1]) ++pos[0].j;
+    pos[0].d = lin[pos[0].j];
+    pos[0].v = pos[0].u - pre[pos[0].j];
+    mf_unit<KIND>(unit[0], pos[0].d, pos[0].v, lane);
+    v4f acc[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    Win buf[DEPTH];
+    mf_seq_issue(buf[0], unit[0], pos[0].d.K, pos[0].win, lane);
+#pragma unroll
+    for (int d = 1; d + 1 < DEPTH; ++d) {
+        pos[d] = mf_next(pos[d - 1], lin, pre, W, total);
+        unit[d] = unit[d - 1];
+        if (pos[d].win == 0) mf_unit<KIND>(unit[d], pos[d].d, pos[d].v, lane);
+        mf_seq_issue(buf[d], unit[d], pos[d].d.K, pos[d].win, lane);
+    }
+    for (;;) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int nd = (d + DEPTH - 1) % DEPTH, pd = (nd + DEPTH - 1) % DEPTH;
+            pos[nd] = mf_next(pos[pd], lin, pre, W, total);
+            unit[nd] = unit[pd];
+            if (pos[nd].win == 0 && pos[nd].more) mf_unit<KIND>(unit[nd], pos[nd].d, pos[nd].v, lane);
+            mf_seq_issue(buf[nd], unit[nd], pos[nd].d.K, pos[nd].win, lane);
+            __builtin_amdgcn_sched_barrier(0);  // keep the newest loads ahead of this window's matrix work
+            mf_seq_compute(buf[d], pos[d].d.K, pos[d].win, lane, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (pos[d].win + 1 == pos[d].d.nwin) {
+                mf_seq_store<TILES>(pos[d].d, pos[d].v, lane, acc);
+#pragma unroll
+                for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            if (!pos[(d + 1) % DEPTH].more) return;
+        }
+    }
+}
+
+template <int KIND>
+int mf_seq_launch(const fp8blk_sequence* seq, int arm, hipStream_t s) {
+    if (!seq || !seq->plan || seq->arm != arm || seq->n < 1 || seq->M < 1 || seq->M > FP8BLK_MAX_M ||
+        seq->units_dense < 1 || seq->grid_dense < 1)
+        return FP8BLK_ERR_ARG;
+    const MfSeqLin* lin = static_cast<const MfSeqLin*>(seq->plan);
+    const int64_t* pre =
+        reinterpret_cast<const int64_t*>(static_cast<const unsigned char*>(seq->plan) + (size_t)seq->n * sizeof(MfSeqLin));
+    const dim3 nb((unsigned)seq->grid_dense), nt(kSeqWaves * kLanes);
+    constexpr int lds = lds_cap_bytes(kMfSeqBlocksPerCU);
+    (void)hipGetLastError();
+    const int M = seq->M;
+    if (M >= 8)
+        k_mfseq<KIND, mf_seq_tiles(8), 4, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+    else if (M > 2)
+        k_mfseq<KIND, mf_seq_tiles(3), 4, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+    else if (M == 2)
+        k_mfseq<KIND, mf_seq_tiles(2), 2, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+    else
+        k_mfseq<KIND, mf_seq_tiles(1), 1, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+    return launch_status();
+}
+
 int mf_check(const void* w, int64_t rows, int64_t cols, const uint16_t* x, int64_t M, float* y) {
     if (!w || !x || !y || !shape_ok(rows, cols) || M < 1 || M > FP8BLK_MAX_M || !aligned(w, 16) ||
         !aligned(x, 16) || !aligned(y, 4))
@@ -388,4 +640,36 @@ extern "C" int bf16_gemv_twin_mfma(const uint16_t* w_bf16, int64_t rows, int64_t
     const int st = mf_check(w_bf16, rows, cols, x_bf16, M, y);
     if (st != FP8BLK_OK) return st;
     return mf_run<1>(w_bf16, nullptr, rows, cols, x_bf16, M, y, reinterpret_cast<hipStream_t>(stream));
+}
+
+namespace fp8blk {
+int64_t mf_sequence_plan(unsigned char* host, bool fp8, const fp8blk_seq_linear* linears, int n) {
+    MfSeqLin* d = reinterpret_cast<MfSeqLin*>(host);
+    int64_t* pre = reinterpret_cast<int64_t*>(host + (size_t)n * sizeof(MfSeqLin));
+    pre[0] = 0;
+    for (int j = 0; j < n; ++j) {
+        const fp8blk_seq_linear& l = linears[j];
+        MfSeqLin& s = d[j];
+        s.w = l.w;
+        s.grid = fp8 ? l.scales_f32 : nullptr;
+        s.x = l.x_bf16;
+        s.y = l.y;
+        s.rows = l.rows;
+        s.K = (int32_t)l.cols;
+        s.M = (int32_t)l.M;
+        s.GC = (int32_t)ceil_div(l.cols, kBlock);
+        s.nwin = s.GC;
+        s.pad = 0;
+        pre[j + 1] = pre[j] + ceil_div(l.rows, (int64_t)kTile * mf_seq_tiles((int)l.M));
+    }
+    return pre[n];
+}
+}  // namespace fp8blk
+
+extern "C" int fp8blk_gemv_mfma_sequence(const fp8blk_sequence* seq, fp8blk_stream_t stream) {
+    return mf_seq_launch<0>(seq, FP8BLK_ARM_FP8_MFMA, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int bf16_gemv_twin_mfma_sequence(const fp8blk_sequence* seq, fp8blk_stream_t stream) {
+    return mf_seq_launch<1>(seq, FP8BLK_ARM_BF16_MFMA, reinterpret_cast<hipStream_t>(stream));
 }

@@ -39,7 +39,6 @@
 namespace fp8blk {
 namespace {
 
-constexpr int kSeqWaves = 4;                  // waves per workgroup
 constexpr int kSeqThreads = kSeqWaves * kLanes;
 constexpr int kSeqBlocksPerCU = 2;            // workgroups per compute unit
 // Each workgroup reserves this much LDS (it uses none), so that no compute
@@ -47,7 +46,7 @@ constexpr int kSeqBlocksPerCU = 2;            // workgroups per compute unit
 // units are dealt to the waves in a fixed rotation, which assumes every wave
 // progresses at the same rate, and a CU holding one workgroup more than
 // another would finish last.
-constexpr int kSeqLdsBytes = 160 * 1024 / (kSeqBlocksPerCU + 1) + 1024;
+constexpr int kSeqLdsBytes = lds_cap_bytes(kSeqBlocksPerCU);
 
 // Device descriptor of one linear: 64 bytes of 32- and 64-bit fields, one
 // scalar load.
@@ -65,9 +64,7 @@ struct alignas(64) SeqLin {
 };
 static_assert(sizeof(SeqLin) == 64, "one scalar load per descriptor");
 
-// The plan in the caller's workspace: n descriptors, then two arrays of n + 1
-// prefix sums (int64): of the dense unit counts, and of the general ones.
-size_t plan_bytes(int n) { return (size_t)n * sizeof(SeqLin) + (size_t)(n + 1) * 2 * sizeof(int64_t); }
+static_assert(sizeof(SeqLin) == kSeqDescBytes, "descriptor size of the plan");
 
 enum Kind { kFp8 = 0, kBf16 = 1 };
 
@@ -337,13 +334,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const SeqLin* __restrict__ 
     const int lane = threadIdx.x % kLanes;
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     SeqPos p0;
-    // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
-    // b % 8); renumber them so that each XCD holds a contiguous range of wave
-    // numbers, and so takes contiguous runs of units: each XCD's L2 then
-    // serves the x chunks and scale rows of fewer linears at a time.
-    const int G = gridDim.x, wg = blockIdx.x, xcd = wg % 8, q = G / 8, r = G % 8;
-    const int bx = xcd * q + min(xcd, r) + wg / 8;
-    p0.u = (int64_t)bx * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     if (p0.u >= total) return;
     p0.k = 0;
     p0.j = 0;
@@ -364,13 +355,6 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const SeqLin* __restrict__ 
     }
 }
 
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    return cus;
-}
-
 }  // namespace
 }  // namespace fp8blk
 
@@ -383,60 +367,75 @@ extern "C" size_t fp8blk_sequence_bytes(int n) {
 
 extern "C" int fp8blk_sequence_init(fp8blk_sequence* seq, int arm, const fp8blk_seq_linear* linears, int n,
                                     void* ws, size_t ws_bytes, fp8blk_stream_t stream) {
-    if (!seq || !linears || n < 1 || n > FP8BLK_MAX_SEQ || (arm != FP8BLK_ARM_FP8 && arm != FP8BLK_ARM_BF16))
+    if (!seq || !linears || n < 1 || n > FP8BLK_MAX_SEQ || arm < FP8BLK_ARM_FP8 || arm > FP8BLK_ARM_BF16_MFMA)
         return FP8BLK_ERR_ARG;
     if (!ws || !aligned(ws, 64) || ws_bytes < plan_bytes(n)) return FP8BLK_ERR_WORKSPACE;
-    std::vector<unsigned char> host(plan_bytes(n));
-    SeqLin* d = reinterpret_cast<SeqLin*>(host.data());
-    int64_t* pre_d = reinterpret_cast<int64_t*>(host.data() + (size_t)n * sizeof(SeqLin));
-    int64_t* pre_g = pre_d + (n + 1);
-    pre_d[0] = pre_g[0] = 0;
+    const bool fp8 = arm == FP8BLK_ARM_FP8 || arm == FP8BLK_ARM_FP8_MFMA;
+    const bool mfma = arm == FP8BLK_ARM_FP8_MFMA || arm == FP8BLK_ARM_BF16_MFMA;
+    const int64_t M = linears[0].M;
     for (int j = 0; j < n; ++j) {
         const fp8blk_seq_linear& l = linears[j];
         if (!l.w || !l.x_bf16 || !l.y || !shape_ok(l.rows, l.cols) || !aligned(l.w, 16) || !aligned(l.x_bf16, 16) ||
-            !aligned(l.y, 4))
+            !aligned(l.y, 4) || l.M != M || M < 1 || M > (mfma ? FP8BLK_MAX_M : 1))
             return FP8BLK_ERR_ARG;
-        if (arm == FP8BLK_ARM_FP8 && (!l.scales_f32 || !aligned(l.scales_f32, 4))) return FP8BLK_ERR_ARG;
-        SeqLin& s = d[j];
-        s.w = l.w;
-        s.grid = arm == FP8BLK_ARM_FP8 ? l.scales_f32 : nullptr;
-        s.x = l.x_bf16;
-        s.y = l.y;
-        s.rows = l.rows;
-        s.K = (int32_t)l.cols;
-        s.T = (int32_t)ceil_div(l.cols, kSegCols);
-        s.tl = s.T >= 3 ? 2 : s.T == 2 ? 1 : 0;
-        s.Q = (int32_t)ceil_div(s.T, 4);
-        // Dense: every chunk slot of a step is a whole chunk of the row it
-        // names (K = 1024, 2048 or a multiple of 4096) and the unit has all
-        // its R rows; a last unit with fewer rows, and every unit of another
-        // K, take the general path.
-        const int64_t R = (arm == FP8BLK_ARM_FP8 ? seq_slots(kFp8) : seq_slots(kBf16)) >> s.tl;
-        const bool dense = l.cols == kSegCols || l.cols == 2 * kSegCols || l.cols % (4 * kSegCols) == 0;
-        s.dense_units = dense ? l.rows / R : 0;
-        pre_d[j + 1] = pre_d[j] + s.dense_units;
-        pre_g[j + 1] = pre_g[j] + (ceil_div(l.rows, R) - s.dense_units);
+        if (fp8 && (!l.scales_f32 || !aligned(l.scales_f32, 4))) return FP8BLK_ERR_ARG;
+    }
+    std::vector<unsigned char> host(plan_bytes(n));
+    int64_t units_first = 0, units_second = 0;
+    if (mfma) {
+        units_first = mf_sequence_plan(host.data(), fp8, linears, n);
+    } else {
+        SeqLin* d = reinterpret_cast<SeqLin*>(host.data());
+        int64_t* pre_d = reinterpret_cast<int64_t*>(host.data() + (size_t)n * sizeof(SeqLin));
+        int64_t* pre_g = pre_d + (n + 1);
+        pre_d[0] = pre_g[0] = 0;
+        for (int j = 0; j < n; ++j) {
+            const fp8blk_seq_linear& l = linears[j];
+            SeqLin& s = d[j];
+            s.w = l.w;
+            s.grid = fp8 ? l.scales_f32 : nullptr;
+            s.x = l.x_bf16;
+            s.y = l.y;
+            s.rows = l.rows;
+            s.K = (int32_t)l.cols;
+            s.T = (int32_t)ceil_div(l.cols, kSegCols);
+            s.tl = s.T >= 3 ? 2 : s.T == 2 ? 1 : 0;
+            s.Q = (int32_t)ceil_div(s.T, 4);
+            // Dense: every chunk slot of a step is a whole chunk of the row it
+            // names (K = 1024, 2048 or a multiple of 4096) and the unit has all
+            // its R rows; a last unit with fewer rows, and every unit of another
+            // K, take the general path.
+            const int64_t R = (fp8 ? seq_slots(kFp8) : seq_slots(kBf16)) >> s.tl;
+            const bool dense = l.cols == kSegCols || l.cols == 2 * kSegCols || l.cols % (4 * kSegCols) == 0;
+            s.dense_units = dense ? l.rows / R : 0;
+            pre_d[j + 1] = pre_d[j] + s.dense_units;
+            pre_g[j + 1] = pre_g[j] + (ceil_div(l.rows, R) - s.dense_units);
+        }
+        units_first = pre_d[n];
+        units_second = pre_g[n];
     }
     const int cus = device_cus();
     if (cus < 1) return FP8BLK_ERR_HIP;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess) return FP8BLK_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return FP8BLK_ERR_HIP;
-    const int64_t waves = (int64_t)cus * kSeqBlocksPerCU * kSeqWaves;
+    const int64_t waves = (int64_t)cus * (mfma ? kMfSeqBlocksPerCU : kSeqBlocksPerCU) * kSeqWaves;
     seq->plan = ws;
-    seq->units_dense = pre_d[n];
-    seq->units_general = pre_g[n];
+    seq->units_dense = units_first;
+    seq->units_general = units_second;
     seq->n = n;
     seq->arm = arm;
-    seq->grid_dense = (int32_t)ceil_div(std::min<int64_t>(waves, pre_d[n]), kSeqWaves);
-    seq->grid_general = (int32_t)ceil_div(std::min<int64_t>(waves, pre_g[n]), kSeqWaves);
+    seq->grid_dense = (int32_t)ceil_div(std::min<int64_t>(waves, units_first), kSeqWaves);
+    seq->grid_general = (int32_t)ceil_div(std::min<int64_t>(waves, units_second), kSeqWaves);
+    seq->M = (int32_t)M;
+    seq->reserved = 0;
     return FP8BLK_OK;
 }
 
 namespace {
 template <int KIND>
 int launch_seq(const fp8blk_sequence* seq, int arm, fp8blk_stream_t stream) {
-    if (!seq || !seq->plan || seq->arm != arm || seq->n < 1 || seq->units_dense < 0 || seq->units_general < 0 ||
+    if (!seq || !seq->plan || seq->arm != arm || seq->n < 1 || seq->M != 1 || seq->units_dense < 0 || seq->units_general < 0 ||
         seq->units_dense + seq->units_general < 1 || (seq->units_dense > 0 && seq->grid_dense < 1) ||
         (seq->units_general > 0 && seq->grid_general < 1))
         return FP8BLK_ERR_ARG;

@@ -236,14 +236,27 @@ int bf16_gemv_twin_mfma(const uint16_t *w_bf16, int64_t rows, int64_t cols, cons
                         int64_t M, float *y, fp8blk_stream_t stream);
 
 /*
- * Sequence launch: a list of independent M = 1 linears, each with its own
- * weights, activation row and output (for example every dense projection of a
- * decode step, read as stored: "Struct Dsv4Gpu" page, field dense_fp8), run by
- * one persistent kernel. Each output gets exactly the arithmetic of a call of
- * its own -- y_j == fp8blk_gemv(linear j) bit for bit, and likewise for the
- * twin -- while the weights of the next linears are already being read as the
- * current ones finish, so HBM stays busy across the whole list instead of
- * ramping up and draining once per linear.
+ * Sequence launch: a list of independent linears, each with its own weights,
+ * activation panel and output (for example every dense projection of a
+ * decode step, read as stored: "Struct Dsv4Gpu" page, field dense_fp8; or of a
+ * verify step, whose panel holds the T <= 16 positions: same page,
+ * spec_greedy_batched_with), run by one persistent kernel. The weights of the
+ * next linears are already being read while the current ones finish, so HBM
+ * stays busy across the whole list instead of ramping up and draining once
+ * per linear.
+ *
+ * Arms (the `arm` of fp8blk_sequence_init and the launch that runs it):
+ *   FP8BLK_ARM_FP8 / FP8BLK_ARM_BF16 -> fp8blk_gemv_sequence /
+ *     bf16_gemv_twin_sequence: M = 1; each y_j == fp8blk_gemv (resp.
+ *     bf16_gemv_twin) of linear j, bit for bit (the documented order above).
+ *   FP8BLK_ARM_FP8_MFMA / FP8BLK_ARM_BF16_MFMA -> fp8blk_gemv_mfma_sequence /
+ *     bf16_gemv_twin_mfma_sequence: 1 <= M <= 16, the same M for every linear;
+ *     the matrix-core arm's arithmetic with the columns of a row taken in one
+ *     part (its 128-column windows in increasing order, all into one
+ *     accumulator): equal bit for bit to fp8blk_gemv_mfma wherever that call
+ *     splits a row into one part, within its tolerance otherwise; the FP8 and
+ *     bf16 arms give identical bits, and row m of the panel equals the M = 1
+ *     sequence on x[m], bit for bit.
  *
  * The list must be independent: no linear's y may overlap any linear's w,
  * scales_f32 or x_bf16, nor another linear's y. A chain in which one linear
@@ -258,41 +271,46 @@ int bf16_gemv_twin_mfma(const uint16_t *w_bf16, int64_t rows, int64_t cols, cons
  *                          the device on `stream` and waits for that copy.
  *                          The plan holds the pointers: the buffers must stay
  *                          allocated, at the same addresses, while seq is used.
- *   fp8blk_gemv_sequence   the whole list on `stream` (FP8 arm; the twin for a
- *   bf16_gemv_twin_sequence  plan built with FP8BLK_ARM_BF16): one persistent
- *                          launch over the full 8-chunk steps of every linear
- *                          whose cols is 1024, 2048 or a multiple of 4096, and
- *                          a second one, only if needed, for the rest (a last
- *                          group of rows, linears of other cols). Enqueued on
+ *   the launch             the whole list on `stream`. The vector arms run one
+ *                          persistent launch over the full steps of every
+ *                          linear whose cols is 1024, 2048 or a multiple of
+ *                          4096, and a second one, only if needed, for the
+ *                          rest (a last group of rows, linears of other cols);
+ *                          the matrix-core arms one launch. Enqueued on
  *                          `stream`; does not wait; may be captured in a HIP
  *                          graph. ws must not be changed meanwhile.
- * Per linear: w = codes (FP8 arm) or bf16 slab (twin arm), scales_f32 = the f32
- * grid (FP8 arm; ignored by the twin arm), rows >= 1, cols as for fp8blk_gemv,
- * x_bf16 = [1, cols], y = [1, rows]; alignment as for fp8blk_gemv.
- * 1 <= n <= FP8BLK_MAX_SEQ. Errors: FP8BLK_ERR_ARG (bad descriptor, arm or
- * seq), FP8BLK_ERR_WORKSPACE (ws NULL, misaligned or too small),
- * FP8BLK_ERR_HIP.
+ * Per linear: w = codes (FP8 arms) or bf16 slab (twin arms), scales_f32 = the
+ * f32 grid (FP8 arms; ignored by the twin arms), rows >= 1, cols as for
+ * fp8blk_gemv, M as above, x_bf16 = [M, cols], y = [M, rows]; alignment as for
+ * fp8blk_gemv. 1 <= n <= FP8BLK_MAX_SEQ. Errors: FP8BLK_ERR_ARG (bad
+ * descriptor, arm, M or seq; a launch whose arm differs from the plan's),
+ * FP8BLK_ERR_WORKSPACE (ws NULL, misaligned or too small), FP8BLK_ERR_HIP.
  */
 #define FP8BLK_MAX_SEQ 65536
 #define FP8BLK_ARM_FP8 0
 #define FP8BLK_ARM_BF16 1
+#define FP8BLK_ARM_FP8_MFMA 2
+#define FP8BLK_ARM_BF16_MFMA 3
 typedef struct fp8blk_seq_linear {
     const void *w;
     const float *scales_f32;
     int64_t rows;
     int64_t cols;
+    int64_t M;
     const uint16_t *x_bf16;
     float *y;
 } fp8blk_seq_linear;
 
 typedef struct fp8blk_sequence {
     const void *plan;      /* device: the plan inside ws */
-    int64_t units_dense;   /* work units of the full-tile path */
-    int64_t units_general; /* work units of the general path (ragged rows or cols) */
+    int64_t units_dense;   /* work units of the first launch */
+    int64_t units_general; /* work units of the second launch (vector arms: ragged rows or cols) */
     int32_t n;             /* linears */
-    int32_t arm;           /* FP8BLK_ARM_FP8 or FP8BLK_ARM_BF16 */
-    int32_t grid_dense;    /* workgroups of each path's launch (from the device's compute units) */
+    int32_t arm;           /* FP8BLK_ARM_* */
+    int32_t grid_dense;    /* workgroups of each launch (from the device's compute units) */
     int32_t grid_general;
+    int32_t M;             /* panel rows (1 for the vector arms) */
+    int32_t reserved;
 } fp8blk_sequence;
 
 size_t fp8blk_sequence_bytes(int n);
@@ -300,6 +318,8 @@ int fp8blk_sequence_init(fp8blk_sequence *seq, int arm, const fp8blk_seq_linear 
                          void *ws, size_t ws_bytes, fp8blk_stream_t stream);
 int fp8blk_gemv_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int bf16_gemv_twin_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
+int fp8blk_gemv_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
+int bf16_gemv_twin_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 
 #ifdef __cplusplus
 }

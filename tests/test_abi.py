@@ -118,30 +118,43 @@ def test_grouped_refusals(lib):
 def test_sequence_refusals(lib):
     S = fb.SeqLinear
     h = fb.SequenceHandle()
-    good = (S * 2)(S(P, P, 4, 16, P, P), S(P, P, 4, 32, P, P))
+    good = (S * 2)(S(P, P, 4, 16, 1, P, P), S(P, P, 4, 32, 1, P, P))
     nb = fb.fp8blk_sequence_bytes(2)
     assert nb >= 2 * 64 + 2 * 3 * 8
     assert fb.fp8blk_sequence_bytes(0) == 0 and fb.fp8blk_sequence_bytes(fb.MAX_SEQ + 1) == 0
     init = lib.fp8blk_sequence_init
     assert init(ctypes.byref(h), fb.ARM_FP8, good, 0, P, nb, None) == fb.ERR_ARG
     assert init(ctypes.byref(h), fb.ARM_FP8, good, fb.MAX_SEQ + 1, P, nb, None) == fb.ERR_ARG
-    assert init(ctypes.byref(h), 2, good, 2, P, nb, None) == fb.ERR_ARG
+    assert init(ctypes.byref(h), 4, good, 2, P, nb, None) == fb.ERR_ARG
+    assert init(ctypes.byref(h), -1, good, 2, P, nb, None) == fb.ERR_ARG
     assert init(None, fb.ARM_FP8, good, 2, P, nb, None) == fb.ERR_ARG
     assert init(ctypes.byref(h), fb.ARM_FP8, None, 2, P, nb, None) == fb.ERR_ARG
     assert init(ctypes.byref(h), fb.ARM_FP8, good, 2, None, nb, None) == fb.ERR_WORKSPACE
     assert init(ctypes.byref(h), fb.ARM_FP8, good, 2, P, nb - 1, None) == fb.ERR_WORKSPACE
     assert init(ctypes.byref(h), fb.ARM_FP8, good, 2, P + 32, nb, None) == fb.ERR_WORKSPACE
-    for bad in (S(P, P, 0, 16, P, P), S(P, P, 4, 24, P, P), S(P, P, 4, 65552, P, P), S(P + 8, P, 4, 16, P, P),
-                S(P, P, 4, 16, P + 2, P), S(P, P, 4, 16, P, P + 2), S(None, P, 4, 16, P, P),
-                S(P, P, 4, 16, None, P), S(P, P, 4, 16, P, None)):
+    for bad in (S(P, P, 0, 16, 1, P, P), S(P, P, 4, 24, 1, P, P), S(P, P, 4, 65552, 1, P, P),
+                S(P + 8, P, 4, 16, 1, P, P), S(P, P, 4, 16, 1, P + 2, P), S(P, P, 4, 16, 1, P, P + 2),
+                S(None, P, 4, 16, 1, P, P), S(P, P, 4, 16, 1, None, P), S(P, P, 4, 16, 1, P, None),
+                S(P, P, 4, 16, 2, P, P), S(P, P, 4, 16, 0, P, P)):
         arr = (S * 2)(good[0], bad)
-        assert init(ctypes.byref(h), fb.ARM_FP8, arr, 2, P, nb, None) == fb.ERR_ARG
-        assert init(ctypes.byref(h), fb.ARM_BF16, arr, 2, P, nb, None) == fb.ERR_ARG
-    # the FP8 arm needs the scale grid, the twin arm ignores it
-    arr = (S * 1)(S(P, None, 4, 16, P, P))
+        for arm in (fb.ARM_FP8, fb.ARM_BF16, fb.ARM_FP8_MFMA, fb.ARM_BF16_MFMA):
+            assert init(ctypes.byref(h), arm, arr, 2, P, nb, None) == fb.ERR_ARG, (arm, bad.M)
+    # the vector arms take M = 1 only; the matrix-core arms M <= 16, the same for all
+    for M in (2, 16):
+        arr = (S * 1)(S(P, P, 4, 16, M, P, P))
+        assert init(ctypes.byref(h), fb.ARM_FP8, arr, 1, P, nb, None) == fb.ERR_ARG
+        assert init(ctypes.byref(h), fb.ARM_BF16, arr, 1, P, nb, None) == fb.ERR_ARG
+    arr = (S * 1)(S(P, P, 4, 16, 17, P, P))
+    assert init(ctypes.byref(h), fb.ARM_FP8_MFMA, arr, 1, P, nb, None) == fb.ERR_ARG
+    arr = (S * 2)(S(P, P, 4, 16, 4, P, P), S(P, P, 4, 16, 8, P, P))
+    assert init(ctypes.byref(h), fb.ARM_FP8_MFMA, arr, 2, P, nb, None) == fb.ERR_ARG
+    # the FP8 arms need the scale grid, the twin arms ignore it
+    arr = (S * 1)(S(P, None, 4, 16, 1, P, P))
     assert init(ctypes.byref(h), fb.ARM_FP8, arr, 1, P, nb, None) == fb.ERR_ARG
+    assert init(ctypes.byref(h), fb.ARM_FP8_MFMA, arr, 1, P, nb, None) == fb.ERR_ARG
     # a launch checks its handle before any device work
-    h.plan, h.units_dense, h.units_general, h.n, h.arm, h.grid_dense, h.grid_general = P, 10, 0, 2, fb.ARM_FP8, 4, 0
+    h.plan, h.units_dense, h.units_general, h.n, h.arm, h.grid_dense, h.grid_general, h.M = \
+        P, 10, 0, 2, fb.ARM_FP8, 4, 0, 1
     assert lib.bf16_gemv_twin_sequence(ctypes.byref(h), None) == fb.ERR_ARG
     assert lib.fp8blk_gemv_sequence(None, None) == fb.ERR_ARG
     h.arm = fb.ARM_BF16
@@ -152,3 +165,13 @@ def test_sequence_refusals(lib):
     assert lib.fp8blk_gemv_sequence(ctypes.byref(h), None) == fb.ERR_ARG
     h.units_general, h.grid_general = 5, 0
     assert lib.fp8blk_gemv_sequence(ctypes.byref(h), None) == fb.ERR_ARG
+    # matrix-core launches check the arm and M
+    h.plan, h.units_dense, h.units_general, h.grid_dense, h.grid_general, h.M = P, 10, 0, 4, 0, 16
+    assert lib.fp8blk_gemv_mfma_sequence(ctypes.byref(h), None) == fb.ERR_ARG  # arm is ARM_FP8
+    h.arm = fb.ARM_FP8_MFMA
+    assert lib.bf16_gemv_twin_mfma_sequence(ctypes.byref(h), None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_sequence(ctypes.byref(h), None) == fb.ERR_ARG
+    h.M = 17
+    assert lib.fp8blk_gemv_mfma_sequence(ctypes.byref(h), None) == fb.ERR_ARG
+    h.M, h.units_dense = 16, 0
+    assert lib.fp8blk_gemv_mfma_sequence(ctypes.byref(h), None) == fb.ERR_ARG
