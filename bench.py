@@ -186,6 +186,33 @@ def time_sweep(torch, fb, sw, steps, warmup, mode, grouped=False):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
+def time_panel_sequence(torch, fb, inputs, sw, M, steps, warmup, dev):
+    """The sweep's linears with an M-row verify panel (one bf16 panel per
+    distinct cols, N(0,1)) as one matrix-core sequence launch per step; returns
+    seconds for `steps` launches, HIP events on the launching stream."""
+    xs = {c: inputs.device_x(c, M, 7 + c, dev) for c in sorted({l["spec"].cols for l in sw.lins})}
+    ys = [torch.empty((M, l["spec"].rows), dtype=torch.float32, device=dev) for l in sw.lins]
+    if sw.arm == "fp8":
+        seq = fb.fp8blk_sequence_init(fb.ARM_FP8_MFMA, [(l["w"], l["grid"], xs[l["spec"].cols], y)
+                                                        for l, y in zip(sw.lins, ys)])
+        call = fb.prepared("fp8blk_gemv_mfma_sequence", seq)
+    else:
+        seq = fb.fp8blk_sequence_init(fb.ARM_BF16_MFMA, [(l["w"], xs[l["spec"].cols], y) for l, y in zip(sw.lins, ys)])
+        call = fb.prepared("bf16_gemv_twin_mfma_sequence", seq)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run_calls([call])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run_calls([call])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del seq
+    return e0.elapsed_time(e1) / 1e3
+
+
 def time_sequence(torch, fb, sw, steps, warmup):
     """Time `steps` sequence launches back to back on the current stream,
     HIP events around all of them (on that stream)."""
@@ -536,6 +563,18 @@ def main():
                                      "note": "q+kv and gate+up each in one launch, graph-replayed"}
     launch_modes["per_linear_shapes"] = shapes
 
+    # The verify step's dense traffic: the same linears with an M-row panel, as
+    # one matrix-core sequence launch.
+    panel = {}
+    if not args.no_extra:
+        for M in (2, 4, 8, 16):
+            t = time_panel_sequence(torch, fb, inputs, sw, M, args.steps, args.warmup, dev)
+            v = sw.weight_bytes * args.steps / t / 1e9
+            panel[str(M)] = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                             "ms_per_step": round(t / args.steps * 1e3, 4)}
+            log(f"sweep with an M={M} verify panel, matrix-core sequence launch: {t / args.steps * 1e3:.4f} ms/step, "
+                f"{v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak)")
+
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -583,6 +622,9 @@ def main():
         "roofline": roof,
         "launch_modes": launch_modes,
         "cpu_baseline": cpu,
+        "panel_sweep_matrix_core_sequence": ({"workload": "the same 259 linears, each with an M-row bf16 verify "
+                                                          "panel, one matrix-core sequence launch per step",
+                                              "by_M": panel} if panel else None),
         "m16_verify_12288x4096": ({"vector_arm": {"weight_GBps": m16[0]["weight_GBps"],
                                                   "pct_hbm_peak": m16[0]["pct_hbm_peak"], "us": m16[0]["us"]},
                                    "matrix_core_arm": {"weight_GBps": m16[0]["mfma_GBps"],

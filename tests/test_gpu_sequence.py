@@ -125,3 +125,50 @@ def test_sequence_whole_step_sweep(gpu):
             y64, yabs = oracle.gemv_f64(ch, sh, xh, nthreads=8)
             assert_within_tolerance(yw, y64, yabs, what=f"{spec.name} rows {r0}..")
     say(f"  {len(lins)} sweep linears equal their single calls")
+
+
+def test_sequence_graph_replays(gpu):
+    """A sequence launch captured in a HIP graph: every replay, with eager work
+    and synchronizations between the replays, gives the eager bits (vector and
+    matrix-core arms)."""
+    from gpu_util import DEV, u32
+    members = _members([(300, 4096), (257, 2048), (13, 1024), (77, 4112)], 31)
+    y_eager = [torch.full((1, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    y_graph = [torch.full((1, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    s_e = fb.fp8blk_sequence_init(fb.ARM_FP8, [(D.codes, D.grid, D.x, y) for (_, D, _), y in zip(members, y_eager)])
+    s_g = fb.fp8blk_sequence_init(fb.ARM_FP8, [(D.codes, D.grid, D.x, y) for (_, D, _), y in zip(members, y_graph)])
+    x16 = [torch.from_numpy(inputs.host_linear(D.rows, D.cols, 16, 9 + k).x.view(np.int16)).to(DEV)
+           for k, (_, D, _) in enumerate(members)]
+    m_e = [torch.full((16, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    m_g = [torch.full((16, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    sm_e = fb.fp8blk_sequence_init(fb.ARM_FP8_MFMA, [(D.codes, D.grid, x, y) for (_, D, _), x, y in
+                                                     zip(members, x16, m_e)])
+    sm_g = fb.fp8blk_sequence_init(fb.ARM_FP8_MFMA, [(D.codes, D.grid, x, y) for (_, D, _), x, y in
+                                                     zip(members, x16, m_g)])
+    call_v = fb.prepared("fp8blk_gemv_sequence", s_g)
+    call_m = fb.prepared("fp8blk_gemv_mfma_sequence", sm_g)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        call_v2 = fb.prepared("fp8blk_gemv_sequence", s_g, stream=cap)
+        call_m2 = fb.prepared("fp8blk_gemv_mfma_sequence", sm_g, stream=cap)
+        assert call_v2() == 0 and call_m2() == 0
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for y in y_graph + m_g:
+            y.fill_(float("nan"))
+        # eager work between replays: change x, run the eager sequences
+        for _, D, _ in members:
+            D.x.copy_(torch.roll(D.x, shifts=rep + 1, dims=1))
+        for x in x16:
+            x.copy_(torch.roll(x, shifts=1, dims=0))
+        fb.fp8blk_gemv_sequence(s_e)
+        fb.fp8blk_gemv_mfma_sequence(sm_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(y_eager + m_e, y_graph + m_g):
+            assert np.array_equal(u32(a), u32(b)), rep
+    assert call_v() == 0 and call_m() == 0
