@@ -374,6 +374,62 @@ def per_config(torch, fb, inputs, dev, reps):
     return rows_out
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def prefill(torch, fb, inputs, dev, reps):
+    """The staged prefill path (bf16 dequant slab + one hipBLASLt GEMM) on the
+    decode-shape and projection linears with a 2048-token bf16 panel: time per
+    call of the whole staged path and of the GEMM alone (events around `reps`
+    back-to-back calls), as TFLOP/s of 2 N rows cols against the bf16
+    matrix-core peak."""
+    import numpy as np
+    out = []
+    rng = np.random.default_rng(11)
+    N = 2048
+    stream = torch.cuda.current_stream()
+    pp = inputs.projection_pair()
+    for L in (inputs.decode_shape(), pp[0], pp[2]):
+        codes = torch.from_numpy(L.codes).to(dev)
+        scales = torch.from_numpy(L.scales).to(dev)
+        grid = torch.empty(scales.shape, dtype=torch.float32, device=dev)
+        fb.fp8blk_load_check(codes, scales, grid, torch.empty(256, dtype=torch.uint8, device=dev))
+        x = torch.from_numpy(inputs.round_to_bf16_bits(rng.standard_normal((N, L.cols), dtype=np.float32))
+                             .view(np.int16)).to(dev)
+        y = torch.empty((N, L.rows), dtype=torch.float32, device=dev)
+        ws = torch.empty(fb.fp8blk_workspace_bytes(fb.OP_GEMM_STAGED, L.rows, L.cols, N), dtype=torch.uint8,
+                         device=dev)
+        wst = torch.empty(fb.fp8blk_workspace_bytes(fb.OP_BF16_GEMM, L.rows, L.cols, N), dtype=torch.uint8,
+                          device=dev)
+        slab = torch.empty((L.rows, L.cols), dtype=torch.int16, device=dev)
+        fb.fp8blk_dequant_bf16(codes, grid, slab)
+        staged = fb.prepared("fp8blk_gemm_staged", codes, grid, x, y, ws)
+        gemm = fb.prepared("bf16_gemm_twin", slab, x, y, wst)
+        res = {}
+        for name, call in (("staged", staged), ("gemm", gemm)):
+            run_calls([call] * 3)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_calls([call] * reps)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / 1e3 / reps
+        flops = 2.0 * N * L.rows * L.cols
+        r = {"linear": L.name, "rows": L.rows, "cols": L.cols, "tokens": N,
+             "staged_us": round(res["staged"] * 1e6, 1), "gemm_us": round(res["gemm"] * 1e6, 1),
+             "staged_TFLOPs": round(flops / res["staged"] / 1e12, 1),
+             "gemm_TFLOPs": round(flops / res["gemm"] / 1e12, 1),
+             "gemm_frac_of_bf16_peak": round(flops / res["gemm"] / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3),
+             "dequant_share": round(1 - res["gemm"] / res["staged"], 3)}
+        out.append(r)
+        log(f"  prefill {L.name} {L.rows}x{L.cols} N={N}: staged {r['staged_us']} us ({r['staged_TFLOPs']} TFLOP/s), "
+            f"GEMM alone {r['gemm_us']} us ({r['gemm_TFLOPs']} TFLOP/s, {100 * r['gemm_frac_of_bf16_peak']:.1f}% of "
+            f"the bf16 matrix-core peak), dequant share {100 * r['dequant_share']:.1f}%")
+        del codes, scales, grid, x, y, ws, wst, slab
+    return out
+
+
 def cpu_baseline(torch, sw, oracle):
     """The oracle's double GEMV (O6) over the sweep's linears, timed on the host
     cores (inputs copied to host memory first, outside the timing)."""
@@ -585,9 +641,12 @@ def main():
         del src, dst
 
     extra = None
+    pre = None
     if not args.no_extra:
         log("per-config cold-cache table")
         extra = per_config(torch, fb, inputs, dev, args.reps)
+        log("staged prefill GEMM")
+        pre = prefill(torch, fb, inputs, dev, args.reps)
 
     cpu = None
     if not args.no_cpu and args.arm == "fp8":
@@ -631,6 +690,7 @@ def main():
                                                        "pct_hbm_peak": m16[0]["mfma_pct_hbm_peak"],
                                                        "us": m16[0]["mfma_us"]}} if m16 else None),
         "per_config": extra,
+        "prefill_staged": pre,
     }
     print(json.dumps(out), flush=True)
 

@@ -21,15 +21,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
 
 OK, ERR_ARG, ERR_SCALE_FF, ERR_NAN_CODE, ERR_INEXACT, ERR_WORKSPACE, ERR_HIP = range(7)
-OP_LOAD_CHECK, OP_DEQUANT_BF16, OP_GEMV, OP_BF16_TWIN = range(4)
-MIN_COLS, MAX_COLS, MAX_M = 16, 65536, 16
+OP_LOAD_CHECK, OP_DEQUANT_BF16, OP_GEMV, OP_BF16_TWIN, OP_GEMM_STAGED, OP_BF16_GEMM = range(6)
+MIN_COLS, MAX_COLS, MAX_M, MAX_PANEL = 16, 65536, 16, 65536
 
 # Every symbol include/fp8blk.h declares.
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
            "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
            "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
-           "bf16_gemv_twin_mfma_sequence")
+           "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin")
 MAX_GROUP = 8
 MAX_SEQ = 65536
 ARM_FP8, ARM_BF16, ARM_FP8_MFMA, ARM_BF16_MFMA = 0, 1, 2, 3
@@ -101,6 +101,10 @@ def load():
     L.fp8blk_gemv_sequence.restype = i32
     L.bf16_gemv_twin_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
     L.bf16_gemv_twin_sequence.restype = i32
+    L.fp8blk_gemm_staged.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, sz, vp]
+    L.fp8blk_gemm_staged.restype = i32
+    L.bf16_gemm_twin.argtypes = [vp, i64, i64, vp, i64, vp, vp, sz, vp]
+    L.bf16_gemm_twin.restype = i32
     L.fp8blk_gemv_mfma_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
     L.fp8blk_gemv_mfma_sequence.restype = i32
     L.bf16_gemv_twin_mfma_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
@@ -359,6 +363,36 @@ def bf16_gemv_twin_mfma_sequence(seq, stream=None, check=True):
     return st
 
 
+def fp8blk_gemm_staged(codes, scales_f32, x_bf16, y, ws, stream=None, check=True):
+    """Prefill: y[N, rows] = x[N, cols] . dequant(codes, scales)^T via the bf16
+    slab (written into ws) and one library GEMM. ws: fp8blk_workspace_bytes(
+    OP_GEMM_STAGED, rows, cols, N) bytes, 256-byte aligned."""
+    import torch
+    rows, cols = codes.shape
+    wsp, wsb = _ws(ws)
+    st = load().fp8blk_gemm_staged(_dev(codes, (torch.uint8,), "codes"),
+                                   _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
+                                   _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
+                                   _dev(y, (torch.float32,), "y"), wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemm_staged")
+    return st
+
+
+def bf16_gemm_twin(w_bf16, x_bf16, y, ws, stream=None, check=True):
+    """The same GEMM over a bf16 slab the caller holds. ws: fp8blk_workspace_bytes(
+    OP_BF16_GEMM, rows, cols, N) bytes, 256-byte aligned."""
+    import torch
+    rows, cols = w_bf16.shape
+    wsp, wsb = _ws(ws)
+    st = load().bf16_gemm_twin(_dev(w_bf16, _bf16_dtypes(), "w_bf16"), rows, cols,
+                               _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
+                               _dev(y, (torch.float32,), "y"), wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "bf16_gemm_twin")
+    return st
+
+
 def raw_call(name: str, *args):
     """Call an exported symbol with raw ctypes arguments (pointers as ints).
     Used by tests that exercise the C ABI's argument checks directly."""
@@ -399,8 +433,20 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         members, x = tensors_and_sizes
         arr, cols = _group(members, name == "fp8blk_gemv_grouped")
         args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], s)
+    elif name == "fp8blk_gemm_staged":
+        codes, grid, x, y, ws = tensors_and_sizes
+        rows, cols = codes.shape
+        wsp, wsb = _ws(ws)
+        args = (_dev(codes, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows, cols,
+                _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], _dev(y, (torch.float32,), "y"), wsp, wsb, s)
+    elif name == "bf16_gemm_twin":
+        w, x, y, ws = tensors_and_sizes
+        rows, cols = w.shape
+        wsp, wsb = _ws(ws)
+        args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
+                _dev(y, (torch.float32,), "y"), wsp, wsb, s)
     elif name in ("fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
-                  "bf16_gemv_twin_mfma_sequence"):
+                  "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin"):
         (seq,) = tensors_and_sizes
         args = (ctypes.byref(seq.handle), s)
     else:

@@ -31,8 +31,12 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+# hipBLASLt provides the staged prefill path's bf16 GEMM.
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def command(out: str = LIB) -> list[str]:
-    return [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out, *sources()]
+    return [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out, *sources(), *LIBS]
 
 
 def build(verbose: bool = False) -> str:

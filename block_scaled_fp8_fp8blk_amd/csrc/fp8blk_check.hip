@@ -149,12 +149,14 @@ extern "C" const char* fp8blk_strerror(int status) {
 }
 
 extern "C" size_t fp8blk_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M) {
-    (void)rows; (void)cols; (void)M;
+    (void)M;
     switch (op) {
         case FP8BLK_OP_LOAD_CHECK: return 256;  // three 64-bit verdict slots, padded
         case FP8BLK_OP_DEQUANT_BF16: return 0;
         case FP8BLK_OP_GEMV: return 0;
         case FP8BLK_OP_BF16_TWIN: return 0;
+        case FP8BLK_OP_GEMM_STAGED:
+        case FP8BLK_OP_BF16_GEMM: return gemm_workspace_bytes(op, rows, cols);
         default: return 0;
     }
 }

@@ -1,0 +1,162 @@
+// Staged prefill GEMM: the FP8-blk weights dequantized to the bf16 slab, then
+// one library GEMM with f32 accumulation and f32 output.
+//
+// "Module dsv4_gpu" page (memra-engine docs), rungs paragraph and DenseBf16:
+// under the FP8 arm, prefill stages the dense weights as a transient bf16
+// copy and runs the bf16 GEMM over it; the slab holds exactly the values the
+// GEMV decodes in registers, so decode and prefill read the same weights. A
+// prefill panel has many rows (tokens), so the product is bound by the matrix
+// cores, not by the weight bytes: the dequant pass (1 B read and 2 B written
+// per weight) is a small part of the work for long panels, and the GEMM is a
+// plain bf16 x bf16 -> f32 GEMM, which hipBLASLt provides for gfx950.
+//
+// y[N, rows] = x[N, cols] . slab[rows, cols]^T. In hipBLASLt's column-major
+// terms: D (rows x N, ld rows) = A^T . B with A = the slab read as a
+// (cols x rows, ld cols) matrix and B = x read as (cols x N, ld cols).
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "fp8blk.h"
+#include "fp8blk_host.hpp"
+
+namespace fp8blk {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// One hipBLASLt handle per device, and the algorithm the library's heuristic
+// picks for each problem shape, created on first use and kept for the
+// process (the handle holds host-side state only; every device buffer is the
+// caller's).
+struct LtCache {
+    std::mutex mu;
+    hipblasLtHandle_t handle[kMaxDevices] = {};
+    std::map<std::tuple<int, int64_t, int64_t, int64_t, size_t>, hipblasLtMatmulAlgo_t> algo;
+};
+LtCache& cache() {
+    static LtCache c;
+    return c;
+}
+
+struct LtGemm {
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+    ~LtGemm() {
+        if (a) hipblasLtMatrixLayoutDestroy(a);
+        if (b) hipblasLtMatrixLayoutDestroy(b);
+        if (c) hipblasLtMatrixLayoutDestroy(c);
+        if (desc) hipblasLtMatmulDescDestroy(desc);
+    }
+};
+
+int lt_gemm(const uint16_t* w, int64_t rows, int64_t cols, const uint16_t* x, int64_t N, float* y, void* ws,
+            size_t ws_bytes, hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8BLK_ERR_HIP;
+    LtCache& C = cache();
+    hipblasLtHandle_t h;
+    {
+        std::lock_guard<std::mutex> lock(C.mu);
+        if (!C.handle[dev] && hipblasLtCreate(&C.handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
+            C.handle[dev] = nullptr;
+            return FP8BLK_ERR_HIP;
+        }
+        h = C.handle[dev];
+    }
+    LtGemm g;
+    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    if (hipblasLtMatmulDescCreate(&g.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&g.a, HIP_R_16BF, (uint64_t)cols, (uint64_t)rows, cols) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&g.b, HIP_R_16BF, (uint64_t)cols, (uint64_t)N, cols) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&g.c, HIP_R_32F, (uint64_t)rows, (uint64_t)N, rows) != HIPBLAS_STATUS_SUCCESS)
+        return FP8BLK_ERR_HIP;
+    hipblasLtMatmulAlgo_t algo;
+    const auto key = std::make_tuple(dev, rows, cols, N, ws_bytes);
+    bool have = false;
+    {
+        std::lock_guard<std::mutex> lock(C.mu);
+        auto it = C.algo.find(key);
+        if (it != C.algo.end()) {
+            algo = it->second;
+            have = true;
+        }
+    }
+    if (!have) {
+        hipblasLtMatmulPreference_t pref = nullptr;
+        if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return FP8BLK_ERR_HIP;
+        const uint64_t wsb = ws_bytes;
+        hipblasLtMatmulHeuristicResult_t res[1];
+        int got = 0;
+        const bool ok =
+            hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
+                                                  sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatmulAlgoGetHeuristic(h, g.desc, g.a, g.b, g.c, g.c, pref, 1, res, &got) ==
+                HIPBLAS_STATUS_SUCCESS &&
+            got >= 1 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= ws_bytes;
+        hipblasLtMatmulPreferenceDestroy(pref);
+        if (!ok) return FP8BLK_ERR_HIP;
+        algo = res[0].algo;
+        std::lock_guard<std::mutex> lock(C.mu);
+        C.algo[key] = algo;
+    }
+    const float alpha = 1.0f, beta = 0.0f;
+    if (hipblasLtMatmul(h, g.desc, &alpha, w, g.a, x, g.b, &beta, y, g.c, y, g.c, &algo, ws, ws_bytes, s) !=
+        HIPBLAS_STATUS_SUCCESS)
+        return FP8BLK_ERR_HIP;
+    return launch_status();
+}
+
+constexpr size_t kGemmWs = size_t(32) << 20;  // library GEMM workspace
+constexpr size_t kAlign = 256;
+
+size_t slab_bytes(int64_t rows, int64_t cols) {
+    return ((size_t)rows * (size_t)cols * 2 + kAlign - 1) / kAlign * kAlign;
+}
+
+bool gemm_args_ok(const void* w, int64_t rows, int64_t cols, const uint16_t* x, int64_t N, const float* y) {
+    return w && x && y && shape_ok(rows, cols) && N >= 1 && N <= FP8BLK_MAX_PANEL && aligned(w, 16) &&
+           aligned(x, 16) && aligned(y, 16);
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int op, int64_t rows, int64_t cols) {
+    if (!shape_ok(rows, cols)) return 0;
+    return op == FP8BLK_OP_GEMM_STAGED ? slab_bytes(rows, cols) + kGemmWs : kGemmWs;
+}
+
+}  // namespace fp8blk
+
+using namespace fp8blk;
+
+extern "C" int fp8blk_gemm_staged(const uint8_t* codes, const float* scales_f32, int64_t rows, int64_t cols,
+                                  const uint16_t* x_bf16, int64_t N, float* y, void* ws, size_t ws_bytes,
+                                  fp8blk_stream_t stream) {
+    if (!gemm_args_ok(codes, rows, cols, x_bf16, N, y) || !scales_f32 || !aligned(scales_f32, 4))
+        return FP8BLK_ERR_ARG;
+    const size_t need = gemm_workspace_bytes(FP8BLK_OP_GEMM_STAGED, rows, cols);
+    if (!ws || ws_bytes < need || !aligned(ws, kAlign)) return FP8BLK_ERR_WORKSPACE;
+    uint16_t* slab = static_cast<uint16_t*>(ws);
+    const int st = fp8blk_dequant_bf16(codes, scales_f32, rows, cols, slab, stream);
+    if (st != FP8BLK_OK) return st;
+    const size_t sb = slab_bytes(rows, cols);
+    return lt_gemm(slab, rows, cols, x_bf16, N, y, static_cast<char*>(ws) + sb, ws_bytes - sb,
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int bf16_gemm_twin(const uint16_t* w_bf16, int64_t rows, int64_t cols, const uint16_t* x_bf16, int64_t N,
+                              float* y, void* ws, size_t ws_bytes, fp8blk_stream_t stream) {
+    if (!gemm_args_ok(w_bf16, rows, cols, x_bf16, N, y)) return FP8BLK_ERR_ARG;
+    if (!ws || ws_bytes < gemm_workspace_bytes(FP8BLK_OP_BF16_GEMM, rows, cols) || !aligned(ws, kAlign))
+        return FP8BLK_ERR_WORKSPACE;
+    return lt_gemm(w_bf16, rows, cols, x_bf16, N, y, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}

@@ -50,4 +50,8 @@ inline int device_cus() {
 // the same for all) into host (plan_bytes(n) bytes); returns its work units.
 int64_t mf_sequence_plan(unsigned char* host, bool fp8, const fp8blk_seq_linear* linears, int n);
 
+// Workspace of the staged prefill GEMM (fp8blk_gemm.hip): the bf16 slab (for
+// FP8BLK_OP_GEMM_STAGED) plus the library GEMM's workspace; 0 for a bad shape.
+size_t gemm_workspace_bytes(int op, int64_t rows, int64_t cols);
+
 }  // namespace fp8blk

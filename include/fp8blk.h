@@ -96,13 +96,16 @@ typedef enum fp8blk_op {
     FP8BLK_OP_LOAD_CHECK = 0,
     FP8BLK_OP_DEQUANT_BF16 = 1,
     FP8BLK_OP_GEMV = 2,
-    FP8BLK_OP_BF16_TWIN = 3
+    FP8BLK_OP_BF16_TWIN = 3,
+    FP8BLK_OP_GEMM_STAGED = 4,
+    FP8BLK_OP_BF16_GEMM = 5
 } fp8blk_op;
 
 /* Shape limits. cols must be a multiple of 16 (one 16-byte code load). */
 #define FP8BLK_MIN_COLS 16
 #define FP8BLK_MAX_COLS 65536
 #define FP8BLK_MAX_M 16
+#define FP8BLK_MAX_PANEL 65536 /* rows of a prefill panel (fp8blk_gemm_staged) */
 
 /* Version of this ABI; bumped on any incompatible change. */
 int fp8blk_abi_version(void);
@@ -320,6 +323,38 @@ int fp8blk_gemv_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int bf16_gemv_twin_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int fp8blk_gemv_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int bf16_gemv_twin_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
+
+/*
+ * Staged prefill GEMM ("Module dsv4_gpu" page, rungs paragraph and
+ * DenseBf16: under the FP8 arm, prefill stages the dense weights as a
+ * transient bf16 copy and runs the bf16 GEMM over it). For a prefill panel of
+ * N tokens:
+ *   y[n, r] = sum over c of slab[r, c] * x[n, c],  slab = fp8blk_dequant_bf16(codes, scales)
+ * fp8blk_gemm_staged writes the slab into the first part of ws (exact, as
+ * fp8blk_dequant_bf16) and then runs one hipBLASLt bf16 x bf16 -> f32 GEMM
+ * (f32 accumulation) over it; bf16_gemm_twin runs the same GEMM over a slab
+ * the caller holds. On weights accepted by fp8blk_load_check the two give
+ * identical bits (the same GEMM on the same values). The GEMM's summation
+ * order is the library's: every product is exact in f32 (bf16 x bf16), so
+ * |y - exact| <= gamma_cols * sum_c |w x| (gamma_k = k u / (1 - k u),
+ * u = 2^-24) whatever the order; the typical error is far smaller.
+ *   codes, w_bf16, x_bf16 [N, cols], y [N, rows]: device, 16-byte aligned;
+ *   scales_f32: device, 4-byte aligned; shape limits as for fp8blk_gemv;
+ *   1 <= N <= FP8BLK_MAX_PANEL.
+ *   ws: device, 256-byte aligned, >= fp8blk_workspace_bytes(FP8BLK_OP_GEMM_STAGED
+ *     or FP8BLK_OP_BF16_GEMM, rows, cols, N) bytes: the slab (staged only)
+ *     plus 32 MB for the library GEMM.
+ * The library keeps one hipBLASLt handle per device and the algorithm chosen
+ * for each shape, for the life of the process (host state; the first call of
+ * a shape queries the library's heuristic). Enqueued on `stream`; does not
+ * wait. Errors: FP8BLK_ERR_ARG, FP8BLK_ERR_WORKSPACE, FP8BLK_ERR_HIP (also
+ * when the library has no algorithm for the shape).
+ */
+int fp8blk_gemm_staged(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,
+                       const uint16_t *x_bf16, int64_t N, float *y, void *ws, size_t ws_bytes,
+                       fp8blk_stream_t stream);
+int bf16_gemm_twin(const uint16_t *w_bf16, int64_t rows, int64_t cols, const uint16_t *x_bf16, int64_t N,
+                   float *y, void *ws, size_t ws_bytes, fp8blk_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -50,6 +50,12 @@ def test_host_helpers(lib):
     assert fb.fp8blk_workspace_bytes(fb.OP_LOAD_CHECK, 4096, 4096) >= 24
     assert fb.fp8blk_workspace_bytes(fb.OP_GEMV, 4096, 4096, 16) == 0
     assert fb.fp8blk_workspace_bytes(77, 1, 16) == 0
+    # the staged prefill GEMM: the bf16 slab (256-byte aligned size) plus 32 MB for the library GEMM
+    lt = 32 << 20
+    assert fb.fp8blk_workspace_bytes(fb.OP_BF16_GEMM, 4096, 4096, 2048) == lt
+    assert fb.fp8blk_workspace_bytes(fb.OP_GEMM_STAGED, 4096, 4096, 2048) == 2 * 4096 * 4096 + lt
+    assert fb.fp8blk_workspace_bytes(fb.OP_GEMM_STAGED, 3, 16, 1) == 256 + lt
+    assert fb.fp8blk_workspace_bytes(fb.OP_GEMM_STAGED, 0, 16, 1) == 0
 
 
 P = 1 << 12  # a fake, 4096-aligned address: never dereferenced, every call below refuses first
@@ -175,3 +181,19 @@ def test_sequence_refusals(lib):
     assert lib.fp8blk_gemv_mfma_sequence(ctypes.byref(h), None) == fb.ERR_ARG
     h.M, h.units_dense = 16, 0
     assert lib.fp8blk_gemv_mfma_sequence(ctypes.byref(h), None) == fb.ERR_ARG
+
+
+def test_gemm_refusals(lib):
+    big = 1 << 40
+    ws = fb.fp8blk_workspace_bytes(fb.OP_GEMM_STAGED, 4, 16, 1)
+    assert lib.fp8blk_gemm_staged(P, P, 4, 16, P, 1, P, P, ws - 1, None) == fb.ERR_WORKSPACE
+    assert lib.fp8blk_gemm_staged(P, P, 4, 16, P, 1, P, None, ws, None) == fb.ERR_WORKSPACE
+    assert lib.fp8blk_gemm_staged(P, P, 4, 16, P, 1, P, P + 16, ws, None) == fb.ERR_WORKSPACE
+    for bad in ((P, P, 4, 16, P, 0, P), (P, P, 4, 16, P, fb.MAX_PANEL + 1, P), (P, P, 4, 24, P, 1, P),
+                (P + 8, P, 4, 16, P, 1, P), (P, None, 4, 16, P, 1, P), (P, P + 2, 4, 16, P, 1, P),
+                (P, P, 4, 16, P + 8, 1, P), (P, P, 4, 16, P, 1, P + 4), (None, P, 4, 16, P, 1, P)):
+        assert lib.fp8blk_gemm_staged(*bad, P, big, None) == fb.ERR_ARG, bad
+    wt = fb.fp8blk_workspace_bytes(fb.OP_BF16_GEMM, 4, 16, 1)
+    assert lib.bf16_gemm_twin(P, 4, 16, P, 1, P, P, wt - 1, None) == fb.ERR_WORKSPACE
+    assert lib.bf16_gemm_twin(P, 4, 16, P, 0, P, P, wt, None) == fb.ERR_ARG
+    assert lib.bf16_gemm_twin(P + 2, 4, 16, P, 1, P, P, wt, None) == fb.ERR_ARG
