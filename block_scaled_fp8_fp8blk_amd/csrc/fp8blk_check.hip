@@ -100,25 +100,44 @@ __global__ void k_codes(const uint8_t* __restrict__ codes, const uint8_t* __rest
 }
 
 // bf16 dequant slab: one 16-code chunk per thread per step. The f32 product
-// e4m3 * scale of an accepted element is a bf16 value, so its low half is
-// zero and the bf16 pattern is the high half (v_perm_b32 gathers two high
-// halves into one dword, lower column in the low half).
-__global__ void k_dequant(const uint8_t* __restrict__ codes, const float* __restrict__ grid,
-                          int64_t rows, int64_t K, int64_t GC, uint16_t* __restrict__ out) {
-    const int64_t cpr = K / kChunk;
-    const int64_t n = rows * cpr;
-    for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < n;
-         g += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = g / cpr, c0 = (g - r * cpr) * kChunk;
-        const uint4 v = *reinterpret_cast<const uint4*>(codes + r * K + c0);
-        const float s = grid[(r >> 7) * GC + (c0 >> 7)];
-        float w[16];
-        decode16_fp8(v, s, w);
-        uint32_t o[8];
-        for (int k = 0; k < 8; ++k) o[k] = __builtin_amdgcn_perm(as_u32(w[2 * k + 1]), as_u32(w[2 * k]), 0x07060302u);
-        uint4* dst = reinterpret_cast<uint4*>(out + r * K + c0);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+// gfx950's v_cvt_scalef32_pk_bf16_fp8 forms e4m3(code) * scale and rounds it
+// to bf16: for an accepted element the product is a bf16 value, so the result
+// is exact (the exhaustive code x scale table is checked against the oracle).
+// Each thread takes U chunks of 16 codes per pass, chunks blockDim apart, all
+// loads first; IDX is the index type (32-bit while rows * cols / 16 fits).
+template <typename IDX, int U>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ grid, IDX rows, IDX cpr, IDX GC,
+                                                      uint16_t* __restrict__ out) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const IDX n = rows * cpr;
+    const IDX step = (IDX)gridDim.x * blockDim.x * U;
+    for (IDX g0 = (IDX)blockIdx.x * blockDim.x * U + threadIdx.x; g0 < n; g0 += step) {
+        uint4 v[U];
+        float sc[U];
+        IDX r[U], c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const IDX g = min(g0 + (IDX)u * blockDim.x, n - 1);  // a chunk past the end repeats the last one
+            r[u] = g / cpr;
+            c[u] = (g - r[u] * cpr) * kChunk;
+            v[u] = load_stream16(codes + (int64_t)g * kChunk);
+            sc[u] = load_global_f32(grid + (r[u] >> 7) * GC + (c[u] >> 7));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (g0 + (IDX)u * blockDim.x >= n) break;
+            const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t o[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[k], sc[u], false));
+                o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[k], sc[u], true));
+            }
+            uint4* dst = reinterpret_cast<uint4*>(out + ((int64_t)r[u] * cpr * kChunk + c[u]));
+            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
     }
 }
 
@@ -198,8 +217,14 @@ extern "C" int fp8blk_dequant_bf16(const uint8_t* codes, const float* scales_f32
         return FP8BLK_ERR_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const int64_t GC = ceil_div(cols, kBlock);
-    k_dequant<<<grid_for(rows * (cols / kChunk), 16384), kThreads, 0, s>>>(codes, scales_f32, rows, cols, GC,
-                                                                           out_bf16);
+    const int64_t GC = ceil_div(cols, kBlock), cpr = cols / kChunk, n = rows * cpr;
+    constexpr int U = 4;
+    const int blocks = grid_for(ceil_div(n, U), 8192);
+    if (n < (INT64_C(1) << 31))
+        k_dequant<uint32_t, U><<<blocks, kThreads, 0, s>>>(codes, scales_f32, (uint32_t)rows, (uint32_t)cpr,
+                                                           (uint32_t)GC, out_bf16);
+    else
+        k_dequant<uint64_t, U><<<blocks, kThreads, 0, s>>>(codes, scales_f32, (uint64_t)rows, (uint64_t)cpr,
+                                                           (uint64_t)GC, out_bf16);
     return launch_status();
 }

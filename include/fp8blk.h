@@ -345,10 +345,13 @@ int bf16_gemv_twin_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t str
  *     or FP8BLK_OP_BF16_GEMM, rows, cols, N) bytes: the slab (staged only)
  *     plus 32 MB for the library GEMM.
  * The library keeps one hipBLASLt handle per device and the algorithm chosen
- * for each shape, for the life of the process (host state; the first call of
- * a shape queries the library's heuristic). Enqueued on `stream`; does not
- * wait. Errors: FP8BLK_ERR_ARG, FP8BLK_ERR_WORKSPACE, FP8BLK_ERR_HIP (also
- * when the library has no algorithm for the shape).
+ * for each shape, for the life of the process (host state). The first call of
+ * a shape times the library's best 8 heuristic candidates on `stream` and
+ * keeps the fastest: that call waits for the stream (under graph capture it
+ * does not time, and takes the first candidate without keeping it). Later
+ * calls are enqueued on `stream` and do not wait. Errors: FP8BLK_ERR_ARG,
+ * FP8BLK_ERR_WORKSPACE, FP8BLK_ERR_HIP (also when the library has no
+ * algorithm for the shape).
  */
 int fp8blk_gemm_staged(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,
                        const uint16_t *x_bf16, int64_t N, float *y, void *ws, size_t ws_bytes,
