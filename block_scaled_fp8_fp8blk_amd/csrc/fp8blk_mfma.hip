@@ -379,7 +379,8 @@ struct alignas(64) MfSeqLin {
     float* y;            // f32 [M, rows]
     int64_t rows;
     int32_t K, M, GC, nwin;
-    int64_t pad;
+    int32_t vec_store;   // 1: y is 16-byte aligned and rows % 4 == 0 (each panel row's outputs store 4 at a time)
+    int32_t pad;
 };
 static_assert(sizeof(MfSeqLin) == kSeqDescBytes, "descriptor size of the plan");
 
@@ -523,19 +524,27 @@ __device__ __forceinline__ void mf_seq_compute(MfWindow<KIND, TILES, XR> b, int 
                                                                  acc[t], 0, 0, 0);
 }
 
+// Lane (n, kg) = (l % 16, l / 16) holds D[4 kg + e][n], e = 0..3: rows
+// 4 kg .. 4 kg + 3 of the tile for panel row n, four consecutive outputs of
+// y[n]. When the linear allows it they leave as one 16-byte store (a tile is
+// one store instruction writing 16 panel rows x 64 bytes), else one by one.
 template <int TILES>
 __device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int lane, v4f* acc) {
-    // lane l holds D[4 (l / 16) + e][l % 16]: row 4 (l / 16) + e of the tile, panel row l % 16
     const int n = lane & 15, kg = lane >> 4;
     const int64_t r0 = v * (TILES * kTile);
-    if (n < d.M) {
+    if (n >= d.M) return;
+    float* yrow = d.y + (int64_t)n * d.rows;
 #pragma unroll
-        for (int t = 0; t < TILES; ++t)
+    for (int t = 0; t < TILES; ++t) {
+        const int64_t r = r0 + t * kTile + 4 * kg;
+        if (d.vec_store && r + 3 < d.rows) {
+            typedef __attribute__((address_space(1))) v4f global_v4f;
+            *(global_v4f*)(yrow + r) = acc[t];
+        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t r = r0 + t * kTile + 4 * kg + e;
-                if (r < d.rows) store_global_f32(d.y + (int64_t)n * d.rows + r, acc[t][e]);
-            }
+            for (int e = 0; e < 4; ++e)
+                if (r + e < d.rows) store_global_f32(yrow + r + e, acc[t][e]);
+        }
     }
 }
 
@@ -659,6 +668,7 @@ int64_t mf_sequence_plan(unsigned char* host, bool fp8, const fp8blk_seq_linear*
         s.M = (int32_t)l.M;
         s.GC = (int32_t)ceil_div(l.cols, kBlock);
         s.nwin = s.GC;
+        s.vec_store = (l.rows % 4 == 0 && aligned(l.y, 16)) ? 1 : 0;
         s.pad = 0;
         pre[j + 1] = pre[j] + ceil_div(l.rows, (int64_t)kTile * mf_seq_tiles((int)l.M));
     }

@@ -172,3 +172,47 @@ def test_sequence_graph_replays(gpu):
         for a, b in zip(y_eager + m_e, y_graph + m_g):
             assert np.array_equal(u32(a), u32(b)), rep
     assert call_v() == 0 and call_m() == 0
+
+
+def test_sequence_many_small_linears(gpu):
+    """600 small linears of mixed shapes (most of them ragged, so both launches
+    run; a wave's next unit often lies several linears ahead): every output
+    equals its single call, on both vector arms and the matrix-core arm."""
+    from gpu_util import DEV, DevLinear, u32
+    rng = np.random.default_rng(17)
+    cols_choices = [16, 48, 512, 1024, 1040, 2048, 3072, 4096]
+    members = []
+    for k in range(600):
+        rows = int(rng.integers(1, 40))
+        cols = int(cols_choices[rng.integers(0, len(cols_choices))])
+        L = inputs.host_linear(rows, cols, 4, 1000 + k)
+        D = DevLinear(L.codes, L.scales, L.x)
+        assert D.check(check=False) == (0, -1)
+        members.append((L, D, D.slab()))
+    x1 = [D.x[:1].contiguous() for _, D, _ in members]
+    y8 = [torch.full((1, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    yt = [torch.full((1, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    ym = [torch.full((4, D.rows), float("nan"), device=DEV) for _, D, _ in members]
+    s8 = fb.fp8blk_sequence_init(fb.ARM_FP8, [(D.codes, D.grid, x, y) for (_, D, _), x, y in zip(members, x1, y8)])
+    st = fb.fp8blk_sequence_init(fb.ARM_BF16, [(s, x, y) for (_, D, s), x, y in zip(members, x1, yt)])
+    sm = fb.fp8blk_sequence_init(fb.ARM_FP8_MFMA, [(D.codes, D.grid, D.x, y) for (_, D, _), y in zip(members, ym)])
+    assert s8.handle.units_general > 0 and s8.handle.units_dense > 0
+    fb.fp8blk_gemv_sequence(s8)
+    fb.bf16_gemv_twin_sequence(st)
+    fb.fp8blk_gemv_mfma_sequence(sm)
+    torch.cuda.synchronize()
+    from gpu_util import assert_within_tolerance
+    for (L, D, _), x, a, b, m in zip(members, x1, y8, yt, ym):
+        ref = D.gemv(x)
+        assert np.array_equal(u32(a), u32(ref)), (D.rows, D.cols)
+        assert np.array_equal(u32(b), u32(ref)), (D.rows, D.cols)
+        # the matrix-core sequence: its own order; within the tolerance of the
+        # double GEMV, and the single matrix-core call's bits where that call
+        # takes each row in one part (at most 7 column windows)
+        mh = m.cpu().numpy()
+        y64, yabs = oracle.gemv_f64(L.codes, L.scales, L.x, nthreads=8)
+        assert_within_tolerance(mh, y64, yabs, what=f"mfma sequence {D.rows}x{D.cols}")
+        if D.cols <= 896:
+            one = torch.full_like(m, float("nan"))
+            fb.fp8blk_gemv_mfma(D.codes, D.grid, D.x, one)
+            assert np.array_equal(u32(mh), u32(one)), (D.rows, D.cols)
