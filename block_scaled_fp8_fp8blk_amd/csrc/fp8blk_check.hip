@@ -109,7 +109,6 @@ template <typename IDX, int U>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ grid, IDX rows, IDX cpr, IDX GC,
                                                       uint16_t* __restrict__ out) {
-    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
     const IDX n = rows * cpr;
     const IDX step = (IDX)gridDim.x * blockDim.x * U;
     for (IDX g0 = (IDX)blockIdx.x * blockDim.x * U + threadIdx.x; g0 < n; g0 += step) {

@@ -65,7 +65,7 @@ int tune(hipblasLtHandle_t h, const LtGemm& g, const hipblasLtMatmulHeuristicRes
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return -1;
     if (hipEventCreate(&e1) != hipSuccess) {
-        hipEventDestroy(e0);
+        (void)hipEventDestroy(e0);
         return -1;
     }
     const float alpha = 1.0f, beta = 0.0f;
@@ -92,8 +92,8 @@ int tune(hipblasLtHandle_t h, const LtGemm& g, const hipblasLtMatmulHeuristicRes
             best = i;
         }
     }
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     return fail ? -1 : best;
 }
 

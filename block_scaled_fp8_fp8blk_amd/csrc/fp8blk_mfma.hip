@@ -387,7 +387,6 @@ static_assert(sizeof(MfSeqLin) == kSeqDescBytes, "descriptor size of the plan");
 // Row tiles per unit: 4 for panels of 8 rows or more (the tiles share a
 // wave's activation loads), else 2. Measured on the whole-step sweep.
 constexpr int mf_seq_tiles(int M) { return M >= 8 ? 4 : 2; }
-constexpr int kMfSeqDepth = 2;  // register sets: windows loaded ahead + 1
 
 // Per-unit addressing, computed once when a wave starts a unit: wave-uniform
 // bases plus 32-bit lane offsets, so that a window's loads need no vector
@@ -548,56 +547,59 @@ __device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int l
     }
 }
 
-// DEPTH register sets in turn: the loads of the window DEPTH - 1 ahead are
-// issued before the matrix work of the current one.
-template <int KIND, int TILES, int XR, int DEPTH>
+// One window of the pipeline: issue the loads of window `nxt` (computing its
+// unit's addressing when it starts a unit), then the matrix work of window
+// `cur`, then, at the end of cur's unit, its stores.
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_seq_stage(const MfPos& nxt, MfUnit<TILES, XR>& un, MfWindow<KIND, TILES, XR>& into,
+                                             const MfPos& cur, const MfWindow<KIND, TILES, XR>& have, int lane,
+                                             v4f* acc) {
+    if (nxt.win == 0 && nxt.more) mf_unit<KIND>(un, nxt.d, nxt.v, lane);
+    mf_seq_issue(into, un, nxt.d.K, nxt.win, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next window's loads ahead of this window's matrix work
+    mf_seq_compute(have, cur.d.K, cur.win, lane, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cur.win + 1 == cur.d.nwin) {
+        mf_seq_store<TILES>(cur.d, cur.v, lane, acc);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+// Two register sets in turn: the loads of the next window are issued before
+// the matrix work of the current one.
+template <int KIND, int TILES, int XR>
 __global__ __launch_bounds__(kSeqWaves * kLanes) void k_mfseq(const MfSeqLin* __restrict__ lin,
                                                                const int64_t* __restrict__ pre, int64_t total) {
     using Win = MfWindow<KIND, TILES, XR>;
     using Unit = MfUnit<TILES, XR>;
     const int lane = threadIdx.x % kLanes;
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
-    MfPos pos[DEPTH];
-    Unit unit[DEPTH];
-    pos[0].u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-    if (pos[0].u >= total) return;
-    pos[0].win = 0;
-    pos[0].j = 0;
-    pos[0].more = true;
-    while (pos[0].u >= pre[pos[0].j + 1]) ++pos[0].j;
-    pos[0].d = lin[pos[0].j];
-    pos[0].v = pos[0].u - pre[pos[0].j];
-    mf_unit<KIND>(unit[0], pos[0].d, pos[0].v, lane);
+    MfPos p0;
+    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    if (p0.u >= total) return;
+    p0.win = 0;
+    p0.j = 0;
+    p0.more = true;
+    while (p0.u >= pre[p0.j + 1]) ++p0.j;
+    p0.d = lin[p0.j];
+    p0.v = p0.u - pre[p0.j];
+    Unit ua, ub;
+    mf_unit<KIND>(ua, p0.d, p0.v, lane);
     v4f acc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    Win buf[DEPTH];
-    mf_seq_issue(buf[0], unit[0], pos[0].d.K, pos[0].win, lane);
-#pragma unroll
-    for (int d = 1; d + 1 < DEPTH; ++d) {
-        pos[d] = mf_next(pos[d - 1], lin, pre, W, total);
-        unit[d] = unit[d - 1];
-        if (pos[d].win == 0) mf_unit<KIND>(unit[d], pos[d].d, pos[d].v, lane);
-        mf_seq_issue(buf[d], unit[d], pos[d].d.K, pos[d].win, lane);
-    }
+    Win a, b;
+    mf_seq_issue(a, ua, p0.d.K, p0.win, lane);
     for (;;) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int nd = (d + DEPTH - 1) % DEPTH, pd = (nd + DEPTH - 1) % DEPTH;
-            pos[nd] = mf_next(pos[pd], lin, pre, W, total);
-            unit[nd] = unit[pd];
-            if (pos[nd].win == 0 && pos[nd].more) mf_unit<KIND>(unit[nd], pos[nd].d, pos[nd].v, lane);
-            mf_seq_issue(buf[nd], unit[nd], pos[nd].d.K, pos[nd].win, lane);
-            __builtin_amdgcn_sched_barrier(0);  // keep the newest loads ahead of this window's matrix work
-            mf_seq_compute(buf[d], pos[d].d.K, pos[d].win, lane, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            if (pos[d].win + 1 == pos[d].d.nwin) {
-                mf_seq_store<TILES>(pos[d].d, pos[d].v, lane, acc);
-#pragma unroll
-                for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-            if (!pos[(d + 1) % DEPTH].more) return;
-        }
+        const MfPos p1 = mf_next(p0, lin, pre, W, total);
+        ub = ua;
+        mf_seq_stage(p1, ub, b, p0, a, lane, acc);
+        if (!p1.more) break;
+        p0 = mf_next(p1, lin, pre, W, total);
+        ua = ub;
+        mf_seq_stage(p0, ua, a, p1, b, lane, acc);
+        if (!p0.more) break;
     }
 }
 
@@ -614,13 +616,13 @@ int mf_seq_launch(const fp8blk_sequence* seq, int arm, hipStream_t s) {
     (void)hipGetLastError();
     const int M = seq->M;
     if (M >= 8)
-        k_mfseq<KIND, mf_seq_tiles(8), 4, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(8), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
     else if (M > 2)
-        k_mfseq<KIND, mf_seq_tiles(3), 4, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(3), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
     else if (M == 2)
-        k_mfseq<KIND, mf_seq_tiles(2), 2, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(2), 2><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
     else
-        k_mfseq<KIND, mf_seq_tiles(1), 1, kMfSeqDepth><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(1), 1><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
     return launch_status();
 }
 

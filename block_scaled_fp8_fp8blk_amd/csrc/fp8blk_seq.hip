@@ -4,9 +4,11 @@
 // "Struct Dsv4Gpu" page, field dense_fp8: a decode step reads its dense
 // linears as stored, and their weights are most of the step's bytes. Small
 // linears launched one at a time leave HBM idle while each launch ramps up
-// and drains; here the whole list is one stream of 4-chunk steps that every
-// wave walks in list order, so the loads of the next linear are in flight
-// while the current one finishes, and there is one launch for the list.
+// and drains; here the whole list is one stream of steps that every wave
+// walks in list order, so the loads of the next linear are in flight while
+// the current one finishes, and there is one launch for the list (two when
+// some linears have ragged rows or cols: those units take a second launch of
+// the same kernel with clamped addresses).
 //
 // Work: a step is S chunk slots per lane (S = 16 on the FP8 arm, 8 on the
 // twin; 16 KB of weights per wave either way). Linear j is cut into units of
@@ -17,7 +19,8 @@
 // in segment order. Units are numbered across the list in order, and wave w
 // of the W waves in the grid takes units w, w + W, w + 2W, ...: the waves
 // move through the list together. Each wave issues the next step's loads
-// (codes, x chunks, block scales) before it computes the current step.
+// (codes, x chunks, block scales) phase by phase, each phase just before it
+// computes the same phase of the current step.
 //
 // Arithmetic per output (the order the library header documents):
 //   lane partial = FMA chain over the chunk's 16 columns from +0.0;
