@@ -525,8 +525,10 @@ __device__ __forceinline__ void mf_seq_compute(MfWindow<KIND, TILES, XR> b, int 
 
 // Lane (n, kg) = (l % 16, l / 16) holds D[4 kg + e][n], e = 0..3: rows
 // 4 kg .. 4 kg + 3 of the tile for panel row n, four consecutive outputs of
-// y[n]. When the linear allows it they leave as one 16-byte store (a tile is
-// one store instruction writing 16 panel rows x 64 bytes), else one by one.
+// y[n]. When the linear allows it they leave as one 16-byte nontemporal store
+// (a tile is one store instruction writing 16 panel rows x 64 bytes; with a
+// 16-row panel the outputs are 1/57 of the bytes the step reads, and the
+// nontemporal hint measured +2% there), else one by one.
 template <int TILES>
 __device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int lane, v4f* acc) {
     const int n = lane & 15, kg = lane >> 4;
@@ -538,7 +540,7 @@ __device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int l
         const int64_t r = r0 + t * kTile + 4 * kg;
         if (d.vec_store && r + 3 < d.rows) {
             typedef __attribute__((address_space(1))) v4f global_v4f;
-            *(global_v4f*)(yrow + r) = acc[t];
+            __builtin_nontemporal_store(acc[t], (global_v4f*)(yrow + r));
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
