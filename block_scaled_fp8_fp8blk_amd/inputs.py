@@ -202,3 +202,108 @@ def device_x(cols: int, M: int, seed: int, device):
     g.manual_seed(seed)
     v = torch.randn((M, cols), generator=g, dtype=torch.float32, device=device)
     return v.to(torch.bfloat16).view(torch.int16)
+
+
+# ---------------------------------------------------------------------------
+# Native expert arm: FP4 (e2m1) weight slabs in the MXFP4 and NVFP4 recipes.
+#   codes  uint8 [rows, cols/2]   two e2m1 codes per byte (even column in the
+#                                 low nibble), drawn as uniform random bytes
+#   scales uint8 [rows, cols/B]   MXFP4 (B = 32): e8m0 codes; NVFP4 (B = 16):
+#                                 e4m3 codes, non-negative and finite
+#   global_scale                  NVFP4's per-tensor f32 output scale (1.0 for
+#                                 MXFP4)
+#   x      uint16 [M, cols]       bf16 activations, N(0,1)
+# Draw order from one generator: codes, scales, global scale, x.
+# ---------------------------------------------------------------------------
+
+MXFP4, NVFP4 = 0, 1
+FP4_BLOCK = {MXFP4: 32, NVFP4: 16}
+FP4_NAMES = {MXFP4: "mxfp4", NVFP4: "nvfp4"}
+# Default scale-code ranges: MXFP4 2^-9 .. 2^-1; NVFP4 e4m3 bytes 0x28 .. 0x58
+# (2^-2 .. 2^4, every mantissa).
+FP4_SCALE_RANGE = {MXFP4: (118, 126), NVFP4: (0x28, 0x58)}
+
+
+@dataclass
+class Fp4Linear:
+    fmt: int
+    rows: int
+    cols: int
+    codes: np.ndarray
+    scales: np.ndarray
+    global_scale: float
+    x: np.ndarray
+    seed: int
+    name: str = ""
+
+    @property
+    def M(self) -> int:
+        return self.x.shape[0]
+
+    def weight_bytes(self) -> int:
+        return fp4_weight_bytes(self.fmt, self.rows, self.cols)
+
+
+def fp4_weight_bytes(fmt: int, rows: int, cols: int) -> int:
+    """Packed codes plus the block-scale bytes: what the expert GEMV must read."""
+    return rows * cols // 2 + rows * (cols // FP4_BLOCK[fmt])
+
+
+def host_fp4_linear(fmt: int, rows: int, cols: int, M: int, seed: int, *, scale_lo: int | None = None,
+                    scale_hi: int | None = None, name: str = "") -> Fp4Linear:
+    """One synthetic FP4 expert linear drawn on the host. NVFP4's global
+    scale is a float32 drawn uniformly in [2^-7, 2^-5)."""
+    B = FP4_BLOCK[fmt]
+    assert cols % B == 0
+    lo, hi = FP4_SCALE_RANGE[fmt]
+    lo = lo if scale_lo is None else scale_lo
+    hi = hi if scale_hi is None else scale_hi
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.int64).astype(np.uint8)
+    scales = rng.integers(lo, hi + 1, size=(rows, cols // B), dtype=np.int64).astype(np.uint8)
+    g = rng.uniform(1.0, 4.0) * 2.0 ** -7
+    g = float(np.float32(g)) if fmt == NVFP4 else 1.0
+    xv = rng.standard_normal((M, cols), dtype=np.float32)
+    return Fp4Linear(fmt, rows, cols, codes, scales, g, round_to_bf16_bits(xv), seed, name)
+
+
+def device_fp4_linear(fmt: int, rows: int, cols: int, seed: int, device):
+    """Codes and scales of an FP4 expert linear drawn on ``device`` with
+    torch's seeded generator (same distributions as host_fp4_linear).
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/B])."""
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    codes = torch.randint(0, 256, (rows, cols // 2), generator=g, dtype=torch.int32, device=device).to(torch.uint8)
+    lo, hi = FP4_SCALE_RANGE[fmt]
+    scales = torch.randint(lo, hi + 1, (rows, cols // FP4_BLOCK[fmt]), generator=g, dtype=torch.int32,
+                           device=device).to(torch.uint8)
+    return codes, scales
+
+
+# Routed-expert projections of one decode step: per layer, the activated
+# experts' gate, up (intermediate 2048 from hidden 4096) and down.
+EXPERT_LAYERS = 43
+EXPERTS_PER_TOKEN = 8
+EXPERT_SHAPES = (("gate", 2048, 4096), ("up", 2048, 4096), ("down", 4096, 2048))
+
+
+@dataclass
+class ExpertSweepLinear:
+    name: str
+    rows: int
+    cols: int
+    seed: int
+
+
+def expert_sweep_plan(layers: int = EXPERT_LAYERS, experts: int = EXPERTS_PER_TOKEN) -> list:
+    """The routed-expert sweep of one decode step: layers x activated experts x
+    (gate, up, down); linear i is drawn with seed 20000 + i."""
+    out = []
+    i = 0
+    for layer in range(layers):
+        for e in range(experts):
+            for nm, r, c in EXPERT_SHAPES:
+                out.append(ExpertSweepLinear(f"L{layer}.e{e}.{nm}", r, c, 20000 + i))
+                i += 1
+    return out
