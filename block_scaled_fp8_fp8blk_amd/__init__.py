@@ -20,7 +20,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
 
-OK, ERR_ARG, ERR_SCALE_FF, ERR_NAN_CODE, ERR_INEXACT, ERR_WORKSPACE, ERR_HIP = range(7)
+OK, ERR_ARG, ERR_SCALE_FF, ERR_NAN_CODE, ERR_INEXACT, ERR_WORKSPACE, ERR_HIP, ERR_BAD_SCALE = range(8)
 OP_LOAD_CHECK, OP_DEQUANT_BF16, OP_GEMV, OP_BF16_TWIN, OP_GEMM_STAGED, OP_BF16_GEMM = range(6)
 MIN_COLS, MAX_COLS, MAX_M, MAX_PANEL = 16, 65536, 16, 65536
 
@@ -29,10 +29,13 @@ EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "f
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
            "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
            "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
-           "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin")
+           "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin", "fp8blk_act_quant",
+           "fp4_load_check", "fp4_dequant_bf16", "fp4_expert_gemv", "fp4_expert_sequence_init",
+           "fp4_expert_sequence")
 MAX_GROUP = 8
 MAX_SEQ = 65536
-ARM_FP8, ARM_BF16, ARM_FP8_MFMA, ARM_BF16_MFMA = 0, 1, 2, 3
+ARM_FP8, ARM_BF16, ARM_FP8_MFMA, ARM_BF16_MFMA, ARM_MXFP4, ARM_NVFP4 = 0, 1, 2, 3, 4, 5
+FMT_MXFP4, FMT_NVFP4 = 0, 1
 
 
 class Linear(ctypes.Structure):
@@ -46,6 +49,13 @@ class SeqLinear(ctypes.Structure):
     """fp8blk_seq_linear: one member of a sequence launch."""
     _fields_ = [("w", ctypes.c_void_p), ("scales_f32", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("M", ctypes.c_int64), ("x_bf16", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class Fp4ExpertLinear(ctypes.Structure):
+    """fp4_expert_linear: one member of an expert sequence launch."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_float),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("M", ctypes.c_int64), ("xq", ctypes.c_void_p),
+                ("xs", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class SequenceHandle(ctypes.Structure):
@@ -109,6 +119,17 @@ def load():
     L.fp8blk_gemv_mfma_sequence.restype = i32
     L.bf16_gemv_twin_mfma_sequence.argtypes = [ctypes.POINTER(SequenceHandle), vp]
     L.bf16_gemv_twin_mfma_sequence.restype = i32
+    f32 = ctypes.c_float
+    L.fp8blk_act_quant.argtypes, L.fp8blk_act_quant.restype = [vp, i64, i64, vp, vp, vp], i32
+    L.fp4_load_check.argtypes = [i32, vp, vp, i64, i64, vp, sz, ctypes.POINTER(i64), vp]
+    L.fp4_load_check.restype = i32
+    L.fp4_dequant_bf16.argtypes, L.fp4_dequant_bf16.restype = [i32, vp, vp, i64, i64, vp, vp], i32
+    L.fp4_expert_gemv.argtypes = [i32, vp, vp, f32, i64, i64, vp, vp, i64, vp, vp]
+    L.fp4_expert_gemv.restype = i32
+    L.fp4_expert_sequence_init.argtypes = [ctypes.POINTER(SequenceHandle), i32, ctypes.POINTER(Fp4ExpertLinear),
+                                           i32, vp, sz, vp]
+    L.fp4_expert_sequence_init.restype = i32
+    L.fp4_expert_sequence.argtypes, L.fp4_expert_sequence.restype = [ctypes.POINTER(SequenceHandle), vp], i32
     _lib = L
     return L
 
@@ -393,6 +414,98 @@ def bf16_gemm_twin(w_bf16, x_bf16, y, ws, stream=None, check=True):
     return st
 
 
+# --- native expert arm ---------------------------------------------------------
+
+def fp8blk_act_quant(x_bf16, xq, xs, stream=None, check=True):
+    """act_quant: x [M, cols] bf16 -> xq [M, cols] e4m3 codes, xs [M, ceil(cols/128)]
+    e8m0 scale codes (uint8 tensors)."""
+    import torch
+    M, cols = x_bf16.shape
+    st = load().fp8blk_act_quant(_dev(x_bf16, _bf16_dtypes(), "x_bf16"), M, cols, _dev(xq, (torch.uint8,), "xq"),
+                                 _dev(xs, (torch.uint8,), "xs"), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_act_quant")
+    return st
+
+
+def fp4_load_check(fmt, codes, scales, ws, stream=None, check=True):
+    """Validate an FP4 slab (codes [rows, cols/2], scales [rows, cols/B]).
+    Waits on the stream. Returns (status, first_bad)."""
+    import torch
+    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    wsp, wsb = _ws(ws)
+    fb = ctypes.c_int64(-1)
+    st = load().fp4_load_check(fmt, _dev(codes, (torch.uint8,), "codes"), _dev(scales, (torch.uint8,), "scales"),
+                               rows, cols, wsp, wsb, ctypes.byref(fb), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp4_load_check", fb.value)
+    return st, fb.value
+
+
+def fp4_dequant_bf16(fmt, codes, scales, out_bf16, stream=None, check=True):
+    """The bf16-dequant arm's exact slab [rows, cols]."""
+    import torch
+    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    st = load().fp4_dequant_bf16(fmt, _dev(codes, (torch.uint8,), "codes"), _dev(scales, (torch.uint8,), "scales"),
+                                 rows, cols, _dev(out_bf16, _bf16_dtypes(), "out_bf16"), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp4_dequant_bf16")
+    return st
+
+
+def fp4_expert_gemv(fmt, codes, scales, global_scale, xq, xs, y, stream=None, check=True):
+    """Native expert GEMV: y[M, rows] = g * act(xq, xs) @ fp4(codes, scales)^T."""
+    import torch
+    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    st = load().fp4_expert_gemv(fmt, _dev(codes, (torch.uint8,), "codes"), _dev(scales, (torch.uint8,), "scales"),
+                                float(global_scale), rows, cols, _dev(xq, (torch.uint8,), "xq"),
+                                _dev(xs, (torch.uint8,), "xs"), xq.shape[0], _dev(y, (torch.float32,), "y"),
+                                _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp4_expert_gemv")
+    return st
+
+
+def fp4_expert_sequence_init(fmt, linears, ws=None, stream=None, check=True):
+    """Plan one launch over expert linears [(codes, scales, global_scale, xq, xs, y), ...]
+    (the same M for all). ws: a device uint8 tensor of at least
+    fp8blk_sequence_bytes(n) bytes, or None to allocate one here."""
+    import torch
+    n = len(linears)
+    arr = (Fp4ExpertLinear * max(n, 1))()
+    keep = []
+    for k, (codes, scales, g, xq, xs, y) in enumerate(linears):
+        rows, cols = codes.shape[0], 2 * codes.shape[1]
+        M = xq.shape[0]
+        if xq.numel() != M * cols or y.numel() != M * rows:
+            raise ValueError(f"linear {k}: xq must be [M, cols={cols}] and y [M, rows={rows}]")
+        arr[k].codes = _dev(codes, (torch.uint8,), "codes")
+        arr[k].scales = _dev(scales, (torch.uint8,), "scales")
+        arr[k].global_scale = float(g)
+        arr[k].rows, arr[k].cols, arr[k].M = rows, cols, M
+        arr[k].xq = _dev(xq, (torch.uint8,), "xq")
+        arr[k].xs = _dev(xs, (torch.uint8,), "xs")
+        arr[k].y = _dev(y, (torch.float32,), "y")
+        keep.append((codes, scales, xq, xs, y))
+    if ws is None:
+        nb = fp8blk_sequence_bytes(n) if 1 <= n <= MAX_SEQ else 64
+        ws = torch.empty(max(nb, 64), dtype=torch.uint8, device=(linears[0][0].device if n else "cuda"))
+    wsp, wsb = _ws(ws)
+    h = SequenceHandle()
+    st = load().fp4_expert_sequence_init(ctypes.byref(h), fmt, arr, n, wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp4_expert_sequence_init")
+    return Sequence(h, ws, keep) if st == OK else st
+
+
+def fp4_expert_sequence(seq, stream=None, check=True):
+    """One persistent launch of every linear of an expert sequence."""
+    st = load().fp4_expert_sequence(ctypes.byref(seq.handle), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp4_expert_sequence")
+    return st
+
+
 def raw_call(name: str, *args):
     """Call an exported symbol with raw ctypes arguments (pointers as ints).
     Used by tests that exercise the C ABI's argument checks directly."""
@@ -405,7 +518,8 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
     (benchmarks, graph capture), where per-call tensor inspection would
     dominate. Supported: "fp8blk_gemv" and "fp8blk_gemv_mfma" (codes,
     scales_f32, x_bf16, y), "bf16_gemv_twin" and "bf16_gemv_twin_mfma" (w_bf16,
-    x_bf16, y); no workspace (these need none)."""
+    x_bf16, y), the grouped launches (members, x_bf16), the staged GEMMs (...,
+    ws) and the sequence launches (a planned Sequence)."""
     import torch
     fn = getattr(load(), name)
     s = _stream(stream)
@@ -446,7 +560,7 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
                 _dev(y, (torch.float32,), "y"), wsp, wsb, s)
     elif name in ("fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
-                  "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin"):
+                  "bf16_gemv_twin_mfma_sequence", "fp4_expert_sequence"):
         (seq,) = tensors_and_sizes
         args = (ctypes.byref(seq.handle), s)
     else:

@@ -22,13 +22,6 @@ __global__ void k_verdict_init(unsigned long long* v) {
     if (threadIdx.x < 3) v[threadIdx.x] = kNone;
 }
 
-// e8m0 code -> f32 by building the exponent field: code c >= 1 is the normal
-// f32 2^(c-127) with exponent field c; code 0 is 2^-127, the f32 subnormal
-// with only mantissa bit 22 set.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
-    return as_f32(c ? (c << 23) : 0x00400000u);
-}
-
 __global__ void k_scales(const uint8_t* __restrict__ s, int64_t n, float* __restrict__ out,
                          unsigned long long* __restrict__ verdict) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -162,6 +155,7 @@ extern "C" const char* fp8blk_strerror(int status) {
         case FP8BLK_ERR_INEXACT: return "element is not exactly a bf16 value";
         case FP8BLK_ERR_WORKSPACE: return "workspace missing or too small";
         case FP8BLK_ERR_HIP: return "HIP runtime error";
+        case FP8BLK_ERR_BAD_SCALE: return "negative or NaN NVFP4 block scale refused";
         default: return "unknown status";
     }
 }

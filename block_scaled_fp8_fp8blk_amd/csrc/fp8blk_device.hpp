@@ -16,6 +16,13 @@ constexpr int kBlock = 128;                   // scale block edge
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// e8m0 code -> f32 by building the exponent field: code c >= 1 is the normal
+// f32 2^(c-127) with exponent field c; code 0 is 2^-127, the f32 subnormal
+// with only mantissa bit 22 set. (0xFF, refused at load, would give +inf.)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+    return as_f32(c ? (c << 23) : 0x00400000u);
+}
+
 // Four e4m3 codes (little-endian bytes of d, lowest column first) times a
 // power-of-two block scale. gfx950's v_cvt_pk_f32_fp8 reads OCP E4M3 and is
 // exact (every e4m3 value is an f32 value); the product by a power of two is

@@ -1,0 +1,739 @@
+// Native expert arm: activations quantized to FP8 per 128 elements times FP4
+// (e2m1) expert slabs as stored, in the MXFP4 and NVFP4 recipes, plus the
+// bf16-dequant arm's exact slab.
+//
+// "Module dsv4_gpu" page (memra-engine docs): enum ExpertArm (the native arm
+// multiplies per-128 FP8 activation codes by the NVFP4 / MXFP4 slabs as
+// stored; the other arm dequantizes exactly to bf16 and runs a bf16 GEMM),
+// enum ExpertKind (trunk experts NVFP4, multi-token-prediction experts MXFP4,
+// anything unexpected refused), the rungs paragraph (routed experts
+// dequantize exactly into a bf16 scratch) and enum DecodePath (the routed
+// experts of a projection go out in one launch).
+//
+// The GEMV decodes both operands in registers to exact bf16 values and runs
+// on the bf16 matrix instruction with f32 accumulation (see "The native
+// GEMV" below). gfx950 also has a scaled FP8 x FP4 matrix instruction
+// (v_mfma_scale_f32_16x16x128_f8f6f4); measured on random codes, it keeps
+// only about 13 bits below the largest product of each instruction (errors
+// near 1e-4 of sum |q w|), so it is not used.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <vector>
+
+#include "fp8blk.h"
+#include "fp8blk_device.hpp"
+#include "fp8blk_host.hpp"
+
+namespace fp8blk {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMX = FP8BLK_FMT_MXFP4, kNV = FP8BLK_FMT_NVFP4;
+constexpr int kActBlock = 128;   // activation scale block (columns)
+constexpr int kStepCols = 128;   // columns per matrix instruction
+constexpr int kTileRows = 16;    // weight rows per matrix instruction
+constexpr int kWin = 2;          // instruction steps per pipeline window
+constexpr unsigned long long kNone = ~0ull;
+
+inline int fp4_block(int fmt) { return fmt == kMX ? 32 : 16; }
+
+// ---------------------------------------------------------------------------
+// act_quant
+
+// Exponent e of a block's scale 2^e from the bf16 pattern a of its largest
+// magnitude, a = f * 2^E with f in [1, 2): amax <= 448 * 2^e = 1.75 * 2^(8+e)
+// holds iff E <= 8 + e when f <= 1.75 (mantissa field <= 96), else iff
+// E <= 7 + e. A zero or bf16-subnormal amax is below 448 * 2^-127.
+__device__ __forceinline__ int act_exp(uint32_t a) {
+    const int E = (int)(a >> 7);
+    if (E == 0) return -127;
+    const int e = E - 135 + ((a & 0x7Fu) > 96u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// e4m3 code nearest to h * 2^-e (h a bf16 pattern), ties to even, sign kept,
+// in integer arithmetic. The magnitude is sig * 2^X with sig at most 8 bits;
+// e4m3 steps by 2^(p-3) in the binade [2^p, 2^(p+1)) for p >= -6 and by 2^-9
+// below 2^-6; n counts steps, and for a normal result the code is the binade's
+// first code plus n - 8 (a carry into the next binade lands on its first
+// code). The caller guarantees |h| * 2^-e <= 448.
+__device__ __forceinline__ uint32_t act_code(uint32_t h, int e) {
+    const uint32_t sign = (h >> 8) & 0x80u;
+    const uint32_t E = (h >> 7) & 0xFFu, m = h & 0x7Fu;
+    const uint32_t sig = E ? (0x80u | m) : m;
+    if (sig == 0) return sign;
+    const int X = (E ? (int)E : 1) - 134 - e;
+    const int p = X + (31 - __clz(sig));
+    const int t = p >= -6 ? p - 3 : -9;
+    const int sh = t - X;
+    uint32_t n;
+    if (sh <= 0) {
+        n = sig << -sh;
+    } else if (sh >= 9) {
+        n = 0;  // sig < 2^8: below half a step
+    } else {
+        n = sig >> sh;
+        const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+        if (rem > half || (rem == half && (n & 1u))) ++n;
+    }
+    return sign | (p >= -6 ? (uint32_t)((p + 7) << 3) + n - 8u : n);
+}
+
+// One wave per (row of the panel, 128-column block); two columns per lane.
+__global__ __launch_bounds__(kLanes) void k_act_quant(const uint16_t* __restrict__ x, int64_t cols, int nb,
+                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+    const int b = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+    const int64_t c = (int64_t)b * kActBlock + 2 * lane;
+    const bool in = c < cols;  // cols is even: both columns or neither
+    uint32_t d = 0;
+    if (in) d = *reinterpret_cast<const uint32_t*>(x + (int64_t)m * cols + c);
+    uint32_t a = max(d & 0x7FFFu, (d >> 16) & 0x7FFFu);  // magnitudes order as their patterns
+    for (int h = 32; h >= 1; h >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, h));
+    const int e = act_exp(a);
+    if (in) {
+        const uint32_t lo = act_code(d & 0xFFFFu, e), hi = act_code(d >> 16, e);
+        *reinterpret_cast<uint16_t*>(xq + (int64_t)m * cols + c) = (uint16_t)(lo | (hi << 8));
+    }
+    if (lane == 0) xs[(int64_t)m * nb + b] = (uint8_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Load check and the bf16 slab
+
+__global__ void k_fp4_verdict_init(unsigned long long* v) {
+    if (threadIdx.x < 3) v[threadIdx.x] = kNone;
+}
+
+// One thread per block scale. verdict[0]: lowest MXFP4 scale 0xFF;
+// verdict[1]: lowest NVFP4 scale that is negative or NaN; verdict[2]: lowest
+// element index of an MXFP4 value past bf16's largest finite value
+// (255 * 2^120 ~ 1.99 * 2^127): with scale 2^126 (code 253) the magnitudes 4
+// and 6 overflow, with 2^127 (code 254) also 2 and 3, i.e. magnitude fields
+// >= 6 and >= 4.
+template <int FMT>
+__global__ void k_fp4_check(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
+                            int64_t cols, unsigned long long* __restrict__ verdict) {
+    constexpr int B = FMT == kMX ? 32 : 16;
+    const int64_t per_row = cols / B, n = rows * per_row;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t s = scales[i];
+        if constexpr (FMT == kNV) {
+            if ((s & 0x80u) || s == 0x7Fu) atomicMin(&verdict[1], (unsigned long long)i);
+        } else {
+            if (s == 0xFFu) {
+                atomicMin(&verdict[0], (unsigned long long)i);
+            } else if (s >= 253u) {
+                const uint32_t lim = s == 253u ? 6u : 4u;
+                const int64_t r = i / per_row, c0 = (i - r * per_row) * B;
+                const uint8_t* p = codes + r * (cols / 2) + c0 / 2;
+                for (int k = 0; k < B; ++k) {
+                    const uint32_t nib = (p[k >> 1] >> (4 * (k & 1))) & 15u;
+                    if ((nib & 7u) >= lim) {
+                        atomicMin(&verdict[2], (unsigned long long)(r * cols + c0 + k));
+                        break;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// e4m3 scale bytes 0 and 1 (or 2 and 3) of d as f32 (exact).
+template <bool HI>
+__device__ __forceinline__ v2f e4m3_pair(uint32_t d) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d, 1.0f, HI);
+}
+
+// e2m1 codes of byte B of d (low nibble first) as f32 (exact).
+template <int B>
+__device__ __forceinline__ v2f e2m1_pair(uint32_t d) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, B);
+}
+
+// Eight e2m1 codes (a dword) times the block scale s, as four dwords of two
+// bf16 patterns each (lower column in the low half).
+__device__ __forceinline__ void fp4x8_bf16(uint32_t d, float s, uint32_t* o) {
+    const v2f f[4] = {e2m1_pair<0>(d), e2m1_pair<1>(d), e2m1_pair<2>(d), e2m1_pair<3>(d)};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o[b] = (as_u32(f[b].x * s) >> 16) | (as_u32(f[b].y * s) & 0xFFFF0000u);
+}
+
+// The bf16 slab: one 16-byte chunk (32 codes, one MXFP4 block or two NVFP4
+// blocks) per thread per pass. Each code is widened to f32 by the hardware
+// conversion and multiplied by its block scale in f32: the product is exact
+// (at most 2 x 4 significant bits) and, for a checked slab, a bf16 value, so
+// its bf16 pattern is the high half of the f32.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int64_t rows, int64_t cols,
+                                                     uint16_t* __restrict__ out) {
+    const int64_t cpr = cols / 32, n = rows * cpr;
+    for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < n; g += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = g / cpr, q = g - r * cpr;
+        const uint4 v = load_stream16(codes + g * 16);
+        float s0, s1;
+        if constexpr (FMT == kMX) {
+            s0 = s1 = e8m0_to_f32(scales[r * cpr + q]);
+        } else {
+            const uint32_t two = *reinterpret_cast<const uint16_t*>(scales + r * (cols / 16) + 2 * q);
+            const v2f s = e4m3_pair<false>(two);
+            s0 = s.x;
+            s1 = s.y;
+        }
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fp4x8_bf16(d[k], k < 2 ? s0 : s1, o + 4 * k);  // codes 0-15: first scale
+        uint4* dst = reinterpret_cast<uint4*>(out + r * cols + 32 * q);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+        dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The native GEMV.
+//
+// The products run on gfx950's v_mfma_f32_16x16x32_bf16, which accumulates in
+// f32 (its sums are as accurate as f32 additions; the scaled FP8 x FP4
+// instruction, by contrast, keeps only about 13 bits below its largest
+// product). Both operands are decoded in registers to exact bf16 values:
+//   A (16 rows): the activation codes times their power-of-two scale, through
+//     the scaled conversion v_cvt_scalef32_pk_bf16_fp8;
+//   B (16 columns = 16 weight rows): the e2m1 codes through
+//     v_cvt_scalef32_pk_bf16_fp4, with the MXFP4 block scale folded into that
+//     conversion (a power of two), or unscaled for NVFP4.
+// One instruction takes 32 columns, one MXFP4 block: lane group g (lanes
+// 16g .. 16g+15) supplies the block's columns 8g .. 8g+7 to both operands.
+// A lane loads 16 bytes of its weight row, i.e. one whole 32-column block;
+// a 4 x 4 transpose across the lane groups (two permlane32 and two permlane16
+// swaps) hands each lane its 8 columns of every block of the 128-column step.
+//
+// MXFP4: A row i is token i (rows past M repeat the last token and are not
+// stored); the instruction accumulates every block of every step into the
+// tile's f32 accumulator.
+// NVFP4: the e4m3 block scale of 16 columns cannot be folded into a bf16
+// operand exactly in one conversion, so A row s of token group o is token
+// 8o + s/2 restricted to 16-column block s % 2 of the instruction's 32
+// columns (zeros elsewhere): result element (s, n) is that block's sum for
+// weight row n. Each lane multiplies its results by their e4m3 scales in f32
+// (fused multiply-add) into one accumulator per (token, block parity); a
+// token's two accumulators are added at the end of the unit.
+//
+// A unit is R tiles of 16 weight rows of one linear across all its columns,
+// 128 columns (a step) at a time, kWin steps per pipeline window. Units are
+// numbered over the list in order; wave w of W takes units w, w + W, ...;
+// each wave issues the loads of its next window before the matrix work of
+// the current one.
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+struct alignas(64) ExLin {
+    const uint8_t* w;   // codes [rows, K/2]
+    const uint8_t* sc;  // block scales [rows, K/32] (MXFP4) or [rows, K/16] (NVFP4)
+    const uint8_t* xq;  // activation codes [M, K]
+    const uint8_t* xs;  // activation scale codes [M, K/128]
+    float* y;           // [M, rows]
+    int64_t rows;
+    int32_t K, M;
+    float g;            // output scale
+    int32_t pad;
+};
+static_assert(sizeof(ExLin) == kSeqDescBytes, "descriptor size of the plan");
+
+// A-operand groups (NVFP4: 8 tokens each) and row tiles per unit.
+constexpr int ex_groups(int fmt, int M) { return fmt == kMX || M <= 8 ? 1 : 2; }
+constexpr int ex_tiles(int fmt, int O) { return fmt == kMX ? 4 : (O == 1 ? 4 : 2); }
+
+template <int FMT, int R, int O>
+struct ExUnit {
+    const uint8_t* w;   // the unit's first row of codes
+    const uint8_t* sc;  // its first row of block scales
+    const uint8_t* xq;
+    const uint8_t* xs;
+    uint32_t woff[R];   // lane: byte offset of its row of tile t + its 16-byte block
+    uint32_t soff[R];   // lane: its row's scale bytes of the step
+    uint32_t xoff[O];   // lane: its token's codes + its 8-column group
+    uint32_t xsoff[O];  // lane: its token's row of activation scales
+};
+
+template <int FMT, int R, int O>
+struct ExWin {
+    uint4 b[kWin][R];                            // weight codes: lane group g holds block g of the step
+    typename std::conditional<FMT == kMX, uint32_t, uint2>::type bs[kWin][R];  // the step's block scales
+    uint2 a[kWin][4][O];                         // activation codes: block b, columns 8g .. 8g+7
+    uint32_t as[kWin][O];                        // activation scale code
+};
+
+struct ExPos {
+    int64_t u, v;  // unit (list numbering) and unit within its linear
+    int win, j;
+    bool more;     // false: past the wave's last window (the position repeats the last one)
+    ExLin d;
+};
+
+__device__ __forceinline__ int ex_steps(const ExLin& d) { return d.K / kStepCols; }
+__device__ __forceinline__ int ex_nwin(const ExLin& d) { return (ex_steps(d) + kWin - 1) / kWin; }
+
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_unit(ExUnit<FMT, R, O>& U, const ExLin& d, int64_t v, int lane) {
+    const int64_t r0 = v * (R * kTileRows);
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t half = d.K / 2, sper = d.K / (FMT == kMX ? 32 : 16);
+    U.w = d.w + r0 * half;
+    U.sc = d.sc + r0 * sper;
+    U.xq = d.xq;
+    U.xs = d.xs;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int64_t row = min(r0 + t * kTileRows + n, d.rows - 1) - r0;  // rows past the end repeat the last
+        U.woff[t] = (uint32_t)(row * half + 16 * g);
+        U.soff[t] = (uint32_t)(row * sper);
+    }
+    const int nb = d.K / kActBlock;
+#pragma unroll
+    for (int o = 0; o < O; ++o) {
+        const int tok = min(FMT == kMX ? n : 8 * o + (n >> 1), d.M - 1);
+        U.xoff[o] = (uint32_t)(tok * d.K + 8 * g);
+        U.xsoff[o] = (uint32_t)(tok * nb);
+    }
+}
+
+template <bool LIST>
+__device__ __forceinline__ ExPos ex_next(const ExPos& p, const ExLin* lin, const int64_t* pre, int64_t W,
+                                         int64_t total) {
+    ExPos n = p;
+    if (!p.more) return n;
+    if (p.win + 1 < ex_nwin(p.d)) {
+        n.win = p.win + 1;
+    } else if (p.u + W < total) {
+        n.u = p.u + W;
+        n.v = p.v + W;
+        n.win = 0;
+        if constexpr (LIST) {
+            if (n.u >= pre[n.j + 1]) {
+                do ++n.j;
+                while (n.u >= pre[n.j + 1]);
+                n.d = lin[n.j];
+                n.v = n.u - pre[n.j];
+            }
+        }
+    } else {
+        n.more = false;
+    }
+    return n;
+}
+
+typedef __attribute__((address_space(1))) const uint8_t global_u8;
+typedef __attribute__((address_space(1))) const uint32_t global_u32;
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const v2u global_v2u;
+__device__ __forceinline__ uint2 load_global8(const void* p) {
+    const v2u v = *(global_v2u*)p;
+    return make_uint2(v.x, v.y);
+}
+
+// The loads of window `win` of a unit. A step past the last one (the second
+// step of a last, half-full window) repeats the last step's addresses; its
+// activations are zeroed in ex_compute. No branch: every window issues the
+// same loads.
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O>& b, const ExUnit<FMT, R, O>& U, int steps, int win) {
+#pragma unroll
+    for (int s = 0; s < kWin; ++s) {
+        const int j = min(win * kWin + s, steps - 1);
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            b.b[s][t] = load_stream16(U.w + U.woff[t] + 64 * j);
+            if constexpr (FMT == kMX)
+                b.bs[s][t] = *(global_u32*)(U.sc + U.soff[t] + 4 * j);
+            else
+                b.bs[s][t] = load_global8(U.sc + U.soff[t] + 8 * j);
+        }
+#pragma unroll
+        for (int o = 0; o < O; ++o) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) b.a[s][k][o] = load_global8(U.xq + U.xoff[o] + kStepCols * j + 32 * k);
+            b.as[s][o] = *(global_u8*)(U.xs + U.xsoff[o] + j);
+        }
+    }
+}
+
+// 4 x 4 transpose across the lane groups: on entry lane group g holds block g
+// (dwords 0..3 = its columns 0-7, 8-15, 16-23, 24-31); on exit register k of
+// lane group g holds columns 8g .. 8g+7 of block k.
+__device__ __forceinline__ void transpose_groups(uint4& v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    const auto r = __builtin_amdgcn_permlane16_swap(p[0], q[0], false, false);
+    const auto t = __builtin_amdgcn_permlane16_swap(p[1], q[1], false, false);
+    v = make_uint4(r[0], r[1], t[0], t[1]);
+}
+
+// Eight e2m1 codes -> bf16 operand, times the power-of-two scale s.
+__device__ __forceinline__ v8bf fp4x8_operand(uint32_t d, float s) {
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 1);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 3);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Eight e4m3 codes -> bf16 operand, times the power-of-two scale s.
+__device__ __forceinline__ v8bf fp8x8_operand(uint2 d, float s) {
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.x, s, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.x, s, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.y, s, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.y, s, true);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t d, int k) { return (d >> (8 * k)) & 0xFFu; }
+
+// MXFP4: acc[t] holds token rows x weight rows of tile t. NVFP4: acc[t * O + o]
+// register e holds, for weight row l % 16, the accumulator of token
+// 8o + 2(l/16) + e/2 over the 16-column blocks of parity e % 2.
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_compute(ExWin<FMT, R, O> b, int steps, int win, int lane, v4f* acc) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < kWin; ++s) {
+        const bool live = win * kWin + s < steps;  // wave-uniform
+        // activation operands of the step's four blocks, shared by the R tiles
+        v8bf A[4][O];
+#pragma unroll
+        for (int o = 0; o < O; ++o) {
+            const float sa = e8m0_to_f32(b.as[s][o]);
+            // NVFP4: selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
+            // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
+            const bool keep = live && (FMT == kMX || (g >> 1) == (lane & 1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint2 d = keep ? b.a[s][k][o] : make_uint2(0, 0);
+                A[k][o] = fp8x8_operand(d, sa);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            uint4 w = b.b[s][t];
+            transpose_groups(w);
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+            if constexpr (FMT == kMX) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        A[k][0], fp4x8_operand(wd[k], e8m0_to_f32(byte_of(b.bs[s][t], k))), acc[t], 0, 0, 0);
+            } else {
+                // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + p
+                const v2f s01 = e4m3_pair<false>(b.bs[s][t].x), s23 = e4m3_pair<true>(b.bs[s][t].x);
+                const v2f s45 = e4m3_pair<false>(b.bs[s][t].y), s67 = e4m3_pair<true>(b.bs[s][t].y);
+                const v2f sc[4] = {s01, s23, s45, s67};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const v8bf B = fp4x8_operand(wd[k], 1.0f);
+#pragma unroll
+                    for (int o = 0; o < O; ++o) {
+                        const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][o], B, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                              0, 0, 0);
+                        v4f& a = acc[t * O + o];
+                        a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
+                        a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
+                        a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
+                        a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// y = g * accumulator. MXFP4: lane (n, g) holds tokens 4g .. 4g+3 of weight
+// row n. NVFP4: lane (n, g) holds tokens 8o + 2g and 8o + 2g + 1, each as two
+// block-parity accumulators, added here.
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, const v4f* acc) {
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t r0 = v * (R * kTileRows);
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int64_t row = r0 + t * kTileRows + n;
+        if (row >= d.rows) continue;
+        if constexpr (FMT == kMX) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tok = 4 * g + e;
+                if (tok < d.M) store_global_f32(d.y + (int64_t)tok * d.rows + row, d.g * acc[t][e]);
+            }
+        } else {
+#pragma unroll
+            for (int o = 0; o < O; ++o) {
+                const v4f& a = acc[t * O + o];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int tok = 8 * o + 2 * g + k;
+                    if (tok < d.M) store_global_f32(d.y + (int64_t)tok * d.rows + row, d.g * (a[2 * k] + a[2 * k + 1]));
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_stage(const ExPos& nxt, ExUnit<FMT, R, O>& un, ExWin<FMT, R, O>& into,
+                                         const ExPos& cur, const ExWin<FMT, R, O>& have, int lane, v4f* acc) {
+    constexpr int NACC = R * O;
+    if (nxt.win == 0 && nxt.more) ex_unit(un, nxt.d, nxt.v, lane);
+    ex_issue(into, un, ex_steps(nxt.d), nxt.win);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next window's loads ahead of this window's matrix work
+    ex_compute(have, ex_steps(cur.d), cur.win, lane, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cur.win + 1 == ex_nwin(cur.d)) {
+        ex_store<FMT, R, O>(cur.d, cur.v, lane, acc);
+#pragma unroll
+        for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+// LIST: descriptors from the plan (lin, pre); else the one linear `one`.
+template <int FMT, int R, int O, bool LIST>
+__global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __restrict__ lin,
+                                                                const int64_t* __restrict__ pre, int64_t total,
+                                                                ExLin one) {
+    constexpr int NACC = R * O;
+    using Win = ExWin<FMT, R, O>;
+    using Unit = ExUnit<FMT, R, O>;
+    const int lane = threadIdx.x % kLanes;
+    const int64_t W = (int64_t)gridDim.x * kSeqWaves;
+    ExPos p0;
+    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    if (p0.u >= total) return;
+    p0.win = 0;
+    p0.j = 0;
+    p0.more = true;
+    if constexpr (LIST) {
+        while (p0.u >= pre[p0.j + 1]) ++p0.j;
+        p0.d = lin[p0.j];
+        p0.v = p0.u - pre[p0.j];
+    } else {
+        p0.d = one;
+        p0.v = p0.u;
+    }
+    Unit ua, ub;
+    ex_unit(ua, p0.d, p0.v, lane);
+    v4f acc[NACC];
+#pragma unroll
+    for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    Win a, b;
+    ex_issue(a, ua, ex_steps(p0.d), p0.win);
+    for (;;) {
+        const ExPos p1 = ex_next<LIST>(p0, lin, pre, W, total);
+        ub = ua;
+        ex_stage(p1, ub, b, p0, a, lane, acc);
+        if (!p1.more) break;
+        p0 = ex_next<LIST>(p1, lin, pre, W, total);
+        ua = ub;
+        ex_stage(p0, ua, a, p1, b, lane, acc);
+        if (!p0.more) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+
+int64_t ex_units(int fmt, int64_t rows, int64_t M) {
+    return ceil_div(rows, (int64_t)ex_tiles(fmt, ex_groups(fmt, (int)M)) * kTileRows);
+}
+
+int ex_grid(int64_t units) {
+    const int cus = device_cus();
+    if (cus < 1) return -1;
+    const int64_t cap = (int64_t)cus * kMfSeqBlocksPerCU;
+    const int64_t need = ceil_div(units, kSeqWaves);
+    return (int)(need < cap ? need : cap);
+}
+
+template <int FMT, int O, bool LIST>
+void ex_launch_o(const ExLin* lin, const int64_t* pre, int64_t total, const ExLin& one, int grid, hipStream_t s) {
+    constexpr int R = ex_tiles(FMT, O);
+    constexpr int lds = lds_cap_bytes(kMfSeqBlocksPerCU);
+    k_expert<FMT, R, O, LIST><<<dim3((unsigned)grid), dim3(kSeqWaves * kLanes), lds, s>>>(lin, pre, total, one);
+}
+
+template <bool LIST>
+int ex_launch(int fmt, int M, const ExLin* lin, const int64_t* pre, int64_t total, const ExLin& one, int grid,
+              hipStream_t s) {
+    (void)hipGetLastError();
+    if (fmt == kMX)
+        ex_launch_o<kMX, 1, LIST>(lin, pre, total, one, grid, s);
+    else if (ex_groups(kNV, M) == 1)
+        ex_launch_o<kNV, 1, LIST>(lin, pre, total, one, grid, s);
+    else
+        ex_launch_o<kNV, 2, LIST>(lin, pre, total, one, grid, s);
+    return launch_status();
+}
+
+bool fmt_ok(int fmt) { return fmt == kMX || fmt == kNV; }
+
+// rows >= 1, cols a multiple of `mult` in [mult, FP8BLK_MAX_COLS], rows * cols bounded.
+bool fp4_shape_ok(int64_t rows, int64_t cols, int64_t mult) {
+    if (rows < 1 || cols < mult || cols > FP8BLK_MAX_COLS || cols % mult != 0) return false;
+    return rows <= (INT64_C(1) << 46) / cols;
+}
+
+int ex_check(int fmt, const uint8_t* codes, const uint8_t* scales, float g, int64_t rows, int64_t cols,
+             const uint8_t* xq, const uint8_t* xs, int64_t M, const float* y) {
+    if (!fmt_ok(fmt) || !codes || !scales || !xq || !xs || !y || !fp4_shape_ok(rows, cols, kStepCols) || M < 1 ||
+        M > FP8BLK_MAX_M || !(g - g == 0.0f) || !aligned(codes, 16) || !aligned(xq, 16) || !aligned(y, 4) ||
+        !aligned(scales, fmt == kMX ? 4 : 8))
+        return FP8BLK_ERR_ARG;
+    return FP8BLK_OK;
+}
+
+ExLin ex_desc(const uint8_t* codes, const uint8_t* scales, float g, int64_t rows, int64_t cols, const uint8_t* xq,
+              const uint8_t* xs, int64_t M, float* y) {
+    ExLin d;
+    d.w = codes;
+    d.sc = scales;
+    d.xq = xq;
+    d.xs = xs;
+    d.y = y;
+    d.rows = rows;
+    d.K = (int32_t)cols;
+    d.M = (int32_t)M;
+    d.g = g;
+    d.pad = 0;
+    return d;
+}
+
+}  // namespace
+}  // namespace fp8blk
+
+using namespace fp8blk;
+
+extern "C" int fp8blk_act_quant(const uint16_t* x_bf16, int64_t M, int64_t cols, uint8_t* xq, uint8_t* xs,
+                                fp8blk_stream_t stream) {
+    if (!x_bf16 || !xq || !xs || M < 1 || M > FP8BLK_MAX_M || !shape_ok(1, cols) || !aligned(x_bf16, 16) ||
+        !aligned(xq, 16))
+        return FP8BLK_ERR_ARG;
+    const int nb = (int)ceil_div(cols, kActBlock);
+    (void)hipGetLastError();
+    k_act_quant<<<dim3((unsigned)nb, (unsigned)M), dim3(kLanes), 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        x_bf16, cols, nb, xq, xs);
+    return launch_status();
+}
+
+extern "C" int fp4_load_check(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                              void* ws, size_t ws_bytes, int64_t* first_bad, fp8blk_stream_t stream) {
+    if (first_bad) *first_bad = -1;
+    if (!fmt_ok(fmt) || !codes || !scales || !fp4_shape_ok(rows, cols, 32) || !aligned(codes, 16))
+        return FP8BLK_ERR_ARG;
+    if (!ws || ws_bytes < fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK, rows, cols, 1) || !aligned(ws, 8))
+        return FP8BLK_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    auto* verdict = static_cast<unsigned long long*>(ws);
+    const int64_t nsc = rows * (cols / fp4_block(fmt));
+    int64_t blocks = ceil_div(nsc, 256);
+    if (blocks > 4096) blocks = 4096;
+    (void)hipGetLastError();
+    k_fp4_verdict_init<<<1, 64, 0, s>>>(verdict);
+    if (fmt == kMX)
+        k_fp4_check<kMX><<<(unsigned)blocks, 256, 0, s>>>(codes, scales, rows, cols, verdict);
+    else
+        k_fp4_check<kNV><<<(unsigned)blocks, 256, 0, s>>>(codes, scales, rows, cols, verdict);
+    if (launch_status() != FP8BLK_OK) return FP8BLK_ERR_HIP;
+    unsigned long long host[3] = {kNone, kNone, kNone};
+    if (hipMemcpyAsync(host, verdict, sizeof host, hipMemcpyDeviceToHost, s) != hipSuccess) return FP8BLK_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return FP8BLK_ERR_HIP;
+    const int kinds[3] = {FP8BLK_ERR_SCALE_FF, FP8BLK_ERR_BAD_SCALE, FP8BLK_ERR_INEXACT};
+    for (int k = 0; k < 3; ++k)
+        if (host[k] != kNone) {
+            if (first_bad) *first_bad = (int64_t)host[k];
+            return kinds[k];
+        }
+    return FP8BLK_OK;
+}
+
+extern "C" int fp4_dequant_bf16(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                uint16_t* out_bf16, fp8blk_stream_t stream) {
+    if (!fmt_ok(fmt) || !codes || !scales || !out_bf16 || !fp4_shape_ok(rows, cols, 32) || !aligned(codes, 16) ||
+        !aligned(out_bf16, 16) || (fmt == kNV && !aligned(scales, 2)))
+        return FP8BLK_ERR_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int64_t blocks = ceil_div(rows * (cols / 32), 256);
+    if (blocks > 8192) blocks = 8192;
+    (void)hipGetLastError();
+    if (fmt == kMX)
+        k_fp4_dequant<kMX><<<(unsigned)blocks, 256, 0, s>>>(codes, scales, rows, cols, out_bf16);
+    else
+        k_fp4_dequant<kNV><<<(unsigned)blocks, 256, 0, s>>>(codes, scales, rows, cols, out_bf16);
+    return launch_status();
+}
+
+extern "C" int fp4_expert_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, float global_scale,
+                               int64_t rows, int64_t cols, const uint8_t* xq, const uint8_t* xs, int64_t M, float* y,
+                               fp8blk_stream_t stream) {
+    const int st = ex_check(fmt, codes, scales, global_scale, rows, cols, xq, xs, M, y);
+    if (st != FP8BLK_OK) return st;
+    const int64_t units = ex_units(fmt, rows, M);
+    const int grid = ex_grid(units);
+    if (grid < 1) return FP8BLK_ERR_HIP;
+    const ExLin one = ex_desc(codes, scales, global_scale, rows, cols, xq, xs, M, y);
+    return ex_launch<false>(fmt, (int)M, nullptr, nullptr, units, one, grid, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp4_expert_sequence_init(fp8blk_sequence* seq, int fmt, const fp4_expert_linear* linears, int n,
+                                        void* ws, size_t ws_bytes, fp8blk_stream_t stream) {
+    if (!seq || !fmt_ok(fmt) || !linears || n < 1 || n > FP8BLK_MAX_SEQ) return FP8BLK_ERR_ARG;
+    const int64_t M = linears[0].M;
+    for (int j = 0; j < n; ++j) {
+        const fp4_expert_linear& l = linears[j];
+        if (l.M != M ||
+            ex_check(fmt, l.codes, l.scales, l.global_scale, l.rows, l.cols, l.xq, l.xs, l.M, l.y) != FP8BLK_OK)
+            return FP8BLK_ERR_ARG;
+    }
+    const size_t bytes = plan_bytes(n);
+    if (!ws || ws_bytes < bytes || !aligned(ws, 64)) return FP8BLK_ERR_WORKSPACE;
+    std::vector<unsigned char> host(bytes, 0);
+    ExLin* d = reinterpret_cast<ExLin*>(host.data());
+    int64_t* pre = reinterpret_cast<int64_t*>(host.data() + (size_t)n * sizeof(ExLin));
+    pre[0] = 0;
+    for (int j = 0; j < n; ++j) {
+        const fp4_expert_linear& l = linears[j];
+        d[j] = ex_desc(l.codes, l.scales, l.global_scale, l.rows, l.cols, l.xq, l.xs, l.M, l.y);
+        pre[j + 1] = pre[j] + ex_units(fmt, l.rows, l.M);
+    }
+    const int grid = ex_grid(pre[n]);
+    if (grid < 1) return FP8BLK_ERR_HIP;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(ws, host.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess) return FP8BLK_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return FP8BLK_ERR_HIP;
+    seq->plan = ws;
+    seq->units_dense = pre[n];
+    seq->units_general = 0;
+    seq->n = n;
+    seq->arm = fmt == kMX ? FP8BLK_ARM_MXFP4 : FP8BLK_ARM_NVFP4;
+    seq->grid_dense = grid;
+    seq->grid_general = 0;
+    seq->M = (int32_t)M;
+    seq->reserved = 0;
+    return FP8BLK_OK;
+}
+
+extern "C" int fp4_expert_sequence(const fp8blk_sequence* seq, fp8blk_stream_t stream) {
+    if (!seq || !seq->plan || (seq->arm != FP8BLK_ARM_MXFP4 && seq->arm != FP8BLK_ARM_NVFP4) || seq->n < 1 ||
+        seq->M < 1 || seq->M > FP8BLK_MAX_M || seq->units_dense < 1 || seq->grid_dense < 1)
+        return FP8BLK_ERR_ARG;
+    const ExLin* lin = static_cast<const ExLin*>(seq->plan);
+    const int64_t* pre =
+        reinterpret_cast<const int64_t*>(static_cast<const unsigned char*>(seq->plan) + (size_t)seq->n * sizeof(ExLin));
+    const int fmt = seq->arm == FP8BLK_ARM_MXFP4 ? kMX : kNV;
+    ExLin none{};
+    return ex_launch<true>(fmt, seq->M, lin, pre, seq->units_dense, none, seq->grid_dense,
+                           reinterpret_cast<hipStream_t>(stream));
+}

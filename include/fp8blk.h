@@ -88,7 +88,8 @@ typedef enum fp8blk_status {
     FP8BLK_ERR_NAN_CODE = 3,  /* a weight code is 0x7F or 0xFF (NaN) */
     FP8BLK_ERR_INEXACT = 4,   /* e4m3(code) * scale is not exactly a bf16 value */
     FP8BLK_ERR_WORKSPACE = 5, /* ws is NULL or ws_bytes is below fp8blk_workspace_bytes */
-    FP8BLK_ERR_HIP = 6        /* a HIP launch or runtime call failed */
+    FP8BLK_ERR_HIP = 6,       /* a HIP launch or runtime call failed */
+    FP8BLK_ERR_BAD_SCALE = 7  /* an NVFP4 block scale is negative or NaN */
 } fp8blk_status;
 
 /* Operation ids for fp8blk_workspace_bytes. */
@@ -358,6 +359,152 @@ int fp8blk_gemm_staged(const uint8_t *codes, const float *scales_f32, int64_t ro
                        fp8blk_stream_t stream);
 int bf16_gemm_twin(const uint16_t *w_bf16, int64_t rows, int64_t cols, const uint16_t *x_bf16, int64_t N,
                    float *y, void *ws, size_t ws_bytes, fp8blk_stream_t stream);
+
+/*
+ * Native expert arm ("Module dsv4_gpu" page, enums ExpertArm and ExpertKind,
+ * and the rungs paragraph). Routed experts keep their FP4 weight slabs as
+ * stored; the activation is quantized to FP8 codes per 128 elements, and the
+ * GEMV multiplies the dequantized codes on gfx950's bf16 matrix instruction
+ * (v_mfma_f32_16x16x32_bf16, f32 accumulation): both operands are decoded in
+ * registers to their exact values, which are bf16 values. (gfx950's scaled
+ * FP8 x FP4 instruction was measured to keep only about 13 bits below the
+ * largest product of each instruction, about 1e-4 of sum |q w| on random
+ * codes, so it is not used.) The bf16-dequant arm, the pages' fallback and
+ * A/B reference, is fp4_dequant_bf16 followed by bf16_gemv_twin.
+ *
+ * Formats (this library's reading; the pages name the recipes only):
+ *   e2m1     OCP FP4: sign, 2 exponent bits (bias 1), 1 mantissa bit; values
+ *            +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}; two per byte, the even column in
+ *            the low nibble.
+ *   MXFP4    (FP8BLK_FMT_MXFP4) one e8m0 scale 2^(s-127) per 32 consecutive
+ *            columns of a row; 0xFF is refused.
+ *   NVFP4    (FP8BLK_FMT_NVFP4) one e4m3 scale per 16 consecutive columns of
+ *            a row (non-negative and finite, else refused), plus one f32
+ *            per-tensor scale that multiplies the GEMV output.
+ *   act_quant per row of the activation and per 128 columns: the scale is
+ *            2^e, the smallest power of two with e in [-127, 127] and
+ *            amax <= 448 * 2^e (its e8m0 code e + 127 is stored); each code
+ *            is the e4m3 value nearest to x / 2^e, ties to even, with the
+ *            sign of x.
+ *
+ * Layouts (row-major, contiguous):
+ *   codes        uint8 [rows, cols/2]    packed e2m1
+ *   scales       uint8 [rows, cols/32] (MXFP4) or [rows, cols/16] (NVFP4)
+ *   xq           uint8 [M, cols]         e4m3 activation codes
+ *   xs           uint8 [M, ceil(cols/128)] e8m0 activation scale codes
+ *   w_bf16       uint16 [rows, cols]     bf16 slab (the dequant arm)
+ *   y            float [M, rows]
+ */
+#define FP8BLK_FMT_MXFP4 0
+#define FP8BLK_FMT_NVFP4 1
+#define FP8BLK_ARM_MXFP4 4
+#define FP8BLK_ARM_NVFP4 5
+
+/*
+ * act_quant as above: x_bf16 [M, cols] -> xq [M, cols], xs [M, ceil(cols/128)].
+ * The last block may be shorter than 128 columns. x must be finite (a block
+ * holding an infinity or NaN gives unspecified codes).
+ *   x_bf16, xq: device, 16-byte aligned; xs: device.
+ *   1 <= M <= FP8BLK_MAX_M; 16 <= cols <= FP8BLK_MAX_COLS; cols % 16 == 0.
+ * Bit-exact: every code and scale is decided in integer arithmetic.
+ * Enqueued on `stream`; does not wait.
+ */
+int fp8blk_act_quant(const uint16_t *x_bf16, int64_t M, int64_t cols, uint8_t *xq, uint8_t *xs,
+                     fp8blk_stream_t stream);
+
+/*
+ * Load-time check of an FP4 expert slab ("Module dsv4_gpu" page, ExpertKind:
+ * an unexpected recipe is refused). In this order of precedence:
+ *   FP8BLK_ERR_SCALE_FF   (MXFP4) a scale code is 0xFF;
+ *   FP8BLK_ERR_BAD_SCALE  (NVFP4) a scale code is negative (sign bit set, -0
+ *                         included) or NaN;
+ *                         *first_bad = lowest index into the scale array;
+ *   FP8BLK_ERR_INEXACT    (MXFP4) an element e2m1 * 2^(s-127) is past bf16's
+ *                         largest finite value (scale codes 253 and 254);
+ *                         *first_bad = lowest element index r * cols + c.
+ * Every e2m1 code is finite and every NVFP4 element is a bf16 value, so
+ * nothing else is refused.
+ *   codes: device, 16-byte aligned; scales: device.
+ *   rows >= 1; 32 <= cols <= FP8BLK_MAX_COLS; cols % 32 == 0.
+ *   ws: device, 8-byte aligned, >= fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK,
+ *     ...) bytes. first_bad: HOST pointer, may be NULL.
+ * Waits for `stream` before returning (it returns a verdict).
+ */
+int fp4_load_check(int fmt, const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                   void *ws, size_t ws_bytes, int64_t *first_bad, fp8blk_stream_t stream);
+
+/*
+ * The bf16-dequant arm's slab ("Module dsv4_gpu" page, rungs paragraph:
+ * routed experts dequantize exactly into a bf16 scratch; ExpertArm
+ * Bf16Dequant): out_bf16[r, c] = e2m1(code) * block scale, exact for slabs
+ * accepted by fp4_load_check. NVFP4's per-tensor scale is not applied (it
+ * multiplies the GEMV output). Then bf16_gemv_twin(out_bf16, x) * global
+ * scale is that arm's GEMV.
+ *   codes, out_bf16: device, 16-byte aligned; scales: device (NVFP4: 2-byte
+ *   aligned). Shape as for fp4_load_check. Enqueued on `stream`.
+ */
+int fp4_dequant_bf16(int fmt, const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                     uint16_t *out_bf16, fp8blk_stream_t stream);
+
+/*
+ * The native expert GEMV ("Module dsv4_gpu" page, ExpertArm Native):
+ *   y[m, r] = g * sum over c of q(m, c) * w(r, c)
+ * with q = e4m3(xq[m, c]) * 2^(xs[m][c/128] - 127), w = e2m1(code) * block
+ * scale and g = global_scale (NVFP4's per-tensor scale; pass 1 for MXFP4).
+ * Every product is exact. Order: for each output, the 32-column blocks in
+ * increasing order; MXFP4: each block's 32 products are summed by one matrix
+ * instruction into the f32 accumulator; NVFP4: the instruction sums each
+ * 16-column block, the sum times its e4m3 scale is added (one fused
+ * multiply-add) into one of two f32 accumulators by block parity, and the
+ * two are added at the end. Hence |y - exact| <= gamma_d * |g| * sum_c |q w|,
+ * d = 33 + cols / 32 (gamma_d = d u / (1 - d u), u = 2^-24; below 1e-5 for
+ * cols <= 4096), assuming the instruction's sum of 32 products is no worse
+ * than 32 f32 additions (measured), while every product and partial sum is
+ * in f32's normal range. The instruction may flush bf16 subnormal operands:
+ * activation blocks with amax below about 2^-109 and MXFP4 scale codes below
+ * 2 are outside the bound.
+ *   codes, xq: device, 16-byte aligned; scales: device, 4-byte (MXFP4) or
+ *   8-byte (NVFP4) aligned; xs: device; y: device, 4-byte aligned.
+ *   rows >= 1; 128 <= cols <= FP8BLK_MAX_COLS; cols % 128 == 0;
+ *   1 <= M <= FP8BLK_MAX_M; global_scale finite.
+ * Row m of an M-row call equals the 1-row call on row m, bit for bit.
+ * y must not overlap the inputs. Enqueued on `stream`; does not wait.
+ */
+int fp4_expert_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, float global_scale, int64_t rows,
+                    int64_t cols, const uint8_t *xq, const uint8_t *xs, int64_t M, float *y,
+                    fp8blk_stream_t stream);
+
+/*
+ * One launch per projection over the activated experts ("Module dsv4_gpu"
+ * page, DecodePath: the device path dispatches the routed experts of a
+ * projection in one launch): a list of independent expert linears of one
+ * format, each with its own slab, activation codes and output, run by one
+ * persistent kernel; y_j is fp4_expert_gemv of linear j, bit for bit.
+ * fp4_expert_sequence_init validates the n descriptors (HOST array), writes a
+ * plan of fp8blk_sequence_bytes(n) bytes into the device buffer ws (64-byte
+ * aligned) and fills *seq (arm FP8BLK_ARM_MXFP4 or FP8BLK_ARM_NVFP4); it
+ * copies the plan on `stream` and waits for the copy. The buffers must stay
+ * at the same addresses while seq is used. Every linear takes the same M;
+ * limits and alignment per linear as for fp4_expert_gemv; no linear's y may
+ * overlap any input or another y. fp4_expert_sequence enqueues the list on
+ * `stream` (may be captured in a HIP graph). Errors as for
+ * fp8blk_sequence_init.
+ */
+typedef struct fp4_expert_linear {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    float global_scale;
+    int64_t rows;
+    int64_t cols;
+    int64_t M;
+    const uint8_t *xq;
+    const uint8_t *xs;
+    float *y;
+} fp4_expert_linear;
+
+int fp4_expert_sequence_init(fp8blk_sequence *seq, int fmt, const fp4_expert_linear *linears, int n,
+                             void *ws, size_t ws_bytes, fp8blk_stream_t stream);
+int fp4_expert_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -44,8 +44,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_host_helpers(lib):
     assert fb.fp8blk_abi_version() == 1
-    for st in range(7):
-        assert fb.fp8blk_strerror(st)
+    for st in range(8):
+        assert fb.fp8blk_strerror(st) != "unknown status"
     assert fb.fp8blk_strerror(99) == "unknown status"
     assert fb.fp8blk_workspace_bytes(fb.OP_LOAD_CHECK, 4096, 4096) >= 24
     assert fb.fp8blk_workspace_bytes(fb.OP_GEMV, 4096, 4096, 16) == 0
@@ -197,3 +197,59 @@ def test_gemm_refusals(lib):
     assert lib.bf16_gemm_twin(P, 4, 16, P, 1, P, P, wt - 1, None) == fb.ERR_WORKSPACE
     assert lib.bf16_gemm_twin(P, 4, 16, P, 0, P, P, wt, None) == fb.ERR_ARG
     assert lib.bf16_gemm_twin(P + 2, 4, 16, P, 1, P, P, wt, None) == fb.ERR_ARG
+
+
+def test_expert_arm_refusals(lib):
+    """The native expert arm's entry points refuse bad formats, shapes, M,
+    pointers and global scales before any device work."""
+    MX, NV = fb.FMT_MXFP4, fb.FMT_NVFP4
+    g = lib.fp4_expert_gemv
+    for bad in ((2, P, P, 1.0, 4, 128, P, P, 1, P), (-1, P, P, 1.0, 4, 128, P, P, 1, P),
+                (MX, P, P, 1.0, 0, 128, P, P, 1, P), (MX, P, P, 1.0, 4, 64, P, P, 1, P),
+                (MX, P, P, 1.0, 4, 192, P, P, 1, P), (MX, P, P, 1.0, 4, 65536 + 128, P, P, 1, P),
+                (MX, P, P, 1.0, 4, 128, P, P, 0, P), (MX, P, P, 1.0, 4, 128, P, P, 17, P),
+                (MX, P, P, float("inf"), 4, 128, P, P, 1, P), (NV, P, P, float("nan"), 4, 128, P, P, 1, P),
+                (MX, None, P, 1.0, 4, 128, P, P, 1, P), (MX, P, None, 1.0, 4, 128, P, P, 1, P),
+                (MX, P, P, 1.0, 4, 128, None, P, 1, P), (MX, P, P, 1.0, 4, 128, P, None, 1, P),
+                (MX, P, P, 1.0, 4, 128, P, P, 1, None), (MX, P + 8, P, 1.0, 4, 128, P, P, 1, P),
+                (MX, P, P, 1.0, 4, 128, P + 8, P, 1, P), (MX, P, P, 1.0, 4, 128, P, P, 1, P + 2),
+                (NV, P, P + 2, 1.0, 4, 128, P, P, 1, P)):
+        assert g(*bad, None) == fb.ERR_ARG, bad
+    # act_quant: M in [1, 16], cols a multiple of 16, 16-byte aligned x and xq
+    q = lib.fp8blk_act_quant
+    for bad in ((P, 0, 128, P, P), (P, 17, 128, P, P), (P, 1, 24, P, P), (P, 1, 8, P, P),
+                (P + 2, 1, 128, P, P), (P, 1, 128, P + 4, P), (None, 1, 128, P, P), (P, 1, 128, P, None)):
+        assert q(*bad, None) == fb.ERR_ARG, bad
+    # load check and dequant: cols a multiple of 32
+    fbi = ctypes.c_int64(5)
+    assert lib.fp4_load_check(MX, P, P, 4, 48, P, 256, ctypes.byref(fbi), None) == fb.ERR_ARG and fbi.value == -1
+    assert lib.fp4_load_check(2, P, P, 4, 64, P, 256, None, None) == fb.ERR_ARG
+    assert lib.fp4_load_check(NV, P, P, 0, 64, P, 256, None, None) == fb.ERR_ARG
+    assert lib.fp4_load_check(NV, P, P, 4, 64, None, 256, None, None) == fb.ERR_WORKSPACE
+    assert lib.fp4_load_check(NV, P, P, 4, 64, P, 8, None, None) == fb.ERR_WORKSPACE
+    assert lib.fp4_dequant_bf16(MX, P, P, 4, 48, P, None) == fb.ERR_ARG
+    assert lib.fp4_dequant_bf16(MX, P, P, 4, 64, P + 8, None) == fb.ERR_ARG
+    assert lib.fp4_dequant_bf16(NV, P, P + 1, 4, 64, P, None) == fb.ERR_ARG
+    assert lib.fp4_dequant_bf16(3, P, P, 4, 64, P, None) == fb.ERR_ARG
+    # the expert sequence: same M for every linear, valid descriptors, workspace
+    E = fb.Fp4ExpertLinear
+    h = fb.SequenceHandle()
+    nb = fb.fp8blk_sequence_bytes(2)
+    init = lib.fp4_expert_sequence_init
+    good = E(P, P, 1.0, 4, 128, 1, P, P, P)
+    arr = (E * 2)(good, good)
+    assert init(ctypes.byref(h), MX, arr, 0, P, nb, None) == fb.ERR_ARG
+    assert init(ctypes.byref(h), 7, arr, 2, P, nb, None) == fb.ERR_ARG
+    assert init(None, MX, arr, 2, P, nb, None) == fb.ERR_ARG
+    assert init(ctypes.byref(h), MX, arr, 2, None, nb, None) == fb.ERR_WORKSPACE
+    assert init(ctypes.byref(h), MX, arr, 2, P, nb - 1, None) == fb.ERR_WORKSPACE
+    assert init(ctypes.byref(h), MX, arr, 2, P + 32, nb, None) == fb.ERR_WORKSPACE
+    for bad in (E(P, P, 1.0, 4, 128, 2, P, P, P), E(P, P, 1.0, 4, 96, 1, P, P, P), E(P, P, 1.0, 0, 128, 1, P, P, P),
+                E(P, P, float("inf"), 4, 128, 1, P, P, P), E(P + 8, P, 1.0, 4, 128, 1, P, P, P),
+                E(P, P, 1.0, 4, 128, 1, None, P, P)):
+        assert init(ctypes.byref(h), NV, (E * 2)(good, bad), 2, P, nb, None) == fb.ERR_ARG
+    h.plan, h.units_dense, h.n, h.arm, h.grid_dense, h.M = P, 10, 2, fb.ARM_FP8, 4, 1
+    assert lib.fp4_expert_sequence(ctypes.byref(h), None) == fb.ERR_ARG  # not an expert plan
+    h.arm, h.M = fb.ARM_NVFP4, 17
+    assert lib.fp4_expert_sequence(ctypes.byref(h), None) == fb.ERR_ARG
+    assert lib.fp4_expert_sequence(None, None) == fb.ERR_ARG
