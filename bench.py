@@ -25,7 +25,11 @@ Output: one JSON line. Besides the headline it carries
   per_config    per-launch times of the single-linear workloads (decode
                 shape, projection pair, verify panel at M=1..16), cold from HBM
                 (graphs over distinct copies), for the vector and matrix-core
-                kernels and their bf16 twins.
+                kernels and their bf16 twins;
+  expert_sweep  the native expert arm: one decode step's routed-expert
+                projections (43 layers x 8 activated experts x gate 2048x4096,
+                up 2048x4096, down 4096x2048 = 1032 FP4 linears, ~4.5 GB) as one
+                sequence launch per step, NVFP4 and MXFP4, M = 1 and 8.
 """
 import argparse
 import json
@@ -57,6 +61,9 @@ def parse():
     p.add_argument("--layers", type=int, default=43, help="layers in the sweep (default: the full 43)")
     p.add_argument("--no-extra", action="store_true", help="skip the per-config cold-cache table")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-expert", action="store_true", help="skip the native expert arm's sweep")
+    p.add_argument("--expert-only", action="store_true",
+                   help="run only the native expert arm's sweep (for profiling) and print its JSON")
     p.add_argument("--reps", type=int, default=10, help="graph replays per config measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a known-size reference for counter runs)")
@@ -211,6 +218,66 @@ def time_panel_sequence(torch, fb, inputs, sw, M, steps, warmup, dev):
     torch.cuda.synchronize()
     del seq
     return e0.elapsed_time(e1) / 1e3
+
+
+def expert_sweep(torch, fb, inputs, dev, steps, warmup, fmt, Ms=(1, 8)):
+    """The native expert arm over one decode step's routed-expert projections
+    (inputs.expert_sweep_plan: 1032 FP4 linears, each load-checked), one
+    sequence launch per step, HIP events on the launching stream. The
+    activation of each distinct width is quantized once by fp8blk_act_quant
+    (outside the timing; its own per-launch time is reported). Returns a dict
+    per M: effective weight GB/s (codes + block scales)."""
+    plan = inputs.expert_sweep_plan()
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    lins = []
+    for spec in plan:
+        codes, scales = inputs.device_fp4_linear(fmt, spec.rows, spec.cols, spec.seed, dev)
+        fb.fp4_load_check(fmt, codes, scales, ws)  # raises on any refusal
+        lins.append((spec, codes, scales))
+    weight_bytes = sum(inputs.fp4_weight_bytes(fmt, sp.rows, sp.cols) for sp, _, _ in lins)
+    g = 1.0 if fmt == inputs.MXFP4 else 2.0 ** -6
+    stream = torch.cuda.current_stream()
+    out = {"format": inputs.FP4_NAMES[fmt], "linears": len(lins), "weight_bytes_per_step": weight_bytes}
+    for M in Ms:
+        acts = {}
+        for c in sorted({sp.cols for sp, _, _ in lins}):
+            x = inputs.device_x(c, M, 70 + c, dev)
+            xq = torch.empty((M, c), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M, c // 128), dtype=torch.uint8, device=dev)
+            fb.fp8blk_act_quant(x, xq, xs)
+            acts[c] = (x, xq, xs)
+        ys = [torch.empty((M, sp.rows), dtype=torch.float32, device=dev) for sp, _, _ in lins]
+        seq = fb.fp4_expert_sequence_init(fmt, [(c_, s_, g, acts[sp.cols][1], acts[sp.cols][2], y)
+                                                for (sp, c_, s_), y in zip(lins, ys)])
+        call = fb.prepared("fp4_expert_sequence", seq)
+        for _ in range(warmup):
+            run_calls([call])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run_calls([call])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3
+        v = weight_bytes * steps / t / 1e9
+        r = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+             "ms_per_step": round(t / steps * 1e3, 4)}
+        if M == Ms[0]:
+            x, xq, xs = acts[4096]
+            e0.record(stream)
+            for _ in range(100):
+                fb.fp8blk_act_quant(x, xq, xs)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            r["act_quant_us_per_call_4096"] = round(e0.elapsed_time(e1) * 10, 2)
+        out[f"M{M}"] = r
+        log(f"expert sweep {out['format']} M={M}: {r['ms_per_step']} ms/step, {r['value']} GB/s "
+            f"({r['pct_hbm_peak']}% of peak)")
+        del seq, ys, acts
+    del lins
+    torch.cuda.synchronize()
+    return out
 
 
 def time_sequence(torch, fb, sw, steps, warmup):
@@ -557,6 +624,10 @@ def main():
 
     fb.load()
     dev = torch.device("cuda:0")
+    if args.expert_only:
+        res = {f: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f) for f in (inputs.NVFP4, inputs.MXFP4)}
+        print(json.dumps({"expert_sweep": {inputs.FP4_NAMES[f]: r for f, r in res.items()}}), flush=True)
+        return
     log(f"setting up the sweep ({args.layers} layers + head, arm {args.arm})")
     t0 = time.perf_counter()
     sw = Sweep(torch, fb, inputs, dev, args.layers, args.arm)
@@ -656,6 +727,11 @@ def main():
         if cpu:
             log(f"  oracle: {cpu['value']} GB/s on {cpu['cores']} threads")
 
+    experts = None
+    if not args.no_expert:
+        experts = {inputs.FP4_NAMES[f]: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f)
+                   for f in (inputs.NVFP4, inputs.MXFP4)}
+
     m16 = [r for r in (extra or []) if r["M"] == 16 and r["rows"] == 12288]
     out = {
         "metric": METRIC,
@@ -691,6 +767,10 @@ def main():
                                                        "us": m16[0]["mfma_us"]}} if m16 else None),
         "per_config": extra,
         "prefill_staged": pre,
+        "expert_sweep": ({"workload": "native expert arm: 43 layers x 8 activated experts x [gate 2048x4096, "
+                                      "up 2048x4096, down 4096x2048] = 1032 FP4 linears (codes + block scales), "
+                                      "one sequence launch per step; activations quantized per 128 by "
+                                      "fp8blk_act_quant", **experts} if experts else None),
     }
     print(json.dumps(out), flush=True)
 

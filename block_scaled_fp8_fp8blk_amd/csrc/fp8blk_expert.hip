@@ -36,7 +36,6 @@ constexpr int kMX = FP8BLK_FMT_MXFP4, kNV = FP8BLK_FMT_NVFP4;
 constexpr int kActBlock = 128;   // activation scale block (columns)
 constexpr int kStepCols = 128;   // columns per matrix instruction
 constexpr int kTileRows = 16;    // weight rows per matrix instruction
-constexpr int kWin = 2;          // instruction steps per pipeline window
 constexpr unsigned long long kNone = ~0ull;
 
 inline int fp4_block(int fmt) { return fmt == kMX ? 32 : 16; }
@@ -210,9 +209,6 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 //     conversion (a power of two), or unscaled for NVFP4.
 // One instruction takes 32 columns, one MXFP4 block: lane group g (lanes
 // 16g .. 16g+15) supplies the block's columns 8g .. 8g+7 to both operands.
-// A lane loads 16 bytes of its weight row, i.e. one whole 32-column block;
-// a 4 x 4 transpose across the lane groups (two permlane32 and two permlane16
-// swaps) hands each lane its 8 columns of every block of the 128-column step.
 //
 // MXFP4: A row i is token i (rows past M repeat the last token and are not
 // stored); the instruction accumulates every block of every step into the
@@ -226,10 +222,20 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 // token's two accumulators are added at the end of the unit.
 //
 // A unit is R tiles of 16 weight rows of one linear across all its columns,
-// 128 columns (a step) at a time, kWin steps per pipeline window. Units are
+// 128 columns (a step) at a time, WIN steps per pipeline window. Units are
 // numbered over the list in order; wave w of W takes units w, w + W, ...;
 // each wave issues the loads of its next window before the matrix work of
 // the current one.
+//
+// Memory access. Every load reads whole 128-byte lines: a weight load covers
+// 8 rows x 128 bytes (two steps of each row; lane l reads row l % 8, bytes
+// 16 (l / 8) .. +15), and three exchanges of a lane bit with a register bit
+// (permlane32, permlane16, and a row-of-16 rotation by 8 with a select) turn
+// the two loads of a tile into the instruction operands of both steps. The
+// activation codes of a step are read as one 32-column block per lane group
+// and exchanged likewise (permlane32, permlane16). Each lane group loads the
+// block scales (and the activation scale) of a different step of the window
+// and the exchanges hand every lane those of all the window's steps.
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -247,28 +253,30 @@ struct alignas(64) ExLin {
 };
 static_assert(sizeof(ExLin) == kSeqDescBytes, "descriptor size of the plan");
 
-// A-operand groups (NVFP4: 8 tokens each) and row tiles per unit.
+// A-operand groups (NVFP4: 8 tokens each), row tiles per unit and steps per
+// window.
 constexpr int ex_groups(int fmt, int M) { return fmt == kMX || M <= 8 ? 1 : 2; }
-constexpr int ex_tiles(int fmt, int O) { return fmt == kMX ? 4 : (O == 1 ? 4 : 2); }
+constexpr int ex_tiles(int, int) { return 2; }
+constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
 
-template <int FMT, int R, int O>
+template <int R, int O>
 struct ExUnit {
-    const uint8_t* w;   // the unit's first row of codes
-    const uint8_t* sc;  // its first row of block scales
+    const uint8_t* w;    // the unit's first row of codes
+    const uint8_t* sc;   // its first row of block scales
     const uint8_t* xq;
     const uint8_t* xs;
-    uint32_t woff[R];   // lane: byte offset of its row of tile t + its 16-byte block
-    uint32_t soff[R];   // lane: its row's scale bytes of the step
-    uint32_t xoff[O];   // lane: its token's codes + its 8-column group
-    uint32_t xsoff[O];  // lane: its token's row of activation scales
+    uint32_t woff[R][2]; // lane: byte offset of its row in tile t, load h (rows 8h .. 8h+7 of the tile)
+    uint32_t soff[R];    // lane: byte offset of the block scales of its row n of tile t
+    uint32_t xoff[O];    // lane: its token's codes + its 32-column block
+    uint32_t xsoff[O];   // lane: its token's row of activation scales
 };
 
-template <int FMT, int R, int O>
+template <int FMT, int R, int O, int WIN>
 struct ExWin {
-    uint4 b[kWin][R];                            // weight codes: lane group g holds block g of the step
-    typename std::conditional<FMT == kMX, uint32_t, uint2>::type bs[kWin][R];  // the step's block scales
-    uint2 a[kWin][4][O];                         // activation codes: block b, columns 8g .. 8g+7
-    uint32_t as[kWin][O];                        // activation scale code
+    uint4 b[WIN / 2][R][2];                      // weights: step pair, tile, load
+    typename std::conditional<FMT == kMX, uint32_t, uint2>::type bs[R];  // block scales of one step of the window
+    uint4 a[WIN][O][2];                          // activation codes: the lane group's 32-column block
+    uint32_t as[O];                              // activation scale code of one step of the window
 };
 
 struct ExPos {
@@ -279,10 +287,11 @@ struct ExPos {
 };
 
 __device__ __forceinline__ int ex_steps(const ExLin& d) { return d.K / kStepCols; }
-__device__ __forceinline__ int ex_nwin(const ExLin& d) { return (ex_steps(d) + kWin - 1) / kWin; }
+template <int WIN>
+__device__ __forceinline__ int ex_nwin(const ExLin& d) { return (ex_steps(d) + WIN - 1) / WIN; }
 
 template <int FMT, int R, int O>
-__device__ __forceinline__ void ex_unit(ExUnit<FMT, R, O>& U, const ExLin& d, int64_t v, int lane) {
+__device__ __forceinline__ void ex_unit(ExUnit<R, O>& U, const ExLin& d, int64_t v, int lane) {
     const int64_t r0 = v * (R * kTileRows);
     const int n = lane & 15, g = lane >> 4;
     const int64_t half = d.K / 2, sper = d.K / (FMT == kMX ? 32 : 16);
@@ -292,25 +301,28 @@ __device__ __forceinline__ void ex_unit(ExUnit<FMT, R, O>& U, const ExLin& d, in
     U.xs = d.xs;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-        const int64_t row = min(r0 + t * kTileRows + n, d.rows - 1) - r0;  // rows past the end repeat the last
-        U.woff[t] = (uint32_t)(row * half + 16 * g);
-        U.soff[t] = (uint32_t)(row * sper);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // rows past the end repeat the last
+            const int64_t row = min(r0 + t * kTileRows + 8 * h + (lane & 7), d.rows - 1) - r0;
+            U.woff[t][h] = (uint32_t)(row * half);
+        }
+        U.soff[t] = (uint32_t)((min(r0 + t * kTileRows + n, d.rows - 1) - r0) * sper);
     }
     const int nb = d.K / kActBlock;
 #pragma unroll
     for (int o = 0; o < O; ++o) {
         const int tok = min(FMT == kMX ? n : 8 * o + (n >> 1), d.M - 1);
-        U.xoff[o] = (uint32_t)(tok * d.K + 8 * g);
+        U.xoff[o] = (uint32_t)(tok * d.K + 32 * g);
         U.xsoff[o] = (uint32_t)(tok * nb);
     }
 }
 
-template <bool LIST>
+template <bool LIST, int WIN>
 __device__ __forceinline__ ExPos ex_next(const ExPos& p, const ExLin* lin, const int64_t* pre, int64_t W,
                                          int64_t total) {
     ExPos n = p;
     if (!p.more) return n;
-    if (p.win + 1 < ex_nwin(p.d)) {
+    if (p.win + 1 < ex_nwin<WIN>(p.d)) {
         n.win = p.win + 1;
     } else if (p.u + W < total) {
         n.u = p.u + W;
@@ -339,41 +351,126 @@ __device__ __forceinline__ uint2 load_global8(const void* p) {
     return make_uint2(v.x, v.y);
 }
 
-// The loads of window `win` of a unit. A step past the last one (the second
-// step of a last, half-full window) repeats the last step's addresses; its
+// The loads of window `win` of a unit. Steps past the last one (in a last,
+// partial window) repeat the last step's addresses, lane by lane; their
 // activations are zeroed in ex_compute. No branch: every window issues the
 // same loads.
-template <int FMT, int R, int O>
-__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O>& b, const ExUnit<FMT, R, O>& U, int steps, int win) {
+template <int FMT, int R, int O, int WIN>
+__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
+                                         int lane) {
+    const int c = lane >> 3, g = lane >> 4;  // weight chunk of the 128-byte line; lane group
+    const int s0 = win * WIN;
 #pragma unroll
-    for (int s = 0; s < kWin; ++s) {
-        const int j = min(win * kWin + s, steps - 1);
+    for (int q = 0; q < WIN / 2; ++q) {
+        const uint32_t coff = 64 * min(s0 + 2 * q + (c >> 2), steps - 1) + 16 * (c & 3);
 #pragma unroll
-        for (int t = 0; t < R; ++t) {
-            b.b[s][t] = load_stream16(U.w + U.woff[t] + 64 * j);
-            if constexpr (FMT == kMX)
-                b.bs[s][t] = *(global_u32*)(U.sc + U.soff[t] + 4 * j);
-            else
-                b.bs[s][t] = load_global8(U.sc + U.soff[t] + 8 * j);
-        }
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) b.b[q][t][h] = load_stream16(U.w + U.woff[t][h] + coff);
+    }
+    const int js = min(s0 + (g % WIN), steps - 1);  // the step whose scales this lane group loads
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        if constexpr (FMT == kMX)
+            b.bs[t] = *(global_u32*)(U.sc + U.soff[t] + 4 * js);
+        else
+            b.bs[t] = load_global8(U.sc + U.soff[t] + 8 * js);
+    }
+#pragma unroll
+    for (int s = 0; s < WIN; ++s) {
+        const int j = min(s0 + s, steps - 1);
 #pragma unroll
         for (int o = 0; o < O; ++o) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) b.a[s][k][o] = load_global8(U.xq + U.xoff[o] + kStepCols * j + 32 * k);
-            b.as[s][o] = *(global_u8*)(U.xs + U.xsoff[o] + j);
+            b.a[s][o][0] = load_global16(U.xq + U.xoff[o] + kStepCols * j);
+            b.a[s][o][1] = load_global16(U.xq + U.xoff[o] + kStepCols * j + 16);
         }
     }
+#pragma unroll
+    for (int o = 0; o < O; ++o) b.as[o] = *(global_u8*)(U.xs + U.xsoff[o] + js);
 }
 
-// 4 x 4 transpose across the lane groups: on entry lane group g holds block g
-// (dwords 0..3 = its columns 0-7, 8-15, 16-23, 24-31); on exit register k of
-// lane group g holds columns 8g .. 8g+7 of block k.
-__device__ __forceinline__ void transpose_groups(uint4& v) {
-    const auto p = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
-    const auto q = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
-    const auto r = __builtin_amdgcn_permlane16_swap(p[0], q[0], false, false);
-    const auto t = __builtin_amdgcn_permlane16_swap(p[1], q[1], false, false);
-    v = make_uint4(r[0], r[1], t[0], t[1]);
+// Exchange of lane bit 5 (permlane32) or 4 (permlane16) with the index of a
+// register pair (x, y): afterwards x holds, in the lanes with that bit set,
+// y's values from the lanes with it clear, and y the reverse.
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+// The same for lane bit 3, through the rotation of each row of 16 lanes by 8
+// (lane l reads lane l ^ 8) and a select.
+__device__ __forceinline__ void swap8(uint32_t& x, uint32_t& y, bool bit3) {
+    const uint32_t xr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowRor8, 0xF, 0xF, false);
+    const uint32_t yr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, kRowRor8, 0xF, 0xF, false);
+    const uint32_t nx = bit3 ? yr : x, ny = bit3 ? y : xr;
+    x = nx;
+    y = ny;
+}
+
+// The two loads of a tile (L[h][d]: load h, dword d; lane l holds row
+// (l % 8) + 8h, chunk l / 8 of the step pair's 128 bytes) -> the operands
+// op[s][k] of step s of the pair, 32-column block k: lane (n, g) = (l % 16,
+// l / 16) holds row n, columns 8g .. 8g+7 of the block. Chunk bits
+// (c2 c1 c0) = lane bits (5 4 3) become (s, k1, k0) = register bits, and
+// (d1, d0, h) become lane bits (5, 4, 3).
+__device__ __forceinline__ void weights_to_operands(const uint4 (&ld)[2], uint32_t (&op)[2][4], bool bit3) {
+    uint32_t L[2][4] = {{ld[0].x, ld[0].y, ld[0].z, ld[0].w}, {ld[1].x, ld[1].y, ld[1].z, ld[1].w}};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        swap32(L[h][0], L[h][2]);  // d1 <-> lane bit 5
+        swap32(L[h][1], L[h][3]);
+        swap16(L[h][0], L[h][1]);  // d0 <-> lane bit 4
+        swap16(L[h][2], L[h][3]);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) swap8(L[0][d], L[1][d], bit3);  // h <-> lane bit 3
+    // register (h, d1, d0) now holds chunk c = 4 d1 + 2 d0 + h: step d1, block 2 d0 + h
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) op[s][k] = L[k & 1][2 * s + (k >> 1)];
+}
+
+// The 32 activation codes of block g held by lane group g (two 16-byte loads,
+// dword pairs p = 0..3 = columns 8p .. 8p+7) -> for each block k the 8 codes
+// of columns 8g .. 8g+7 (dword pair k).
+__device__ __forceinline__ void act_to_operands(const uint4 (&ld)[2], uint2 (&op)[4]) {
+    uint32_t D[8] = {ld[0].x, ld[0].y, ld[0].z, ld[0].w, ld[1].x, ld[1].y, ld[1].z, ld[1].w};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        swap32(D[0 + e], D[4 + e]);  // pair bit 1 <-> lane bit 5
+        swap32(D[2 + e], D[6 + e]);
+        swap16(D[0 + e], D[2 + e]);  // pair bit 0 <-> lane bit 4
+        swap16(D[4 + e], D[6 + e]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) op[k] = make_uint2(D[2 * k], D[2 * k + 1]);
+}
+
+// One value per lane group (the lane group's step of the window) -> the
+// values of the first WIN lane groups, in every lane.
+template <int WIN>
+__device__ __forceinline__ void gather_groups(uint32_t v, uint32_t (&out)[WIN]) {
+    uint32_t a = v, b = v;
+    if constexpr (WIN == 4) {
+        swap32(a, b);  // a: groups 0, 1; b: groups 2, 3 (in both halves)
+        uint32_t a1 = a, b1 = b;
+        swap16(a, a1);
+        swap16(b, b1);
+        out[0] = a;
+        out[1] = a1;
+        out[2] = b;
+        out[3] = b1;
+    } else {
+        swap16(a, b);  // groups 0 and 1 (2 and 3 repeat them)
+        out[0] = a;
+        out[1] = b;
+    }
 }
 
 // Eight e2m1 codes -> bf16 operand, times the power-of-two scale s.
@@ -399,53 +496,69 @@ __device__ __forceinline__ uint32_t byte_of(uint32_t d, int k) { return (d >> (8
 // MXFP4: acc[t] holds token rows x weight rows of tile t. NVFP4: acc[t * O + o]
 // register e holds, for weight row l % 16, the accumulator of token
 // 8o + 2(l/16) + e/2 over the 16-column blocks of parity e % 2.
-template <int FMT, int R, int O>
-__device__ __forceinline__ void ex_compute(ExWin<FMT, R, O> b, int steps, int win, int lane, v4f* acc) {
+template <int FMT, int R, int O, int WIN>
+__device__ __forceinline__ void ex_compute(const ExWin<FMT, R, O, WIN>& b, int steps, int win, int lane, v4f* acc) {
     const int g = lane >> 4;
+    const bool bit3 = (lane & 8) != 0;
+    // every step's block scales and activation scales, from the lane groups that loaded them
+    uint32_t ws[R][WIN], ws_hi[R][WIN], as[O][WIN];
 #pragma unroll
-    for (int s = 0; s < kWin; ++s) {
-        const bool live = win * kWin + s < steps;  // wave-uniform
-        // activation operands of the step's four blocks, shared by the R tiles
-        v8bf A[4][O];
-#pragma unroll
-        for (int o = 0; o < O; ++o) {
-            const float sa = e8m0_to_f32(b.as[s][o]);
-            // NVFP4: selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
-            // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
-            const bool keep = live && (FMT == kMX || (g >> 1) == (lane & 1));
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint2 d = keep ? b.a[s][k][o] : make_uint2(0, 0);
-                A[k][o] = fp8x8_operand(d, sa);
-            }
+    for (int t = 0; t < R; ++t) {
+        if constexpr (FMT == kMX) {
+            gather_groups<WIN>(b.bs[t], ws[t]);
+        } else {
+            gather_groups<WIN>(b.bs[t].x, ws[t]);
+            gather_groups<WIN>(b.bs[t].y, ws_hi[t]);
         }
+    }
 #pragma unroll
-        for (int t = 0; t < R; ++t) {
-            uint4 w = b.b[s][t];
-            transpose_groups(w);
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-            if constexpr (FMT == kMX) {
+    for (int o = 0; o < O; ++o) gather_groups<WIN>(b.as[o], as[o]);
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        A[k][0], fp4x8_operand(wd[k], e8m0_to_f32(byte_of(b.bs[s][t], k))), acc[t], 0, 0, 0);
-            } else {
-                // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + p
-                const v2f s01 = e4m3_pair<false>(b.bs[s][t].x), s23 = e4m3_pair<true>(b.bs[s][t].x);
-                const v2f s45 = e4m3_pair<false>(b.bs[s][t].y), s67 = e4m3_pair<true>(b.bs[s][t].y);
-                const v2f sc[4] = {s01, s23, s45, s67};
+    for (int q = 0; q < WIN / 2; ++q) {
+        uint32_t wop[R][2][4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const v8bf B = fp4x8_operand(wd[k], 1.0f);
+        for (int t = 0; t < R; ++t) weights_to_operands(b.b[q][t], wop[t], bit3);
 #pragma unroll
-                    for (int o = 0; o < O; ++o) {
-                        const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][o], B, v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                              0, 0, 0);
-                        v4f& a = acc[t * O + o];
-                        a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
-                        a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
-                        a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
-                        a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * q + s2;
+            const bool live = win * WIN + s < steps;  // wave-uniform
+            v8bf A[4][O];
+#pragma unroll
+            for (int o = 0; o < O; ++o) {
+                uint2 ap[4];
+                act_to_operands(b.a[s][o], ap);
+                const float sa = e8m0_to_f32(byte_of(as[o][s], 0));
+                // NVFP4: selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
+                // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
+                const bool keep = live && (FMT == kMX || (g >> 1) == (lane & 1));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
+            }
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                if constexpr (FMT == kMX) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            A[k][0], fp4x8_operand(wop[t][s2][k], e8m0_to_f32(byte_of(ws[t][s], k))), acc[t], 0, 0,
+                            0);
+                } else {
+                    // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + parity
+                    const v2f sc[4] = {e4m3_pair<false>(ws[t][s]), e4m3_pair<true>(ws[t][s]),
+                                       e4m3_pair<false>(ws_hi[t][s]), e4m3_pair<true>(ws_hi[t][s])};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const v8bf B = fp4x8_operand(wop[t][s2][k], 1.0f);
+#pragma unroll
+                        for (int o = 0; o < O; ++o) {
+                            const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][o], B,
+                                                                                  v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                            v4f& a = acc[t * O + o];
+                            a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
+                            a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
+                            a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
+                            a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
+                        }
                     }
                 }
             }
@@ -484,16 +597,16 @@ __device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, co
     }
 }
 
-template <int FMT, int R, int O>
-__device__ __forceinline__ void ex_stage(const ExPos& nxt, ExUnit<FMT, R, O>& un, ExWin<FMT, R, O>& into,
-                                         const ExPos& cur, const ExWin<FMT, R, O>& have, int lane, v4f* acc) {
+template <int FMT, int R, int O, int WIN>
+__device__ __forceinline__ void ex_stage(const ExPos& nxt, ExUnit<R, O>& un, ExWin<FMT, R, O, WIN>& into,
+                                         const ExPos& cur, const ExWin<FMT, R, O, WIN>& have, int lane, v4f* acc) {
     constexpr int NACC = R * O;
-    if (nxt.win == 0 && nxt.more) ex_unit(un, nxt.d, nxt.v, lane);
-    ex_issue(into, un, ex_steps(nxt.d), nxt.win);
+    if (nxt.win == 0 && nxt.more) ex_unit<FMT>(un, nxt.d, nxt.v, lane);
+    ex_issue(into, un, ex_steps(nxt.d), nxt.win, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the next window's loads ahead of this window's matrix work
     ex_compute(have, ex_steps(cur.d), cur.win, lane, acc);
     __builtin_amdgcn_sched_barrier(0);
-    if (cur.win + 1 == ex_nwin(cur.d)) {
+    if (cur.win + 1 == ex_nwin<WIN>(cur.d)) {
         ex_store<FMT, R, O>(cur.d, cur.v, lane, acc);
 #pragma unroll
         for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -501,13 +614,13 @@ __device__ __forceinline__ void ex_stage(const ExPos& nxt, ExUnit<FMT, R, O>& un
 }
 
 // LIST: descriptors from the plan (lin, pre); else the one linear `one`.
-template <int FMT, int R, int O, bool LIST>
+template <int FMT, int R, int O, int WIN, bool LIST>
 __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __restrict__ lin,
                                                                 const int64_t* __restrict__ pre, int64_t total,
                                                                 ExLin one) {
     constexpr int NACC = R * O;
-    using Win = ExWin<FMT, R, O>;
-    using Unit = ExUnit<FMT, R, O>;
+    using Win = ExWin<FMT, R, O, WIN>;
+    using Unit = ExUnit<R, O>;
     const int lane = threadIdx.x % kLanes;
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     ExPos p0;
@@ -525,18 +638,18 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
         p0.v = p0.u;
     }
     Unit ua, ub;
-    ex_unit(ua, p0.d, p0.v, lane);
+    ex_unit<FMT>(ua, p0.d, p0.v, lane);
     v4f acc[NACC];
 #pragma unroll
     for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     Win a, b;
-    ex_issue(a, ua, ex_steps(p0.d), p0.win);
+    ex_issue(a, ua, ex_steps(p0.d), p0.win, lane);
     for (;;) {
-        const ExPos p1 = ex_next<LIST>(p0, lin, pre, W, total);
+        const ExPos p1 = ex_next<LIST, WIN>(p0, lin, pre, W, total);
         ub = ua;
         ex_stage(p1, ub, b, p0, a, lane, acc);
         if (!p1.more) break;
-        p0 = ex_next<LIST>(p1, lin, pre, W, total);
+        p0 = ex_next<LIST, WIN>(p1, lin, pre, W, total);
         ua = ub;
         ex_stage(p0, ua, a, p1, b, lane, acc);
         if (!p0.more) break;
@@ -560,9 +673,9 @@ int ex_grid(int64_t units) {
 
 template <int FMT, int O, bool LIST>
 void ex_launch_o(const ExLin* lin, const int64_t* pre, int64_t total, const ExLin& one, int grid, hipStream_t s) {
-    constexpr int R = ex_tiles(FMT, O);
+    constexpr int R = ex_tiles(FMT, O), WIN = ex_win(FMT, O);
     constexpr int lds = lds_cap_bytes(kMfSeqBlocksPerCU);
-    k_expert<FMT, R, O, LIST><<<dim3((unsigned)grid), dim3(kSeqWaves * kLanes), lds, s>>>(lin, pre, total, one);
+    k_expert<FMT, R, O, WIN, LIST><<<dim3((unsigned)grid), dim3(kSeqWaves * kLanes), lds, s>>>(lin, pre, total, one);
 }
 
 template <bool LIST>
