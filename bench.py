@@ -64,6 +64,11 @@ def parse():
     p.add_argument("--no-expert", action="store_true", help="skip the native expert arm's sweep")
     p.add_argument("--expert-only", action="store_true",
                    help="run only the native expert arm's sweep (for profiling) and print its JSON")
+    p.add_argument("--expert-m", default="1,8", help="panel rows of the expert sweep (comma-separated)")
+    p.add_argument("--summarize-expert-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
+                   help="write the expert kernel's rocprofv3 --stats summary (markdown) and exit")
+    p.add_argument("--summarize-expert-counters", nargs=2, metavar=("FETCH_SIZE_CSV", "WRITE_SIZE_CSV"),
+                   help="calibrate the expert kernel's FETCH_SIZE / WRITE_SIZE, write its counters JSON, print markdown")
     p.add_argument("--reps", type=int, default=10, help="graph replays per config measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a known-size reference for counter runs)")
@@ -250,7 +255,7 @@ def expert_sweep(torch, fb, inputs, dev, steps, warmup, fmt, Ms=(1, 8)):
         seq = fb.fp4_expert_sequence_init(fmt, [(c_, s_, g, acts[sp.cols][1], acts[sp.cols][2], y)
                                                 for (sp, c_, s_), y in zip(lins, ys)])
         call = fb.prepared("fp4_expert_sequence", seq)
-        for _ in range(warmup):
+        for _ in range(max(warmup, 50)):  # the set-up above leaves the GPU idle: bring its clocks up first
             run_calls([call])
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -261,8 +266,18 @@ def expert_sweep(torch, fb, inputs, dev, steps, warmup, fmt, Ms=(1, 8)):
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 1e3
         v = weight_bytes * steps / t / 1e9
+        # algorithmic bytes of the launch: weights (codes + block scales), each
+        # linear's activation codes and scales, and its f32 outputs
+        algo = weight_bytes + sum(M * sp.cols + M * (sp.cols // 128) + 4 * M * sp.rows for sp, _, _ in lins)
+        ach = algo * steps / t / 1e9
+        traffic = expert_traffic(fmt) if M == 1 else None
         r = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
-             "ms_per_step": round(t / steps * 1e3, 4)}
+             "ms_per_step": round(t / steps * 1e3, 4),
+             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                          "kernel": f"k_expert ({inputs.FP4_NAMES[fmt]}), one launch per step",
+                          "avg_launch_us": round(t / steps * 1e6, 2), "avg_algo_bytes_per_launch": algo,
+                          "source_hash": source_hash(EXPERT_SOURCES)}}
         if M == Ms[0]:
             x, xq, xs = acts[4096]
             e0.record(stream)
@@ -336,13 +351,33 @@ KERNEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_sca
                   "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
 
 
-def source_hash():
+EXPERT_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_expert.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+
+
+def source_hash(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def expert_counters_path():
+    return os.path.join(ROOT, "profiles", "expert_fp4_sweep_m1_counters.json")
+
+
+def expert_traffic(fmt):
+    """HBM bytes per M=1 launch of the expert kernel from the committed counter
+    summary (None when absent or taken on other kernel sources)."""
+    try:
+        with open(expert_counters_path()) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(EXPERT_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch", {}).get(str(fmt))
 
 
 def counters_path(arm, mode):
@@ -548,6 +583,77 @@ def summarize_trace(stats_csv, trace_csv, command, mode="sequence"):
     print("\n".join(lines))
 
 
+def summarize_expert_trace(stats_csv, command, trace_csv=None):
+    """Markdown: rocprofv3 --stats rows of the expert arm's kernels, and the
+    median and minimum launch of the expert kernel per format from the
+    per-dispatch trace (the stats average includes the warm-up launches)."""
+    import csv
+    import collections
+    names = {"0": "MXFP4", "1": "NVFP4"}
+    lines = ["# rocprofv3 kernel trace: native expert arm, routed-expert sweep (1032 FP4 linears), M=1", "",
+             f"Command: `{command}`" if command else "", "",
+             "k_expert<format, tiles, token groups, steps per window, list>; format 0 = MXFP4, 1 = NVFP4. "
+             "Each k_expert launch is one whole step (every linear of the sweep).", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        n = r["Name"]
+        if "k_expert" in n or "k_act_quant" in n or "k_fp4" in n:
+            short = _short(n)
+            if "k_expert<" in short:
+                short += f" ({names.get(short.split('<')[1][0], '?')})"
+            lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']):.1f} | {r['MinNs']} | {r['MaxNs']} |")
+    if trace_csv:
+        by = collections.defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            if "k_expert<" in r["Kernel_Name"]:
+                by[r["Kernel_Name"].split("k_expert<")[1][0]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines += ["", "Per dispatch, from the kernel trace:", "", "| kernel | launches | median us | min us |",
+                  "|---|---|---|---|"]
+        for f, v in sorted(by.items()):
+            v.sort()
+            lines.append(f"| k_expert ({names.get(f, f)}) | {len(v)} | {v[len(v) // 2] / 1e3:.1f} | {v[0] / 1e3:.1f} |")
+    print("\n".join(lines))
+
+
+def summarize_expert_counters(fetch_csv, write_csv, command):
+    """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the three
+    1 GiB copies of --copy-calibration and give the HBM bytes per M=1 launch of
+    the expert kernel, per format (median over its dispatches)."""
+    import csv
+    import collections
+
+    def load(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
+        per = collections.defaultdict(list)
+        for r in rows:
+            n = r["Kernel_Name"]
+            if "k_expert<" in n:
+                per[n.split("k_expert<")[1][0]].append(float(r["Counter_Value"]))
+        return copies, {f: sorted(v)[len(v) // 2] for f, v in per.items()}
+
+    fc, ff = load(fetch_csv)
+    wc, wf = load(write_csv)
+    gib_kib = 1 << 20
+    f_factor = gib_kib / sorted(fc)[len(fc) // 2]
+    w_factor = gib_kib / sorted(wc)[len(wc) // 2]
+    per = {f: int((ff[f] * f_factor + wf[f] * w_factor) * 1024) for f in ff}
+    rec = {"source_hash": source_hash(EXPERT_SOURCES), "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": per, "kib": {f: {"fetch": ff[f], "write": wf[f]} for f in ff}, "command": command}
+    with open(expert_counters_path(), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    names = {"0": "MXFP4", "1": "NVFP4"}
+    lines = ["# rocprofv3 counters: native expert arm, routed-expert sweep (1032 FP4 linears), M=1", "",
+             f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
+             f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
+             f"WRITE_SIZE x {w_factor:.3f} give bytes.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch |", "|---|---|---|---|"]
+    for f in sorted(per):
+        lines.append(f"| k_expert ({names.get(f, f)}) | {ff[f]:.1f} | {wf[f]:.1f} | {per[f] / 1e6:.3f} |")
+    lines += ["", f"Source hash {rec['source_hash']}."]
+    print("\n".join(lines))
+
+
 def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"):
     """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the 1 GiB
     copies of --copy-calibration, then give the HBM bytes per launch of the
@@ -611,6 +717,12 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.command, args.arm, args.mode)
         return
+    if args.summarize_expert_trace:
+        summarize_expert_trace(args.summarize_expert_trace[0], args.command, args.summarize_expert_trace[1])
+        return
+    if args.summarize_expert_counters:
+        summarize_expert_counters(*args.summarize_expert_counters, args.command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the FP8-blk "
@@ -624,8 +736,17 @@ def main():
 
     fb.load()
     dev = torch.device("cuda:0")
+    expert_ms = tuple(int(v) for v in args.expert_m.split(","))
     if args.expert_only:
-        res = {f: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f) for f in (inputs.NVFP4, inputs.MXFP4)}
+        res = {f: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f, expert_ms)
+               for f in (inputs.NVFP4, inputs.MXFP4)}
+        if args.copy_calibration:
+            src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copy calibration: 3 x 1 GiB device copies done")
         print(json.dumps({"expert_sweep": {inputs.FP4_NAMES[f]: r for f, r in res.items()}}), flush=True)
         return
     log(f"setting up the sweep ({args.layers} layers + head, arm {args.arm})")
@@ -729,7 +850,7 @@ def main():
 
     experts = None
     if not args.no_expert:
-        experts = {inputs.FP4_NAMES[f]: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f)
+        experts = {inputs.FP4_NAMES[f]: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f, expert_ms)
                    for f in (inputs.NVFP4, inputs.MXFP4)}
 
     m16 = [r for r in (extra or []) if r["M"] == 16 and r["rows"] == 12288]

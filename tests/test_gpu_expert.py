@@ -233,3 +233,41 @@ def test_sequence_equals_single_calls(gpu, gu, fmt, M):
     torch.cuda.synchronize()
     for a, t in zip(first, ins):
         assert torch.equal(a.view(torch.int32), t[-1].view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt,M", [(MX, 1), (NV, 1), (NV, 12)])
+def test_sequence_many_units_per_wave(gpu, gu, fmt, M):
+    """Far more units than the persistent kernel has waves (each wave walks
+    several units of different linears, carrying its addressing across unit
+    and register-set boundaries), with reductions of 1 to 5 pipeline windows
+    and ragged rows: every output equals its single call bit for bit; a sample
+    is checked against the oracle."""
+    rng = np.random.default_rng(500 + fmt + M)
+    rows_choices, cols_choices = (48, 100, 2048, 4096), (384, 640, 1152, 2176, 4096)
+    lins, ins = [], []
+    acts = {}
+    for k in range(360):
+        r, c = int(rng.choice(rows_choices)), int(rng.choice(cols_choices))
+        if c not in acts:
+            x = I.host_fp4_linear(fmt, 1, c, M, 700 + c).x
+            xq_d, xs_d = act_quant_gpu(gpu, dev(gu, x))
+            acts[c] = (x, xq_d, xs_d)
+        codes, scales = I.device_fp4_linear(fmt, r, c, 800 + k, gu.DEV)
+        y = torch.full((M, r), float("nan"), dtype=torch.float32, device=gu.DEV)
+        ins.append((r, c, codes, scales, y))
+        lins.append((codes, scales, 0.75, acts[c][1], acts[c][2], y))
+    units = sum(-(-r // 32) for r, *_ in ins)
+    gu.say(f"expert sequence fmt {fmt} M {M}: {len(lins)} linears, {units} units")
+    seq = gpu.fp4_expert_sequence_init(fmt, lins)
+    assert seq.handle.units_dense == units and units > 4 * seq.handle.grid_dense * 4  # waves
+    gpu.fp4_expert_sequence(seq)
+    torch.cuda.synchronize()
+    for k, (r, c, codes, scales, y) in enumerate(ins):
+        single = expert_gemv_gpu(gpu, fmt, codes, scales, 0.75, acts[c][1], acts[c][2], r)
+        assert torch.equal(y.view(torch.int32), single.view(torch.int32)), (k, r, c)
+    for k in (0, 7, 123, 359):
+        r, c, codes, scales, y = ins[k]
+        x, _, _ = acts[c]
+        xq, xs = oracle.act_quant(x)
+        y64, yabs = oracle.fp4_gemv_f64(fmt, codes.cpu().numpy(), scales.cpu().numpy(), xq, xs, 0.75)
+        gu.assert_within_tolerance(y.cpu().numpy(), y64, yabs, what=f"linear {k} {r}x{c}")
