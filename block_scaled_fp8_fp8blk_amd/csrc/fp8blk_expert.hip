@@ -223,9 +223,11 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 //
 // A unit is R tiles of 16 weight rows of one linear across all its columns,
 // 128 columns (a step) at a time, WIN steps per pipeline window. Units are
-// numbered over the list in order; wave w of W takes units w, w + W, ...;
-// each wave issues the loads of its next window before the matrix work of
-// the current one.
+// numbered over the list in order; wave w of W takes units w, w + W, ...
+// Two register sets hold a wave's consecutive windows; as the matrix work of
+// a window consumes each phase (step pair) of its set, that phase is refilled
+// with the loads of the window after next, so loads stay in flight while the
+// wave computes.
 //
 // Memory access. Every load reads whole 128-byte lines: a weight load covers
 // 8 rows x 128 bytes (two steps of each row; lane l reads row l % 8, bytes
@@ -351,33 +353,33 @@ __device__ __forceinline__ uint2 load_global8(const void* p) {
     return make_uint2(v.x, v.y);
 }
 
-// The loads of window `win` of a unit. Steps past the last one (in a last,
-// partial window) repeat the last step's addresses, lane by lane; their
-// activations are zeroed in ex_compute. No branch: every window issues the
-// same loads.
+// The loads of phase q (steps 2q and 2q + 1) of window `win` of a unit; phase 0
+// also loads the window's block scales and activation scales. Steps past the
+// last one (in a last, partial window) repeat the last step's addresses, lane
+// by lane; their activations are zeroed in ex_compute_phase. No branch: every
+// window issues the same loads.
 template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
-                                         int lane) {
+__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
+                                               int q, int lane) {
     const int c = lane >> 3, g = lane >> 4;  // weight chunk of the 128-byte line; lane group
     const int s0 = win * WIN;
+    const uint32_t coff = 64 * min(s0 + 2 * q + (c >> 2), steps - 1) + 16 * (c & 3);
 #pragma unroll
-    for (int q = 0; q < WIN / 2; ++q) {
-        const uint32_t coff = 64 * min(s0 + 2 * q + (c >> 2), steps - 1) + 16 * (c & 3);
+    for (int t = 0; t < R; ++t)
 #pragma unroll
-        for (int t = 0; t < R; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) b.b[q][t][h] = load_stream16(U.w + U.woff[t][h] + coff);
-    }
+        for (int h = 0; h < 2; ++h) b.b[q][t][h] = load_stream16(U.w + U.woff[t][h] + coff);
     const int js = min(s0 + (g % WIN), steps - 1);  // the step whose scales this lane group loads
+    if (q == 0) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-        if constexpr (FMT == kMX)
-            b.bs[t] = *(global_u32*)(U.sc + U.soff[t] + 4 * js);
-        else
-            b.bs[t] = load_global8(U.sc + U.soff[t] + 8 * js);
+        for (int t = 0; t < R; ++t) {
+            if constexpr (FMT == kMX)
+                b.bs[t] = *(global_u32*)(U.sc + U.soff[t] + 4 * js);
+            else
+                b.bs[t] = load_global8(U.sc + U.soff[t] + 8 * js);
+        }
     }
 #pragma unroll
-    for (int s = 0; s < WIN; ++s) {
+    for (int s = 2 * q; s < 2 * q + 2; ++s) {
         const int j = min(s0 + s, steps - 1);
 #pragma unroll
         for (int o = 0; o < O; ++o) {
@@ -385,8 +387,17 @@ __device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<
             b.a[s][o][1] = load_global16(U.xq + U.xoff[o] + kStepCols * j + 16);
         }
     }
+    if (q == 0) {
 #pragma unroll
-    for (int o = 0; o < O; ++o) b.as[o] = *(global_u8*)(U.xs + U.xsoff[o] + js);
+        for (int o = 0; o < O; ++o) b.as[o] = *(global_u8*)(U.xs + U.xsoff[o] + js);
+    }
+}
+
+template <int FMT, int R, int O, int WIN>
+__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
+                                         int lane) {
+#pragma unroll
+    for (int q = 0; q < WIN / 2; ++q) ex_issue_phase(b, U, steps, win, q, lane);
 }
 
 // Exchange of lane bit 5 (permlane32) or 4 (permlane16) with the index of a
@@ -493,72 +504,79 @@ __device__ __forceinline__ v8bf fp8x8_operand(uint2 d, float s) {
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t d, int k) { return (d >> (8 * k)) & 0xFFu; }
 
+// Every step's block scales and activation scales of a window, from the lane
+// groups that loaded them (MXFP4 uses ws only; NVFP4 ws and ws_hi).
+template <int R, int O, int WIN>
+struct ExScales {
+    uint32_t ws[R][WIN], ws_hi[R][WIN], as[O][WIN];
+};
+
+template <int FMT, int R, int O, int WIN>
+__device__ __forceinline__ void ex_gather(const ExWin<FMT, R, O, WIN>& b, ExScales<R, O, WIN>& S) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        if constexpr (FMT == kMX) {
+            gather_groups<WIN>(b.bs[t], S.ws[t]);
+        } else {
+            gather_groups<WIN>(b.bs[t].x, S.ws[t]);
+            gather_groups<WIN>(b.bs[t].y, S.ws_hi[t]);
+        }
+    }
+#pragma unroll
+    for (int o = 0; o < O; ++o) gather_groups<WIN>(b.as[o], S.as[o]);
+}
+
+// The matrix work of phase q (steps 2q, 2q + 1) of a window.
 // MXFP4: acc[t] holds token rows x weight rows of tile t. NVFP4: acc[t * O + o]
 // register e holds, for weight row l % 16, the accumulator of token
 // 8o + 2(l/16) + e/2 over the 16-column blocks of parity e % 2.
 template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_compute(const ExWin<FMT, R, O, WIN>& b, int steps, int win, int lane, v4f* acc) {
+__device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN>& b, const ExScales<R, O, WIN>& S,
+                                                 int steps, int win, int q, int lane, v4f* acc) {
     const int g = lane >> 4;
     const bool bit3 = (lane & 8) != 0;
-    // every step's block scales and activation scales, from the lane groups that loaded them
-    uint32_t ws[R][WIN], ws_hi[R][WIN], as[O][WIN];
+    uint32_t wop[R][2][4];
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-        if constexpr (FMT == kMX) {
-            gather_groups<WIN>(b.bs[t], ws[t]);
-        } else {
-            gather_groups<WIN>(b.bs[t].x, ws[t]);
-            gather_groups<WIN>(b.bs[t].y, ws_hi[t]);
+    for (int t = 0; t < R; ++t) weights_to_operands(b.b[q][t], wop[t], bit3);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * q + s2;
+        const bool live = win * WIN + s < steps;  // wave-uniform
+        v8bf A[4][O];
+#pragma unroll
+        for (int o = 0; o < O; ++o) {
+            uint2 ap[4];
+            act_to_operands(b.a[s][o], ap);
+            const float sa = e8m0_to_f32(byte_of(S.as[o][s], 0));
+            // NVFP4: selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
+            // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
+            const bool keep = live && (FMT == kMX || (g >> 1) == (lane & 1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
         }
-    }
 #pragma unroll
-    for (int o = 0; o < O; ++o) gather_groups<WIN>(b.as[o], as[o]);
+        for (int t = 0; t < R; ++t) {
+            if constexpr (FMT == kMX) {
 #pragma unroll
-    for (int q = 0; q < WIN / 2; ++q) {
-        uint32_t wop[R][2][4];
+                for (int k = 0; k < 4; ++k)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        A[k][0], fp4x8_operand(wop[t][s2][k], e8m0_to_f32(byte_of(S.ws[t][s], k))), acc[t], 0, 0, 0);
+            } else {
+                // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + parity
+                const v2f sc[4] = {e4m3_pair<false>(S.ws[t][s]), e4m3_pair<true>(S.ws[t][s]),
+                                   e4m3_pair<false>(S.ws_hi[t][s]), e4m3_pair<true>(S.ws_hi[t][s])};
 #pragma unroll
-        for (int t = 0; t < R; ++t) weights_to_operands(b.b[q][t], wop[t], bit3);
+                for (int k = 0; k < 4; ++k) {
+                    const v8bf B = fp4x8_operand(wop[t][s2][k], 1.0f);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int s = 2 * q + s2;
-            const bool live = win * WIN + s < steps;  // wave-uniform
-            v8bf A[4][O];
-#pragma unroll
-            for (int o = 0; o < O; ++o) {
-                uint2 ap[4];
-                act_to_operands(b.a[s][o], ap);
-                const float sa = e8m0_to_f32(byte_of(as[o][s], 0));
-                // NVFP4: selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
-                // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
-                const bool keep = live && (FMT == kMX || (g >> 1) == (lane & 1));
-#pragma unroll
-                for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
-            }
-#pragma unroll
-            for (int t = 0; t < R; ++t) {
-                if constexpr (FMT == kMX) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            A[k][0], fp4x8_operand(wop[t][s2][k], e8m0_to_f32(byte_of(ws[t][s], k))), acc[t], 0, 0,
-                            0);
-                } else {
-                    // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + parity
-                    const v2f sc[4] = {e4m3_pair<false>(ws[t][s]), e4m3_pair<true>(ws[t][s]),
-                                       e4m3_pair<false>(ws_hi[t][s]), e4m3_pair<true>(ws_hi[t][s])};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const v8bf B = fp4x8_operand(wop[t][s2][k], 1.0f);
-#pragma unroll
-                        for (int o = 0; o < O; ++o) {
-                            const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][o], B,
-                                                                                  v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                            v4f& a = acc[t * O + o];
-                            a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
-                            a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
-                            a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
-                            a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
-                        }
+                    for (int o = 0; o < O; ++o) {
+                        const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][o], B, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                              0, 0, 0);
+                        v4f& a = acc[t * O + o];
+                        a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
+                        a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
+                        a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
+                        a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
                     }
                 }
             }
@@ -597,14 +615,26 @@ __device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, co
     }
 }
 
+// One window of the pipeline on register set `set`: the matrix work of
+// window `cur`, phase by phase, each phase's registers refilled with the
+// loads of window `nxt` (two windows ahead) as soon as they are consumed, so
+// that about two windows of loads stay in flight while the wave computes;
+// then the stores of cur's outputs. `un` addresses the windows of `set`.
 template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_stage(const ExPos& nxt, ExUnit<R, O>& un, ExWin<FMT, R, O, WIN>& into,
-                                         const ExPos& cur, const ExWin<FMT, R, O, WIN>& have, int lane, v4f* acc) {
+__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, ExUnit<R, O>& un,
+                                         ExWin<FMT, R, O, WIN>& set, int lane, v4f* acc) {
     constexpr int NACC = R * O;
+    ExScales<R, O, WIN> S;
+    ex_gather(set, S);
     if (nxt.win == 0 && nxt.more) ex_unit<FMT>(un, nxt.d, nxt.v, lane);
-    ex_issue(into, un, ex_steps(nxt.d), nxt.win, lane);
-    __builtin_amdgcn_sched_barrier(0);  // keep the next window's loads ahead of this window's matrix work
-    ex_compute(have, ex_steps(cur.d), cur.win, lane, acc);
+    const int csteps = ex_steps(cur.d), nsteps = ex_steps(nxt.d);
+#pragma unroll
+    for (int q = 0; q < WIN / 2; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        ex_compute_phase(set, S, csteps, cur.win, q, lane, acc);
+        __builtin_amdgcn_sched_barrier(0);  // the phase's registers are free: refill them
+        ex_issue_phase(set, un, nsteps, nxt.win, q, lane);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (cur.win + 1 == ex_nwin<WIN>(cur.d)) {
         ex_store<FMT, R, O>(cur.d, cur.v, lane, acc);
@@ -614,6 +644,8 @@ __device__ __forceinline__ void ex_stage(const ExPos& nxt, ExUnit<R, O>& un, ExW
 }
 
 // LIST: descriptors from the plan (lin, pre); else the one linear `one`.
+// Two register sets: set a holds windows p0, p2, ..., set b windows p1, p3, ...
+// (consecutive windows of the wave, possibly of different units).
 template <int FMT, int R, int O, int WIN, bool LIST>
 __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __restrict__ lin,
                                                                 const int64_t* __restrict__ pre, int64_t total,
@@ -644,15 +676,23 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     Win a, b;
     ex_issue(a, ua, ex_steps(p0.d), p0.win, lane);
+    ExPos p1 = ex_next<LIST, WIN>(p0, lin, pre, W, total);
+    ub = ua;
+    if (p1.win == 0 && p1.more) ex_unit<FMT>(ub, p1.d, p1.v, lane);
+    ex_issue(b, ub, ex_steps(p1.d), p1.win, lane);
     for (;;) {
-        const ExPos p1 = ex_next<LIST, WIN>(p0, lin, pre, W, total);
-        ub = ua;
-        ex_stage(p1, ub, b, p0, a, lane, acc);
-        if (!p1.more) break;
-        p0 = ex_next<LIST, WIN>(p1, lin, pre, W, total);
+        // the window issued into a set follows the one in the other set: it
+        // continues that window's unit unless it starts a new one
+        const ExPos p2 = ex_next<LIST, WIN>(p1, lin, pre, W, total);
         ua = ub;
-        ex_stage(p0, ua, a, p1, b, lane, acc);
-        if (!p0.more) break;
+        ex_stage(p0, p2, ua, a, lane, acc);
+        if (!p1.more) break;
+        const ExPos p3 = ex_next<LIST, WIN>(p2, lin, pre, W, total);
+        ub = ua;
+        ex_stage(p1, p3, ub, b, lane, acc);
+        if (!p2.more) break;
+        p0 = p2;
+        p1 = p3;
     }
 }
 
