@@ -271,3 +271,78 @@ def test_sequence_many_units_per_wave(gpu, gu, fmt, M):
         xq, xs = oracle.act_quant(x)
         y64, yabs = oracle.fp4_gemv_f64(fmt, codes.cpu().numpy(), scales.cpu().numpy(), xq, xs, 0.75)
         gu.assert_within_tolerance(y.cpu().numpy(), y64, yabs, what=f"linear {k} {r}x{c}")
+
+
+@pytest.mark.parametrize("fmt", [MX, NV])
+def test_expert_sweep_as_benchmarked(gpu, gu, fmt):
+    """The benchmark's launch: the 1032 routed-expert linears of one decode
+    step (device-drawn, load-checked) in one sequence launch at M = 1. Every
+    output equals its single call bitwise; 32-row windows of a few linears are
+    checked against the oracle."""
+    plan = I.expert_sweep_plan()
+    ws = torch.empty(256, dtype=torch.uint8, device=gu.DEV)
+    acts = {}
+    for c in sorted({sp.cols for sp in plan}):
+        x = gu.to_dev(I.host_fp4_linear(fmt, 1, c, 1, 70 + c).x)
+        acts[c] = (x, *act_quant_gpu(gpu, x))
+    g = 1.0 if fmt == MX else 2.0 ** -6
+    lins, ins = [], []
+    for sp in plan:
+        codes, scales = I.device_fp4_linear(fmt, sp.rows, sp.cols, sp.seed, gu.DEV)
+        assert gpu.fp4_load_check(fmt, codes, scales, ws, check=False) == (0, -1), sp.name
+        y = torch.full((1, sp.rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+        ins.append((sp, codes, scales, y))
+        lins.append((codes, scales, g, acts[sp.cols][1], acts[sp.cols][2], y))
+    seq = gpu.fp4_expert_sequence_init(fmt, lins)
+    gpu.fp4_expert_sequence(seq)
+    torch.cuda.synchronize()
+    gu.say(f"  expert sweep fmt {fmt}: {len(lins)} linears launched")
+    for i, (sp, codes, scales, y) in enumerate(ins):
+        single = expert_gemv_gpu(gpu, fmt, codes, scales, g, acts[sp.cols][1], acts[sp.cols][2], sp.rows)
+        assert torch.equal(y.view(torch.int32), single.view(torch.int32)), (i, sp.name)
+        if i in (0, 1, 2, 517, len(ins) - 1):
+            r0 = 32 * ((sp.rows // 32) // 2)
+            ch, sh = codes[r0:r0 + 32].cpu().numpy(), scales[r0:r0 + 32].cpu().numpy()
+            xq, xs = oracle.act_quant(acts[sp.cols][0].cpu().numpy().view(np.uint16))
+            y64, yabs = oracle.fp4_gemv_f64(fmt, ch, sh, xq, xs, g)
+            gu.assert_within_tolerance(y[:, r0:r0 + 32].cpu().numpy(), y64, yabs, what=f"{sp.name} rows {r0}..")
+
+
+def test_expert_sequence_graph_replays(gpu, gu):
+    """An expert sequence captured in a HIP graph: every replay, with eager
+    work and synchronizations between the replays, gives the eager bits."""
+    shapes = [(2048, 4096), (300, 512), (4096, 2048), (17, 384)]
+    for fmt in (MX, NV):
+        lins_e, lins_g, ys_e, ys_g = [], [], [], []
+        for k, (r, c) in enumerate(shapes):
+            L = I.host_fp4_linear(fmt, r, c, 1, 900 + k)
+            xq, xs = act_quant_gpu(gpu, dev(gu, L.x))
+            codes, scales = dev(gu, L.codes), dev(gu, L.scales)
+            ye = torch.full((1, r), float("nan"), dtype=torch.float32, device=gu.DEV)
+            yg = torch.full((1, r), float("nan"), dtype=torch.float32, device=gu.DEV)
+            lins_e.append((codes, scales, L.global_scale, xq, xs, ye))
+            lins_g.append((codes, scales, L.global_scale, xq, xs, yg))
+            ys_e.append(ye)
+            ys_g.append(yg)
+        s_e = gpu.fp4_expert_sequence_init(fmt, lins_e)
+        s_g = gpu.fp4_expert_sequence_init(fmt, lins_g)
+        gpu.fp4_expert_sequence(s_e)
+        torch.cuda.synchronize()
+        assert gpu.prepared("fp4_expert_sequence", s_g)() == gpu.OK  # an eager launch first
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            assert gpu.prepared("fp4_expert_sequence", s_g, stream=cap)() == gpu.OK
+        for rep in range(3):
+            for y in ys_g:
+                y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            junk = torch.randn(1 << 20, device=gu.DEV).sum()  # eager work between replays
+            torch.cuda.synchronize()
+            for ye, yg in zip(ys_e, ys_g):
+                assert torch.equal(ye.view(torch.int32), yg.view(torch.int32)), (fmt, rep)
+        del junk
