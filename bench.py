@@ -69,6 +69,15 @@ def parse():
                    help="write the expert kernel's rocprofv3 --stats summary (markdown) and exit")
     p.add_argument("--summarize-expert-counters", nargs=2, metavar=("FETCH_SIZE_CSV", "WRITE_SIZE_CSV"),
                    help="calibrate the expert kernel's FETCH_SIZE / WRITE_SIZE, write its counters JSON, print markdown")
+    p.add_argument("--panel-only", action="store_true",
+                   help="run only the M-row verify panel sweep (matrix-core sequence launch; for profiling) and "
+                        "print its JSON")
+    p.add_argument("--panel-m", default="2,4,8,16", help="panel rows of the verify panel sweep (comma-separated)")
+    p.add_argument("--summarize-panel-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
+                   help="write the panel sweep kernel's rocprofv3 --stats summary (markdown) and exit")
+    p.add_argument("--summarize-panel-counters", nargs=2, metavar=("FETCH_SIZE_CSV", "WRITE_SIZE_CSV"),
+                   help="calibrate the panel sweep kernel's FETCH_SIZE / WRITE_SIZE (one --panel-m value), write "
+                        "its counters JSON, print markdown")
     p.add_argument("--reps", type=int, default=10, help="graph replays per config measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a known-size reference for counter runs)")
@@ -212,7 +221,7 @@ def time_panel_sequence(torch, fb, inputs, sw, M, steps, warmup, dev):
         seq = fb.fp8blk_sequence_init(fb.ARM_BF16_MFMA, [(l["w"], xs[l["spec"].cols], y) for l, y in zip(sw.lins, ys)])
         call = fb.prepared("bf16_gemv_twin_mfma_sequence", seq)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
+    for _ in range(max(warmup, 50)):  # the set-up above leaves the GPU idle: bring its clocks up first
         run_calls([call])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -223,6 +232,31 @@ def time_panel_sequence(torch, fb, inputs, sw, M, steps, warmup, dev):
     torch.cuda.synchronize()
     del seq
     return e0.elapsed_time(e1) / 1e3
+
+
+def panel_sweep(torch, fb, inputs, sw, dev, steps, warmup, Ms):
+    """The verify step's dense traffic: the sweep's linears with an M-row
+    panel, one matrix-core sequence launch per step, for each M. Per M: the
+    effective weight GB/s (the metric's bytes: codes + f32 grid) and the
+    roofline of the launch (algorithmic bytes: weights, each linear's bf16
+    panel read once and its f32 outputs written once)."""
+    out = {}
+    for M in Ms:
+        t = time_panel_sequence(torch, fb, inputs, sw, M, steps, warmup, dev)
+        v = sw.weight_bytes * steps / t / 1e9
+        algo = sum(sw.algo_bytes(l["spec"]) + 2 * (M - 1) * l["spec"].cols + 4 * (M - 1) * l["spec"].rows
+                   for l in sw.lins)
+        ach = algo * steps / t / 1e9
+        out[str(M)] = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+                       "ms_per_step": round(t / steps * 1e3, 4),
+                       "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": panel_traffic(sw.arm, M),
+                                    "kernel": f"k_mfseq ({sw.arm}), one launch per step",
+                                    "avg_launch_us": round(t / steps * 1e6, 2), "avg_algo_bytes_per_launch": algo,
+                                    "source_hash": source_hash(PANEL_SOURCES)}}
+        log(f"sweep with an M={M} verify panel, matrix-core sequence launch: {t / steps * 1e3:.4f} ms/step, "
+            f"{v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak); {ach:.1f} GB/s algorithmic")
+    return out
 
 
 def expert_sweep(torch, fb, inputs, dev, steps, warmup, fmt, Ms=(1, 8)):
@@ -352,6 +386,7 @@ KERNEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_sca
 
 
 EXPERT_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_expert.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+PANEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_mfma.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
 
 
 def source_hash(sources=KERNEL_SOURCES):
@@ -378,6 +413,23 @@ def expert_traffic(fmt):
     if rec.get("source_hash") != source_hash(EXPERT_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch", {}).get(str(fmt))
+
+
+def panel_counters_path(arm, M):
+    return os.path.join(ROOT, "profiles", f"gemv_{arm}_panel_sweep_m{M}_counters.json")
+
+
+def panel_traffic(arm, M):
+    """HBM bytes per launch of the panel sweep kernel from the committed
+    counter summary for this M (None when absent or taken on other sources)."""
+    try:
+        with open(panel_counters_path(arm, M)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(PANEL_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def counters_path(arm, mode):
@@ -654,6 +706,70 @@ def summarize_expert_counters(fetch_csv, write_csv, command):
     print("\n".join(lines))
 
 
+def summarize_panel_trace(stats_csv, trace_csv, command, M):
+    """Markdown: rocprofv3 --stats rows of the matrix-core sequence kernel and
+    its per-dispatch median and minimum from the trace (the stats average
+    includes the warm-up launches)."""
+    import csv
+    import collections
+    lines = [f"# rocprofv3 kernel trace: verify panel sweep (259 FP8-blk linears, M={M} bf16 panel), one "
+             "matrix-core sequence launch per step", "",
+             f"Command: `{command}`" if command else "", "",
+             "k_mfseq<kind, tiles, panel registers>: kind 0 = FP8 arm. Each launch is one whole step.", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        if "k_mfseq" in r["Name"]:
+            lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.1f} | {r['MinNs']} | "
+                         f"{r['MaxNs']} |")
+    by = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if "k_mfseq" in r["Kernel_Name"]:
+            by[_short(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["", "Per dispatch, from the kernel trace:", "", "| kernel | launches | median us | min us |",
+              "|---|---|---|---|"]
+    for k, v in sorted(by.items()):
+        v.sort()
+        lines.append(f"| {k} | {len(v)} | {v[len(v) // 2] / 1e3:.1f} | {v[0] / 1e3:.1f} |")
+    print("\n".join(lines))
+
+
+def summarize_panel_counters(fetch_csv, write_csv, command, M, arm="fp8"):
+    """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the three
+    1 GiB copies of --copy-calibration and give the HBM bytes per launch of
+    the matrix-core sequence kernel (median over its dispatches; one panel
+    size per run)."""
+    import csv
+
+    def load(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
+        v = sorted(float(r["Counter_Value"]) for r in rows if "k_mfseq" in r["Kernel_Name"])
+        return copies, v[len(v) // 2]
+
+    fc, fk = load(fetch_csv)
+    wc, wk = load(write_csv)
+    gib_kib = 1 << 20
+    f_factor = gib_kib / sorted(fc)[len(fc) // 2]
+    w_factor = gib_kib / sorted(wc)[len(wc) // 2]
+    per = int((fk * f_factor + wk * w_factor) * 1024)
+    rec = {"source_hash": source_hash(PANEL_SOURCES), "arm": arm, "M": M, "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": per,
+           "kib": {"fetch": fk, "write": wk}, "command": command}
+    with open(panel_counters_path(arm, M), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines = [f"# rocprofv3 counters: verify panel sweep (259 FP8-blk linears, M={M} bf16 panel), one matrix-core "
+             "sequence launch per step", "",
+             f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
+             f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
+             f"WRITE_SIZE x {w_factor:.3f} give bytes.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB | HBM MB per launch |",
+             "|---|---|---|---|---|---|",
+             f"| k_mfseq ({arm}) | {fk:.1f} | {wk:.1f} | {fk * f_factor * 1024 / 1e6:.3f} | "
+             f"{wk * w_factor * 1024 / 1e6:.3f} | {per / 1e6:.3f} |", "",
+             f"Source hash {rec['source_hash']}."]
+    print("\n".join(lines))
+
+
 def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"):
     """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the 1 GiB
     copies of --copy-calibration, then give the HBM bytes per launch of the
@@ -723,6 +839,12 @@ def main():
     if args.summarize_expert_counters:
         summarize_expert_counters(*args.summarize_expert_counters, args.command)
         return
+    if args.summarize_panel_trace:
+        summarize_panel_trace(*args.summarize_panel_trace, args.command, int(args.panel_m))
+        return
+    if args.summarize_panel_counters:
+        summarize_panel_counters(*args.summarize_panel_counters, args.command, int(args.panel_m), args.arm)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the FP8-blk "
@@ -748,6 +870,19 @@ def main():
             torch.cuda.synchronize()
             log("copy calibration: 3 x 1 GiB device copies done")
         print(json.dumps({"expert_sweep": {inputs.FP4_NAMES[f]: r for f, r in res.items()}}), flush=True)
+        return
+    panel_ms = tuple(int(v) for v in args.panel_m.split(","))
+    if args.panel_only:
+        sw = Sweep(torch, fb, inputs, dev, args.layers, args.arm)
+        panel = panel_sweep(torch, fb, inputs, sw, dev, args.steps, args.warmup, panel_ms)
+        if args.copy_calibration:
+            src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copy calibration: 3 x 1 GiB device copies done")
+        print(json.dumps({"panel_sweep_matrix_core_sequence": panel}), flush=True)
         return
     log(f"setting up the sweep ({args.layers} layers + head, arm {args.arm})")
     t0 = time.perf_counter()
@@ -813,15 +948,7 @@ def main():
 
     # The verify step's dense traffic: the same linears with an M-row panel, as
     # one matrix-core sequence launch.
-    panel = {}
-    if not args.no_extra:
-        for M in (2, 4, 8, 16):
-            t = time_panel_sequence(torch, fb, inputs, sw, M, args.steps, args.warmup, dev)
-            v = sw.weight_bytes * args.steps / t / 1e9
-            panel[str(M)] = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
-                             "ms_per_step": round(t / args.steps * 1e3, 4)}
-            log(f"sweep with an M={M} verify panel, matrix-core sequence launch: {t / args.steps * 1e3:.4f} ms/step, "
-                f"{v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak)")
+    panel = panel_sweep(torch, fb, inputs, sw, dev, args.steps, args.warmup, panel_ms) if not args.no_extra else {}
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
