@@ -525,61 +525,187 @@ __device__ __forceinline__ void mf_seq_compute(MfWindow<KIND, TILES, XR> b, int 
 
 // Lane (n, kg) = (l % 16, l / 16) holds D[4 kg + e][n], e = 0..3: rows
 // 4 kg .. 4 kg + 3 of the tile for panel row n, four consecutive outputs of
-// y[n]. When the linear allows it they leave as one 16-byte nontemporal store
-// (a tile is one store instruction writing 16 panel rows x 64 bytes; with a
-// 16-row panel the outputs are 1/57 of the bytes the step reads, and the
-// nontemporal hint measured +2% there), else one by one.
+// y[n]. yu points at y[0][first row of the unit], `rows` is the row stride of
+// y and `left` the rows of the unit that exist (rows - first row, at most
+// TILES * 16). When vec is set (the linear allows it) four outputs leave as
+// one 16-byte nontemporal store (a tile is one store instruction writing 16
+// panel rows x 64 bytes), else one by one.
 template <int TILES>
-__device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int lane, v4f* acc) {
+__device__ __forceinline__ void mf_seq_store_at(float* yu, int64_t rows, int left, bool vec, int M, int lane,
+                                                const v4f* acc) {
     const int n = lane & 15, kg = lane >> 4;
-    const int64_t r0 = v * (TILES * kTile);
-    if (n >= d.M) return;
-    float* yrow = d.y + (int64_t)n * d.rows;
+    if (n >= M) return;
+    float* yrow = yu + (int64_t)n * rows;
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-        const int64_t r = r0 + t * kTile + 4 * kg;
-        if (d.vec_store && r + 3 < d.rows) {
+        const int r = t * kTile + 4 * kg;
+        if (vec && r + 3 < left) {
             typedef __attribute__((address_space(1))) v4f global_v4f;
             __builtin_nontemporal_store(acc[t], (global_v4f*)(yrow + r));
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (r + e < d.rows) store_global_f32(yrow + r + e, acc[t][e]);
+                if (r + e < left) store_global_f32(yrow + r + e, acc[t][e]);
         }
     }
 }
 
+// Where a finished unit's outputs go. A stream of reads runs markedly slower
+// while writes are mixed into it than when the same bytes are written in one
+// burst after it (measured with a bare 3 GiB read by 2048 waves: 1 KB written
+// per 64 KB read costs 13% of the read rate, the same bytes written at each
+// wave's end 6%). With a panel of 8 or more rows the outputs are 1/57 (M = 16)
+// of the bytes read, so each wave keeps the outputs of its first units in its
+// own part of the workgroup's LDS (on the FP8 arm the next PARK in registers)
+// and writes them after its last unit; units past that are written when they
+// finish. Smaller panels write when each unit finishes. Only where and when
+// the outputs are stored changes, never their values.
+//
+// An LDS slot holds one unit: lane (n, kg) with n < M puts tile t's four
+// outputs at 16 ((t M + n) 4 + kg) bytes. Where unit k goes is recorded in
+// lane k of five registers (its y address, y's row stride, and its row count
+// with the vector-store flag), so the final writes need no loads but LDS.
+constexpr int kMfSeqLdsBytes = 80 * 1024;                       // per workgroup: at most 2 per compute unit
+constexpr int kMfSeqWaveLds = kMfSeqLdsBytes / kSeqWaves;       // per wave
+constexpr int kMfSeqHoldMinM = 8;                               // smallest panel whose outputs are held back
+static_assert(kMfSeqBlocksPerCU * kMfSeqLdsBytes <= 160 * 1024 && (kMfSeqBlocksPerCU + 1) * kMfSeqLdsBytes > 160 * 1024,
+              "the LDS of a workgroup caps a compute unit at kMfSeqBlocksPerCU of them");
+
+struct MfOut {
+    unsigned char* lds;  // the wave's part of the workgroup's LDS
+    int M;               // panel rows of the list (the plan's; every descriptor holds the same)
+    int slot_bytes;      // TILES * M * 64
+    int slots;           // units the LDS part holds (0 below kMfSeqHoldMinM)
+    int k;               // units finished so far
+    uint32_t y_lo, y_hi, rows_lo, rows_hi, left_vec;  // lane k: record of held unit k
+};
+
+template <int TILES, int PARK>
+struct MfPark {
+    v4f acc[PARK > 0 ? PARK : 1][TILES];  // acc[i]: held unit slots + i
+};
+
+template <int TILES>
+__device__ __forceinline__ void mf_seq_store(const MfSeqLin& d, int64_t v, int lane, const v4f* acc) {
+    const int64_t r0 = v * (TILES * kTile);
+    mf_seq_store_at<TILES>(d.y + r0, d.rows, (int)min(d.rows - r0, (int64_t)(TILES * kTile)), d.vec_store != 0, d.M,
+                           lane, acc);
+}
+
+// Outputs are held back only with 4-tile units, the units of panels of
+// kMfSeqHoldMinM rows or more; the smaller panels' kernels leave the holding
+// code out.
+template <int TILES>
+constexpr bool mf_seq_holds() { return TILES == mf_seq_tiles(kMfSeqHoldMinM); }
+
+template <int TILES, int PARK>
+__device__ __forceinline__ void mf_seq_retire(const MfSeqLin& d, int64_t v, int lane, const v4f* acc, MfOut& o,
+                                              MfPark<TILES, PARK>& park) {
+    if (mf_seq_holds<TILES>() && o.k < o.slots + PARK) {
+        const int64_t r0 = v * (TILES * kTile);
+        const uint64_t yu = reinterpret_cast<uint64_t>(d.y + r0);
+        const uint32_t lv = (uint32_t)min(d.rows - r0, (int64_t)(TILES * kTile)) | (d.vec_store ? 0x10000u : 0u);
+        const bool mine = lane == o.k;  // lane k keeps unit k's record
+        o.y_lo = mine ? (uint32_t)yu : o.y_lo;
+        o.y_hi = mine ? (uint32_t)(yu >> 32) : o.y_hi;
+        o.rows_lo = mine ? (uint32_t)d.rows : o.rows_lo;
+        o.rows_hi = mine ? (uint32_t)((uint64_t)d.rows >> 32) : o.rows_hi;
+        o.left_vec = mine ? lv : o.left_vec;
+        if (o.k < o.slots) {
+            const int n = lane & 15, kg = lane >> 4;
+            if (n < o.M) {
+                unsigned char* slot = o.lds + o.k * o.slot_bytes;
+#pragma unroll
+                for (int t = 0; t < TILES; ++t) *reinterpret_cast<v4f*>(slot + ((t * o.M + n) * 4 + kg) * 16) = acc[t];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PARK; ++i)
+                if (o.k == o.slots + i)
+#pragma unroll
+                    for (int t = 0; t < TILES; ++t) park.acc[i][t] = acc[t];
+        }
+    } else {
+        mf_seq_store<TILES>(d, v, lane, acc);
+    }
+    ++o.k;
+}
+
+// Held unit k's outputs, from its record.
+template <int TILES>
+__device__ __forceinline__ void mf_seq_store_held(const MfOut& o, int k, int lane, const v4f* acc) {
+    const uint64_t yu = ((uint64_t)__builtin_amdgcn_readlane(o.y_hi, k) << 32) | (uint32_t)__builtin_amdgcn_readlane(o.y_lo, k);
+    const int64_t rows = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(o.rows_hi, k) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane(o.rows_lo, k));
+    const uint32_t lv = __builtin_amdgcn_readlane(o.left_vec, k);
+    mf_seq_store_at<TILES>(reinterpret_cast<float*>(yu), rows, (int)(lv & 0xffffu), (lv >> 16) != 0, o.M, lane, acc);
+}
+
+// After the wave's last unit: the held units go out in order. (Called from
+// inside the pipeline loop, at the last unit: after the loop, the same code
+// makes the compiler keep ~50 more registers live across the loop.)
+template <int TILES, int PARK>
+__device__ __forceinline__ void mf_seq_flush(int lane, const MfOut& o, const MfPark<TILES, PARK>& park) {
+    if (!mf_seq_holds<TILES>()) return;
+    const int in_lds = min(o.k, o.slots);
+    const int n = lane & 15, kg = lane >> 4;
+#pragma unroll 1
+    for (int k = 0; k < in_lds; ++k) {
+        v4f acc[TILES];
+        const unsigned char* slot = o.lds + k * o.slot_bytes;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+            acc[t] = n < o.M ? *reinterpret_cast<const v4f*>(slot + ((t * o.M + n) * 4 + kg) * 16) : v4f{0.f, 0.f, 0.f, 0.f};
+        mf_seq_store_held<TILES>(o, k, lane, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < PARK; ++i)
+        if (o.slots + i < o.k) mf_seq_store_held<TILES>(o, o.slots + i, lane, park.acc[i]);
+}
+
 // One window of the pipeline: issue the loads of window `nxt` (computing its
 // unit's addressing when it starts a unit), then the matrix work of window
-// `cur`, then, at the end of cur's unit, its stores.
-template <int KIND, int TILES, int XR>
+// `cur`, then, at the end of cur's unit, hand its outputs on; after the wave's
+// last unit (nothing follows cur), write out what LDS holds.
+template <int KIND, int TILES, int XR, int PARK>
 __device__ __forceinline__ void mf_seq_stage(const MfPos& nxt, MfUnit<TILES, XR>& un, MfWindow<KIND, TILES, XR>& into,
                                              const MfPos& cur, const MfWindow<KIND, TILES, XR>& have, int lane,
-                                             v4f* acc) {
+                                             v4f* acc, MfOut& out, MfPark<TILES, PARK>& park) {
     if (nxt.win == 0 && nxt.more) mf_unit<KIND>(un, nxt.d, nxt.v, lane);
     mf_seq_issue(into, un, nxt.d.K, nxt.win, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the next window's loads ahead of this window's matrix work
     mf_seq_compute(have, cur.d.K, cur.win, lane, acc);
     __builtin_amdgcn_sched_barrier(0);
     if (cur.win + 1 == cur.d.nwin) {
-        mf_seq_store<TILES>(cur.d, cur.v, lane, acc);
+        mf_seq_retire<TILES, PARK>(cur.d, cur.v, lane, acc, out, park);
 #pragma unroll
         for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        if (!nxt.more) mf_seq_flush<TILES, PARK>(lane, out, park);
     }
 }
 
 // Two register sets in turn: the loads of the next window are issued before
-// the matrix work of the current one.
+// the matrix work of the current one. M is the panel rows of every linear of
+// the list.
 template <int KIND, int TILES, int XR>
 __global__ __launch_bounds__(kSeqWaves * kLanes) void k_mfseq(const MfSeqLin* __restrict__ lin,
-                                                               const int64_t* __restrict__ pre, int64_t total) {
+                                                               const int64_t* __restrict__ pre, int64_t total, int M) {
     using Win = MfWindow<KIND, TILES, XR>;
     using Unit = MfUnit<TILES, XR>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char mf_lds[];
     const int lane = threadIdx.x % kLanes;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     MfPos p0;
-    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + wave;
     if (p0.u >= total) return;
+    MfOut out;
+    out.lds = mf_lds + wave * kMfSeqWaveLds;
+    out.M = M;
+    out.slot_bytes = TILES * M * 64;
+    out.slots = mf_seq_holds<TILES>() && M >= kMfSeqHoldMinM ? kMfSeqWaveLds / out.slot_bytes : 0;
+    out.k = 0;
+    out.y_lo = out.y_hi = out.rows_lo = out.rows_hi = out.left_vec = 0;
     p0.win = 0;
     p0.j = 0;
     p0.more = true;
@@ -591,16 +717,20 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_mfseq(const MfSeqLin* __
     v4f acc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // Registers for two more held units where they are free: the FP8 arm
+    // where outputs are held. The bf16 arm's larger windows leave no room.
+    constexpr int PARK = (KIND == 0 && mf_seq_holds<TILES>()) ? 2 : 0;
+    MfPark<TILES, PARK> park;
     Win a, b;
     mf_seq_issue(a, ua, p0.d.K, p0.win, lane);
     for (;;) {
         const MfPos p1 = mf_next(p0, lin, pre, W, total);
         ub = ua;
-        mf_seq_stage(p1, ub, b, p0, a, lane, acc);
+        mf_seq_stage(p1, ub, b, p0, a, lane, acc, out, park);
         if (!p1.more) break;
         p0 = mf_next(p1, lin, pre, W, total);
         ua = ub;
-        mf_seq_stage(p0, ua, a, p1, b, lane, acc);
+        mf_seq_stage(p0, ua, a, p1, b, lane, acc, out, park);
         if (!p0.more) break;
     }
 }
@@ -614,17 +744,17 @@ int mf_seq_launch(const fp8blk_sequence* seq, int arm, hipStream_t s) {
     const int64_t* pre =
         reinterpret_cast<const int64_t*>(static_cast<const unsigned char*>(seq->plan) + (size_t)seq->n * sizeof(MfSeqLin));
     const dim3 nb((unsigned)seq->grid_dense), nt(kSeqWaves * kLanes);
-    constexpr int lds = lds_cap_bytes(kMfSeqBlocksPerCU);
+    constexpr int lds = kMfSeqLdsBytes;
     (void)hipGetLastError();
     const int M = seq->M;
     if (M >= 8)
-        k_mfseq<KIND, mf_seq_tiles(8), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(8), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense, M);
     else if (M > 2)
-        k_mfseq<KIND, mf_seq_tiles(3), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(3), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense, M);
     else if (M == 2)
-        k_mfseq<KIND, mf_seq_tiles(2), 2><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(2), 2><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense, M);
     else
-        k_mfseq<KIND, mf_seq_tiles(1), 1><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense);
+        k_mfseq<KIND, mf_seq_tiles(1), 1><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense, M);
     return launch_status();
 }
 

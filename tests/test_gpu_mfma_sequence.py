@@ -146,3 +146,40 @@ def test_mfma_sequence_whole_step_sweep(gpu):
         assert_within_tolerance(yw, y64, yabs, what=f"{spec.name} rows {r0}.. M=16")
     assert all(not torch.isnan(y).any() for y in ys)
     say(f"  {len(lins)} sweep linears at M=16 checked")
+
+
+@pytest.mark.parametrize("M", [8, 16])
+def test_mfma_sequence_more_units_than_held(gpu, M):
+    """A list long enough that every wave finishes more units than its LDS part
+    and its registers hold (about 14 units per wave with 1.8M rows of 128
+    columns): the outputs kept back to the end of the launch, the ones parked in
+    registers and the ones written when they finish all equal the single
+    matrix-core call (one part at these cols), and the twin, bit for bit."""
+    from gpu_util import DEV, DevLinear, assert_within_tolerance, say, u32
+    shapes = [(900000, 128), (5000, 256), (900001, 128)]
+    members, y8, yt, slabs = [], [], [], []
+    for k, (rows, cols) in enumerate(shapes):
+        codes, scales = inputs.device_linear(rows, cols, 900 + k, DEV)
+        D = DevLinear(codes, scales, inputs.device_x(cols, M, 950 + k, DEV))
+        assert D.check(check=False) == (0, -1)
+        members.append(D)
+        slabs.append(D.slab())
+        y8.append(torch.full((M, rows), float("nan"), device=DEV))
+        yt.append(torch.full((M, rows), float("nan"), device=DEV))
+    s8 = fb.fp8blk_sequence_init(fb.ARM_FP8_MFMA, [(D.codes, D.grid, D.x, y) for D, y in zip(members, y8)])
+    st = fb.fp8blk_sequence_init(fb.ARM_BF16_MFMA, [(s, D.x, y) for D, s, y in zip(members, slabs, yt)])
+    say(f"  long mfma sequence M={M}: {s8.handle.units_dense} units over {s8.handle.grid_dense * 4} waves")
+    fb.fp8blk_gemv_mfma_sequence(s8)
+    fb.bf16_gemv_twin_mfma_sequence(st)
+    torch.cuda.synchronize()
+    for D, a, b in zip(members, y8, yt):
+        ref = torch.full_like(a, float("nan"))
+        fb.fp8blk_gemv_mfma(D.codes, D.grid, D.x, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), ref.view(torch.int32)), (D.rows, D.cols, "sequence != single call")
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (D.rows, D.cols, "FP8 != twin")
+        r0 = 128 * ((D.rows - 200) // 128)  # the last rows, from a scale-block boundary
+        ch = D.codes[r0:].cpu().numpy()
+        sh = D.scales[r0 // 128:].cpu().numpy()
+        y64, yabs = oracle.gemv_f64(ch, sh, D.x.cpu().numpy().view(np.uint16), nthreads=NTHREADS)
+        assert_within_tolerance(a[:, r0:].cpu().numpy(), y64, yabs, what=f"{D.rows}x{D.cols} tail M={M}")
