@@ -399,22 +399,37 @@ struct Plan {
 };
 
 // Plan: a pure function of (rows, cols, M); it never changes bits.
-// M = 1 and at most 16 segments: the single-row kernel with four chunks per
-// lane -- TPW segments per wave (the next power of two >= T, at most 4), the
-// rest of a row over sw waves, R = 4 / TPW rows. Measured on the whole-step
-// sweep: more chunks per lane (fewer, longer waves) or fewer (more waves) are
-// both slower. Otherwise the panel kernel with R = 4 rows per wave, splitting
-// the segments of a row over 2 or 4 waves while fewer than 4096 waves would
-// run.
+// M = 1 and at most 16 segments: the single-row kernel, TPW segments per wave
+// and the rest of a row over sw waves (T <= TPW * sw):
+// - T <= 2: TPW = T, R = 4 / TPW rows (four chunks per lane).
+// - T >= 3 and fewer than 4096 rows: TPW = 4, R = 1. Small linears want the
+//   most waves; measured on the whole-step sweep's launches, more chunks per
+//   lane (fewer, longer waves) or fewer (more waves) are both slower.
+// - T >= 3, 4096 rows or more: R = 2, which halves the activation chunks a
+//   wave reads per weight chunk (every wave reads the x of its segments from
+//   L2); TPW = 2 from 16384 rows when T <= 8, else 4. Measured, single cold
+//   launches at cols 4096: 4096 rows 42.0% -> 43.2% of HBM peak, 12288 rows
+//   60.9% -> 65.0%, 16384 rows 63.2% -> 67.6%, 129280 rows 75.7% -> 89.3%;
+//   4096 x 16384 (split over 4 waves) 48.5% -> 56.7%.
+// Otherwise the panel kernel with R = 4 rows per wave, splitting the segments
+// of a row over 2 or 4 waves while fewer than 4096 waves would run.
 Plan make_plan(int64_t rows, int64_t K, int64_t M) {
     Plan p;
     const int64_t T = ceil_div(K, kSegCols);
     p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     if (p.MT == 1 && T <= 16) {
         p.m1 = true;
-        p.tpw = T >= 3 ? 4 : (int)T;
+        if (T <= 2) {
+            p.tpw = (int)T;
+            p.R = 4 / p.tpw;
+        } else if (rows < 4096) {
+            p.tpw = 4;
+            p.R = 1;
+        } else {
+            p.tpw = rows >= 16384 && T <= 8 ? 2 : 4;
+            p.R = 2;
+        }
         p.sw = T <= p.tpw ? 1 : T <= 2 * p.tpw ? 2 : 4;
-        p.R = 4 / p.tpw;
         return p;
     }
     p.m1 = false;
@@ -477,7 +492,7 @@ int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s)
     if (p.m1) {
 #define FP8BLK_M1(RR, TT) \
     if (p.R == RR && p.tpw == TT) launch_m1<KIND, RR, TT>(g, blocks, s)
-        FP8BLK_M1(1, 4); else FP8BLK_M1(2, 2); else FP8BLK_M1(4, 1);
+        FP8BLK_M1(1, 4); else FP8BLK_M1(2, 4); else FP8BLK_M1(2, 2); else FP8BLK_M1(4, 1);
 #undef FP8BLK_M1
     } else {
         switch (p.MT) {
