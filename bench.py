@@ -381,15 +381,22 @@ def per_shape_launches(torch, fb, sw, reps=10):
     return out
 
 
-KERNEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_seq.hip",
-                  "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+# The sources each dominant kernel is built from: a counter summary is used
+# only while they are unchanged.
+SEQ_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_seq.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+PER_LINEAR_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip",
+                      "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+
+
+def mode_sources(mode):
+    return SEQ_SOURCES if mode == "sequence" else PER_LINEAR_SOURCES
 
 
 EXPERT_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_expert.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
 PANEL_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_mfma.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
 
 
-def source_hash(sources=KERNEL_SOURCES):
+def source_hash(sources):
     import hashlib
     h = hashlib.sha256()
     for rel in sources:
@@ -447,7 +454,7 @@ def counted_traffic(arm, mode):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(mode_sources(mode)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -626,8 +633,9 @@ def summarize_trace(stats_csv, trace_csv, command, mode="sequence"):
     for r in csv.DictReader(open(trace_csv)):
         if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"] or "k_seq" in r["Kernel_Name"]:
             by[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines += ["", "Per launch shape (grid = threads; one launch per linear: q/o 262144, kv 65536, gate/up/down "
-              "131072, head 8273920; the sequence kernel: its persistent grid):", "",
+    lines += ["", "Per launch shape (kernel<arm, rows per wave, segments per wave>, grid = threads; one launch per "
+              "linear: q/o 4096x4096, kv 1024x4096, gate/up 2048x4096, down 4096x2048, head 129280x4096; the "
+              "sequence kernel: its persistent grid):", "",
               "| kernel | grid | launches | median us | min us |", "|---|---|---|---|---|"]
     for (k, g), v in sorted(by.items(), key=lambda kv: kv[0][1]):
         v.sort()
@@ -770,11 +778,31 @@ def summarize_panel_counters(fetch_csv, write_csv, command, M, arm="fp8"):
     print("\n".join(lines))
 
 
+def m1_launch_key(rows, cols):
+    """(kernel instance, grid threads) of fp8blk_gemv's launch for an M = 1
+    linear, as the library's plan picks it (rows per wave R, segments per wave
+    TPW, waves per row sw; 4-wave workgroups): used to tell the sweep's
+    launches apart in counter and trace summaries."""
+    T = -(-cols // 1024)
+    if T <= 2:
+        tpw, R = T, 4 // T
+    elif rows < 4096:
+        tpw, R = 4, 1
+    else:
+        tpw, R = (2 if rows >= 16384 and T <= 8 else 4), 2
+    sw = 1 if T <= tpw else 2 if T <= 2 * tpw else 4
+    blocks = -(-(-(-rows // R)) // (4 // sw))
+    return (f"k_gemv_m1<0, {R}, {tpw}>", blocks * 256)
+
+
 def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"):
     """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the 1 GiB
     copies of --copy-calibration, then give the HBM bytes per launch of the
     dominant kernel: the sequence kernel (one dispatch per step), or the mean
-    over one step's per-linear launches (taken per launch shape)."""
+    over every dispatch of the per-linear kernel. (In the one-launch-per-linear
+    run every such dispatch belongs to whole sweep steps: the timed steps, and
+    per shape a graph of that shape's launches of one step, replayed, so the
+    mix of shapes is that of a step.)"""
     import csv
     import collections
 
@@ -786,27 +814,30 @@ def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"
         for r in rows:
             name = r["Kernel_Name"]
             if mode == "sequence" and "k_seq" in name:
-                gem["seq"].append(float(r["Counter_Value"]))
-            elif mode != "sequence" and ("k_gemv_m1" in name or "k_panel" in name):
-                gem[int(r["Grid_Size"])].append(float(r["Counter_Value"]))
-        return copies, {g: sorted(v)[len(v) // 2] for g, v in gem.items()}
+                gem["k_seq"].append(float(r["Counter_Value"]))
+            elif mode != "sequence" and "k_gemv_m1<" in name:
+                gem[(_short(name), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return copies, gem
 
     fc, fg = load(fetch_csv)
     wc, wg = load(write_csv)
     gib_kib = 1 << 20
     f_factor = gib_kib / (sorted(fc)[len(fc) // 2])
     w_factor = gib_kib / (sorted(wc)[len(wc) // 2])
+    mean_bytes = {k: (sum(fg[k]) / len(fg[k]) * f_factor + sum(wg[k]) / len(wg[k]) * w_factor) * 1024 for k in fg}
     if mode == "sequence":
-        per_step = {"seq": 1}
+        per_step = {"k_seq": 1}
     else:
-        # launches per sweep step by grid size (threads): q,o 262144 (86), kv 65536 (43),
-        # gate,up,down 131072 (129), head 8273920 (1)
-        per_step = {262144: 86, 65536: 43, 131072: 129, 8273920: 1}
-    tot = sum(per_step[g] * (fg[g] * f_factor + wg[g] * w_factor) * 1024 for g in per_step)
-    launches = sum(per_step.values())
-    rec = {"source_hash": source_hash(), "arm": arm, "mode": mode, "fetch_factor": round(f_factor, 4),
-           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": int(tot / launches),
-           "per_grid_kib": {str(g): {"fetch": fg[g], "write": wg[g]} for g in per_step},
+        # launches of each kernel instance and grid in one sweep step
+        per_step = collections.Counter(m1_launch_key(l.rows, l.cols) for l in __import__(
+            "block_scaled_fp8_fp8blk_amd.inputs", fromlist=["sweep_plan"]).sweep_plan().linears)
+    n = sum(per_step.values())
+    tot = sum(per_step[k] * mean_bytes[k] for k in per_step)
+    rec = {"source_hash": source_hash(mode_sources(mode)), "arm": arm, "mode": mode, "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": int(tot / n),
+           "per_dispatch_kib": {str(k): {"launches_per_step": per_step[k], "dispatches_counted": len(fg[k]),
+                                         "fetch_mean": sum(fg[k]) / len(fg[k]),
+                                         "write_mean": sum(wg[k]) / len(wg[k])} for k in per_step},
            "command": command}
     with open(counters_path(arm, mode), "w") as f:
         json.dump(rec, f, indent=1)
@@ -815,12 +846,14 @@ def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"
              f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
              f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
              f"WRITE_SIZE x {w_factor:.3f} give bytes.", "",
-             "| dispatch | launches per step | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch |",
-             "|---|---|---|---|---|"]
-    for g in per_step:
-        lines.append(f"| {'k_seq' if g == 'seq' else f'grid {g}'} | {per_step[g]} | {fg[g]:.1f} | {wg[g]:.1f} | "
-                     f"{(fg[g] * f_factor + wg[g] * w_factor) * 1024 / 1e6:.3f} |")
-    lines += ["", f"Average HBM bytes per launch over one step: {tot / launches / 1e6:.3f} MB "
+             "| kernel | grid (threads) | launches per step | dispatches counted | FETCH_SIZE KiB (mean) | "
+             "WRITE_SIZE KiB (mean) | HBM MB per launch |",
+             "|---|---|---|---|---|---|---|"]
+    for k in sorted(per_step, key=str):
+        fm, wm = sum(fg[k]) / len(fg[k]), sum(wg[k]) / len(wg[k])
+        kn, grid = (k, "persistent") if k == "k_seq" else k
+        lines.append(f"| {kn} | {grid} | {per_step[k]} | {len(fg[k])} | {fm:.1f} | {wm:.1f} | {mean_bytes[k] / 1e6:.3f} |")
+    lines += ["", f"Average HBM bytes per launch over one step: {tot / n / 1e6:.3f} MB "
               f"(source hash {rec['source_hash']})."]
     print("\n".join(lines))
 
@@ -929,7 +962,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
             "launches_per_step": launches, "avg_launch_us": round(avg_launch * 1e6, 3),
-            "avg_algo_bytes_per_launch": int(algo_per_launch), "source_hash": source_hash()}
+            "avg_algo_bytes_per_launch": int(algo_per_launch), "source_hash": source_hash(mode_sources(args.mode))}
     log(f"roofline: {kname}, avg launch {roof['avg_launch_us']} us, {achieved:.1f} GB/s algorithmic "
         f"({100 * roof['frac']:.1f}%)")
     shapes = per_shape_launches(torch, fb, sw)
