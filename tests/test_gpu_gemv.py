@@ -45,6 +45,21 @@ def test_gemv_parity(gpu, rows, cols, M, kind):
     full_parity(L, L.codes, L.scales, L.x, y8, yt, what=f"{rows}x{cols} M={M}")
 
 
+# M = 1 linears of 4096 rows or more take two rows per wave; from 16384 rows
+# (at most 8 segments) two segments per wave, the row split over 2 or 4
+# waves. Ragged rows and cols on each of these paths.
+PLAN_CASES = [(4097, 3088), (8191, 8192), (16385, 2064), (16391, 5136)]
+
+
+@pytest.mark.parametrize("rows,cols", PLAN_CASES)
+def test_gemv_parity_two_rows_per_wave(gpu, rows, cols):
+    from gpu_util import full_parity, say
+    say(f"gemv parity rows={rows} cols={cols} M=1 (two rows per wave)")
+    L = inputs.host_linear(rows, cols, 1, 11 * rows + cols)
+    _D, _s, y8, yt = _run(L)
+    full_parity(L, L.codes, L.scales, L.x, y8, yt, nthreads=16, what=f"{rows}x{cols} M=1")
+
+
 def test_gemv_tiny_config(gpu):
     from gpu_util import full_parity
     L = inputs.tiny()
