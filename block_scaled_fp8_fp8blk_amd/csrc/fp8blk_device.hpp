@@ -23,6 +23,31 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
     return as_f32(c ? (c << 23) : 0x00400000u);
 }
 
+// An e8m0 code as the scale operand of gfx950's scaled conversions
+// (v_cvt_scalef32_*). Those read only the exponent field of their f32 scale
+// and multiply by 2^(field - 127): measured over every code byte of the FP4
+// and FP8 conversions, a scale of 0.0, -0.0 or any f32 subnormal acts as
+// 2^-127, 1.5 and -1.0 act as 1.0. So byte k of a dword of codes, moved into
+// the exponent field (bits 23..30) by one shift, is its scale, code 0 (2^-127)
+// included, whatever the shift leaves in the sign and mantissa bits.
+template <int K>
+__device__ __forceinline__ float e8m0_cvt_scale(uint32_t d) {
+    static_assert(K >= 0 && K < 4, "byte of a dword");
+    return as_f32(K < 3 ? d << (23 - 8 * K) : d >> 1);
+}
+
+// Exchange lane bit 3 with the index of a register pair (x, y) inside each row
+// of 16 lanes: x'[l] = bit 3 of l ? y[l ^ 8] : x[l], y'[l] = bit 3 of l ? y[l]
+// : x[l ^ 8]. Each is one DPP move (rotate the row by 8) whose bank mask
+// writes only the lanes that change (banks 2 and 3 are lanes 8..15 of a row);
+// the other lanes keep the old value.
+__device__ __forceinline__ void swap_lane_bit3(uint32_t& x, uint32_t& y) {
+    const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)y, 0x128, 0xF, 0xC, false);
+    const uint32_t ny = (uint32_t)__builtin_amdgcn_update_dpp((int)y, (int)x, 0x128, 0xF, 0x3, false);
+    x = nx;
+    y = ny;
+}
+
 // Four e4m3 codes (little-endian bytes of d, lowest column first) times a
 // power-of-two block scale. gfx950's v_cvt_pk_f32_fp8 reads OCP E4M3 and is
 // exact (every e4m3 value is an f32 value); the product by a power of two is

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 // Memory access. Every load reads whole 128-byte lines: a weight load covers
 // 8 rows x 128 bytes (two steps of each row; lane l reads row l % 8, bytes
 // 16 (l / 8) .. +15), and three exchanges of a lane bit with a register bit
-// (permlane32, permlane16, and a row-of-16 rotation by 8 with a select) turn
+// (permlane32, permlane16, and a row-of-16 rotation by 8 under a bank mask) turn
 // the two loads of a tile into the instruction operands of both steps. The
 // activation codes of a step are read as one 32-column block per lane group
 // and exchanged likewise (permlane32, permlane16). Each lane group loads the
@@ -261,17 +261,36 @@ constexpr int ex_groups(int fmt, int M) { return fmt == kMX || M <= 8 ? 1 : 2; }
 constexpr int ex_tiles(int, int) { return 2; }
 constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
 
+// A unit's loads go through buffer resources: a resource in scalar
+// registers (base, byte count) plus a 32-bit per-lane offset that is fixed for
+// the unit, so a load needs no vector arithmetic. The weight and block-scale
+// resources of a phase start at its first step and end at the linear's last
+// byte: the hardware's range check returns zeros for any offset past that, so
+// a step past a row's end (in a last, partial window) reads the next row's
+// bytes, or zeros after the linear's last row, and never leaves the buffers.
+// Those steps are dropped in ex_compute_phase.
 template <int R, int O>
 struct ExUnit {
     const uint8_t* w;    // the unit's first row of codes
     const uint8_t* sc;   // its first row of block scales
     const uint8_t* xq;
     const uint8_t* xs;
-    uint32_t woff[R][2]; // lane: byte offset of its row in tile t, load h (rows 8h .. 8h+7 of the tile)
-    uint32_t soff[R];    // lane: byte offset of the block scales of its row n of tile t
+    int64_t w_left;      // bytes of codes from w to the linear's end
+    int64_t sc_left;     // bytes of block scales from sc to the linear's end
+    int32_t xq_bytes;    // M * K
+    int32_t xs_bytes;    // M * K / 128
+    uint32_t woff[R][2]; // lane: offset of its row in tile t, load h (rows 8h .. 8h+7 of the tile) + its chunk
+    uint32_t soff[R];    // lane: offset of the block scales of its row n of tile t + its lane group's step
     uint32_t xoff[O];    // lane: its token's codes + its 32-column block
-    uint32_t xsoff[O];   // lane: its token's row of activation scales
+    uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step
 };
+
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 on gfx9-family targets: raw 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ex_rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufferWord3);
+}
 
 template <int FMT, int R, int O, int WIN>
 struct ExWin {
@@ -292,30 +311,36 @@ __device__ __forceinline__ int ex_steps(const ExLin& d) { return d.K / kStepCols
 template <int WIN>
 __device__ __forceinline__ int ex_nwin(const ExLin& d) { return (ex_steps(d) + WIN - 1) / WIN; }
 
-template <int FMT, int R, int O>
+template <int FMT, int R, int O, int WIN>
 __device__ __forceinline__ void ex_unit(ExUnit<R, O>& U, const ExLin& d, int64_t v, int lane) {
     const int64_t r0 = v * (R * kTileRows);
-    const int n = lane & 15, g = lane >> 4;
+    const int n = lane & 15, g = lane >> 4, c = lane >> 3;
     const int64_t half = d.K / 2, sper = d.K / (FMT == kMX ? 32 : 16);
     U.w = d.w + r0 * half;
     U.sc = d.sc + r0 * sper;
     U.xq = d.xq;
     U.xs = d.xs;
+    U.w_left = (d.rows - r0) * half;
+    U.sc_left = (d.rows - r0) * sper;
+    const int nb = d.K / kActBlock;
+    U.xq_bytes = d.M * d.K;
+    U.xs_bytes = d.M * nb;
+    const uint32_t chunk = 64 * (c >> 2) + 16 * (c & 3);  // the lane's 16 bytes of a step pair's 128
 #pragma unroll
     for (int t = 0; t < R; ++t) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {  // rows past the end repeat the last
             const int64_t row = min(r0 + t * kTileRows + 8 * h + (lane & 7), d.rows - 1) - r0;
-            U.woff[t][h] = (uint32_t)(row * half);
+            U.woff[t][h] = (uint32_t)(row * half) + chunk;
         }
-        U.soff[t] = (uint32_t)((min(r0 + t * kTileRows + n, d.rows - 1) - r0) * sper);
+        U.soff[t] = (uint32_t)((min(r0 + t * kTileRows + n, d.rows - 1) - r0) * sper) +
+                    (FMT == kMX ? 4 : 8) * (g % WIN);
     }
-    const int nb = d.K / kActBlock;
 #pragma unroll
     for (int o = 0; o < O; ++o) {
         const int tok = min(FMT == kMX ? n : 8 * o + (n >> 1), d.M - 1);
         U.xoff[o] = (uint32_t)(tok * d.K + 32 * g);
-        U.xsoff[o] = (uint32_t)(tok * nb);
+        U.xsoff[o] = (uint32_t)(tok * nb) + g % WIN;
     }
 }
 
@@ -344,60 +369,61 @@ __device__ __forceinline__ ExPos ex_next(const ExPos& p, const ExLin* lin, const
     return n;
 }
 
-typedef __attribute__((address_space(1))) const uint8_t global_u8;
-typedef __attribute__((address_space(1))) const uint32_t global_u32;
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) const v2u global_v2u;
-__device__ __forceinline__ uint2 load_global8(const void* p) {
-    const v2u v = *(global_v2u*)p;
-    return make_uint2(v.x, v.y);
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, bool stream) {
+    const auto v = stream ? __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 2)   // nontemporal
+                          : __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // The loads of phase q (steps 2q and 2q + 1) of window `win` of a unit; phase 0
-// also loads the window's block scales and activation scales. Steps past the
-// last one (in a last, partial window) repeat the last step's addresses, lane
-// by lane; their activations are zeroed in ex_compute_phase. No branch: every
-// window issues the same loads.
+// also loads the window's block scales and activation scales. No branch:
+// every window issues the same loads. The activation steps are clamped to
+// the last step (uniformly); the weight and scale resources of a step past
+// the end read what ExUnit describes.
 template <int FMT, int R, int O, int WIN>
 __device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
-                                               int q, int lane) {
-    const int c = lane >> 3, g = lane >> 4;  // weight chunk of the 128-byte line; lane group
+                                               int q) {
     const int s0 = win * WIN;
-    const uint32_t coff = 64 * min(s0 + 2 * q + (c >> 2), steps - 1) + 16 * (c & 3);
+    const int sp = s0 + 2 * q;  // first step of the phase
+    const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 64 * sp, U.w_left - 64 * sp);
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) b.b[q][t][h] = load_stream16(U.w + U.woff[t][h] + coff);
-    const int js = min(s0 + (g % WIN), steps - 1);  // the step whose scales this lane group loads
+        for (int h = 0; h < 2; ++h) b.b[q][t][h] = buf_load16(wr, U.woff[t][h], 0, true);
     if (q == 0) {
+        constexpr int SB = FMT == kMX ? 4 : 8;  // block-scale bytes of a row per step
+        const __amdgpu_buffer_rsrc_t sr = ex_rsrc(U.sc + SB * s0, U.sc_left - SB * s0);
 #pragma unroll
         for (int t = 0; t < R; ++t) {
-            if constexpr (FMT == kMX)
-                b.bs[t] = *(global_u32*)(U.sc + U.soff[t] + 4 * js);
-            else
-                b.bs[t] = load_global8(U.sc + U.soff[t] + 8 * js);
+            if constexpr (FMT == kMX) {
+                b.bs[t] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)U.soff[t], 0, 0);
+            } else {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)U.soff[t], 0, 0);
+                b.bs[t] = make_uint2(v[0], v[1]);
+            }
         }
     }
+    const __amdgpu_buffer_rsrc_t xr = ex_rsrc(U.xq, U.xq_bytes);
 #pragma unroll
     for (int s = 2 * q; s < 2 * q + 2; ++s) {
         const int j = min(s0 + s, steps - 1);
 #pragma unroll
         for (int o = 0; o < O; ++o) {
-            b.a[s][o][0] = load_global16(U.xq + U.xoff[o] + kStepCols * j);
-            b.a[s][o][1] = load_global16(U.xq + U.xoff[o] + kStepCols * j + 16);
+            b.a[s][o][0] = buf_load16(xr, U.xoff[o], kStepCols * j, false);
+            b.a[s][o][1] = buf_load16(xr, U.xoff[o] + 16, kStepCols * j, false);
         }
     }
     if (q == 0) {
+        const __amdgpu_buffer_rsrc_t ar = ex_rsrc(U.xs + s0, U.xs_bytes - s0);
 #pragma unroll
-        for (int o = 0; o < O; ++o) b.as[o] = *(global_u8*)(U.xs + U.xsoff[o] + js);
+        for (int o = 0; o < O; ++o) b.as[o] = __builtin_amdgcn_raw_buffer_load_b8(ar, (int)U.xsoff[o], 0, 0);
     }
 }
 
 template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
-                                         int lane) {
+__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win) {
 #pragma unroll
-    for (int q = 0; q < WIN / 2; ++q) ex_issue_phase(b, U, steps, win, q, lane);
+    for (int q = 0; q < WIN / 2; ++q) ex_issue_phase(b, U, steps, win, q);
 }
 
 // Exchange of lane bit 5 (permlane32) or 4 (permlane16) with the index of a
@@ -413,23 +439,13 @@ __device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
     x = r[0];
     y = r[1];
 }
-// The same for lane bit 3, through the rotation of each row of 16 lanes by 8
-// (lane l reads lane l ^ 8) and a select.
-__device__ __forceinline__ void swap8(uint32_t& x, uint32_t& y, bool bit3) {
-    const uint32_t xr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowRor8, 0xF, 0xF, false);
-    const uint32_t yr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, kRowRor8, 0xF, 0xF, false);
-    const uint32_t nx = bit3 ? yr : x, ny = bit3 ? y : xr;
-    x = nx;
-    y = ny;
-}
-
 // The two loads of a tile (L[h][d]: load h, dword d; lane l holds row
 // (l % 8) + 8h, chunk l / 8 of the step pair's 128 bytes) -> the operands
 // op[s][k] of step s of the pair, 32-column block k: lane (n, g) = (l % 16,
 // l / 16) holds row n, columns 8g .. 8g+7 of the block. Chunk bits
 // (c2 c1 c0) = lane bits (5 4 3) become (s, k1, k0) = register bits, and
 // (d1, d0, h) become lane bits (5, 4, 3).
-__device__ __forceinline__ void weights_to_operands(const uint4 (&ld)[2], uint32_t (&op)[2][4], bool bit3) {
+__device__ __forceinline__ void weights_to_operands(const uint4 (&ld)[2], uint32_t (&op)[2][4]) {
     uint32_t L[2][4] = {{ld[0].x, ld[0].y, ld[0].z, ld[0].w}, {ld[1].x, ld[1].y, ld[1].z, ld[1].w}};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -439,7 +455,7 @@ __device__ __forceinline__ void weights_to_operands(const uint4 (&ld)[2], uint32
         swap16(L[h][2], L[h][3]);
     }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) swap8(L[0][d], L[1][d], bit3);  // h <-> lane bit 3
+    for (int d = 0; d < 4; ++d) swap_lane_bit3(L[0][d], L[1][d]);  // h <-> lane bit 3
     // register (h, d1, d0) now holds chunk c = 4 d1 + 2 d0 + h: step d1, block 2 d0 + h
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -502,7 +518,6 @@ __device__ __forceinline__ v8bf fp8x8_operand(uint2 d, float s) {
     return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ uint32_t byte_of(uint32_t d, int k) { return (d >> (8 * k)) & 0xFFu; }
 
 // Every step's block scales and activation scales of a window, from the lane
 // groups that loaded them (MXFP4 uses ws only; NVFP4 ws and ws_hi).
@@ -534,33 +549,43 @@ template <int FMT, int R, int O, int WIN>
 __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN>& b, const ExScales<R, O, WIN>& S,
                                                  int steps, int win, int q, int lane, v4f* acc) {
     const int g = lane >> 4;
-    const bool bit3 = (lane & 8) != 0;
     uint32_t wop[R][2][4];
 #pragma unroll
-    for (int t = 0; t < R; ++t) weights_to_operands(b.b[q][t], wop[t], bit3);
+    for (int t = 0; t < R; ++t) weights_to_operands(b.b[q][t], wop[t]);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
         const int s = 2 * q + s2;
         const bool live = win * WIN + s < steps;  // wave-uniform
+        // MXFP4: a step past the row's end (in a last, partial window) adds
+        // nothing; a wave-uniform branch skips it.
+        if (FMT == kMX && !live) continue;
         v8bf A[4][O];
 #pragma unroll
         for (int o = 0; o < O; ++o) {
             uint2 ap[4];
             act_to_operands(b.a[s][o], ap);
-            const float sa = e8m0_to_f32(byte_of(S.as[o][s], 0));
-            // NVFP4: selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
-            // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
-            const bool keep = live && (FMT == kMX || (g >> 1) == (lane & 1));
+            const float sa = e8m0_cvt_scale<0>(S.as[o][s]);
+            if constexpr (FMT == kMX) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
+                for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(ap[k], sa);
+            } else {
+                // selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
+                // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
+                const bool keep = live && (g >> 1) == (lane & 1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
+            }
         }
 #pragma unroll
         for (int t = 0; t < R; ++t) {
             if constexpr (FMT == kMX) {
+                const uint32_t ws = S.ws[t][s];
+                const float sw[4] = {e8m0_cvt_scale<0>(ws), e8m0_cvt_scale<1>(ws), e8m0_cvt_scale<2>(ws),
+                                     e8m0_cvt_scale<3>(ws)};
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        A[k][0], fp4x8_operand(wop[t][s2][k], e8m0_to_f32(byte_of(S.ws[t][s], k))), acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][0], fp4x8_operand(wop[t][s2][k], sw[k]),
+                                                                     acc[t], 0, 0, 0);
             } else {
                 // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + parity
                 const v2f sc[4] = {e4m3_pair<false>(S.ws[t][s]), e4m3_pair<true>(S.ws[t][s]),
@@ -626,14 +651,14 @@ __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, ExU
     constexpr int NACC = R * O;
     ExScales<R, O, WIN> S;
     ex_gather(set, S);
-    if (nxt.win == 0 && nxt.more) ex_unit<FMT>(un, nxt.d, nxt.v, lane);
+    if (nxt.win == 0 && nxt.more) ex_unit<FMT, R, O, WIN>(un, nxt.d, nxt.v, lane);
     const int csteps = ex_steps(cur.d), nsteps = ex_steps(nxt.d);
 #pragma unroll
     for (int q = 0; q < WIN / 2; ++q) {
         __builtin_amdgcn_sched_barrier(0);
         ex_compute_phase(set, S, csteps, cur.win, q, lane, acc);
         __builtin_amdgcn_sched_barrier(0);  // the phase's registers are free: refill them
-        ex_issue_phase(set, un, nsteps, nxt.win, q, lane);
+        ex_issue_phase(set, un, nsteps, nxt.win, q);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (cur.win + 1 == ex_nwin<WIN>(cur.d)) {
@@ -670,16 +695,16 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
         p0.v = p0.u;
     }
     Unit ua, ub;
-    ex_unit<FMT>(ua, p0.d, p0.v, lane);
+    ex_unit<FMT, R, O, WIN>(ua, p0.d, p0.v, lane);
     v4f acc[NACC];
 #pragma unroll
     for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     Win a, b;
-    ex_issue(a, ua, ex_steps(p0.d), p0.win, lane);
+    ex_issue(a, ua, ex_steps(p0.d), p0.win);
     ExPos p1 = ex_next<LIST, WIN>(p0, lin, pre, W, total);
     ub = ua;
-    if (p1.win == 0 && p1.more) ex_unit<FMT>(ub, p1.d, p1.v, lane);
-    ex_issue(b, ub, ex_steps(p1.d), p1.win, lane);
+    if (p1.win == 0 && p1.more) ex_unit<FMT, R, O, WIN>(ub, p1.d, p1.v, lane);
+    ex_issue(b, ub, ex_steps(p1.d), p1.win);
     for (;;) {
         // the window issued into a set follows the one in the other set: it
         // continues that window's unit unless it starts a new one
