@@ -609,22 +609,21 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN>& b,
     }
 }
 
-// y = g * accumulator. MXFP4: lane (n, g) holds tokens 4g .. 4g+3 of weight
-// row n. NVFP4: lane (n, g) holds tokens 8o + 2g and 8o + 2g + 1, each as two
-// block-parity accumulators, added here.
-template <int FMT, int R, int O>
-__device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, const v4f* acc) {
+// The unit's outputs y = g * accumulator, handed one by one to put(token,
+// row within the unit, value). MXFP4: lane (n, g) holds tokens 4g .. 4g+3 of
+// weight row n. NVFP4: lane (n, g) holds tokens 8o + 2g and 8o + 2g + 1, each
+// as two block-parity accumulators, added here.
+template <int FMT, int R, int O, typename Put>
+__device__ __forceinline__ void ex_outputs(const ExLin& d, int lane, const v4f* acc, Put put) {
     const int n = lane & 15, g = lane >> 4;
-    const int64_t r0 = v * (R * kTileRows);
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-        const int64_t row = r0 + t * kTileRows + n;
-        if (row >= d.rows) continue;
+        const int r = t * kTileRows + n;
         if constexpr (FMT == kMX) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tok = 4 * g + e;
-                if (tok < d.M) store_global_f32(d.y + (int64_t)tok * d.rows + row, d.g * acc[t][e]);
+                if (tok < d.M) put(tok, r, d.g * acc[t][e]);
             }
         } else {
 #pragma unroll
@@ -633,8 +632,101 @@ __device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, co
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
                     const int tok = 8 * o + 2 * g + k;
-                    if (tok < d.M) store_global_f32(d.y + (int64_t)tok * d.rows + row, d.g * (a[2 * k] + a[2 * k + 1]));
+                    if (tok < d.M) put(tok, r, d.g * (a[2 * k] + a[2 * k + 1]));
                 }
+            }
+        }
+    }
+}
+
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, const v4f* acc) {
+    const int64_t r0 = v * (R * kTileRows);
+    ex_outputs<FMT, R, O>(d, lane, acc, [&](int tok, int r, float val) {
+        if (r0 + r < d.rows) store_global_f32(d.y + (int64_t)tok * d.rows + r0 + r, val);
+    });
+}
+
+// Where a finished unit's outputs go. A stream of reads runs markedly slower
+// while writes are mixed into it than when the same bytes are written in one
+// burst after it (measured with a bare 3 GiB read by 2048 waves: 1 KB written
+// per 64 KB read costs 13% of the read rate, the same bytes written at each
+// wave's end 6%). From 8 activation rows on, the outputs are 1/50 of the
+// bytes a step reads, so each wave keeps the outputs of its first units in its
+// own part of the workgroup's LDS and writes them after its last unit; the
+// units past what that part holds are written when they finish. Only where
+// and when the outputs are stored changes, never their values.
+//
+// A slot holds one unit's outputs as y holds them: [token][row of the unit],
+// M x 32 floats. Where held unit k goes is recorded in lane k of five
+// registers (its y address, y's row stride, and its row count with the flag
+// for 16-byte stores), so the final writes load nothing but LDS.
+constexpr int kExLdsBytes = 80 * 1024;                      // per workgroup: at most 2 per compute unit
+constexpr int kExWaveLds = kExLdsBytes / kSeqWaves;         // per wave
+constexpr int kExHoldMinM = 8;                              // smallest panel whose outputs are held back
+constexpr int kExUnitRows = ex_tiles(kMX, 1) * kTileRows;   // rows of a unit (both formats)
+static_assert(ex_tiles(kNV, 2) * kTileRows == kExUnitRows, "one unit height");
+static_assert(kMfSeqBlocksPerCU * kExLdsBytes <= 160 * 1024 && (kMfSeqBlocksPerCU + 1) * kExLdsBytes > 160 * 1024,
+              "the LDS of a workgroup caps a compute unit at kMfSeqBlocksPerCU of them");
+
+struct ExOut {
+    float* lds;      // the wave's part of the workgroup's LDS
+    int slots;       // units it holds (0 below kExHoldMinM activation rows)
+    int k;           // units finished so far
+    uint32_t y_lo, y_hi, rows_lo, rows_hi, left_vec;  // lane k: record of held unit k
+};
+
+template <int FMT, int R, int O>
+__device__ __forceinline__ void ex_retire(const ExLin& d, int64_t v, int lane, const v4f* acc, ExOut& o) {
+    if (o.k < o.slots) {
+        const int64_t r0 = v * (R * kTileRows);
+        const uint64_t yu = reinterpret_cast<uint64_t>(d.y + r0);
+        const bool vec = (d.rows & 3) == 0 && (reinterpret_cast<uint64_t>(d.y) & 15) == 0;
+        const uint32_t lv = (uint32_t)min(d.rows - r0, (int64_t)kExUnitRows) | (vec ? 0x10000u : 0u);
+        const bool mine = lane == o.k;  // lane k keeps unit k's record
+        o.y_lo = mine ? (uint32_t)yu : o.y_lo;
+        o.y_hi = mine ? (uint32_t)(yu >> 32) : o.y_hi;
+        o.rows_lo = mine ? (uint32_t)d.rows : o.rows_lo;
+        o.rows_hi = mine ? (uint32_t)((uint64_t)d.rows >> 32) : o.rows_hi;
+        o.left_vec = mine ? lv : o.left_vec;
+        float* slot = o.lds + o.k * d.M * kExUnitRows;
+        ex_outputs<FMT, R, O>(d, lane, acc, [&](int tok, int r, float val) { slot[tok * kExUnitRows + r] = val; });
+    } else {
+        ex_store<FMT, R, O>(d, v, lane, acc);
+    }
+    ++o.k;
+}
+
+// After the wave's last unit: the held units go out in order, each as M rows
+// of 32 outputs, four per lane (one 16-byte store where the linear allows it).
+// (Called from inside the pipeline loop, at the last unit, as in the
+// matrix-core sequence: code after the loop makes the compiler keep more
+// registers live across it.)
+__device__ __forceinline__ void ex_flush(int lane, int M, const ExOut& o) {
+    const int held = min(o.k, o.slots);
+    constexpr int Q = kExUnitRows / 4;  // lanes per token row
+#pragma unroll 1
+    for (int k = 0; k < held; ++k) {
+        const uint64_t yu =
+            ((uint64_t)__builtin_amdgcn_readlane(o.y_hi, k) << 32) | (uint32_t)__builtin_amdgcn_readlane(o.y_lo, k);
+        const int64_t rows = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(o.rows_hi, k) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane(o.rows_lo, k));
+        const uint32_t lv = __builtin_amdgcn_readlane(o.left_vec, k);
+        const int left = (int)(lv & 0xffffu);
+        const bool vec = (lv >> 16) != 0;
+        const float* slot = o.lds + k * M * kExUnitRows;
+        float* y = reinterpret_cast<float*>(yu);
+        for (int i = lane; i < M * Q; i += kLanes) {
+            const int tok = i / Q, r = 4 * (i % Q);
+            const v4f val = *reinterpret_cast<const v4f*>(slot + tok * kExUnitRows + r);
+            float* dst = y + (int64_t)tok * rows + r;
+            if (vec && r + 3 < left) {
+                typedef __attribute__((address_space(1))) v4f global_v4f;
+                __builtin_nontemporal_store(val, (global_v4f*)dst);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (r + e < left) store_global_f32(dst + e, val[e]);
             }
         }
     }
@@ -644,10 +736,11 @@ __device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, co
 // window `cur`, phase by phase, each phase's registers refilled with the
 // loads of window `nxt` (two windows ahead) as soon as they are consumed, so
 // that about two windows of loads stay in flight while the wave computes;
-// then the stores of cur's outputs. `un` addresses the windows of `set`.
+// then, at the end of cur's unit, its outputs; after the wave's last window
+// (`last`), what LDS holds. `un` addresses the windows of `set`.
 template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, ExUnit<R, O>& un,
-                                         ExWin<FMT, R, O, WIN>& set, int lane, v4f* acc) {
+__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnit<R, O>& un,
+                                         ExWin<FMT, R, O, WIN>& set, int lane, v4f* acc, ExOut& out) {
     constexpr int NACC = R * O;
     ExScales<R, O, WIN> S;
     ex_gather(set, S);
@@ -662,9 +755,10 @@ __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, ExU
     }
     __builtin_amdgcn_sched_barrier(0);
     if (cur.win + 1 == ex_nwin<WIN>(cur.d)) {
-        ex_store<FMT, R, O>(cur.d, cur.v, lane, acc);
+        ex_retire<FMT, R, O>(cur.d, cur.v, lane, acc, out);
 #pragma unroll
         for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        if (last) ex_flush(lane, cur.d.M, out);
     }
 }
 
@@ -678,10 +772,12 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     constexpr int NACC = R * O;
     using Win = ExWin<FMT, R, O, WIN>;
     using Unit = ExUnit<R, O>;
+    extern __shared__ __attribute__((aligned(16))) float ex_lds[];
     const int lane = threadIdx.x % kLanes;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     ExPos p0;
-    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + wave;
     if (p0.u >= total) return;
     p0.win = 0;
     p0.j = 0;
@@ -694,6 +790,13 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
         p0.d = one;
         p0.v = p0.u;
     }
+    // Every linear of a list has the same M (the plan checks it).
+    ExOut out;
+    out.lds = ex_lds + wave * (kExWaveLds / 4);
+    const int slot_floats = p0.d.M * kExUnitRows;
+    out.slots = p0.d.M >= kExHoldMinM ? min(kLanes, kExWaveLds / 4 / slot_floats) : 0;
+    out.k = 0;
+    out.y_lo = out.y_hi = out.rows_lo = out.rows_hi = out.left_vec = 0;
     Unit ua, ub;
     ex_unit<FMT, R, O, WIN>(ua, p0.d, p0.v, lane);
     v4f acc[NACC];
@@ -710,11 +813,11 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
         // continues that window's unit unless it starts a new one
         const ExPos p2 = ex_next<LIST, WIN>(p1, lin, pre, W, total);
         ua = ub;
-        ex_stage(p0, p2, ua, a, lane, acc);
+        ex_stage(p0, p2, !p1.more, ua, a, lane, acc, out);
         if (!p1.more) break;
         const ExPos p3 = ex_next<LIST, WIN>(p2, lin, pre, W, total);
         ub = ua;
-        ex_stage(p1, p3, ub, b, lane, acc);
+        ex_stage(p1, p3, !p2.more, ub, b, lane, acc, out);
         if (!p2.more) break;
         p0 = p2;
         p1 = p3;
@@ -739,7 +842,7 @@ int ex_grid(int64_t units) {
 template <int FMT, int O, bool LIST>
 void ex_launch_o(const ExLin* lin, const int64_t* pre, int64_t total, const ExLin& one, int grid, hipStream_t s) {
     constexpr int R = ex_tiles(FMT, O), WIN = ex_win(FMT, O);
-    constexpr int lds = lds_cap_bytes(kMfSeqBlocksPerCU);
+    constexpr int lds = kExLdsBytes;
     k_expert<FMT, R, O, WIN, LIST><<<dim3((unsigned)grid), dim3(kSeqWaves * kLanes), lds, s>>>(lin, pre, total, one);
 }
 

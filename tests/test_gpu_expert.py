@@ -243,7 +243,7 @@ def test_sequence_many_units_per_wave(gpu, gu, fmt, M):
     and ragged rows: every output equals its single call bit for bit; a sample
     is checked against the oracle."""
     rng = np.random.default_rng(500 + fmt + M)
-    rows_choices, cols_choices = (48, 100, 2048, 4096), (384, 640, 1152, 2176, 4096)
+    rows_choices, cols_choices = (45, 48, 100, 2048, 4096), (384, 640, 1152, 2176, 4096)
     lins, ins = [], []
     acts = {}
     for k in range(360):
@@ -273,30 +273,32 @@ def test_sequence_many_units_per_wave(gpu, gu, fmt, M):
         gu.assert_within_tolerance(y.cpu().numpy(), y64, yabs, what=f"linear {k} {r}x{c}")
 
 
-@pytest.mark.parametrize("fmt", [MX, NV])
-def test_expert_sweep_as_benchmarked(gpu, gu, fmt):
+@pytest.mark.parametrize("fmt,M", [(MX, 1), (NV, 1), (MX, 8), (NV, 8)])
+def test_expert_sweep_as_benchmarked(gpu, gu, fmt, M):
     """The benchmark's launch: the 1032 routed-expert linears of one decode
-    step (device-drawn, load-checked) in one sequence launch at M = 1. Every
-    output equals its single call bitwise; 32-row windows of a few linears are
-    checked against the oracle."""
+    step (device-drawn, load-checked) in one sequence launch, at M = 1 and with
+    an 8-row panel (then each wave finishes ~43 units, more than it holds back
+    to the end of the launch: the held and the directly written outputs are
+    both checked). Every output equals its single call bitwise; 32-row windows
+    of a few linears are checked against the oracle."""
     plan = I.expert_sweep_plan()
     ws = torch.empty(256, dtype=torch.uint8, device=gu.DEV)
     acts = {}
     for c in sorted({sp.cols for sp in plan}):
-        x = gu.to_dev(I.host_fp4_linear(fmt, 1, c, 1, 70 + c).x)
+        x = gu.to_dev(I.host_fp4_linear(fmt, 1, c, M, 70 + c).x)
         acts[c] = (x, *act_quant_gpu(gpu, x))
     g = 1.0 if fmt == MX else 2.0 ** -6
     lins, ins = [], []
     for sp in plan:
         codes, scales = I.device_fp4_linear(fmt, sp.rows, sp.cols, sp.seed, gu.DEV)
         assert gpu.fp4_load_check(fmt, codes, scales, ws, check=False) == (0, -1), sp.name
-        y = torch.full((1, sp.rows), float("nan"), dtype=torch.float32, device=gu.DEV)
+        y = torch.full((M, sp.rows), float("nan"), dtype=torch.float32, device=gu.DEV)
         ins.append((sp, codes, scales, y))
         lins.append((codes, scales, g, acts[sp.cols][1], acts[sp.cols][2], y))
     seq = gpu.fp4_expert_sequence_init(fmt, lins)
     gpu.fp4_expert_sequence(seq)
     torch.cuda.synchronize()
-    gu.say(f"  expert sweep fmt {fmt}: {len(lins)} linears launched")
+    gu.say(f"  expert sweep fmt {fmt} M {M}: {len(lins)} linears launched")
     for i, (sp, codes, scales, y) in enumerate(ins):
         single = expert_gemv_gpu(gpu, fmt, codes, scales, g, acts[sp.cols][1], acts[sp.cols][2], sp.rows)
         assert torch.equal(y.view(torch.int32), single.view(torch.int32)), (i, sp.name)
