@@ -95,11 +95,15 @@ __device__ __forceinline__ void exchange(uint4& p, uint4& q, bool hi) {
     uint32_t* qq = reinterpret_cast<uint32_t*>(&q);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t px = lane_flip<B>(pp[d]), qx = lane_flip<B>(qq[d]);
-        const uint32_t np = hi ? qx : pp[d];
-        const uint32_t nq = hi ? qq[d] : px;
-        pp[d] = np;
-        qq[d] = nq;
+        if constexpr (B == 3) {
+            swap_lane_bit3(pp[d], qq[d]);  // two bank-masked DPP moves, no selects
+        } else {
+            const uint32_t px = lane_flip<B>(pp[d]), qx = lane_flip<B>(qq[d]);
+            const uint32_t np = hi ? qx : pp[d];
+            const uint32_t nq = hi ? qq[d] : px;
+            pp[d] = np;
+            qq[d] = nq;
+        }
     }
 }
 
