@@ -148,7 +148,7 @@ def test_mfma_sequence_whole_step_sweep(gpu):
     say(f"  {len(lins)} sweep linears at M=16 checked")
 
 
-@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("M", [8, 11, 16])
 def test_mfma_sequence_more_units_than_held(gpu, M):
     """A list long enough that every wave finishes more units than its LDS part
     and its registers hold (about 14 units per wave with 1.8M rows of 128
