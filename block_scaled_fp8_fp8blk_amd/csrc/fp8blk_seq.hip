@@ -125,7 +125,15 @@ __device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, in
     const int64_t r0 = v * (S >> tl);
     const char* b0 = static_cast<const char*>(L.w) + (r0 * L.K + (int64_t)k * 4 * kSegCols) * E;
     const int64_t H = (tl == 2 ? L.K : 4 * kSegCols) * E;
-    const uint32_t lo = (uint32_t)lane * (kChunk * E);
+    // FP8: lane l reads its chunk's 16 bytes, one 1 KB run per instruction.
+    // bf16: a chunk is 32 bytes, and two loads of lane l's own 16-byte halves
+    // would each touch every line of the segment's 2 KB half-used. Instead
+    // load 0 reads the first KB and load 1 the second, lane m taking 16-byte
+    // piece 2m (m < 32) or 2(m - 32) + 1 (m >= 32) of it; the exchange of the
+    // two lane halves in twin_chunk then hands lane l pieces 2l and 2l + 1,
+    // its chunk. Measured on the whole-step sweep: 1.14 -> 0.92 ms per step
+    // with contiguous loads.
+    const uint32_t lo = KIND == kFp8 ? (uint32_t)lane * kChunk : 16u * (lane < 32 ? 2 * lane : 2 * lane - 63);
 #pragma unroll
     for (int s = p; s < S; s += 4) {
         const char* a = b0 + (s >> 2) * H + p * kSegCols * E + lo;
@@ -133,7 +141,7 @@ __device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, in
             raw.c[s] = load_stream16(a);
         } else {
             raw.c[s][0] = load_stream16(a);
-            raw.c[s][1] = load_stream16(a + 16);
+            raw.c[s][1] = load_stream16(a + kSegCols);
         }
     }
     const char* xp = reinterpret_cast<const char*>(L.x) + ((int64_t)k * 4 + (p & tm)) * kSegCols * 2 + (uint32_t)lane * 32;
@@ -191,6 +199,26 @@ __device__ __forceinline__ void load_step(const SeqLin& L, int64_t v, int k, int
     for (int p = 0; p < 4; ++p) load_phase<KIND, DENSE>(L, v, k, lane, p, raw);
 }
 
+// The dense path's two bf16 loads of a slot -> lane l's chunk (columns
+// 16 l .. 16 l + 15 of the segment, lower half first). permlane32_swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes
+// of its second: afterwards the first holds piece 2l (lanes < 32: their own
+// load 0; lanes >= 32: load 1 of lane l - 32) and the second piece 2l + 1
+// (load 0 of lane l + 32; their own load 1).
+__device__ __forceinline__ void twin_chunk(const uint4 (&ld)[2], uint4& lo, uint4& hi) {
+    const uint32_t a[4] = {ld[0].x, ld[0].y, ld[0].z, ld[0].w};
+    const uint32_t b[4] = {ld[1].x, ld[1].y, ld[1].z, ld[1].w};
+    uint32_t x[4], y[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
+        x[d] = r[0];
+        y[d] = r[1];
+    }
+    lo = make_uint4(x[0], x[1], x[2], x[3]);
+    hi = make_uint4(y[0], y[1], y[2], y[3]);
+}
+
 // Phase p of the arithmetic of step k: the lane partials of slots p, p + 4,
 // ... (one FMA chain over each chunk's 16 columns, from +0.0), into part.
 template <int KIND, bool DENSE>
@@ -207,6 +235,11 @@ __device__ __forceinline__ void compute_phase(const SeqLin& L, int k, int lane, 
         float w[kChunk];
         if constexpr (KIND == kFp8) {
             decode16_fp8_scaled(raw.c[s], raw.s[p], w);
+        } else if constexpr (DENSE) {
+            uint4 lo, hi;
+            twin_chunk(raw.c[s], lo, hi);
+            widen8_bf16(lo, w);
+            widen8_bf16(hi, w + 8);
         } else {
             widen8_bf16(raw.c[s][0], w);
             widen8_bf16(raw.c[s][1], w + 8);
