@@ -48,6 +48,22 @@ __device__ __forceinline__ void swap_lane_bit3(uint32_t& x, uint32_t& y) {
     y = ny;
 }
 
+// Exchange the upper 32 lanes of a with the lower 32 lanes of b, dword by
+// dword (permlane32_swap): afterwards a[l] = l < 32 ? a[l] : b[l - 32] and
+// b[l] = l < 32 ? a[l + 32] : b[l]. The bf16 slab kernels load 16-byte pieces
+// so that each load instruction reads whole lines; this swap then hands lane
+// l the two halves of its own 32-byte chunk.
+__device__ __forceinline__ void swap_lane_halves(uint4& a, uint4& b) {
+    uint32_t* pa = reinterpret_cast<uint32_t*>(&a);
+    uint32_t* pb = reinterpret_cast<uint32_t*>(&b);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(pa[d], pb[d], false, false);
+        pa[d] = r[0];
+        pb[d] = r[1];
+    }
+}
+
 // Four e4m3 codes (little-endian bytes of d, lowest column first) times a
 // power-of-two block scale. gfx950's v_cvt_pk_f32_fp8 reads OCP E4M3 and is
 // exact (every e4m3 value is an f32 value); the product by a power of two is

@@ -44,6 +44,7 @@ struct GemvArgs {
     int sw;              // waves per row stream: 1, 2 or 4
     int sw_log2;         // log2(sw)
     int tpw;             // segments per wave, ceil(T / sw)
+    int whole;           // 1: cols is a multiple of 1024 (every segment whole; bf16 loads read whole lines)
 };
 
 enum Kind { kFp8 = 0, kBf16 = 1 };
@@ -66,7 +67,9 @@ struct Fetch<kFp8> {
         raw.s = a.grid[(r >> 7) * a.GC + (q >> 3)];  // chunk q lies in column block q / 8
         return raw;
     }
-    __device__ __forceinline__ static void weights(const Raw& raw, float* w) { decode16_fp8_scaled(raw.c, raw.s, w); }
+    __device__ __forceinline__ static void weights(const Raw& raw, float* w, bool) {
+        decode16_fp8_scaled(raw.c, raw.s, w);
+    }
     // Codes only of rows r0 .. r0 + n - 1 (clamped to the last row) of chunk
     // q; the scales are filled in by the caller.
     template <int N, int TPW>
@@ -91,6 +94,13 @@ struct Fetch<kFp8> {
     }
 };
 
+// The bf16 slab: a chunk is 32 bytes. Loading a lane's own two halves would
+// make each load instruction read every other 16 bytes of the segment's 2 KB
+// (half of every line it touches). When every segment is whole (a.whole), load
+// 0 reads the segment's first KB and load 1 the second, lane m taking 16-byte
+// piece 2m (m < 32) or 2(m - 32) + 1, i.e. elements +0 / +512 (m < 32) or
+// -504 / +8 (m >= 32) from its own chunk, and swap_lane_halves hands every
+// lane its own two halves back before the arithmetic.
 template <>
 struct Fetch<kBf16> {
     struct Raw {
@@ -98,14 +108,18 @@ struct Fetch<kBf16> {
     };
     __device__ __forceinline__ static Raw load(const GemvArgs& a, int64_t r, int q) {
         const uint16_t* p = static_cast<const uint16_t*>(a.w) + r * a.K + (int64_t)q * kChunk;
+        const bool upper = (threadIdx.x & 32) != 0;  // lanes 32..63 of the wave
+        const int d0 = a.whole && upper ? -504 : 0, d1 = !a.whole ? 8 : upper ? 8 : 512;
         Raw raw;
-        raw.lo = load_stream16(p);
-        raw.hi = load_stream16(p + 8);
+        raw.lo = load_stream16(p + d0);
+        raw.hi = load_stream16(p + d1);
         return raw;
     }
-    __device__ __forceinline__ static void weights(const Raw& raw, float* w) {
-        widen8_bf16(raw.lo, w);
-        widen8_bf16(raw.hi, w + 8);
+    __device__ __forceinline__ static void weights(const Raw& raw, float* w, bool whole) {
+        uint4 lo = raw.lo, hi = raw.hi;
+        if (whole) swap_lane_halves(lo, hi);
+        widen8_bf16(lo, w);
+        widen8_bf16(hi, w + 8);
     }
     template <int N, int TPW>
     __device__ __forceinline__ static void load_rows(const GemvArgs& a, int64_t r0, int n, int q, Raw (&raw)[N][TPW],
@@ -164,7 +178,7 @@ __device__ __forceinline__ void panel_body(const GemvArgs& a, int64_t block) {
         const int qc = min(q, last_q);
         float w[R][kChunk];
 #pragma unroll
-        for (int i = 0; i < R; ++i) F::weights(raw[i][0], w[i]);
+        for (int i = 0; i < R; ++i) F::weights(raw[i][0], w[i], a.whole != 0);
         float v[VP];
 #pragma unroll
         for (int k = 0; k < VP; ++k) v[k] = 0.0f;
@@ -294,7 +308,7 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             float w[kChunk];
-            F::weights(raw[i][u], w);
+            F::weights(raw[i][u], w, a.whole != 0);
             float s = 0.0f;
 #pragma unroll
             for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[j], xf[j], s);
@@ -484,6 +498,7 @@ int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s)
     a.sw = p.sw;
     a.sw_log2 = p.sw == 4 ? 2 : p.sw == 2 ? 1 : 0;
     a.tpw = (int)ceil_div(a.T, p.sw);
+    a.whole = KIND == kBf16 && cols % kSegCols == 0;
     g.start[0] = 0;
     for (int j = 0; j < g.n; ++j) g.start[j + 1] = g.start[j] + blocks_for(p, g.rows[j]);
     const int64_t blocks = g.start[g.n];

@@ -117,13 +117,14 @@ struct MfFetch<0> {  // FP8: 16 codes per row half, decoded in registers
         uint4 c[2];  // [row half q]
     };
     // col: first column of the lane's chunk (already clamped into the row)
-    __device__ __forceinline__ static void load(Raw& raw, const MfArgs& a, int64_t r_lo, int64_t r_hi, int col) {
+    __device__ __forceinline__ static void load(Raw& raw, const MfArgs& a, int64_t r_lo, int64_t r_hi, int col, bool,
+                                                int) {
         const uint8_t* w = static_cast<const uint8_t*>(a.w);
         raw.c[0] = load_stream16(w + r_lo * a.K + col);
         raw.c[1] = load_stream16(w + r_hi * a.K + col);
     }
     // The four 8-wide operands, [u][v], after the exchange.
-    __device__ __forceinline__ static void operands(Raw raw, float sc, bool hi, v8bf op[2][2]) {
+    __device__ __forceinline__ static void operands(Raw raw, float sc, bool hi, bool, v8bf op[2][2]) {
         exchange<3>(raw.c[0], raw.c[1], hi);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -142,19 +143,40 @@ struct MfFetch<0> {  // FP8: 16 codes per row half, decoded in registers
     }
 };
 
+// The bf16 slab: a lane's 16 columns are 32 bytes of its row. Loading its own
+// two 16-byte halves would make each load instruction read every other 16
+// bytes of the rows' 256-byte windows (half of every line it touches). In a
+// full window, load 0 reads the first 128 bytes of the row and load 1 the
+// second, lane chunk c = l / 8 taking 16-byte piece 2c (c < 4) or 2(c - 4) + 1
+// (c >= 4), i.e. bytes +0 / +128 (c < 4) or -112 / +16 (c >= 4) from its own
+// chunk; swap_lane_halves (lanes l and l + 32 hold chunks c and c + 4 of the
+// same rows) then hands every lane its own two halves. A ragged last window
+// keeps the per-lane loads (no swap).
+__device__ __forceinline__ uint32_t twin_piece_shift(int lane) { return lane >= 32 ? (uint32_t)-112 : 0u; }
+
 template <>
 struct MfFetch<1> {  // bf16 slab: the same 16 columns are 32 bytes, two loads per row half
     struct Raw {
         uint4 c[2][2];  // [h][row half q]
     };
-    __device__ __forceinline__ static void load(Raw& raw, const MfArgs& a, int64_t r_lo, int64_t r_hi, int col) {
-        const uint16_t* w = static_cast<const uint16_t*>(a.w);
-        raw.c[0][0] = load_stream16(w + r_lo * a.K + col);
-        raw.c[1][0] = load_stream16(w + r_lo * a.K + col + 8);
-        raw.c[0][1] = load_stream16(w + r_hi * a.K + col);
-        raw.c[1][1] = load_stream16(w + r_hi * a.K + col + 8);
+    // col: first column of the lane's chunk (already clamped into the row);
+    // full: the window's 128 columns all exist (wave-uniform)
+    __device__ __forceinline__ static void load(Raw& raw, const MfArgs& a, int64_t r_lo, int64_t r_hi, int col,
+                                                bool full, int lane) {
+        const char* w = static_cast<const char*>(a.w);
+        const uint32_t d0 = full ? twin_piece_shift(lane) : 0u, d1 = full ? d0 + 128u : 16u;
+        const char* lo = w + (r_lo * a.K + col) * 2;
+        const char* hi = w + (r_hi * a.K + col) * 2;
+        raw.c[0][0] = load_stream16(lo + (int32_t)d0);
+        raw.c[1][0] = load_stream16(lo + (int32_t)d1);
+        raw.c[0][1] = load_stream16(hi + (int32_t)d0);
+        raw.c[1][1] = load_stream16(hi + (int32_t)d1);
     }
-    __device__ __forceinline__ static void operands(Raw raw, float, bool hi, v8bf op[2][2]) {
+    __device__ __forceinline__ static void operands(Raw raw, float, bool hi, bool full, v8bf op[2][2]) {
+        if (full) {
+            swap_lane_halves(raw.c[0][0], raw.c[1][0]);
+            swap_lane_halves(raw.c[0][1], raw.c[1][1]);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             exchange<3>(raw.c[h][0], raw.c[h][1], hi);
@@ -182,6 +204,7 @@ struct MfLane {
     int xcol;                 // 8 G
     const uint16_t* xrow[4];  // panel rows 8 l3 + 4 l2 + 2 n1 + n0, clamped to M - 1
     bool b0, b1, b3;          // lane bits 0, 1, 3
+    int lane;
 };
 
 template <int KIND, int TILES, int XR>
@@ -192,7 +215,7 @@ __device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, XR>& b, const MfA
     for (int t = 0; t < TILES; ++t) {
         const int64_t lo = min(L.r0 + t * kTile + L.r, a.rows - 1);
         const int64_t hi = min(L.r0 + t * kTile + 8 + L.r, a.rows - 1);
-        MfFetch<KIND>::load(b.w[t], a, lo, hi, wcol);
+        MfFetch<KIND>::load(b.w[t], a, lo, hi, wcol, base + kBlock <= a.K, L.lane);
     }
     const int xc = min(base + L.xcol, a.K - 8);
 #pragma unroll
@@ -220,7 +243,7 @@ __device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, XR> b, const Mf
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
         v8bf op[2][2];
-        MfFetch<KIND>::operands(b.w[t], b.sc, L.b3, op);
+        MfFetch<KIND>::operands(b.w[t], b.sc, L.b3, base + kBlock <= a.K, op);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -253,6 +276,7 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
     L.b0 = (lane & 1) != 0;
     L.b1 = (lane & 2) != 0;
     L.b3 = (lane & 8) != 0;
+    L.lane = lane;
     const int wb = sp * a.bpp;
     const int we = min(a.nwin, wb + a.bpp);
 
@@ -481,10 +505,14 @@ __device__ __forceinline__ void mf_seq_issue(MfWindow<KIND, TILES, XR>& b, const
             b.w[t].c[0] = load_stream16(wsrc + lo);
             b.w[t].c[1] = load_stream16(wsrc + hi);
         } else {
-            b.w[t].c[0][0] = load_stream16(wsrc + lo);
-            b.w[t].c[1][0] = load_stream16(wsrc + lo + 16);
-            b.w[t].c[0][1] = load_stream16(wsrc + hi);
-            b.w[t].c[1][1] = load_stream16(wsrc + hi + 16);
+            // contiguous pieces in a full window (see MfFetch<1>); not with 4
+            // tiles, whose registers could then hold only one wave per SIMD
+            const bool full = TILES < 4 && base + kBlock <= K;
+            const uint32_t d0 = full ? twin_piece_shift(lane) : 0u, d1 = full ? d0 + 128u : 16u;
+            b.w[t].c[0][0] = load_stream16(wsrc + (uint32_t)(lo + d0));
+            b.w[t].c[1][0] = load_stream16(wsrc + (uint32_t)(lo + d1));
+            b.w[t].c[0][1] = load_stream16(wsrc + (uint32_t)(hi + d0));
+            b.w[t].c[1][1] = load_stream16(wsrc + (uint32_t)(hi + d1));
         }
     }
 #pragma unroll
@@ -516,7 +544,7 @@ __device__ __forceinline__ void mf_seq_compute(MfWindow<KIND, TILES, XR> b, int 
     // still takes (u, v) = (0,0), (0,1), (1,0), (1,1) in that order.
     v8bf op[TILES][2][2];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) MfFetch<KIND>::operands(b.w[t], b.sc, b3, op[t]);
+    for (int t = 0; t < TILES; ++t) MfFetch<KIND>::operands(b.w[t], b.sc, b3, TILES < 4 && base + kBlock <= K, op[t]);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll

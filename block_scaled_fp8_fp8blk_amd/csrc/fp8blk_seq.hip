@@ -129,9 +129,8 @@ __device__ __forceinline__ void load_dense(const SeqLin& L, int64_t v, int k, in
     // bf16: a chunk is 32 bytes, and two loads of lane l's own 16-byte halves
     // would each touch every line of the segment's 2 KB half-used. Instead
     // load 0 reads the first KB and load 1 the second, lane m taking 16-byte
-    // piece 2m (m < 32) or 2(m - 32) + 1 (m >= 32) of it; the exchange of the
-    // two lane halves in twin_chunk then hands lane l pieces 2l and 2l + 1,
-    // its chunk. Measured on the whole-step sweep: 1.14 -> 0.92 ms per step
+    // piece 2m (m < 32) or 2(m - 32) + 1 (m >= 32) of it; swap_lane_halves in
+    // compute_phase then hands lane l pieces 2l and 2l + 1, its chunk. Measured on the whole-step sweep: 1.14 -> 0.92 ms per step
     // with contiguous loads.
     const uint32_t lo = KIND == kFp8 ? (uint32_t)lane * kChunk : 16u * (lane < 32 ? 2 * lane : 2 * lane - 63);
 #pragma unroll
@@ -199,26 +198,6 @@ __device__ __forceinline__ void load_step(const SeqLin& L, int64_t v, int k, int
     for (int p = 0; p < 4; ++p) load_phase<KIND, DENSE>(L, v, k, lane, p, raw);
 }
 
-// The dense path's two bf16 loads of a slot -> lane l's chunk (columns
-// 16 l .. 16 l + 15 of the segment, lower half first). permlane32_swap
-// exchanges the upper 32 lanes of its first operand with the lower 32 lanes
-// of its second: afterwards the first holds piece 2l (lanes < 32: their own
-// load 0; lanes >= 32: load 1 of lane l - 32) and the second piece 2l + 1
-// (load 0 of lane l + 32; their own load 1).
-__device__ __forceinline__ void twin_chunk(const uint4 (&ld)[2], uint4& lo, uint4& hi) {
-    const uint32_t a[4] = {ld[0].x, ld[0].y, ld[0].z, ld[0].w};
-    const uint32_t b[4] = {ld[1].x, ld[1].y, ld[1].z, ld[1].w};
-    uint32_t x[4], y[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const auto r = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
-        x[d] = r[0];
-        y[d] = r[1];
-    }
-    lo = make_uint4(x[0], x[1], x[2], x[3]);
-    hi = make_uint4(y[0], y[1], y[2], y[3]);
-}
-
 // Phase p of the arithmetic of step k: the lane partials of slots p, p + 4,
 // ... (one FMA chain over each chunk's 16 columns, from +0.0), into part.
 template <int KIND, bool DENSE>
@@ -236,8 +215,10 @@ __device__ __forceinline__ void compute_phase(const SeqLin& L, int k, int lane, 
         if constexpr (KIND == kFp8) {
             decode16_fp8_scaled(raw.c[s], raw.s[p], w);
         } else if constexpr (DENSE) {
-            uint4 lo, hi;
-            twin_chunk(raw.c[s], lo, hi);
+            // the dense path's pieces (load_dense) -> the lane's own chunk,
+            // lower half first
+            uint4 lo = raw.c[s][0], hi = raw.c[s][1];
+            swap_lane_halves(lo, hi);
             widen8_bf16(lo, w);
             widen8_bf16(hi, w + 8);
         } else {
