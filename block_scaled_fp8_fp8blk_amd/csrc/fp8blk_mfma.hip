@@ -701,8 +701,8 @@ __device__ __forceinline__ void mf_seq_flush(int lane, const MfOut& o, const MfP
 // last unit (nothing follows cur), write out what LDS holds.
 template <int KIND, int TILES, int XR, int PARK>
 __device__ __forceinline__ void mf_seq_stage(const MfPos& nxt, MfUnit<TILES, XR>& un, MfWindow<KIND, TILES, XR>& into,
-                                             const MfPos& cur, const MfWindow<KIND, TILES, XR>& have, int lane,
-                                             v4f* acc, MfOut& out, MfPark<TILES, PARK>& park) {
+                                             const MfPos& cur, const MfWindow<KIND, TILES, XR>& have, bool last,
+                                             int lane, v4f* acc, MfOut& out, MfPark<TILES, PARK>& park) {
     if (nxt.win == 0 && nxt.more) mf_unit<KIND>(un, nxt.d, nxt.v, lane);
     mf_seq_issue(into, un, nxt.d.K, nxt.win, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the next window's loads ahead of this window's matrix work
@@ -712,7 +712,7 @@ __device__ __forceinline__ void mf_seq_stage(const MfPos& nxt, MfUnit<TILES, XR>
         mf_seq_retire<TILES, PARK>(cur.d, cur.v, lane, acc, out, park);
 #pragma unroll
         for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        if (!nxt.more) mf_seq_flush<TILES, PARK>(lane, out, park);
+        if (last) mf_seq_flush<TILES, PARK>(lane, out, park);
     }
 }
 
@@ -753,17 +753,44 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_mfseq(const MfSeqLin* __
     // where outputs are held. The bf16 arm's larger windows leave no room.
     constexpr int PARK = (KIND == 0 && mf_seq_holds<TILES>()) ? 2 : 0;
     MfPark<TILES, PARK> park;
-    Win a, b;
-    mf_seq_issue(a, ua, p0.d.K, p0.win, lane);
-    for (;;) {
-        const MfPos p1 = mf_next(p0, lin, pre, W, total);
-        ub = ua;
-        mf_seq_stage(p1, ub, b, p0, a, lane, acc, out, park);
-        if (!p1.more) break;
-        p0 = mf_next(p1, lin, pre, W, total);
-        ua = ub;
-        mf_seq_stage(p0, ua, a, p1, b, lane, acc, out, park);
-        if (!p0.more) break;
+    if constexpr (TILES == 4) {
+        // Two register sets in turn: the loads of the next window are issued
+        // before the matrix work of the current one.
+        Win a, b;
+        mf_seq_issue(a, ua, p0.d.K, p0.win, lane);
+        for (;;) {
+            const MfPos p1 = mf_next(p0, lin, pre, W, total);
+            ub = ua;
+            mf_seq_stage(p1, ub, b, p0, a, !p1.more, lane, acc, out, park);
+            if (!p1.more) break;
+            p0 = mf_next(p1, lin, pre, W, total);
+            ua = ub;
+            mf_seq_stage(p0, ua, a, p1, b, !p0.more, lane, acc, out, park);
+            if (!p0.more) break;
+        }
+    } else {
+        // Two-tile units hold half the bytes per window and leave registers
+        // free: three sets in turn, the loads of the next two windows in
+        // flight while a window's matrix work runs. `ua` follows the windows
+        // as they are issued.
+        Win a, b, c;
+        mf_seq_issue(a, ua, p0.d.K, p0.win, lane);
+        MfPos p1 = mf_next(p0, lin, pre, W, total);
+        if (p1.win == 0 && p1.more) mf_unit<KIND>(ua, p1.d, p1.v, lane);
+        mf_seq_issue(b, ua, p1.d.K, p1.win, lane);
+        for (;;) {
+            const MfPos p2 = mf_next(p1, lin, pre, W, total);
+            mf_seq_stage(p2, ua, c, p0, a, !p1.more, lane, acc, out, park);
+            if (!p1.more) break;
+            const MfPos p3 = mf_next(p2, lin, pre, W, total);
+            mf_seq_stage(p3, ua, a, p1, b, !p2.more, lane, acc, out, park);
+            if (!p2.more) break;
+            const MfPos p4 = mf_next(p3, lin, pre, W, total);
+            mf_seq_stage(p4, ua, b, p2, c, !p3.more, lane, acc, out, park);
+            if (!p3.more) break;
+            p0 = p3;
+            p1 = p4;
+        }
     }
 }
 
