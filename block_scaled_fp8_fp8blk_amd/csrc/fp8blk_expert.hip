@@ -281,11 +281,12 @@ struct ExUnit {
     int32_t xs_bytes;    // M * K / 128
     uint32_t woff[R][2]; // lane: offset of its row in tile t, load h (rows 8h .. 8h+7 of the tile) + its chunk
     uint32_t soff[R];    // lane: offset of the block scales of its row n of tile t + its lane group's step
-    uint32_t xoff[O];    // lane: its token's codes + its 32-column block
-    uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step
+    uint32_t xoff[O];    // lane: its token's codes + its 32-column block (kPastEnd: a row past M)
+    uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step (likewise)
 };
 
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 on gfx9-family targets: raw 32-bit data
+constexpr uint32_t kPastEnd = 0x40000000u;   // a lane offset past every resource's end (all are < 2^31 bytes)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ex_rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
@@ -336,11 +337,16 @@ __device__ __forceinline__ void ex_unit(ExUnit<R, O>& U, const ExLin& d, int64_t
         U.soff[t] = (uint32_t)((min(r0 + t * kTileRows + n, d.rows - 1) - r0) * sper) +
                     (FMT == kMX ? 4 : 8) * (g % WIN);
     }
+    // A row of the matrix instruction holds a token (NVFP4: 8o + row / 2);
+    // rows of tokens >= M are never stored, so their lanes read nothing: an
+    // offset past the resource's end makes the range check return zeros
+    // without touching memory (at M = 1, 15 of every 16 lanes).
 #pragma unroll
     for (int o = 0; o < O; ++o) {
-        const int tok = min(FMT == kMX ? n : 8 * o + (n >> 1), d.M - 1);
-        U.xoff[o] = (uint32_t)(tok * d.K + 32 * g);
-        U.xsoff[o] = (uint32_t)(tok * nb) + g % WIN;
+        const int tok = FMT == kMX ? n : 8 * o + (n >> 1);
+        const bool live = tok < d.M;
+        U.xoff[o] = live ? (uint32_t)(tok * d.K + 32 * g) : kPastEnd;
+        U.xsoff[o] = live ? (uint32_t)(tok * nb) + g % WIN : kPastEnd;
     }
 }
 
