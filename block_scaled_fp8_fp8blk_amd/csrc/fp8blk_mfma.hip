@@ -47,6 +47,8 @@ constexpr int kMfMinWaves = 4;   // waves of a workgroup: max(4, sw)
 constexpr int kMfMaxWaves = 8;
 constexpr int kMfMaxThreads = kMfMaxWaves * kLanes;
 constexpr int kTile = 16;    // rows per matrix tile, and the padded panel
+constexpr int kBufferWord3 = 0x00020000;    // buffer resource word 3 on gfx9-family targets: raw 32-bit data
+constexpr uint32_t kPastEnd = 0x40000000u;  // a lane offset past a panel's end (panels are < 2 MB)
 
 struct MfArgs {
     const void* w;        // uint8 codes or uint16 bf16 slab, [rows, K]
@@ -424,9 +426,10 @@ template <int TILES, int XR>
 struct MfUnit {
     const char* w;              // weights of the unit's first row
     const char* x;              // the linear's activation panel
+    int32_t x_bytes;            // its bytes, M * K * 2
     const float* g;             // the unit's row of block scales (FP8 arm)
     uint32_t roff[TILES][2];    // lane: byte offset of its rows (lo, hi) + its chunk's first column
-    uint32_t xoff[XR];          // lane: byte offset of its panel rows + its column group
+    uint32_t xoff[XR];          // lane: byte offset of its panel rows + its column group (kPastEnd: rows >= M)
 };
 
 struct MfPos {
@@ -442,6 +445,7 @@ __device__ __forceinline__ void mf_unit(MfUnit<TILES, XR>& U, const MfSeqLin& d,
     const int64_t r0 = v * (TILES * kTile);
     U.w = static_cast<const char*>(d.w) + r0 * d.K * E;
     U.x = reinterpret_cast<const char*>(d.x);
+    U.x_bytes = d.M * d.K * 2;
     U.g = d.grid + (r0 >> 7) * d.GC;
     const int r = lane & 7, wchunk = 16 * (lane >> 3);
 #pragma unroll
@@ -454,7 +458,11 @@ __device__ __forceinline__ void mf_unit(MfUnit<TILES, XR>& U, const MfSeqLin& d,
     const int xr_base = 8 * ((lane >> 3) & 1) + 4 * ((lane >> 2) & 1);
     const int xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
 #pragma unroll
-    for (int k = 0; k < XR; ++k) U.xoff[k] = (uint32_t)((min(xr_base + k, d.M - 1) * d.K + xcol) * 2);
+    // Panel rows >= M are never stored: their lanes take an offset past the
+    // panel's end, and the buffer range check gives zeros without a memory
+    // access (at M <= 4, three of every four lanes; at M = 8, half).
+    for (int k = 0; k < XR; ++k)
+        U.xoff[k] = xr_base + k < d.M ? (uint32_t)(((xr_base + k) * d.K + xcol) * 2) : kPastEnd;
 }
 
 __device__ __forceinline__ MfPos mf_next(const MfPos& p, const MfSeqLin* lin, const int64_t* pre, int64_t W,
@@ -494,7 +502,6 @@ __device__ __forceinline__ void mf_seq_issue(MfWindow<KIND, TILES, XR>& b, const
     constexpr int E = KIND == 0 ? 1 : 2;
     const int base = win * kBlock;
     const char* wsrc = U.w + base * E;
-    const char* xsrc = U.x + base * 2;
     const int wchunk = 16 * (lane >> 3), xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
     const uint32_t wshift = (uint32_t)((min(base + wchunk, K - 16) - base - wchunk) * E);  // 0, or minus the overrun
     const uint32_t xshift = (uint32_t)((min(base + xcol, K - 8) - base - xcol) * 2);
@@ -515,8 +522,13 @@ __device__ __forceinline__ void mf_seq_issue(MfWindow<KIND, TILES, XR>& b, const
             b.w[t].c[1][1] = load_stream16(wsrc + (uint32_t)(hi + d1));
         }
     }
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(U.x), (short)0, U.x_bytes, kBufferWord3);
 #pragma unroll
-    for (int k = 0; k < XR; ++k) b.x[k] = load_global16(xsrc + (uint32_t)(U.xoff[k] + xshift));
+    for (int k = 0; k < XR; ++k) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(U.xoff[k] + xshift), base * 2, 0);
+        b.x[k] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
     b.sc = 1.0f;
     if constexpr (KIND == 0) b.sc = *(constant_f32*)(U.g + win);
 }
