@@ -323,18 +323,20 @@ def test_expert_sweep_as_benchmarked(gpu, gu, fmt, M):
             gu.assert_within_tolerance(y[:, r0:r0 + 32].cpu().numpy(), y64, yabs, what=f"{sp.name} rows {r0}..")
 
 
-def test_expert_sequence_graph_replays(gpu, gu):
+@pytest.mark.parametrize("M", [1, 8])
+def test_expert_sequence_graph_replays(gpu, gu, M):
     """An expert sequence captured in a HIP graph: every replay, with eager
-    work and synchronizations between the replays, gives the eager bits."""
+    work and synchronizations between the replays, gives the eager bits (at
+    M = 8 the outputs are held in LDS until each wave's last unit)."""
     shapes = [(2048, 4096), (300, 512), (4096, 2048), (17, 384)]
     for fmt in (MX, NV):
         lins_e, lins_g, ys_e, ys_g = [], [], [], []
         for k, (r, c) in enumerate(shapes):
-            L = I.host_fp4_linear(fmt, r, c, 1, 900 + k)
+            L = I.host_fp4_linear(fmt, r, c, M, 900 + k)
             xq, xs = act_quant_gpu(gpu, dev(gu, L.x))
             codes, scales = dev(gu, L.codes), dev(gu, L.scales)
-            ye = torch.full((1, r), float("nan"), dtype=torch.float32, device=gu.DEV)
-            yg = torch.full((1, r), float("nan"), dtype=torch.float32, device=gu.DEV)
+            ye = torch.full((M, r), float("nan"), dtype=torch.float32, device=gu.DEV)
+            yg = torch.full((M, r), float("nan"), dtype=torch.float32, device=gu.DEV)
             lins_e.append((codes, scales, L.global_scale, xq, xs, ye))
             lins_g.append((codes, scales, L.global_scale, xq, xs, yg))
             ys_e.append(ye)
