@@ -615,6 +615,10 @@ constexpr int kMfSeqHoldMinM = 8;                               // smallest pane
 static_assert(kMfSeqBlocksPerCU * kMfSeqLdsBytes <= 160 * 1024 && (kMfSeqBlocksPerCU + 1) * kMfSeqLdsBytes > 160 * 1024,
               "the LDS of a workgroup caps a compute unit at kMfSeqBlocksPerCU of them");
 
+static_assert(mf_seq_blocks_per_cu(true, kMfSeqHoldMinM) == kMfSeqBlocksPerCU &&
+                  mf_seq_blocks_per_cu(false, 1) == kMfSeqBlocksPerCU,
+              "panels whose outputs are held, and the bf16 arm, run two workgroups per compute unit");
+
 struct MfOut {
     unsigned char* lds;  // the wave's part of the workgroup's LDS
     int M;               // panel rows of the list (the plan's; every descriptor holds the same)
@@ -815,9 +819,13 @@ int mf_seq_launch(const fp8blk_sequence* seq, int arm, hipStream_t s) {
     const int64_t* pre =
         reinterpret_cast<const int64_t*>(static_cast<const unsigned char*>(seq->plan) + (size_t)seq->n * sizeof(MfSeqLin));
     const dim3 nb((unsigned)seq->grid_dense), nt(kSeqWaves * kLanes);
-    constexpr int lds = kMfSeqLdsBytes;
-    (void)hipGetLastError();
     const int M = seq->M;
+    // Where no outputs are held, the workgroup reserves only enough LDS to cap
+    // a compute unit at the plan's workgroups (the units are dealt to the
+    // waves in a fixed rotation, which assumes they progress at one rate).
+    const int per_cu = mf_seq_blocks_per_cu(KIND == 0, M);
+    const int lds = per_cu == kMfSeqBlocksPerCU ? kMfSeqLdsBytes : lds_cap_bytes(per_cu);
+    (void)hipGetLastError();
     if (M >= 8)
         k_mfseq<KIND, mf_seq_tiles(8), 4><<<nb, nt, lds, s>>>(lin, pre, seq->units_dense, M);
     else if (M > 2)

@@ -436,7 +436,7 @@ extern "C" int fp8blk_sequence_init(fp8blk_sequence* seq, int arm, const fp8blk_
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st) != hipSuccess) return FP8BLK_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return FP8BLK_ERR_HIP;
-    const int64_t waves = (int64_t)cus * (mfma ? kMfSeqBlocksPerCU : kSeqBlocksPerCU) * kSeqWaves;
+    const int64_t waves = (int64_t)cus * (mfma ? mf_seq_blocks_per_cu(fp8, M) : kSeqBlocksPerCU) * kSeqWaves;
     seq->plan = ws;
     seq->units_dense = units_first;
     seq->units_general = units_second;
