@@ -148,13 +148,16 @@ def test_mfma_sequence_whole_step_sweep(gpu):
     say(f"  {len(lins)} sweep linears at M=16 checked")
 
 
-@pytest.mark.parametrize("M", [8, 11, 16])
+@pytest.mark.parametrize("M", [2, 5, 8, 11, 16])
 def test_mfma_sequence_more_units_than_held(gpu, M):
     """A list long enough that every wave finishes more units than its LDS part
     and its registers hold (about 14 units per wave with 1.8M rows of 128
     columns): the outputs kept back to the end of the launch, the ones parked in
     registers and the ones written when they finish all equal the single
-    matrix-core call (one part at these cols), and the twin, bit for bit."""
+    matrix-core call (one part at these cols), and the twin, bit for bit.
+    Below 8 rows nothing is held, and the FP8 arm runs three workgroups per
+    compute unit against the twin's two: the two arms deal the same units to
+    different waves, and their bits must still agree."""
     from gpu_util import DEV, DevLinear, assert_within_tolerance, say, u32
     shapes = [(900000, 128), (5000, 256), (900001, 128)]
     members, y8, yt, slabs = [], [], [], []
