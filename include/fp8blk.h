@@ -311,7 +311,7 @@ typedef struct fp8blk_sequence {
     int64_t units_general; /* work units of the second launch (vector arms: ragged rows or cols) */
     int32_t n;             /* linears */
     int32_t arm;           /* FP8BLK_ARM_* */
-    int32_t grid_dense;    /* workgroups of each launch (from the device's compute units) */
+    int32_t grid_dense;    /* workgroups of each launch (from the device's compute units, the arm and M) */
     int32_t grid_general;
     int32_t M;             /* panel rows (1 for the vector arms) */
     int32_t reserved;
