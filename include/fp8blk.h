@@ -224,13 +224,18 @@ int bf16_gemv_twin_grouped(const fp8blk_linear *linears, int n, int64_t cols, co
  *   - the matrix core adds the 32 products of an instruction in an order the
  *     hardware does not document, so the bits differ from fp8blk_gemv's
  *     documented order; the result is within 1e-5 * sum_c |w x| of the exact
- *     sum for inputs in the bf16 normal range (bf16 subnormal operands may be
- *     flushed by the matrix core).
- * Column order: blocks of 64 columns in increasing order; in block p, lane
- * group kg (0..3) feeds columns [64p + 16kg, 64p + 16kg + 8) to one
- * instruction and the next 8 to the following one, both into the same f32
- * accumulator; a row's blocks may be split into 2 or 4 contiguous parts, as a
- * function of (rows, cols) only, whose partial sums are added in part order.
+ *     sum for every weight the load check accepts, bf16-subnormal weights and
+ *     activations included (gfx950's matrix core keeps bf16 subnormal
+ *     operands and f32 subnormal sums; tested at scale codes 0..9 and
+ *     238..246, on the subnormal e4m3 codes and on subnormal activations).
+ * Column order: windows of 128 columns (one scale-block column) in increasing
+ * order; in window w, lane group kg (0..3) feeds the 8 columns starting at
+ * 128 w + 32 kg + 16 u + 8 v to instruction (u, v) = (0,0), (0,1), (1,0),
+ * (1,1), all four into the same f32 accumulator. A row's windows may be split
+ * into 2, 4 or 8 contiguous parts, as a function of (rows, cols) only (the
+ * largest split that leaves at least 8 windows per part, or at least 4 while
+ * fewer than 1024 single-tile waves would run), whose partial sums are added
+ * in part order.
  * Arguments, limits, alignment, ownership and stream as for fp8blk_gemv /
  * bf16_gemv_twin; no workspace. Enqueued on `stream`; does not wait.
  */

@@ -146,6 +146,19 @@ def test_mfma_sequence_whole_step_sweep(gpu):
         assert_within_tolerance(yw, y64, yabs, what=f"{spec.name} rows {r0}.. M=16")
     assert all(not torch.isnan(y).any() for y in ys)
     say(f"  {len(lins)} sweep linears at M=16 checked")
+    # The decode / verify pairing of this arm ("Struct Dsv4Gpu" page,
+    # spec_greedy_batched_with): row m of the 16-row verify sweep equals the
+    # one-row sweep on x[m], bit for bit, for every output of every linear.
+    for m in range(16):
+        y1 = [torch.full((1, spec.rows), float("nan"), device=DEV) for spec, _ in lins]
+        s1 = fb.fp8blk_sequence_init(fb.ARM_FP8_MFMA, [(D.codes, D.grid, D.x[m:m + 1], y)
+                                                       for (_, D), y in zip(lins, y1)])
+        fb.fp8blk_gemv_mfma_sequence(s1)
+        torch.cuda.synchronize()
+        bad = [lins[i][0].name for i in range(len(lins))
+               if not torch.equal(ys[i][m].view(torch.int32), y1[i][0].view(torch.int32))]
+        assert not bad, (m, bad[:5])
+    say("  M=16 sweep rows == M=1 sweeps on each x[m], bit for bit")
 
 
 @pytest.mark.parametrize("M", [2, 5, 8, 11, 16])
