@@ -26,6 +26,7 @@ MIN_COLS, MAX_COLS, MAX_M, MAX_PANEL = 16, 65536, 16, 65536
 
 # Every symbol include/fp8blk.h declares.
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
+           "fp8blk_load_check_noalloc",
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
            "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
            "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
@@ -92,6 +93,8 @@ def load():
     L.fp8blk_workspace_bytes.argtypes, L.fp8blk_workspace_bytes.restype = [i32, i64, i64, i64], sz
     L.fp8blk_load_check.argtypes = [vp, vp, i64, i64, vp, vp, sz, ctypes.POINTER(i64), vp]
     L.fp8blk_load_check.restype = i32
+    L.fp8blk_load_check_noalloc.argtypes = [vp, vp, i64, i64, vp, ctypes.POINTER(i64), vp]
+    L.fp8blk_load_check_noalloc.restype = i32
     L.fp8blk_dequant_bf16.argtypes, L.fp8blk_dequant_bf16.restype = [vp, vp, i64, i64, vp, vp], i32
     L.fp8blk_gemv.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, sz, vp]
     L.fp8blk_gemv.restype = i32
@@ -189,6 +192,27 @@ def fp8blk_load_check(codes, scales_e8m0, scales_f32_out, ws, stream=None, check
                                   ctypes.byref(fb), _stream(stream))
     if check and st != OK:
         raise Fp8BlkError(st, "fp8blk_load_check", fb.value)
+    return st, fb.value
+
+
+def fp8blk_load_check_noalloc(codes, scales_e8m0, scales_f32_out, stream=None, check=True):
+    """fp8blk_load_check with the library's static scratch instead of a
+    workspace: allocates nothing. Calls that overlap on one GPU race.
+    Returns (status, first_bad); raises Fp8BlkError on a refusal if check."""
+    import torch
+    rows, cols = codes.shape
+    grid = (-(-rows // 128), -(-cols // 128))
+    if scales_e8m0.numel() != grid[0] * grid[1] or scales_f32_out.numel() != grid[0] * grid[1]:
+        raise ValueError(f"scales_e8m0 and scales_f32_out must hold the {grid[0]}x{grid[1]} block grid")
+    if scales_e8m0.device != codes.device or scales_f32_out.device != codes.device:
+        raise ValueError("codes, scales_e8m0 and scales_f32_out must be on one device")
+    fb = ctypes.c_int64(-1)
+    st = load().fp8blk_load_check_noalloc(_dev(codes, (torch.uint8,), "codes"),
+                                          _dev(scales_e8m0, (torch.uint8,), "scales_e8m0"), rows, cols,
+                                          _dev(scales_f32_out, (torch.float32,), "scales_f32_out"),
+                                          ctypes.byref(fb), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_load_check_noalloc", fb.value)
     return st, fb.value
 
 

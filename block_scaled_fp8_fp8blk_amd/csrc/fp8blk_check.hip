@@ -8,6 +8,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fp8blk.h"
 #include "fp8blk_device.hpp"
 #include "fp8blk_host.hpp"
@@ -139,6 +142,60 @@ int grid_for(int64_t work, int64_t cap) {
     return (int)(b < 1 ? 1 : b);
 }
 
+// The load check's three verdict slots, run on a caller's buffer of at least
+// fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK) bytes. k_verdict_init clears
+// them first (a kernel, not a memset), so the buffer's earlier contents never
+// matter.
+int run_load_check(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t cols,
+                   float* scales_f32_out, unsigned long long* verdict, int64_t* first_bad, hipStream_t s) {
+    (void)hipGetLastError();
+    const int64_t GR = ceil_div(rows, kBlock), GC = ceil_div(cols, kBlock);
+    k_verdict_init<<<1, 64, 0, s>>>(verdict);
+    k_scales<<<grid_for(GR * GC, 1024), kThreads, 0, s>>>(scales_e8m0, GR * GC, scales_f32_out, verdict);
+    k_codes<<<grid_for(rows * (cols / kChunk), 8192), kThreads, 0, s>>>(codes, scales_e8m0, rows, cols, GC,
+                                                                       verdict);
+    if (launch_status() != FP8BLK_OK) return FP8BLK_ERR_HIP;
+    unsigned long long host[3] = {kNone, kNone, kNone};
+    if (hipMemcpyAsync(host, verdict, sizeof host, hipMemcpyDeviceToHost, s) != hipSuccess) return FP8BLK_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return FP8BLK_ERR_HIP;
+    const int kinds[3] = {FP8BLK_ERR_SCALE_FF, FP8BLK_ERR_NAN_CODE, FP8BLK_ERR_INEXACT};
+    for (int k = 0; k < 3; ++k)
+        if (host[k] != kNone) {
+            if (first_bad) *first_bad = (int64_t)host[k];
+            return kinds[k];
+        }
+    return FP8BLK_OK;
+}
+
+// Scratch of fp8blk_load_check_noalloc: the verdict slots in a static device
+// array, one copy per GPU, held until the process ends. Host code never passes
+// `scratch` itself to a kernel (on the host the name is only a stand-in): it
+// passes the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept here.
+constexpr size_t kScratchBytes = 256;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned long long scratch[kScratchBytes / sizeof(unsigned long long)];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, or NULL (HIP error).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        p = q;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 }  // namespace fp8blk
 
@@ -182,25 +239,22 @@ extern "C" int fp8blk_load_check(const uint8_t* codes, const uint8_t* scales_e8m
         return FP8BLK_ERR_ARG;
     if (!ws || ws_bytes < fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK, rows, cols, 1) || !aligned(ws, 8))
         return FP8BLK_ERR_WORKSPACE;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    auto* verdict = static_cast<unsigned long long*>(ws);
-    const int64_t GR = ceil_div(rows, kBlock), GC = ceil_div(cols, kBlock);
-    k_verdict_init<<<1, 64, 0, s>>>(verdict);
-    k_scales<<<grid_for(GR * GC, 1024), kThreads, 0, s>>>(scales_e8m0, GR * GC, scales_f32_out, verdict);
-    k_codes<<<grid_for(rows * (cols / kChunk), 8192), kThreads, 0, s>>>(codes, scales_e8m0, rows, cols, GC,
-                                                                       verdict);
-    if (launch_status() != FP8BLK_OK) return FP8BLK_ERR_HIP;
-    unsigned long long host[3] = {kNone, kNone, kNone};
-    if (hipMemcpyAsync(host, verdict, sizeof host, hipMemcpyDeviceToHost, s) != hipSuccess) return FP8BLK_ERR_HIP;
-    if (hipStreamSynchronize(s) != hipSuccess) return FP8BLK_ERR_HIP;
-    const int kinds[3] = {FP8BLK_ERR_SCALE_FF, FP8BLK_ERR_NAN_CODE, FP8BLK_ERR_INEXACT};
-    for (int k = 0; k < 3; ++k)
-        if (host[k] != kNone) {
-            if (first_bad) *first_bad = (int64_t)host[k];
-            return kinds[k];
-        }
-    return FP8BLK_OK;
+    return run_load_check(codes, scales_e8m0, rows, cols, scales_f32_out, static_cast<unsigned long long*>(ws),
+                          first_bad, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8blk_load_check_noalloc(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows,
+                                         int64_t cols, float* scales_f32_out, int64_t* first_bad,
+                                         fp8blk_stream_t stream) {
+    if (first_bad) *first_bad = -1;
+    if (!codes || !scales_e8m0 || !scales_f32_out || !shape_ok(rows, cols) || !aligned(codes, 16) ||
+        !aligned(scales_f32_out, 4))
+        return FP8BLK_ERR_ARG;
+    if (fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK, rows, cols, 1) > kScratchBytes) return FP8BLK_ERR_WORKSPACE;
+    void* verdict = scratch_for_current_device();
+    if (!verdict) return FP8BLK_ERR_HIP;
+    return run_load_check(codes, scales_e8m0, rows, cols, scales_f32_out, static_cast<unsigned long long*>(verdict),
+                          first_bad, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int fp8blk_dequant_bf16(const uint8_t* codes, const float* scales_f32, int64_t rows, int64_t cols,

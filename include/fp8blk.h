@@ -144,6 +144,27 @@ int fp8blk_load_check(const uint8_t *codes, const uint8_t *scales_e8m0, int64_t 
                       int64_t *first_bad, fp8blk_stream_t stream);
 
 /*
+ * fp8blk_load_check for callers that cannot allocate device memory (a loader
+ * running under an allocation-free harness or inside a serving loop that
+ * forbids hipMalloc): the same checks, the same statuses, the same first_bad
+ * and the same f32 grid, with no ws argument. Its scratch (the three 64-bit
+ * verdict slots) is a static 256-byte device array inside the library, one
+ * per GPU, held until the process ends; its device address is looked up once
+ * per device on the first call there. The call allocates and frees nothing
+ * (no hipMalloc, hipFree or allocating library routine) and clears the slots
+ * with a kernel before use. Every call on one GPU shares that GPU's array:
+ * calls that overlap on the same GPU (several host threads, several
+ * streams) race and may return each other's verdicts; serialize them.
+ * Arguments, limits, alignment and errors as for fp8blk_load_check, plus
+ * FP8BLK_ERR_WORKSPACE if the check would need more than the 256 bytes the
+ * array holds (it needs fp8blk_workspace_bytes(FP8BLK_OP_LOAD_CHECK, ...),
+ * 256 for every shape today). Waits for `stream` before returning.
+ */
+int fp8blk_load_check_noalloc(const uint8_t *codes, const uint8_t *scales_e8m0, int64_t rows,
+                              int64_t cols, float *scales_f32_out, int64_t *first_bad,
+                              fp8blk_stream_t stream);
+
+/*
  * The bf16 dequant slab ("Module dsv4_gpu" page, rungs paragraph and
  * DenseBf16): out_bf16[r, c] = bf16 pattern of e4m3(codes[r, c]) *
  * scales_f32[r/128][c/128]. Exact (no rounding) for weights accepted by
