@@ -72,13 +72,21 @@ def parse():
     p.add_argument("--panel-only", action="store_true",
                    help="run only the M-row verify panel sweep (matrix-core sequence launch; for profiling) and "
                         "print its JSON")
-    p.add_argument("--panel-m", default="2,4,8,16", help="panel rows of the verify panel sweep (comma-separated)")
+    p.add_argument("--panel-m", default="1,2,4,8,16", help="panel rows of the verify panel sweep (comma-separated)")
     p.add_argument("--summarize-panel-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
                    help="write the panel sweep kernel's rocprofv3 --stats summary (markdown) and exit")
     p.add_argument("--summarize-panel-counters", nargs=2, metavar=("FETCH_SIZE_CSV", "WRITE_SIZE_CSV"),
                    help="calibrate the panel sweep kernel's FETCH_SIZE / WRITE_SIZE (one --panel-m value), write "
                         "its counters JSON, print markdown")
     p.add_argument("--reps", type=int, default=10, help="graph replays per config measurement")
+    p.add_argument("--config-only", action="store_true",
+                   help="run only the per-config cold-launch table (for rocprofv3 runs of those launches)")
+    p.add_argument("--manifest", default="",
+                   help="with --config-only: write the order and count of the timed GEMV dispatches here")
+    p.add_argument("--summarize-config-trace", metavar="KERNEL_TRACE_CSV",
+                   help="markdown summary of a --config-only kernel trace (needs --manifest)")
+    p.add_argument("--summarize-config-counters", nargs=2, metavar=("FETCH_SIZE_CSV", "WRITE_SIZE_CSV"),
+                   help="counter summary of --config-only runs (needs --manifest); writes profiles/")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a known-size reference for counter runs)")
     p.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
@@ -205,6 +213,118 @@ def time_sweep(torch, fb, sw, steps, warmup, mode, grouped=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / 1e3, wall
+
+
+class Chain:
+    """The sweep's linears as a dependent decode chain: per layer [q, kv] read
+    the layer input, o reads q's output, [gate, up] read o's output, down reads
+    gate's output and the next layer reads down's output; the head reads the
+    last layer's output. A group is one launch (q + kv and gate + up as one
+    grouped launch, "Module dsv4_gpu" page, DecodePath: one launch per
+    projection). Between groups a glue step, standing in for the engine's
+    norms, attention and activations (not part of this library), writes the
+    next input: x = bf16(c * y), one torch kernel, with c fixed per group from
+    an eager pass so the values stay near unit scale."""
+
+    def __init__(self, torch, fb, sw, dev):
+        self.torch, self.fb, self.sw = torch, fb, sw
+        assert sw.arm == "fp8"
+        lins = sw.lins
+        self.layers = (len(lins) - 1) // 6
+        bf = torch.bfloat16
+        self.x_in = [torch.empty((1, 4096), dtype=bf, device=dev) for _ in range(self.layers + 1)]
+        self.x_in[0].copy_(sw.xs[4096].view(bf))
+        self.x_o = [torch.empty((1, 4096), dtype=bf, device=dev) for _ in range(self.layers)]
+        self.x_g = [torch.empty((1, 4096), dtype=bf, device=dev) for _ in range(self.layers)]
+        self.x_d = [torch.empty((1, 2048), dtype=bf, device=dev) for _ in range(self.layers)]
+        self.c = None
+        # (kind, members, x): members are sweep linears (dicts with w, grid, y)
+        self.groups = []
+        for l in range(self.layers):
+            q, kv, o, gate, up, down = lins[6 * l:6 * l + 6]
+            self.groups += [("launch", [q, kv], self.x_in[l]), ("glue", q["y"], self.x_o[l]),
+                            ("launch", [o], self.x_o[l]), ("glue", o["y"], self.x_g[l]),
+                            ("launch", [gate, up], self.x_g[l]), ("glue", gate["y"], self.x_d[l]),
+                            ("launch", [down], self.x_d[l]), ("glue", down["y"], self.x_in[l + 1])]
+        self.groups.append(("launch", [lins[-1]], self.x_in[self.layers]))
+        self.n_launches = sum(1 for g in self.groups if g[0] == "launch")
+        self.n_glue = len(self.groups) - self.n_launches
+
+    def calls(self, stream=None):
+        """The chain's launches and glue steps, in order, as callables."""
+        torch, fb = self.torch, self.fb
+        out, gi = [], 0
+        for kind, a, b in self.groups:
+            if kind == "launch":
+                if len(a) == 1:
+                    out.append(fb.prepared("fp8blk_gemv", a[0]["w"], a[0]["grid"], b, a[0]["y"], stream=stream))
+                else:
+                    out.append(fb.prepared("fp8blk_gemv_grouped", [(m["w"], m["grid"], m["y"]) for m in a], b,
+                                           stream=stream))
+            else:
+                c = self.c[gi]
+                out.append(lambda y=a, x=b, c=c: (torch.mul(y, c, out=x), 0)[1])
+                gi += 1
+        return out
+
+    def calibrate(self):
+        """Run the chain eagerly once, fixing each glue step's scale so that
+        its output has unit root mean square."""
+        torch = self.torch
+        self.c = [1.0] * self.n_glue
+        gi = 0
+        for kind, a, b in self.groups:
+            if kind == "launch":
+                run_calls(Chain._one(self, kind, a, b))
+            else:
+                rms = float(a.float().pow(2).mean().sqrt())
+                self.c[gi] = 1.0 / rms if rms > 0 and rms == rms and rms != float("inf") else 1.0
+                torch.mul(a, self.c[gi], out=b)
+                gi += 1
+        torch.cuda.synchronize()
+
+    def _one(self, kind, a, b):
+        fb = self.fb
+        if len(a) == 1:
+            return [fb.prepared("fp8blk_gemv", a[0]["w"], a[0]["grid"], b, a[0]["y"])]
+        return [fb.prepared("fp8blk_gemv_grouped", [(m["w"], m["grid"], m["y"]) for m in a], b)]
+
+
+def chain_sweep(torch, fb, sw, steps, warmup, dev):
+    """Time the dependent chain (Chain) as one HIP graph replayed per step,
+    events around `steps` replays on the replaying stream."""
+    ch = Chain(torch, fb, sw, dev)
+    ch.calibrate()
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        run_calls(ch.calls())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run_calls(ch.calls(stream=cap))
+    torch.cuda.synchronize()
+    for _ in range(max(warmup, 20)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    v = sw.weight_bytes * steps / t / 1e9
+    finite = all(bool(torch.isfinite(l["y"]).all()) for l in sw.lins)
+    log(f"dependent chain ({ch.n_launches} GEMV launches + {ch.n_glue} glue kernels per step, graph): "
+        f"{t / steps * 1e3:.4f} ms/step, {v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak); outputs finite: {finite}")
+    return {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
+            "ms_per_step": round(t / steps * 1e3, 4), "gemv_launches_per_step": ch.n_launches,
+            "glue_kernels_per_step": ch.n_glue, "outputs_finite": finite,
+            "workload": "the sweep's 259 linears as a dependent decode chain: per layer [q+kv] -> o -> [gate+up] "
+                        "-> down -> next layer, then the head; one launch per group, x = bf16(c*y) between "
+                        "groups (one torch kernel), one HIP graph per step"}
 
 
 def time_panel_sequence(torch, fb, inputs, sw, M, steps, warmup, dev):
@@ -459,15 +579,46 @@ def counted_traffic(arm, mode):
     return rec.get("hbm_bytes_per_launch")
 
 
-def per_config(torch, fb, inputs, dev, reps):
+# Kernels of the single-linear GEMV entry points (one dispatch per call).
+CONFIG_KERNELS = ("k_gemv_m1<", "k_panel<", "k_mfma<")
+CONFIG_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_mfma.hip",
+                  "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
+CONFIG_ARMS = (("vec", "fp8blk_gemv"), ("vec_twin", "bf16_gemv_twin"), ("mfma", "fp8blk_gemv_mfma"),
+               ("mfma_twin", "bf16_gemv_twin_mfma"))
+
+
+def config_counters_path():
+    return os.path.join(ROOT, "profiles", "gemv_per_config_counters.json")
+
+
+def config_traffic():
+    """{(linear, M, arm): HBM bytes per launch} from the committed counter
+    summary of the per-config launches ({} when absent or taken on other
+    kernel sources)."""
+    try:
+        with open(config_counters_path()) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("source_hash") != source_hash(CONFIG_SOURCES):
+        return {}
+    return {(r["linear"], r["M"], r["arm"]): r["hbm_bytes_per_launch"] for r in rec.get("blocks", [])}
+
+
+def per_config(torch, fb, inputs, dev, reps, manifest=None):
     """Per-launch times of the single-linear workloads (decode shape,
     projection pair, verify panel at M = 1..16), both arms of both kernels.
     Like the sweep: a HIP graph launches the GEMV on enough distinct copies of
     the linear to exceed 512 MB (twice the Infinity Cache), so every launch
-    reads cold from HBM, and `reps` replays are timed between events."""
+    reads cold from HBM, and `reps` replays are timed between events.
+    manifest: a list that receives, in launch order, one entry per timed block
+    with its number of GEMV dispatches (an eager warm-up pass, one untimed
+    replay, `reps` timed replays), so that a profiler's per-dispatch records
+    can be assigned to the blocks."""
     ws = torch.empty(256, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     rows_out = []
+    counted = config_traffic()
 
     def timed(make_calls):
         cap = torch.cuda.Stream()
@@ -505,14 +656,20 @@ def per_config(torch, fb, inputs, dev, reps):
             x = xall[:M].contiguous()
             y = torch.empty((M, L.rows), dtype=torch.float32, device=dev)
             t = {}
-            for arm, fn, ws_ in (("vec", "fp8blk_gemv", cs), ("vec_twin", "bf16_gemv_twin", ss),
-                                 ("mfma", "fp8blk_gemv_mfma", cs), ("mfma_twin", "bf16_gemv_twin_mfma", ss)):
+            for arm, fn in CONFIG_ARMS:
+                ws_ = cs if fn.startswith("fp8blk") else ss
                 if fn.startswith("fp8blk"):
                     mk = lambda st, fn=fn, ws_=ws_: [fb.prepared(fn, w, grid, x, y, stream=st) for w in ws_]  # noqa: E731
                 else:
                     mk = lambda st, fn=fn, ws_=ws_: [fb.prepared(fn, w, x, y, stream=st) for w in ws_]  # noqa: E731
                 t[arm] = timed(mk)
+                if manifest is not None:
+                    manifest.append({"linear": name, "rows": L.rows, "cols": L.cols, "M": M, "arm": arm,
+                                     "dispatches": copies * (reps + 2), "timed_dispatches": copies * reps})
             pct = lambda sec: round(100 * wbytes / sec / 1e9 / HBM_PEAK_GBS, 1)  # noqa: E731
+            # algorithmic bytes of one launch: weights (+ grid on the FP8 arms), x, y
+            algo = {a: (wbytes if a in ("vec", "mfma") else 2 * L.rows * L.cols) + 2 * M * L.cols + 4 * M * L.rows
+                    for a, _ in CONFIG_ARMS}
             rows_out.append(dict(linear=name, rows=L.rows, cols=L.cols, M=M, copies=copies,
                                  us=round(t["vec"] * 1e6, 2), weight_GBps=round(wbytes / t["vec"] / 1e9, 1),
                                  pct_hbm_peak=pct(t["vec"]),
@@ -520,7 +677,10 @@ def per_config(torch, fb, inputs, dev, reps):
                                  twin_GBps=round(2 * L.rows * L.cols / t["vec_twin"] / 1e9, 1),
                                  mfma_us=round(t["mfma"] * 1e6, 2), mfma_GBps=round(wbytes / t["mfma"] / 1e9, 1),
                                  mfma_pct_hbm_peak=pct(t["mfma"]),
-                                 mfma_twin_GBps=round(2 * L.rows * L.cols / t["mfma_twin"] / 1e9, 1)))
+                                 mfma_twin_us=round(t["mfma_twin"] * 1e6, 2),
+                                 mfma_twin_GBps=round(2 * L.rows * L.cols / t["mfma_twin"] / 1e9, 1),
+                                 algo_bytes={a: algo[a] for a, _ in CONFIG_ARMS},
+                                 traffic={a: counted.get((name, M, a)) for a, _ in CONFIG_ARMS}))
             r = rows_out[-1]
             log(f"  {name} M={M}: vector arm {r['us']} us, {r['weight_GBps']} GB/s ({r['pct_hbm_peak']}%), twin "
                 f"{r['twin_GBps']} GB/s | matrix-core arm {r['mfma_us']} us, {r['mfma_GBps']} GB/s "
@@ -778,6 +938,96 @@ def summarize_panel_counters(fetch_csv, write_csv, command, M, arm="fp8"):
     print("\n".join(lines))
 
 
+def _config_blocks(rows_by_dispatch, manifest):
+    """Assign the GEMV dispatches of a --config-only run, in launch order, to
+    the manifest's blocks. rows_by_dispatch: per-dispatch records (dicts with
+    Kernel_Name) in dispatch order, every kernel of the run."""
+    gemv = [r for r in rows_by_dispatch if any(k in r["Kernel_Name"] for k in CONFIG_KERNELS)]
+    need = sum(b["dispatches"] for b in manifest)
+    if len(gemv) != need:
+        raise SystemExit(f"config summary: {len(gemv)} GEMV dispatches in the profile, {need} in the manifest")
+    out, i = [], 0
+    for b in manifest:
+        out.append(gemv[i:i + b["dispatches"]])
+        i += b["dispatches"]
+    return out
+
+
+def summarize_config_trace(trace_csv, manifest_path, command):
+    """Markdown: per config block (linear, M, arm), the kernel, its grid and
+    the median / mean duration of the timed launches from a rocprofv3 kernel
+    trace of a --config-only run, with the weight GB/s the median gives."""
+    import csv
+    manifest = json.load(open(manifest_path))
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    blocks = _config_blocks(rows, manifest)
+    lines = ["# rocprofv3 kernel trace: single-linear workloads, cold single launches", "",
+             f"Command: `{command}`" if command else "", "",
+             "Each launch reads its own copy of the linear (copies > 512 MB in all), so every launch is cold. "
+             "Timed launches: the graph replays (the eager warm-up pass and the first replay excluded). Weight "
+             "bytes: codes + f32 grid (FP8 arms) or the bf16 slab (twins). vec = fp8blk_gemv, vec_twin = "
+             "bf16_gemv_twin, mfma = fp8blk_gemv_mfma, mfma_twin = bf16_gemv_twin_mfma.", "",
+             "| linear | M | arm | kernel | grid (threads) | timed launches | median us | mean us | "
+             "weight GB/s (median) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for b, recs in zip(manifest, blocks):
+        timed = recs[-b["timed_dispatches"]:]
+        d = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed)
+        med, mean = d[len(d) // 2] / 1e3, sum(d) / len(d) / 1e3
+        gr, gc = -(-b["rows"] // 128), -(-b["cols"] // 128)
+        wb = b["rows"] * b["cols"] + 4 * gr * gc if b["arm"] in ("vec", "mfma") else 2 * b["rows"] * b["cols"]
+        names = {(_short(r["Kernel_Name"]), r.get("Grid_Size", r.get("Grid_Size_X", "?"))) for r in timed}
+        k, g = sorted(names)[0]
+        lines.append(f"| {b['linear']} | {b['M']} | {b['arm']} | {k} | {g} | {len(d)} | {med:.2f} | {mean:.2f} | "
+                     f"{wb / med / 1e3:.1f} | {100 * wb / med / 1e3 / HBM_PEAK_GBS:.1f} |")
+    print("\n".join(lines))
+
+
+def summarize_config_counters(fetch_csv, write_csv, manifest_path, command):
+    """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the three
+    1 GiB copies of --copy-calibration, then give the HBM bytes per launch of
+    each config block (median over its dispatches, all cold); writes the JSON
+    that bench.py's per_config rows take their traffic from."""
+    import csv
+
+    def load(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
+        return copies, _config_blocks(rows, manifest)
+
+    manifest = json.load(open(manifest_path))
+    fc, fb_ = load(fetch_csv)
+    wc, wb_ = load(write_csv)
+    gib_kib = 1 << 20
+    f_factor = gib_kib / sorted(fc)[len(fc) // 2]
+    w_factor = gib_kib / sorted(wc)[len(wc) // 2]
+    recs = []
+    lines = ["# rocprofv3 counters: single-linear workloads, cold single launches", "",
+             f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
+             f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
+             f"WRITE_SIZE x {w_factor:.3f} give bytes. Per block: the median over its dispatches (each reads its "
+             "own cold copy). Algorithmic bytes: weights (codes + f32 grid, or the bf16 slab), x and y.", "",
+             "| linear | M | arm | read MB | written MB | HBM MB per launch | algorithmic MB | HBM / algorithmic |",
+             "|---|---|---|---|---|---|---|---|"]
+    for b, fr, wr in zip(manifest, fb_, wb_):
+        fk = sorted(float(r["Counter_Value"]) for r in fr)[len(fr) // 2]
+        wk = sorted(float(r["Counter_Value"]) for r in wr)[len(wr) // 2]
+        rd, wt = fk * f_factor * 1024, wk * w_factor * 1024
+        gr, gc = -(-b["rows"] // 128), -(-b["cols"] // 128)
+        wbytes = b["rows"] * b["cols"] + 4 * gr * gc if b["arm"] in ("vec", "mfma") else 2 * b["rows"] * b["cols"]
+        algo = wbytes + 2 * b["M"] * b["cols"] + 4 * b["M"] * b["rows"]
+        recs.append({"linear": b["linear"], "M": b["M"], "arm": b["arm"], "hbm_bytes_per_launch": int(rd + wt),
+                     "read_bytes": int(rd), "write_bytes": int(wt), "algo_bytes": algo,
+                     "kib": {"fetch": fk, "write": wk}})
+        lines.append(f"| {b['linear']} | {b['M']} | {b['arm']} | {rd / 1e6:.3f} | {wt / 1e6:.3f} | "
+                     f"{(rd + wt) / 1e6:.3f} | {algo / 1e6:.3f} | {(rd + wt) / algo:.3f} |")
+    rec = {"source_hash": source_hash(CONFIG_SOURCES), "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "blocks": recs, "command": command}
+    with open(config_counters_path(), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    lines += ["", f"Source hash {rec['source_hash']}."]
+    print("\n".join(lines))
+
+
 def m1_launch_key(rows, cols):
     """(kernel instance, grid threads) of fp8blk_gemv's launch for an M = 1
     linear, as the library's plan picks it (rows per wave R, segments per wave
@@ -858,6 +1108,31 @@ def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"
     print("\n".join(lines))
 
 
+def warm_clocks(torch, dev, seconds=0.5):
+    """Keep the GPU busy for a moment so that its clocks are up before timing
+    (a run that starts with the table would otherwise time its first rows at
+    idle clocks)."""
+    a = torch.randn(4096, 4096, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        a = a @ a
+        a.div_(a.abs().max())
+        torch.cuda.synchronize()
+    del a
+
+
+def copy_calibration(torch, dev):
+    """Three 1 GiB device copies: the counter summaries scale FETCH_SIZE and
+    WRITE_SIZE by what these read for known bytes."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x 1 GiB device copies done")
+    del src, dst
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -878,6 +1153,12 @@ def main():
     if args.summarize_panel_counters:
         summarize_panel_counters(*args.summarize_panel_counters, args.command, int(args.panel_m), args.arm)
         return
+    if args.summarize_config_trace:
+        summarize_config_trace(args.summarize_config_trace, args.manifest, args.command)
+        return
+    if args.summarize_config_counters:
+        summarize_config_counters(*args.summarize_config_counters, args.manifest, args.command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the FP8-blk "
@@ -896,25 +1177,26 @@ def main():
         res = {f: expert_sweep(torch, fb, inputs, dev, args.steps, args.warmup, f, expert_ms)
                for f in (inputs.NVFP4, inputs.MXFP4)}
         if args.copy_calibration:
-            src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            log("copy calibration: 3 x 1 GiB device copies done")
+            copy_calibration(torch, dev)
         print(json.dumps({"expert_sweep": {inputs.FP4_NAMES[f]: r for f, r in res.items()}}), flush=True)
+        return
+    if args.config_only:
+        warm_clocks(torch, dev)
+        manifest = []
+        extra = per_config(torch, fb, inputs, dev, args.reps, manifest)
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        if args.manifest:
+            with open(args.manifest, "w") as f:
+                json.dump(manifest, f)
+        print(json.dumps({"per_config": extra}), flush=True)
         return
     panel_ms = tuple(int(v) for v in args.panel_m.split(","))
     if args.panel_only:
         sw = Sweep(torch, fb, inputs, dev, args.layers, args.arm)
         panel = panel_sweep(torch, fb, inputs, sw, dev, args.steps, args.warmup, panel_ms)
         if args.copy_calibration:
-            src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            log("copy calibration: 3 x 1 GiB device copies done")
+            copy_calibration(torch, dev)
         print(json.dumps({"panel_sweep_matrix_core_sequence": panel}), flush=True)
         return
     log(f"setting up the sweep ({args.layers} layers + head, arm {args.arm})")
@@ -979,18 +1261,16 @@ def main():
                                      "note": "q+kv and gate+up each in one launch, graph-replayed"}
     launch_modes["per_linear_shapes"] = shapes
 
+    # The same linears as a dependent decode chain (each group's input is the
+    # previous group's output).
+    chain = chain_sweep(torch, fb, sw, args.steps, args.warmup, dev) if args.arm == "fp8" else None
+
     # The verify step's dense traffic: the same linears with an M-row panel, as
     # one matrix-core sequence launch.
     panel = panel_sweep(torch, fb, inputs, sw, dev, args.steps, args.warmup, panel_ms) if not args.no_extra else {}
 
     if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device copies done")
-        del src, dst
+        copy_calibration(torch, dev)
 
     extra = None
     pre = None
@@ -1037,6 +1317,7 @@ def main():
                    "weight_bytes_per_step": sw.weight_bytes, "cold_cache": "working set 12x the 256 MB MALL"},
         "roofline": roof,
         "launch_modes": launch_modes,
+        "dependent_chain": chain,
         "cpu_baseline": cpu,
         "panel_sweep_matrix_core_sequence": ({"workload": "the same 259 linears, each with an M-row bf16 verify "
                                                           "panel, one matrix-core sequence launch per step",
