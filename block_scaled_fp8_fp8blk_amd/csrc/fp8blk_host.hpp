@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp8blk.h"
 
 namespace fp8blk {
@@ -45,10 +47,16 @@ inline size_t plan_bytes(int n) { return (size_t)n * kSeqDescBytes + (size_t)(n 
 // progresses at the same rate.
 constexpr int lds_cap_bytes(int per_cu) { return 160 * 1024 / (per_cu + 1) + 1024; }
 
+// Compute units of the current device (-1 on a HIP error), looked up once per
+// device.
 inline int device_cus() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < kMaxDev && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return cus;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < kMaxDev) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 

@@ -200,17 +200,34 @@ struct MfWindow {
 
 // Per-lane constants of the layout.
 struct MfLane {
-    int64_t r0;               // first row of the wave
-    int r;                    // l & 7
-    int wchunk;               // 16 (l >> 3)
-    int xcol;                 // 8 G
-    const uint16_t* xrow[4];  // panel rows 8 l3 + 4 l2 + 2 n1 + n0, clamped to M - 1
-    bool b0, b1, b3;          // lane bits 0, 1, 3
+    int64_t r0;         // first row of the wave
+    int r;              // l & 7
+    int wchunk;         // 16 (l >> 3)
+    int xcol;           // 8 G
+    uint32_t xrow[4];   // byte offset of panel row 8 l3 + 4 l2 + 2 n1 + n0 in x; kPastEnd for rows >= M
+    bool b0, b1, b3;    // lane bits 0, 1, 3
     int lane;
 };
 
+// What one window of a single call needs: the tiles' weights, the panel
+// window, and each tile's block scale (a wave's tiles may lie in two 128-row
+// scale blocks when it takes three of them).
 template <int KIND, int TILES, int XR>
-__device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, XR>& b, const MfArgs& a, const MfLane& L, int win) {
+struct MfCallWindow {
+    typename MfFetch<KIND>::Raw w[TILES];
+    uint4 x[4];  // [2 n1 + n0] as loaded, [2 u + v] after the exchanges
+    float sc[TILES];
+};
+
+typedef __attribute__((address_space(4))) const float constant_f32;
+
+// The activations come through a buffer resource over the panel: a lane whose
+// panel row is >= M has an offset past the panel's end, and the range check
+// returns zeros without touching memory (at M = 1, three lanes in four; at
+// M = 8, half), so a short panel costs only its own bytes.
+template <int KIND, int TILES, int XR>
+__device__ __forceinline__ void mf_issue(MfCallWindow<KIND, TILES, XR>& b, const MfArgs& a, const MfLane& L,
+                                         __amdgpu_buffer_rsrc_t xr, int win) {
     const int base = win * kBlock;
     const int wcol = min(base + L.wchunk, a.K - 16);  // a chunk past the last column re-reads the last one
 #pragma unroll
@@ -219,15 +236,21 @@ __device__ __forceinline__ void mf_issue(MfWindow<KIND, TILES, XR>& b, const MfA
         const int64_t hi = min(L.r0 + t * kTile + 8 + L.r, a.rows - 1);
         MfFetch<KIND>::load(b.w[t], a, lo, hi, wcol, base + kBlock <= a.K, L.lane);
     }
-    const int xc = min(base + L.xcol, a.K - 8);
+    const uint32_t xc = (uint32_t)(min(base + L.xcol, a.K - 8) - base) * 2;
 #pragma unroll
-    for (int k = 0; k < XR; ++k) b.x[k] = load_global16(L.xrow[k] + xc);
-    b.sc = 1.0f;
-    if constexpr (KIND == 0) b.sc = load_global_f32(a.grid + (min(L.r0, a.rows - 1) >> 7) * a.GC + win);
+    for (int k = 0; k < XR; ++k) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(L.xrow[k] + xc), base * 2, 0);
+        b.x[k] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+        b.sc[t] = 1.0f;
+        if constexpr (KIND == 0) b.sc[t] = *(constant_f32*)(a.grid + (min(L.r0 + t * kTile, a.rows - 1) >> 7) * a.GC + win);
+    }
 }
 
 template <int KIND, int TILES, int XR>
-__device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, XR> b, const MfArgs& a, const MfLane& L, int win,
+__device__ __forceinline__ void mf_compute(MfCallWindow<KIND, TILES, XR> b, const MfArgs& a, const MfLane& L, int win,
                                            v4f* acc) {
     const int base = win * kBlock;
     if (base + kBlock > a.K && base + L.xcol + 8 > a.K) {
@@ -242,26 +265,29 @@ __device__ __forceinline__ void mf_compute(MfWindow<KIND, TILES, XR> b, const Mf
     exchange<0>(b.x[2], b.x[3], L.b0);
     exchange<1>(b.x[0], b.x[2], L.b1);
     exchange<1>(b.x[1], b.x[3], L.b1);
+    // every tile's operands first, then the matrix instructions with the tile
+    // innermost (independent accumulator chains); each tile still takes
+    // (u, v) = (0,0), (0,1), (1,0), (1,1) in that order
+    v8bf op[TILES][2][2];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        v8bf op[2][2];
-        MfFetch<KIND>::operands(b.w[t], b.sc, L.b3, base + kBlock <= a.K, op);
+    for (int t = 0; t < TILES; ++t) MfFetch<KIND>::operands(b.w[t], b.sc[t], L.b3, base + kBlock <= a.K, op[t]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[u][v], __builtin_bit_cast(v8bf, b.x[2 * u + v]),
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int t = 0; t < TILES; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[t][u][v], __builtin_bit_cast(v8bf, b.x[2 * u + v]),
                                                                  acc[t], 0, 0, 0);
-    }
 }
 
-// A wave owns TILES tiles of 16 consecutive rows (inside one 128-row scale
-// block) and one part of the windows; the loads of the next DEPTH - 1 windows
-// are in flight while a window is multiplied. Loads are unconditional: past
-// the end of the part they re-read its last window, which is then not used.
+// A wave owns TILES tiles of 16 consecutive rows and one part of the windows;
+// the loads of the next DEPTH - 1 windows are in flight while a window is
+// multiplied. Loads are unconditional: past the end of the part they re-read
+// its last window, which is then not used.
 template <int KIND, int TILES, int XR, int DEPTH>
 __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
-    using Win = MfWindow<KIND, TILES, XR>;
+    using Win = MfCallWindow<KIND, TILES, XR>;
     __shared__ v4f part[kMfMaxWaves][TILES][kLanes];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
@@ -274,11 +300,13 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
     L.xcol = 8 * (((lane >> 4) << 2) | (lane & 3));
     const int xr_base = 8 * ((lane >> 3) & 1) + 4 * ((lane >> 2) & 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) L.xrow[k] = a.x + (int64_t)min(xr_base + k, a.M - 1) * a.K;
+    for (int k = 0; k < 4; ++k) L.xrow[k] = xr_base + k < a.M ? (uint32_t)((xr_base + k) * a.K * 2) : kPastEnd;
     L.b0 = (lane & 1) != 0;
     L.b1 = (lane & 2) != 0;
     L.b3 = (lane & 8) != 0;
     L.lane = lane;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), (short)0, a.M * a.K * 2, kBufferWord3);
     const int wb = sp * a.bpp;
     const int we = min(a.nwin, wb + a.bpp);
 
@@ -289,11 +317,11 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
     if (wb < we) {
         Win buf[DEPTH];
 #pragma unroll
-        for (int d = 0; d + 1 < DEPTH; ++d) mf_issue(buf[d], a, L, min(wb + d, we - 1));
+        for (int d = 0; d + 1 < DEPTH; ++d) mf_issue(buf[d], a, L, xr, min(wb + d, we - 1));
         for (int w = wb; w < we; w += DEPTH) {
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
-                mf_issue(buf[(d + DEPTH - 1) % DEPTH], a, L, min(w + d + DEPTH - 1, we - 1));
+                mf_issue(buf[(d + DEPTH - 1) % DEPTH], a, L, xr, min(w + d + DEPTH - 1, we - 1));
                 __builtin_amdgcn_sched_barrier(0);
                 if (w + d < we) mf_compute(buf[d], a, L, w + d, acc);
                 __builtin_amdgcn_sched_barrier(0);
@@ -334,37 +362,51 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
 // order of the sums -- : the largest of 1, 2, 4, 8 that leaves >= 8 windows
 // per part, or >= 4 windows while fewer than 1024 single-tile waves would run.
 // TILES only changes which wave computes an output, not its order, so it may
-// follow M: from M = 8 on, a wave takes 4 row tiles, which share its
-// activation loads, as long as >= 768 waves remain; else 1 tile, for the most
-// waves in flight. Measured on 12288 x 4096, 4096 x 4096, 4096 x 16384 and
-// 16384 x 4096 at M = 1, 8, 16.
+// follow the device: a wave takes the most row tiles (up to 4) that still
+// leave at least one workgroup per compute unit. Row tiles in one wave share
+// its activation loads, and the activations, not the weights, are what a
+// wave's loads mostly carry from a 4-row panel on (16 panel rows x 128
+// columns of bf16 per window, against 16 rows x 128 codes per tile); but a
+// compute unit without a workgroup reads nothing. On 12288 x 4096 this is 3
+// tiles (256 workgroups): 42 -> 50% of HBM peak at M = 16, 45 -> 53% at
+// M = 8, against 4 tiles (192 workgroups, a quarter of the compute units
+// idle) and 1 tile (768 workgroups, three times the activation loads).
 struct MfPlan {
     int tiles, sw, depth;
 };
-MfPlan mf_plan(int64_t rows, int64_t K, int64_t M) {
+MfPlan mf_plan(int64_t rows, int64_t K, int cus) {
     MfPlan p;
     const int64_t nwin = ceil_div(K, (int64_t)kBlock);
     const int64_t groups1 = ceil_div(rows, (int64_t)kTile);
     p.sw = 1;
     while (p.sw < kMfMaxWaves && (nwin >= 16 * p.sw || (nwin >= 8 * p.sw && groups1 * p.sw < 1024))) p.sw *= 2;
+    const int streams = (p.sw >= kMfMinWaves ? p.sw : kMfMinWaves) / p.sw;  // row groups per workgroup
     p.tiles = 1;
-    if (M >= 8 && ceil_div(rows, (int64_t)kTile * 4) * p.sw >= 768) p.tiles = 4;
+    for (int t = 4; t > 1; --t)
+        if (ceil_div(ceil_div(groups1, (int64_t)t), (int64_t)streams) >= cus) {
+            p.tiles = t;
+            break;
+        }
     p.depth = 2;
     return p;
 }
 
 template <int KIND, int XR>
 void mf_launch(const MfPlan& p, dim3 nb, dim3 nt, hipStream_t s, const MfArgs& a) {
-    if (p.tiles == 4)
-        k_mfma<KIND, 4, XR, 2><<<nb, nt, 0, s>>>(a);
-    else
-        k_mfma<KIND, 1, XR, 2><<<nb, nt, 0, s>>>(a);
+    switch (p.tiles) {
+        case 4: k_mfma<KIND, 4, XR, 2><<<nb, nt, 0, s>>>(a); break;
+        case 3: k_mfma<KIND, 3, XR, 2><<<nb, nt, 0, s>>>(a); break;
+        case 2: k_mfma<KIND, 2, XR, 2><<<nb, nt, 0, s>>>(a); break;
+        default: k_mfma<KIND, 1, XR, 2><<<nb, nt, 0, s>>>(a); break;
+    }
 }
 
 template <int KIND>
 int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const uint16_t* x, int64_t M, float* y,
            hipStream_t s) {
-    const MfPlan p = mf_plan(rows, cols, M);
+    const int cus = device_cus();
+    if (cus <= 0) return FP8BLK_ERR_HIP;
+    const MfPlan p = mf_plan(rows, cols, cus);
     MfArgs a;
     a.w = w;
     a.grid = grid;
@@ -487,7 +529,6 @@ __device__ __forceinline__ MfPos mf_next(const MfPos& p, const MfSeqLin* lin, co
     return n;
 }
 
-typedef __attribute__((address_space(4))) const float constant_f32;
 
 // The loads of window `win` of a unit: the unit's bases plus the lane
 // offsets. In the last window of a row whose cols is not a multiple of 128,
