@@ -613,8 +613,13 @@ __device__ __forceinline__ void mf_seq_compute(MfWindow<KIND, TILES, XR> b, int 
 // y[n]. yu points at y[0][first row of the unit], `rows` is the row stride of
 // y and `left` the rows of the unit that exist (rows - first row, at most
 // TILES * 16). When vec is set (the linear allows it) four outputs leave as
-// one 16-byte nontemporal store (a tile is one store instruction writing 16
-// panel rows x 64 bytes), else one by one.
+// one 16-byte store (a tile is one store instruction writing 16 panel rows x
+// 64 bytes, half of a 128-byte line each; the next tile writes the other
+// half), else one by one. The stores go through L2, which merges the two
+// halves of a line before it reaches HBM: with the nontemporal hint each half
+// went out on its own and HBM took 28% more bytes than the outputs hold at
+// M = 16 (71.8 MB written against 56.2 MB; plain stores: 56.2 MB), for no
+// gain in time.
 template <int TILES>
 __device__ __forceinline__ void mf_seq_store_at(float* yu, int64_t rows, int left, bool vec, int M, int lane,
                                                 const v4f* acc) {
@@ -626,7 +631,7 @@ __device__ __forceinline__ void mf_seq_store_at(float* yu, int64_t rows, int lef
         const int r = t * kTile + 4 * kg;
         if (vec && r + 3 < left) {
             typedef __attribute__((address_space(1))) v4f global_v4f;
-            __builtin_nontemporal_store(acc[t], (global_v4f*)(yrow + r));
+            *(global_v4f*)(yrow + r) = acc[t];
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -720,36 +725,67 @@ __device__ __forceinline__ void mf_seq_retire(const MfSeqLin& d, int64_t v, int 
     ++o.k;
 }
 
-// Held unit k's outputs, from its record.
+// Held unit k's outputs, from its LDS slot, written so that every store
+// instruction covers whole 128-byte lines of y: instruction i takes panel rows
+// 4i .. 4i + 3; lane l carries piece p = l % 16 (rows 4p .. 4p + 3 of the
+// unit: tile p / 4, lane group p % 4) of panel row 4i + l / 16. A unit's 64
+// outputs of a panel row are then 256 contiguous bytes from 16 lanes of one
+// instruction, so the nontemporal stores (0.5 point faster than plain ones at
+// M = 16) reach HBM as whole lines: 56.2 MB written at M = 16, the outputs'
+// own bytes. (With the register layout, each store writes half lines and the
+// nontemporal ones went out as 71.8 MB.)
 template <int TILES>
-__device__ __forceinline__ void mf_seq_store_held(const MfOut& o, int k, int lane, const v4f* acc) {
+__device__ __forceinline__ void mf_seq_store_slot(const MfOut& o, int k, const unsigned char* slot, int lane) {
+    static_assert(TILES * 4 == 16, "a held unit is 64 rows: 16 pieces of 4 outputs per panel row");
     const uint64_t yu = ((uint64_t)__builtin_amdgcn_readlane(o.y_hi, k) << 32) | (uint32_t)__builtin_amdgcn_readlane(o.y_lo, k);
     const int64_t rows = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(o.rows_hi, k) << 32) |
                                    (uint32_t)__builtin_amdgcn_readlane(o.rows_lo, k));
     const uint32_t lv = __builtin_amdgcn_readlane(o.left_vec, k);
-    mf_seq_store_at<TILES>(reinterpret_cast<float*>(yu), rows, (int)(lv & 0xffffu), (lv >> 16) != 0, o.M, lane, acc);
+    const int left = (int)(lv & 0xffffu);
+    const bool vec = (lv >> 16) != 0;
+    const int p = lane & 15;
+    float* y = reinterpret_cast<float*>(yu);
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+        const int n = 4 * i + (lane >> 4);
+        if (n < o.M) {
+            const v4f v = *reinterpret_cast<const v4f*>(slot + (((p >> 2) * o.M + n) * 4 + (p & 3)) * 16);
+            float* dst = y + (int64_t)n * rows + 4 * p;
+            if (vec && 4 * p + 3 < left) {
+                typedef __attribute__((address_space(1))) v4f global_v4f;
+                __builtin_nontemporal_store(v, (global_v4f*)dst);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * p + e < left) store_global_f32(dst + e, v[e]);
+            }
+        }
+    }
 }
 
-// After the wave's last unit: the held units go out in order. (Called from
-// inside the pipeline loop, at the last unit: after the loop, the same code
-// makes the compiler keep ~50 more registers live across the loop.)
+// After the wave's last unit: the held units go out in order, each through
+// its LDS slot (the units parked in registers pass through a slot already
+// written out). (Called from inside the pipeline loop, at the last unit:
+// after the loop, the same code makes the compiler keep ~50 more registers
+// live across the loop.)
 template <int TILES, int PARK>
 __device__ __forceinline__ void mf_seq_flush(int lane, const MfOut& o, const MfPark<TILES, PARK>& park) {
-    if (!mf_seq_holds<TILES>()) return;
-    const int in_lds = min(o.k, o.slots);
-    const int n = lane & 15, kg = lane >> 4;
+    if constexpr (mf_seq_holds<TILES>()) {
+        const int in_lds = min(o.k, o.slots);
+        const int n = lane & 15, kg = lane >> 4;
 #pragma unroll 1
-    for (int k = 0; k < in_lds; ++k) {
-        v4f acc[TILES];
-        const unsigned char* slot = o.lds + k * o.slot_bytes;
+        for (int k = 0; k < in_lds; ++k) mf_seq_store_slot<TILES>(o, k, o.lds + k * o.slot_bytes, lane);
 #pragma unroll
-        for (int t = 0; t < TILES; ++t)
-            acc[t] = n < o.M ? *reinterpret_cast<const v4f*>(slot + ((t * o.M + n) * 4 + kg) * 16) : v4f{0.f, 0.f, 0.f, 0.f};
-        mf_seq_store_held<TILES>(o, k, lane, acc);
+        for (int i = 0; i < PARK; ++i)
+            if (o.slots + i < o.k) {
+                unsigned char* slot = o.lds + i * o.slot_bytes;  // slot i is written out: slots = 80 / M >= 5 > PARK
+                if (n < o.M)
+#pragma unroll
+                    for (int t = 0; t < TILES; ++t)
+                        *reinterpret_cast<v4f*>(slot + ((t * o.M + n) * 4 + kg) * 16) = park.acc[i][t];
+                mf_seq_store_slot<TILES>(o, o.slots + i, slot, lane);
+            }
     }
-#pragma unroll
-    for (int i = 0; i < PARK; ++i)
-        if (o.slots + i < o.k) mf_seq_store_held<TILES>(o, o.slots + i, lane, park.acc[i]);
 }
 
 // One window of the pipeline: issue the loads of window `nxt` (computing its
