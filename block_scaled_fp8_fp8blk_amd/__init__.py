@@ -173,6 +173,52 @@ def _bf16_dtypes():
     return (torch.bfloat16, torch.int16, torch.uint16)
 
 
+# Shape checks. The C ABI takes plain pointers and sizes and cannot see how
+# large a buffer is, so every wrapper checks here, before any launch, that
+# each tensor holds exactly what the shapes it passes imply and that all of
+# them are on one device; a mismatch raises ValueError.
+
+def _grid_cells(rows, cols):
+    return (-(-rows // 128)) * (-(-cols // 128))
+
+
+def _weights(w, name="codes"):
+    if w.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [rows, cols] tensor, got shape {tuple(w.shape)}")
+    return w.shape
+
+
+def _numel(t, n, name, what):
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements ({what}), it holds {t.numel()}")
+
+
+def _one_device(*ts):
+    devs = {str(t.device) for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(devs)}")
+
+
+def _panel(x, rows, cols, y, xname="x_bf16"):
+    """x is [M, cols] and y holds M * rows elements; returns M."""
+    if x.dim() != 2 or x.shape[1] != cols:
+        raise ValueError(f"{xname} must be [M, cols={cols}], got shape {tuple(x.shape)}")
+    M = x.shape[0]
+    _numel(y, M * rows, "y", f"[M={M}, rows={rows}]")
+    return M
+
+
+def _check_linear(w, grid, x, y, wname="codes"):
+    """A linear's weights [rows, cols], f32 grid (FP8 arms; None for a slab),
+    panel x [M, cols] and output y [M, rows]; returns (rows, cols, M)."""
+    rows, cols = _weights(w, wname)
+    if grid is not None:
+        _numel(grid, _grid_cells(rows, cols), "scales_f32", "the ceil(rows/128) x ceil(cols/128) grid")
+    M = _panel(x, rows, cols, y)
+    _one_device(w, grid, x, y)
+    return rows, cols, M
+
+
 def _ws(ws):
     if ws is None:
         return None, 0
@@ -183,7 +229,10 @@ def fp8blk_load_check(codes, scales_e8m0, scales_f32_out, ws, stream=None, check
     """Validate codes/scales and decode the f32 scale grid. Waits on the stream.
     Returns (status, first_bad); raises Fp8BlkError on a refusal if check."""
     import torch
-    rows, cols = codes.shape
+    rows, cols = _weights(codes)
+    _numel(scales_e8m0, _grid_cells(rows, cols), "scales_e8m0", "the block grid")
+    _numel(scales_f32_out, _grid_cells(rows, cols), "scales_f32_out", "the block grid")
+    _one_device(codes, scales_e8m0, scales_f32_out, ws)
     wsp, wsb = _ws(ws)
     fb = ctypes.c_int64(-1)
     st = load().fp8blk_load_check(_dev(codes, (torch.uint8,), "codes"),
@@ -200,12 +249,10 @@ def fp8blk_load_check_noalloc(codes, scales_e8m0, scales_f32_out, stream=None, c
     workspace: allocates nothing. Calls that overlap on one GPU race.
     Returns (status, first_bad); raises Fp8BlkError on a refusal if check."""
     import torch
-    rows, cols = codes.shape
-    grid = (-(-rows // 128), -(-cols // 128))
-    if scales_e8m0.numel() != grid[0] * grid[1] or scales_f32_out.numel() != grid[0] * grid[1]:
-        raise ValueError(f"scales_e8m0 and scales_f32_out must hold the {grid[0]}x{grid[1]} block grid")
-    if scales_e8m0.device != codes.device or scales_f32_out.device != codes.device:
-        raise ValueError("codes, scales_e8m0 and scales_f32_out must be on one device")
+    rows, cols = _weights(codes)
+    _numel(scales_e8m0, _grid_cells(rows, cols), "scales_e8m0", "the block grid")
+    _numel(scales_f32_out, _grid_cells(rows, cols), "scales_f32_out", "the block grid")
+    _one_device(codes, scales_e8m0, scales_f32_out)
     fb = ctypes.c_int64(-1)
     st = load().fp8blk_load_check_noalloc(_dev(codes, (torch.uint8,), "codes"),
                                           _dev(scales_e8m0, (torch.uint8,), "scales_e8m0"), rows, cols,
@@ -218,7 +265,10 @@ def fp8blk_load_check_noalloc(codes, scales_e8m0, scales_f32_out, stream=None, c
 
 def fp8blk_dequant_bf16(codes, scales_f32, out_bf16, stream=None, check=True):
     import torch
-    rows, cols = codes.shape
+    rows, cols = _weights(codes)
+    _numel(scales_f32, _grid_cells(rows, cols), "scales_f32", "the block grid")
+    _numel(out_bf16, rows * cols, "out_bf16", f"[rows={rows}, cols={cols}]")
+    _one_device(codes, scales_f32, out_bf16)
     st = load().fp8blk_dequant_bf16(_dev(codes, (torch.uint8,), "codes"),
                                     _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
                                     _dev(out_bf16, _bf16_dtypes(), "out_bf16"), _stream(stream))
@@ -230,8 +280,8 @@ def fp8blk_dequant_bf16(codes, scales_f32, out_bf16, stream=None, check=True):
 def fp8blk_gemv(codes, scales_f32, x_bf16, y, ws=None, stream=None, check=True):
     """y[M, rows] = decode(codes, scales) @ x^T, in the library's fixed order."""
     import torch
-    rows, cols = codes.shape
-    M = x_bf16.shape[0]
+    rows, cols, M = _check_linear(codes, scales_f32, x_bf16, y)
+    _one_device(codes, ws)
     wsp, wsb = _ws(ws)
     st = load().fp8blk_gemv(_dev(codes, (torch.uint8,), "codes"),
                             _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
@@ -244,10 +294,10 @@ def fp8blk_gemv(codes, scales_f32, x_bf16, y, ws=None, stream=None, check=True):
 
 def bf16_gemv_twin(w_bf16, x_bf16, y, ws=None, stream=None, check=True):
     """The bf16-slab twin of fp8blk_gemv (same order, same bits)."""
-    rows, cols = w_bf16.shape
-    M = x_bf16.shape[0]
-    wsp, wsb = _ws(ws)
     import torch
+    rows, cols, M = _check_linear(w_bf16, None, x_bf16, y, "w_bf16")
+    _one_device(w_bf16, ws)
+    wsp, wsb = _ws(ws)
     st = load().bf16_gemv_twin(_dev(w_bf16, _bf16_dtypes(), "w_bf16"), rows, cols,
                                _dev(x_bf16, _bf16_dtypes(), "x_bf16"), M,
                                _dev(y, (torch.float32,), "y"), wsp, wsb, _stream(stream))
@@ -256,16 +306,17 @@ def bf16_gemv_twin(w_bf16, x_bf16, y, ws=None, stream=None, check=True):
     return st
 
 
-def _group(members, fp8):
+def _group(members, fp8, x):
     import torch
     arr = (Linear * len(members))()
     cols = None
     for k, mem in enumerate(members):
         w, grid, y = mem if fp8 else (mem[0], None, mem[1])
-        rows, c = w.shape
+        rows, c = _weights(w, "w")
         cols = c if cols is None else cols
         if c != cols:
             raise ValueError("grouped linears must share cols")
+        _check_linear(w, grid, x, y, "w")
         arr[k].w = _dev(w, (torch.uint8,) if fp8 else _bf16_dtypes(), "w")
         arr[k].scales_f32 = _dev(grid, (torch.float32,), "scales_f32") if fp8 else None
         arr[k].rows = rows
@@ -276,7 +327,7 @@ def _group(members, fp8):
 def fp8blk_gemv_grouped(members, x_bf16, stream=None, check=True):
     """One launch for [(codes, scales_f32, y), ...] sharing x (same bits as
     separate fp8blk_gemv calls)."""
-    arr, cols = _group(members, True)
+    arr, cols = _group(members, True, x_bf16)
     st = load().fp8blk_gemv_grouped(arr, len(members), cols, _dev(x_bf16, _bf16_dtypes(), "x_bf16"),
                                     x_bf16.shape[0], _stream(stream))
     if check and st != OK:
@@ -286,7 +337,7 @@ def fp8blk_gemv_grouped(members, x_bf16, stream=None, check=True):
 
 def bf16_gemv_twin_grouped(members, x_bf16, stream=None, check=True):
     """One launch for [(w_bf16, y), ...] sharing x."""
-    arr, cols = _group(members, False)
+    arr, cols = _group(members, False, x_bf16)
     st = load().bf16_gemv_twin_grouped(arr, len(members), cols, _dev(x_bf16, _bf16_dtypes(), "x_bf16"),
                                        x_bf16.shape[0], _stream(stream))
     if check and st != OK:
@@ -297,7 +348,7 @@ def bf16_gemv_twin_grouped(members, x_bf16, stream=None, check=True):
 def fp8blk_gemv_mfma(codes, scales_f32, x_bf16, y, stream=None, check=True):
     """Matrix-core arm of fp8blk_gemv (bitwise twin of bf16_gemv_twin_mfma)."""
     import torch
-    rows, cols = codes.shape
+    rows, cols, _M = _check_linear(codes, scales_f32, x_bf16, y)
     st = load().fp8blk_gemv_mfma(_dev(codes, (torch.uint8,), "codes"),
                                  _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
                                  _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
@@ -309,7 +360,7 @@ def fp8blk_gemv_mfma(codes, scales_f32, x_bf16, y, stream=None, check=True):
 
 def bf16_gemv_twin_mfma(w_bf16, x_bf16, y, stream=None, check=True):
     import torch
-    rows, cols = w_bf16.shape
+    rows, cols, _M = _check_linear(w_bf16, None, x_bf16, y, "w_bf16")
     st = load().bf16_gemv_twin_mfma(_dev(w_bf16, _bf16_dtypes(), "w_bf16"), rows, cols,
                                     _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
                                     _dev(y, (torch.float32,), "y"), _stream(stream))
@@ -348,19 +399,17 @@ def fp8blk_sequence_init(arm: int, linears, ws=None, stream=None, check=True):
     keep = []
     fp8 = arm in (ARM_FP8, ARM_FP8_MFMA)
     for k, lin in enumerate(linears):
+        w, grid, x, y = lin if fp8 else (lin[0], None, lin[1], lin[2])
+        try:
+            rows, cols, M = _check_linear(w, grid, x, y, "w")
+        except ValueError as e:
+            raise ValueError(f"linear {k}: {e}") from None
         if fp8:
-            w, grid, x, y = lin
             arr[k].w = _dev(w, (torch.uint8,), "codes")
             arr[k].scales_f32 = _dev(grid, (torch.float32,), "scales_f32")
         else:
-            w, x, y = lin
-            grid = None
             arr[k].w = _dev(w, _bf16_dtypes(), "w_bf16")
             arr[k].scales_f32 = None
-        rows, cols = w.shape
-        M = x.shape[0] if x.dim() == 2 else 1
-        if x.numel() != M * cols or y.numel() != M * rows:
-            raise ValueError(f"linear {k}: x must be [M, cols={cols}] and y [M, rows={rows}]")
         arr[k].rows, arr[k].cols, arr[k].M = rows, cols, M
         arr[k].x_bf16 = _dev(x, _bf16_dtypes(), "x_bf16")
         arr[k].y = _dev(y, (torch.float32,), "y")
@@ -413,7 +462,8 @@ def fp8blk_gemm_staged(codes, scales_f32, x_bf16, y, ws, stream=None, check=True
     slab (written into ws) and one library GEMM. ws: fp8blk_workspace_bytes(
     OP_GEMM_STAGED, rows, cols, N) bytes, 256-byte aligned."""
     import torch
-    rows, cols = codes.shape
+    rows, cols, _N = _check_linear(codes, scales_f32, x_bf16, y)
+    _one_device(codes, ws)
     wsp, wsb = _ws(ws)
     st = load().fp8blk_gemm_staged(_dev(codes, (torch.uint8,), "codes"),
                                    _dev(scales_f32, (torch.float32,), "scales_f32"), rows, cols,
@@ -428,7 +478,8 @@ def bf16_gemm_twin(w_bf16, x_bf16, y, ws, stream=None, check=True):
     """The same GEMM over a bf16 slab the caller holds. ws: fp8blk_workspace_bytes(
     OP_BF16_GEMM, rows, cols, N) bytes, 256-byte aligned."""
     import torch
-    rows, cols = w_bf16.shape
+    rows, cols, _N = _check_linear(w_bf16, None, x_bf16, y, "w_bf16")
+    _one_device(w_bf16, ws)
     wsp, wsb = _ws(ws)
     st = load().bf16_gemm_twin(_dev(w_bf16, _bf16_dtypes(), "w_bf16"), rows, cols,
                                _dev(x_bf16, _bf16_dtypes(), "x_bf16"), x_bf16.shape[0],
@@ -444,7 +495,12 @@ def fp8blk_act_quant(x_bf16, xq, xs, stream=None, check=True):
     """act_quant: x [M, cols] bf16 -> xq [M, cols] e4m3 codes, xs [M, ceil(cols/128)]
     e8m0 scale codes (uint8 tensors)."""
     import torch
+    if x_bf16.dim() != 2:
+        raise ValueError(f"x_bf16 must be [M, cols], got shape {tuple(x_bf16.shape)}")
     M, cols = x_bf16.shape
+    _numel(xq, M * cols, "xq", f"[M={M}, cols={cols}]")
+    _numel(xs, M * (-(-cols // 128)), "xs", f"[M={M}, ceil(cols/128)]")
+    _one_device(x_bf16, xq, xs)
     st = load().fp8blk_act_quant(_dev(x_bf16, _bf16_dtypes(), "x_bf16"), M, cols, _dev(xq, (torch.uint8,), "xq"),
                                  _dev(xs, (torch.uint8,), "xs"), _stream(stream))
     if check and st != OK:
@@ -452,11 +508,23 @@ def fp8blk_act_quant(x_bf16, xq, xs, stream=None, check=True):
     return st
 
 
+def _fp4_slab(fmt, codes, scales):
+    """FP4 codes [rows, cols/2] and block scales [rows, cols/B]; returns (rows, cols)."""
+    rows, half = _weights(codes)
+    cols = 2 * half
+    B = {FMT_MXFP4: 32, FMT_NVFP4: 16}.get(fmt)
+    if B is not None:
+        _numel(scales, rows * (cols // B), "scales", f"[rows={rows}, cols/{B}]")
+    _one_device(codes, scales)
+    return rows, cols
+
+
 def fp4_load_check(fmt, codes, scales, ws, stream=None, check=True):
     """Validate an FP4 slab (codes [rows, cols/2], scales [rows, cols/B]).
     Waits on the stream. Returns (status, first_bad)."""
     import torch
-    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    rows, cols = _fp4_slab(fmt, codes, scales)
+    _one_device(codes, ws)
     wsp, wsb = _ws(ws)
     fb = ctypes.c_int64(-1)
     st = load().fp4_load_check(fmt, _dev(codes, (torch.uint8,), "codes"), _dev(scales, (torch.uint8,), "scales"),
@@ -469,7 +537,9 @@ def fp4_load_check(fmt, codes, scales, ws, stream=None, check=True):
 def fp4_dequant_bf16(fmt, codes, scales, out_bf16, stream=None, check=True):
     """The bf16-dequant arm's exact slab [rows, cols]."""
     import torch
-    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    rows, cols = _fp4_slab(fmt, codes, scales)
+    _numel(out_bf16, rows * cols, "out_bf16", f"[rows={rows}, cols={cols}]")
+    _one_device(codes, out_bf16)
     st = load().fp4_dequant_bf16(fmt, _dev(codes, (torch.uint8,), "codes"), _dev(scales, (torch.uint8,), "scales"),
                                  rows, cols, _dev(out_bf16, _bf16_dtypes(), "out_bf16"), _stream(stream))
     if check and st != OK:
@@ -480,7 +550,10 @@ def fp4_dequant_bf16(fmt, codes, scales, out_bf16, stream=None, check=True):
 def fp4_expert_gemv(fmt, codes, scales, global_scale, xq, xs, y, stream=None, check=True):
     """Native expert GEMV: y[M, rows] = g * act(xq, xs) @ fp4(codes, scales)^T."""
     import torch
-    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    rows, cols = _fp4_slab(fmt, codes, scales)
+    M = _panel(xq, rows, cols, y, "xq")
+    _numel(xs, M * (-(-cols // 128)), "xs", f"[M={M}, ceil(cols/128)]")
+    _one_device(codes, xq, xs, y)
     st = load().fp4_expert_gemv(fmt, _dev(codes, (torch.uint8,), "codes"), _dev(scales, (torch.uint8,), "scales"),
                                 float(global_scale), rows, cols, _dev(xq, (torch.uint8,), "xq"),
                                 _dev(xs, (torch.uint8,), "xs"), xq.shape[0], _dev(y, (torch.float32,), "y"),
@@ -499,10 +572,13 @@ def fp4_expert_sequence_init(fmt, linears, ws=None, stream=None, check=True):
     arr = (Fp4ExpertLinear * max(n, 1))()
     keep = []
     for k, (codes, scales, g, xq, xs, y) in enumerate(linears):
-        rows, cols = codes.shape[0], 2 * codes.shape[1]
-        M = xq.shape[0]
-        if xq.numel() != M * cols or y.numel() != M * rows:
-            raise ValueError(f"linear {k}: xq must be [M, cols={cols}] and y [M, rows={rows}]")
+        try:
+            rows, cols = _fp4_slab(fmt, codes, scales)
+            M = _panel(xq, rows, cols, y, "xq")
+            _numel(xs, M * (-(-cols // 128)), "xs", f"[M={M}, ceil(cols/128)]")
+            _one_device(codes, xq, xs, y)
+        except ValueError as e:
+            raise ValueError(f"linear {k}: {e}") from None
         arr[k].codes = _dev(codes, (torch.uint8,), "codes")
         arr[k].scales = _dev(scales, (torch.uint8,), "scales")
         arr[k].global_scale = float(g)
@@ -549,37 +625,39 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
     s = _stream(stream)
     if name == "fp8blk_gemv":
         codes, grid, x, y = tensors_and_sizes
-        rows, cols = codes.shape
+        rows, cols, _M = _check_linear(codes, grid, x, y)
         args = (_dev(codes, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows, cols,
                 _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], _dev(y, (torch.float32,), "y"), None, 0, s)
     elif name == "bf16_gemv_twin":
         w, x, y = tensors_and_sizes
-        rows, cols = w.shape
+        rows, cols, _M = _check_linear(w, None, x, y, "w_bf16")
         args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
                 _dev(y, (torch.float32,), "y"), None, 0, s)
     elif name == "fp8blk_gemv_mfma":
         codes, grid, x, y = tensors_and_sizes
-        rows, cols = codes.shape
+        rows, cols, _M = _check_linear(codes, grid, x, y)
         args = (_dev(codes, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows, cols,
                 _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], _dev(y, (torch.float32,), "y"), s)
     elif name == "bf16_gemv_twin_mfma":
         w, x, y = tensors_and_sizes
-        rows, cols = w.shape
+        rows, cols, _M = _check_linear(w, None, x, y, "w_bf16")
         args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
                 _dev(y, (torch.float32,), "y"), s)
     elif name in ("fp8blk_gemv_grouped", "bf16_gemv_twin_grouped"):
         members, x = tensors_and_sizes
-        arr, cols = _group(members, name == "fp8blk_gemv_grouped")
+        arr, cols = _group(members, name == "fp8blk_gemv_grouped", x)
         args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], s)
     elif name == "fp8blk_gemm_staged":
         codes, grid, x, y, ws = tensors_and_sizes
-        rows, cols = codes.shape
+        rows, cols, _N = _check_linear(codes, grid, x, y)
+        _one_device(codes, ws)
         wsp, wsb = _ws(ws)
         args = (_dev(codes, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows, cols,
                 _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], _dev(y, (torch.float32,), "y"), wsp, wsb, s)
     elif name == "bf16_gemm_twin":
         w, x, y, ws = tensors_and_sizes
-        rows, cols = w.shape
+        rows, cols, _N = _check_linear(w, None, x, y, "w_bf16")
+        _one_device(w, ws)
         wsp, wsb = _ws(ws)
         args = (_dev(w, _bf16_dtypes(), "w_bf16"), rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0],
                 _dev(y, (torch.float32,), "y"), wsp, wsb, s)

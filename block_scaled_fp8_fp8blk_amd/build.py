@@ -13,8 +13,14 @@ LIB = os.path.join(PKG, "libfp8blk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
-# explicitly, nothing else may be contracted. Packed FP32 instructions are
-# disabled. f32 subnormals are kept (the default; stated for the reader).
+# explicitly, nothing else may be contracted. "-Xclang -target-feature -Xclang
+# -packed-fp32-ops" turns packed FP32 instructions off in the gfx950 device
+# pass; the host (x86) pass does not know the feature and prints "not a
+# recognized feature for this target", which is harmless.
+# tests/test_build_code.py disassembles the built code objects and checks
+# that no packed FP32 add, multiply or fused multiply-add is left (and that no
+# kernel spills to scratch). f32 subnormals are kept (the default; stated for
+# the reader).
 # Matrix-core accumulators live in ordinary VGPRs (-amdgpu-mfma-vgpr-form):
 # with AGPR accumulators the compiler copies them between the two register
 # files around every loop iteration of the sequence kernel.

@@ -30,14 +30,16 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// One hipBLASLt handle per device, and the algorithm the library's heuristic
-// picks for each problem shape, created on first use and kept for the
+// One hipBLASLt handle per device, and the algorithm chosen for each problem
+// shape (device, rows, cols, N), created on first use and kept for the
 // process (the handle holds host-side state only; every device buffer is the
-// caller's).
+// caller's). Both entry points hand the library the same workspace size and
+// look the shape up in the same map, so the staged call and the twin run the
+// same algorithm and give the same bits.
 struct LtCache {
     std::mutex mu;
     hipblasLtHandle_t handle[kMaxDevices] = {};
-    std::map<std::tuple<int, int64_t, int64_t, int64_t, size_t>, hipblasLtMatmulAlgo_t> algo;
+    std::map<std::tuple<int, int64_t, int64_t, int64_t>, hipblasLtMatmulAlgo_t> algo;
 };
 LtCache& cache() {
     static LtCache c;
@@ -159,7 +161,7 @@ int lt_gemm(const uint16_t* w, int64_t rows, int64_t cols, const uint16_t* x, in
         hipblasLtMatrixLayoutCreate(&g.c, HIP_R_32F, (uint64_t)rows, (uint64_t)N, rows) != HIPBLAS_STATUS_SUCCESS)
         return FP8BLK_ERR_HIP;
     hipblasLtMatmulAlgo_t algo;
-    const auto key = std::make_tuple(dev, rows, cols, N, ws_bytes);
+    const auto key = std::make_tuple(dev, rows, cols, N);
     bool have = false;
     {
         std::lock_guard<std::mutex> lock(C.mu);
@@ -173,8 +175,12 @@ int lt_gemm(const uint16_t* w, int64_t rows, int64_t cols, const uint16_t* x, in
         // First call of this shape: take the library's best kTune heuristic
         // candidates and keep the fastest, timed on this stream (the call
         // waits for the stream; ~60 ms of tuning for the shapes measured).
-        // Under graph capture there is no timing: the first candidate is used
-        // and not cached.
+        // A first call under graph capture cannot time anything, and taking
+        // an untimed candidate there would let a later call choose another
+        // algorithm (other bits): it is refused instead.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cap) != hipSuccess) return FP8BLK_ERR_HIP;
+        if (cap != hipStreamCaptureStatusNone) return FP8BLK_ERR_ARG;
         hipblasLtMatmulPreference_t pref = nullptr;
         if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return FP8BLK_ERR_HIP;
         const uint64_t wsb = ws_bytes;
@@ -192,17 +198,13 @@ int lt_gemm(const uint16_t* w, int64_t rows, int64_t cols, const uint16_t* x, in
         for (int i = 0; i < got && best < 0; ++i)
             if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) best = i;
         if (best < 0) return FP8BLK_ERR_HIP;
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(s, &cap) != hipSuccess) return FP8BLK_ERR_HIP;
-        if (cap == hipStreamCaptureStatusNone && got > 1) {
+        if (got > 1) {
             best = tune(h, g, res.data(), got, w, x, y, ws, ws_bytes, s, best);
             if (best < 0) return FP8BLK_ERR_HIP;
         }
-        algo = res[best].algo;
-        if (cap == hipStreamCaptureStatusNone) {
-            std::lock_guard<std::mutex> lock(C.mu);
-            C.algo[key] = algo;
-        }
+        std::lock_guard<std::mutex> lock(C.mu);
+        // two threads may have timed the same shape at once: the first result kept wins for both
+        algo = C.algo.emplace(key, res[best].algo).first->second;
     }
     const float alpha = 1.0f, beta = 0.0f;
     if (hipblasLtMatmul(h, g.desc, &alpha, w, g.a, x, g.b, &beta, y, g.c, y, g.c, &algo, ws, ws_bytes, s) !=
@@ -245,7 +247,7 @@ extern "C" int fp8blk_gemm_staged(const uint8_t* codes, const float* scales_f32,
     const int st = fp8blk_dequant_bf16(codes, scales_f32, rows, cols, slab, stream);
     if (st != FP8BLK_OK) return st;
     const size_t sb = slab_bytes(rows, cols);
-    return lt_gemm(slab, rows, cols, x_bf16, N, y, static_cast<char*>(ws) + sb, ws_bytes - sb,
+    return lt_gemm(slab, rows, cols, x_bf16, N, y, static_cast<char*>(ws) + sb, kGemmWs,
                    reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -254,5 +256,5 @@ extern "C" int bf16_gemm_twin(const uint16_t* w_bf16, int64_t rows, int64_t cols
     if (!gemm_args_ok(w_bf16, rows, cols, x_bf16, N, y)) return FP8BLK_ERR_ARG;
     if (!ws || ws_bytes < gemm_workspace_bytes(FP8BLK_OP_BF16_GEMM, rows, cols) || !aligned(ws, kAlign))
         return FP8BLK_ERR_WORKSPACE;
-    return lt_gemm(w_bf16, rows, cols, x_bf16, N, y, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+    return lt_gemm(w_bf16, rows, cols, x_bf16, N, y, ws, kGemmWs, reinterpret_cast<hipStream_t>(stream));
 }

@@ -372,11 +372,16 @@ int bf16_gemv_twin_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t str
  *     or FP8BLK_OP_BF16_GEMM, rows, cols, N) bytes: the slab (staged only)
  *     plus 32 MB for the library GEMM.
  * The library keeps one hipBLASLt handle per device and the algorithm chosen
- * for each shape, for the life of the process (host state). The first call of
- * a shape times the library's best 8 heuristic candidates on `stream` and
- * keeps the fastest: that call waits for the stream (under graph capture it
- * does not time, and takes the first candidate without keeping it). Later
- * calls are enqueued on `stream` and do not wait. Errors: FP8BLK_ERR_ARG,
+ * for each shape (device, rows, cols, N), for the life of the process (host
+ * state; no device memory). The first call of a shape, staged or twin, times
+ * the library's best 64 heuristic candidates on `stream` (each given a 32 MB
+ * workspace, whatever ws_bytes holds beyond that) and keeps the fastest: that
+ * call waits for the stream, and it may not be made under graph capture
+ * (FP8BLK_ERR_ARG). Every later call of the shape, either entry point,
+ * captured or not, runs that algorithm, so the staged call and the twin give
+ * identical bits within a process; another process may time a different
+ * algorithm and so give other bits, within the same bound. Later calls are
+ * enqueued on `stream` and do not wait. Errors: FP8BLK_ERR_ARG,
  * FP8BLK_ERR_WORKSPACE, FP8BLK_ERR_HIP (also when the library has no
  * algorithm for the shape).
  */

@@ -120,3 +120,65 @@ def test_staged_gemm_workloads(gpu):
                                     nthreads=NTHREADS)
         got = y[torch.from_numpy(tok).to(DEV)][:, r0:r0 + 128].cpu().numpy().astype(np.float64)
         assert np.all(np.abs(got - y64) <= gamma(L.cols) * yabs)
+
+
+def test_staged_and_twin_share_the_algorithm(gpu):
+    """Workspaces of different sizes and a graph-captured call still run the
+    algorithm the shape's first call chose: staged == twin bitwise, and every
+    replay of a captured twin call equals the eager call."""
+    from gpu_util import DEV, DevLinear, say
+    rows, cols, N = 768, 2048, 96
+    L = inputs.host_linear(rows, cols, N, 4242)
+    D = DevLinear(L.codes, L.scales, L.x)
+    D.check()
+    need_s = fb.fp8blk_workspace_bytes(fb.OP_GEMM_STAGED, rows, cols, N)
+    need_t = fb.fp8blk_workspace_bytes(fb.OP_BF16_GEMM, rows, cols, N)
+    ws_s = torch.empty(need_s + (3 << 20), dtype=torch.uint8, device=DEV)   # larger than needed
+    ws_t = torch.empty(need_t + (9 << 20), dtype=torch.uint8, device=DEV)   # larger still
+    y_s = torch.full((N, rows), float("nan"), device=DEV)
+    fb.fp8blk_gemm_staged(D.codes, D.grid, D.x, y_s, ws_s)
+    slab = ws_s[: rows * cols * 2].view(torch.int16).view(rows, cols).clone()
+    y_t = torch.full((N, rows), float("nan"), device=DEV)
+    fb.bf16_gemm_twin(slab, D.x, y_t, ws_t)
+    torch.cuda.synchronize()
+    assert torch.equal(y_s.view(torch.int32), y_t.view(torch.int32))
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    y_g = torch.full((N, rows), float("nan"), device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        fb.bf16_gemm_twin(slab, D.x, y_g, ws_t, stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"  captured prefill GEMM replay {rep}")
+        y_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int32), y_s.view(torch.int32)), rep
+        _ = torch.randn(1 << 18, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_first_call_of_a_shape_under_capture_is_refused(gpu):
+    """A shape's first call times the candidates, which capture cannot do: it
+    returns FP8BLK_ERR_ARG, and an eager call afterwards works."""
+    from gpu_util import DEV, DevLinear
+    rows, cols, N = 384, 1024, 40  # a shape no other test uses
+    L = inputs.host_linear(rows, cols, N, 4343)
+    D = DevLinear(L.codes, L.scales, L.x)
+    D.check()
+    slab = D.slab()
+    ws = _ws(fb.OP_BF16_GEMM, rows, cols, N)
+    y = torch.full((N, rows), float("nan"), device=DEV)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        st = fb.bf16_gemm_twin(slab, D.x, y, ws, stream=cap, check=False)
+    torch.cuda.synchronize()
+    assert st == fb.ERR_ARG
+    fb.bf16_gemm_twin(slab, D.x, y, ws)
+    torch.cuda.synchronize()
+    y64, yabs = oracle.gemv_f64(L.codes, L.scales, L.x, nthreads=NTHREADS)
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - y64) <= gamma(cols) * yabs)
