@@ -292,36 +292,49 @@ class Chain:
 
 def chain_sweep(torch, fb, sw, steps, warmup, dev):
     """Time the dependent chain (Chain) as one HIP graph replayed per step,
-    events around `steps` replays on the replaying stream."""
+    events around `steps` replays on the replaying stream; and the same
+    graph without the glue kernels (the GEMV launches alone, in the same
+    order and on the same buffers: what the chain costs the dense linears)."""
     ch = Chain(torch, fb, sw, dev)
     ch.calibrate()
     stream = torch.cuda.current_stream()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        run_calls(ch.calls())
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=cap):
-        run_calls(ch.calls(stream=cap))
-    torch.cuda.synchronize()
-    for _ in range(max(warmup, 20)):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3
+
+    def graph_of(calls_of):
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            run_calls(calls_of(None))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            run_calls(calls_of(cap))
+        torch.cuda.synchronize()
+        for _ in range(max(warmup, 20)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    t = graph_of(lambda st: ch.calls(stream=st))
     v = sw.weight_bytes * steps / t / 1e9
     finite = all(bool(torch.isfinite(l["y"]).all()) for l in sw.lins)
+    launches_only = lambda st: [c for (kind, _a, _b), c in zip(ch.groups, ch.calls(stream=st)) if kind == "launch"]  # noqa: E731
+    t0 = graph_of(launches_only)
+    v0 = sw.weight_bytes * steps / t0 / 1e9
     log(f"dependent chain ({ch.n_launches} GEMV launches + {ch.n_glue} glue kernels per step, graph): "
-        f"{t / steps * 1e3:.4f} ms/step, {v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak); outputs finite: {finite}")
+        f"{t / steps * 1e3:.4f} ms/step, {v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak); outputs finite: {finite}; "
+        f"the GEMV launches alone {t0 / steps * 1e3:.4f} ms/step, {v0:.1f} GB/s ({100 * v0 / HBM_PEAK_GBS:.1f}%)")
     return {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
             "ms_per_step": round(t / steps * 1e3, 4), "gemv_launches_per_step": ch.n_launches,
             "glue_kernels_per_step": ch.n_glue, "outputs_finite": finite,
+            "gemv_launches_alone": {"value": round(v0, 1), "unit": "GB/s",
+                                    "pct_hbm_peak": round(100 * v0 / HBM_PEAK_GBS, 2),
+                                    "ms_per_step": round(t0 / steps * 1e3, 4)},
             "workload": "the sweep's 259 linears as a dependent decode chain: per layer [q+kv] -> o -> [gate+up] "
                         "-> down -> next layer, then the head; one launch per group, x = bf16(c*y) between "
                         "groups (one torch kernel), one HIP graph per step"}
