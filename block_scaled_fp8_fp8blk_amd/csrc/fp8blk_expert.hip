@@ -269,7 +269,7 @@ constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
 // a step past a row's end (in a last, partial window) reads the next row's
 // bytes, or zeros after the linear's last row, and never leaves the buffers.
 // Those steps are dropped in ex_compute_phase.
-template <int R, int O>
+template <int R, int O, bool ONE>
 struct ExUnit {
     const uint8_t* w;    // the unit's first row of codes
     const uint8_t* sc;   // its first row of block scales
@@ -283,6 +283,10 @@ struct ExUnit {
     uint32_t soff[R];    // lane: offset of the block scales of its row n of tile t + its lane group's step
     uint32_t xoff[O];    // lane: its token's codes + its 32-column block (kPastEnd: a row past M)
     uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step (likewise)
+    // ONE (a single token): one load per step pair; lane (n, g), n < 4, reads
+    // half n % 2 of block g of step n / 2 of the pair (kPastEnd for n >= 4);
+    // xhi selects the lanes of the pair's second step.
+    uint32_t xoff1, xhi;
 };
 
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 on gfx9-family targets: raw 32-bit data
@@ -293,11 +297,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ex_rsrc(const void* base, int6
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufferWord3);
 }
 
-template <int FMT, int R, int O, int WIN>
+template <int FMT, int R, int O, int WIN, bool ONE>
 struct ExWin {
     uint4 b[WIN / 2][R][2];                      // weights: step pair, tile, load
     typename std::conditional<FMT == kMX, uint32_t, uint2>::type bs[R];  // block scales of one step of the window
-    uint4 a[WIN][O][2];                          // activation codes: the lane group's 32-column block
+    // activation codes: the lane group's 32-column block of each step
+    // [step][o][half]; ONE: the step pair's single load [pair][0][0]
+    uint4 a[ONE ? WIN / 2 : WIN][O][ONE ? 1 : 2];
     uint32_t as[O];                              // activation scale code of one step of the window
 };
 
@@ -312,8 +318,8 @@ __device__ __forceinline__ int ex_steps(const ExLin& d) { return d.K / kStepCols
 template <int WIN>
 __device__ __forceinline__ int ex_nwin(const ExLin& d) { return (ex_steps(d) + WIN - 1) / WIN; }
 
-template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_unit(ExUnit<R, O>& U, const ExLin& d, int64_t v, int lane) {
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_unit(ExUnit<R, O, ONE>& U, const ExLin& d, int64_t v, int lane) {
     const int64_t r0 = v * (R * kTileRows);
     const int n = lane & 15, g = lane >> 4, c = lane >> 3;
     const int64_t half = d.K / 2, sper = d.K / (FMT == kMX ? 32 : 16);
@@ -347,6 +353,10 @@ __device__ __forceinline__ void ex_unit(ExUnit<R, O>& U, const ExLin& d, int64_t
         const bool live = tok < d.M;
         U.xoff[o] = live ? (uint32_t)(tok * d.K + 32 * g) : kPastEnd;
         U.xsoff[o] = live ? (uint32_t)(tok * nb) + g % WIN : kPastEnd;
+    }
+    if constexpr (ONE) {
+        U.xoff1 = n < 4 ? (uint32_t)(32 * g + 16 * (n & 1)) : kPastEnd;
+        U.xhi = n < 4 && (n >> 1) == 1 ? ~0u : 0u;
     }
 }
 
@@ -386,9 +396,9 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // every window issues the same loads. The activation steps are clamped to
 // the last step (uniformly); the weight and scale resources of a step past
 // the end read what ExUnit describes.
-template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win,
-                                               int q) {
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+                                               int win, int q) {
     const int s0 = win * WIN;
     const int sp = s0 + 2 * q;  // first step of the phase
     const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 64 * sp, U.w_left - 64 * sp);
@@ -410,13 +420,20 @@ __device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN>& b, const E
         }
     }
     const __amdgpu_buffer_rsrc_t xr = ex_rsrc(U.xq, U.xq_bytes);
+    if constexpr (ONE) {
+        // both steps of the pair in one load (a step past the end repeats the last)
+        const int j0 = min(sp, steps - 1);
+        const uint32_t d1 = (uint32_t)(min(sp + 1, steps - 1) - j0) * kStepCols;  // 0 or one step, uniform
+        b.a[q][0][0] = buf_load16(xr, U.xoff1 + (U.xhi & d1), kStepCols * j0, false);
+    } else {
 #pragma unroll
-    for (int s = 2 * q; s < 2 * q + 2; ++s) {
-        const int j = min(s0 + s, steps - 1);
+        for (int s = 2 * q; s < 2 * q + 2; ++s) {
+            const int j = min(s0 + s, steps - 1);
 #pragma unroll
-        for (int o = 0; o < O; ++o) {
-            b.a[s][o][0] = buf_load16(xr, U.xoff[o], kStepCols * j, false);
-            b.a[s][o][1] = buf_load16(xr, U.xoff[o] + 16, kStepCols * j, false);
+            for (int o = 0; o < O; ++o) {
+                b.a[s][o][0] = buf_load16(xr, U.xoff[o], kStepCols * j, false);
+                b.a[s][o][1] = buf_load16(xr, U.xoff[o] + 16, kStepCols * j, false);
+            }
         }
     }
     if (q == 0) {
@@ -426,8 +443,9 @@ __device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN>& b, const E
     }
 }
 
-template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN>& b, const ExUnit<R, O>& U, int steps, int win) {
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+                                         int win) {
 #pragma unroll
     for (int q = 0; q < WIN / 2; ++q) ex_issue_phase(b, U, steps, win, q);
 }
@@ -532,8 +550,8 @@ struct ExScales {
     uint32_t ws[R][WIN], ws_hi[R][WIN], as[O][WIN];
 };
 
-template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_gather(const ExWin<FMT, R, O, WIN>& b, ExScales<R, O, WIN>& S) {
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_gather(const ExWin<FMT, R, O, WIN, ONE>& b, ExScales<R, O, WIN>& S) {
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         if constexpr (FMT == kMX) {
@@ -551,8 +569,18 @@ __device__ __forceinline__ void ex_gather(const ExWin<FMT, R, O, WIN>& b, ExScal
 // MXFP4: acc[t] holds token rows x weight rows of tile t. NVFP4: acc[t * O + o]
 // register e holds, for weight row l % 16, the accumulator of token
 // 8o + 2(l/16) + e/2 over the 16-column blocks of parity e % 2.
-template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN>& b, const ExScales<R, O, WIN>& S,
+// Lane n % 4 = k of each quad of lanes, in all four lanes of the quad.
+template <int K>
+__device__ __forceinline__ uint4 quad_broadcast(uint4 v) {
+    constexpr int ctrl = K | (K << 2) | (K << 4) | (K << 6);  // quad_perm [K, K, K, K]
+    return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctrl, 0xF, 0xF, true),
+                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctrl, 0xF, 0xF, true),
+                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, ctrl, 0xF, 0xF, true),
+                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xF, 0xF, true));
+}
+
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE>& b, const ExScales<R, O, WIN>& S,
                                                  int steps, int win, int q, int lane, v4f* acc) {
     const int g = lane >> 4;
     uint32_t wop[R][2][4];
@@ -569,7 +597,16 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN>& b,
 #pragma unroll
         for (int o = 0; o < O; ++o) {
             uint2 ap[4];
-            act_to_operands(b.a[s][o], ap);
+            if constexpr (ONE) {
+                // lanes n = 0..3 of a lane group loaded (step, half) = (0, 0), (0, 1), (1, 0), (1, 1) of
+                // the pair; the token's rows (MXFP4: n = 0; NVFP4: n = 0, 1) take both halves of step s2
+                const uint4 R0 = b.a[q][0][0];
+                const uint4 lo = s2 == 0 ? (FMT == kMX ? R0 : quad_broadcast<0>(R0)) : quad_broadcast<2>(R0);
+                const uint4 half[2] = {lo, s2 == 0 ? quad_broadcast<1>(R0) : quad_broadcast<3>(R0)};
+                act_to_operands(half, ap);
+            } else {
+                act_to_operands(b.a[s][o], ap);
+            }
             const float sa = e8m0_cvt_scale<0>(S.as[o][s]);
             if constexpr (FMT == kMX) {
 #pragma unroll
@@ -744,13 +781,13 @@ __device__ __forceinline__ void ex_flush(int lane, int M, const ExOut& o) {
 // that about two windows of loads stay in flight while the wave computes;
 // then, at the end of cur's unit, its outputs; after the wave's last window
 // (`last`), what LDS holds. `un` addresses the windows of `set`.
-template <int FMT, int R, int O, int WIN>
-__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnit<R, O>& un,
-                                         ExWin<FMT, R, O, WIN>& set, int lane, v4f* acc, ExOut& out) {
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnit<R, O, ONE>& un,
+                                         ExWin<FMT, R, O, WIN, ONE>& set, int lane, v4f* acc, ExOut& out) {
     constexpr int NACC = R * O;
     ExScales<R, O, WIN> S;
     ex_gather(set, S);
-    if (nxt.win == 0 && nxt.more) ex_unit<FMT, R, O, WIN>(un, nxt.d, nxt.v, lane);
+    if (nxt.win == 0 && nxt.more) ex_unit<FMT, R, O, WIN, ONE>(un, nxt.d, nxt.v, lane);
     const int csteps = ex_steps(cur.d), nsteps = ex_steps(nxt.d);
 #pragma unroll
     for (int q = 0; q < WIN / 2; ++q) {
@@ -771,13 +808,13 @@ __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, boo
 // LIST: descriptors from the plan (lin, pre); else the one linear `one`.
 // Two register sets: set a holds windows p0, p2, ..., set b windows p1, p3, ...
 // (consecutive windows of the wave, possibly of different units).
-template <int FMT, int R, int O, int WIN, bool LIST>
+template <int FMT, int R, int O, int WIN, bool LIST, bool ONE>
 __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __restrict__ lin,
                                                                 const int64_t* __restrict__ pre, int64_t total,
                                                                 ExLin one) {
     constexpr int NACC = R * O;
-    using Win = ExWin<FMT, R, O, WIN>;
-    using Unit = ExUnit<R, O>;
+    using Win = ExWin<FMT, R, O, WIN, ONE>;
+    using Unit = ExUnit<R, O, ONE>;
     extern __shared__ __attribute__((aligned(16))) float ex_lds[];
     const int lane = threadIdx.x % kLanes;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
@@ -804,7 +841,7 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     out.k = 0;
     out.y_lo = out.y_hi = out.rows_lo = out.rows_hi = out.left_vec = 0;
     Unit ua, ub;
-    ex_unit<FMT, R, O, WIN>(ua, p0.d, p0.v, lane);
+    ex_unit<FMT, R, O, WIN, ONE>(ua, p0.d, p0.v, lane);
     v4f acc[NACC];
 #pragma unroll
     for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -812,7 +849,7 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     ex_issue(a, ua, ex_steps(p0.d), p0.win);
     ExPos p1 = ex_next<LIST, WIN>(p0, lin, pre, W, total);
     ub = ua;
-    if (p1.win == 0 && p1.more) ex_unit<FMT, R, O, WIN>(ub, p1.d, p1.v, lane);
+    if (p1.win == 0 && p1.more) ex_unit<FMT, R, O, WIN, ONE>(ub, p1.d, p1.v, lane);
     ex_issue(b, ub, ex_steps(p1.d), p1.win);
     for (;;) {
         // the window issued into a set follows the one in the other set: it
@@ -845,23 +882,33 @@ int ex_grid(int64_t units) {
     return (int)(need < cap ? need : cap);
 }
 
-template <int FMT, int O, bool LIST>
+template <int FMT, int O, bool LIST, bool ONE>
 void ex_launch_o(const ExLin* lin, const int64_t* pre, int64_t total, const ExLin& one, int grid, hipStream_t s) {
     constexpr int R = ex_tiles(FMT, O), WIN = ex_win(FMT, O);
     constexpr int lds = kExLdsBytes;
-    k_expert<FMT, R, O, WIN, LIST><<<dim3((unsigned)grid), dim3(kSeqWaves * kLanes), lds, s>>>(lin, pre, total, one);
+    k_expert<FMT, R, O, WIN, LIST, ONE><<<dim3((unsigned)grid), dim3(kSeqWaves * kLanes), lds, s>>>(lin, pre, total,
+                                                                                                   one);
 }
 
+// A single activation row (M = 1) takes the kernels whose activation loads
+// serve both steps of a pair at once (ExUnit, ONE).
 template <bool LIST>
 int ex_launch(int fmt, int M, const ExLin* lin, const int64_t* pre, int64_t total, const ExLin& one, int grid,
               hipStream_t s) {
     (void)hipGetLastError();
-    if (fmt == kMX)
-        ex_launch_o<kMX, 1, LIST>(lin, pre, total, one, grid, s);
-    else if (ex_groups(kNV, M) == 1)
-        ex_launch_o<kNV, 1, LIST>(lin, pre, total, one, grid, s);
-    else
-        ex_launch_o<kNV, 2, LIST>(lin, pre, total, one, grid, s);
+    if (fmt == kMX) {
+        if (M == 1)
+            ex_launch_o<kMX, 1, LIST, true>(lin, pre, total, one, grid, s);
+        else
+            ex_launch_o<kMX, 1, LIST, false>(lin, pre, total, one, grid, s);
+    } else if (ex_groups(kNV, M) == 1) {
+        if (M == 1)
+            ex_launch_o<kNV, 1, LIST, true>(lin, pre, total, one, grid, s);
+        else
+            ex_launch_o<kNV, 1, LIST, false>(lin, pre, total, one, grid, s);
+    } else {
+        ex_launch_o<kNV, 2, LIST, false>(lin, pre, total, one, grid, s);
+    }
     return launch_status();
 }
 
