@@ -35,6 +35,10 @@
  *      smallest power of two 2^e, e in [-127, 127], with amax <= 448 * 2^e;
  *      each code is x / 2^e (exact) rounded to the nearest e4m3 value, ties to
  *      even, keeping the sign of x (so -0 and small negatives give 0x80).
+      Parity unpinned as to the choice of scale rule: the pages say only
+      that activations become FP8 codes per 128 elements, so nothing on
+      them rules out another rule (an f32 scale amax / 448, say). What the
+      tests pin is that this routine computes R4 exactly as stated.
  *   R5 the native GEMV: y[m][r] = g * sum over c of q(m, c) * w(r, c), with q
  *      the dequantized activation code and w the element value; the pages fix
  *      no summation order, so the library is checked against this sum by
