@@ -36,6 +36,7 @@ constexpr int kMX = FP8BLK_FMT_MXFP4, kNV = FP8BLK_FMT_NVFP4;
 constexpr int kActBlock = 128;   // activation scale block (columns)
 constexpr int kStepCols = 128;   // columns per matrix instruction
 constexpr int kTileRows = 16;    // weight rows per matrix instruction
+constexpr int kExWaveLdsBytes = 80 * 1024 / 4;  // LDS of one wave of the native GEMV (a quarter of a workgroup's)
 constexpr unsigned long long kNone = ~0ull;
 
 inline int fp4_block(int fmt) { return fmt == kMX ? 32 : 16; }
@@ -283,10 +284,14 @@ struct ExUnit {
     uint32_t soff[R];    // lane: offset of the block scales of its row n of tile t + its lane group's step
     uint32_t xoff[O];    // lane: its token's codes + its 32-column block (kPastEnd: a row past M)
     uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step (likewise)
-    // ONE (a single token): one load per step pair; lane (n, g), n < 4, reads
-    // half n % 2 of block g of step n / 2 of the pair (kPastEnd for n >= 4);
-    // xhi selects the lanes of the pair's second step.
+    // ONE (a single token): one 8-byte load per step pair; lane (n, g) reads
+    // the 8 codes of piece p = n / 2 (step p / 4 of the pair, columns
+    // 32 (p % 4) + 8g .. +7); xhi selects the lanes of the pair's second step.
     uint32_t xoff1, xhi;
+    // ONE: weight load (q, t, h) reads rows 16t + 8h + 4q .. +3 of the unit,
+    // 256 bytes (the window's 4 steps) each; lane l: row l / 16, bytes
+    // 16 (l % 16) .. +15.
+    uint32_t wq[ONE ? 2 : 1][R][2];
 };
 
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 on gfx9-family targets: raw 32-bit data
@@ -302,17 +307,23 @@ struct ExWin {
     uint4 b[WIN / 2][R][2];                      // weights: step pair, tile, load
     typename std::conditional<FMT == kMX, uint32_t, uint2>::type bs[R];  // block scales of one step of the window
     // activation codes: the lane group's 32-column block of each step
-    // [step][o][half]; ONE: the step pair's single load [pair][0][0]
-    uint4 a[ONE ? WIN / 2 : WIN][O][ONE ? 1 : 2];
+    // [step][o][half]; ONE: the step pair's single 8-byte load [pair][0][0]
+    typename std::conditional<ONE, uint2, uint4>::type a[ONE ? WIN / 2 : WIN][O][ONE ? 1 : 2];
     uint32_t as[O];                              // activation scale code of one step of the window
 };
 
+// Every byte is a named scalar field (ExLin is 64-byte aligned): copies of a
+// position then copy fields only, which the compiler keeps in registers or
+// drops; implicit padding was copied through scratch memory.
 struct ExPos {
     int64_t u, v;  // unit (list numbering) and unit within its linear
-    int win, j;
-    bool more;     // false: past the wave's last window (the position repeats the last one)
+    int32_t win, j;
+    int32_t more;  // 0: past the wave's last window (the position repeats the last one)
+    int32_t spare0;
+    int64_t spare1, spare2, spare3, spare4;
     ExLin d;
 };
+static_assert(sizeof(ExPos) == 64 + sizeof(ExLin), "no padding in a position");
 
 __device__ __forceinline__ int ex_steps(const ExLin& d) { return d.K / kStepCols; }
 template <int WIN>
@@ -355,8 +366,18 @@ __device__ __forceinline__ void ex_unit(ExUnit<R, O, ONE>& U, const ExLin& d, in
         U.xsoff[o] = live ? (uint32_t)(tok * nb) + g % WIN : kPastEnd;
     }
     if constexpr (ONE) {
-        U.xoff1 = n < 4 ? (uint32_t)(32 * g + 16 * (n & 1)) : kPastEnd;
-        U.xhi = n < 4 && (n >> 1) == 1 ? ~0u : 0u;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int t = 0; t < R; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t row = min(r0 + 16 * t + 8 * h + 4 * q + (lane >> 4), d.rows - 1) - r0;
+                    U.wq[q][t][h] = (uint32_t)(row * half) + 16 * (lane & 15);
+                }
+        const int pc = n >> 1;
+        U.xoff1 = (uint32_t)(32 * (pc & 3) + 8 * g);
+        U.xhi = pc >= 4 ? ~0u : 0u;
     }
 }
 
@@ -380,7 +401,7 @@ __device__ __forceinline__ ExPos ex_next(const ExPos& p, const ExLin* lin, const
             }
         }
     } else {
-        n.more = false;
+        n.more = 0;
     }
     return n;
 }
@@ -397,15 +418,32 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // the last step (uniformly); the weight and scale resources of a step past
 // the end read what ExUnit describes.
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
-                                               int win, int q) {
+__device__ __forceinline__ void ex_issue_weights(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int win,
+                                                 int q) {
+    if constexpr (ONE) {
+        static_assert(WIN == 4, "a single-token window is 4 steps (256 bytes of a row)");
+        const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 256 * win, U.w_left - 256 * win);
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) b.b[q][t][h] = buf_load16(wr, U.wq[q][t][h], 0, true);
+    } else {
+        const int sp = win * WIN + 2 * q;  // first step of the phase
+        const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 64 * sp, U.w_left - 64 * sp);
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) b.b[q][t][h] = buf_load16(wr, U.woff[t][h], 0, true);
+    }
+}
+
+// The rest of a phase's loads: block and activation scales (phase 0) and
+// activation codes.
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_issue_rest(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+                                              int win, int q) {
     const int s0 = win * WIN;
     const int sp = s0 + 2 * q;  // first step of the phase
-    const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 64 * sp, U.w_left - 64 * sp);
-#pragma unroll
-    for (int t = 0; t < R; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) b.b[q][t][h] = buf_load16(wr, U.woff[t][h], 0, true);
     if (q == 0) {
         constexpr int SB = FMT == kMX ? 4 : 8;  // block-scale bytes of a row per step
         const __amdgpu_buffer_rsrc_t sr = ex_rsrc(U.sc + SB * s0, U.sc_left - SB * s0);
@@ -424,7 +462,8 @@ __device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, co
         // both steps of the pair in one load (a step past the end repeats the last)
         const int j0 = min(sp, steps - 1);
         const uint32_t d1 = (uint32_t)(min(sp + 1, steps - 1) - j0) * kStepCols;  // 0 or one step, uniform
-        b.a[q][0][0] = buf_load16(xr, U.xoff1 + (U.xhi & d1), kStepCols * j0, false);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(xr, (int)(U.xoff1 + (U.xhi & d1)), kStepCols * j0, 0);
+        b.a[q][0][0] = make_uint2(v[0], v[1]);
     } else {
 #pragma unroll
         for (int s = 2 * q; s < 2 * q + 2; ++s) {
@@ -441,6 +480,13 @@ __device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, co
 #pragma unroll
         for (int o = 0; o < O; ++o) b.as[o] = __builtin_amdgcn_raw_buffer_load_b8(ar, (int)U.xsoff[o], 0, 0);
     }
+}
+
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+                                               int win, int q) {
+    ex_issue_weights(b, U, win, q);
+    ex_issue_rest(b, U, steps, win, q);
 }
 
 template <int FMT, int R, int O, int WIN, bool ONE>
@@ -569,23 +615,87 @@ __device__ __forceinline__ void ex_gather(const ExWin<FMT, R, O, WIN, ONE>& b, E
 // MXFP4: acc[t] holds token rows x weight rows of tile t. NVFP4: acc[t * O + o]
 // register e holds, for weight row l % 16, the accumulator of token
 // 8o + 2(l/16) + e/2 over the 16-column blocks of parity e % 2.
-// Lane n % 4 = k of each quad of lanes, in all four lanes of the quad.
-template <int K>
-__device__ __forceinline__ uint4 quad_broadcast(uint4 v) {
-    constexpr int ctrl = K | (K << 2) | (K << 4) | (K << 6);  // quad_perm [K, K, K, K]
-    return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctrl, 0xF, 0xF, true),
-                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctrl, 0xF, 0xF, true),
-                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, ctrl, 0xF, 0xF, true),
-                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xF, 0xF, true));
+// Lane n + M of each row of 16 lanes into lane n (lanes past the row's end
+// read 0): the piece loaded by lane 2p reaches lanes 0 and 1 with M = 2p.
+template <int M>
+__device__ __forceinline__ uint2 row_shift(uint2 v) {
+    if constexpr (M == 0) {
+        return v;
+    } else {
+        constexpr int ctrl = 0x100 + M;  // row_shl:M
+        return make_uint2((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctrl, 0xF, 0xF, true),
+                          (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctrl, 0xF, 0xF, true));
+    }
+}
+
+// The single-token kernels read the weights of a window (32 rows x 256
+// bytes) as 8 loads of 4 rows x 256 bytes: runs of 256 bytes read faster than
+// k_expert's pieces of 128 bytes of 8 rows (routed-expert sweep, MXFP4: 81.8
+// against 75.9% of HBM peak with the same arithmetic). The loads go to the
+// wave's part of LDS as they are and come back in the matrix instruction's
+// operand layout (so no lane exchanges either), which frees their registers
+// for the window after next before the matrix work starts.
+// Region (dwords): block (step s, tile t) at (2s + t) kExBlkDw + 8s, holding
+// [row n (stride kExRowDw)][8-column group g][32-column block k]. The row
+// padding (20 dwords for 16) puts the 8 lanes of a 16-byte read on distinct
+// banks, the 8s shift does the same for the 32 lanes of a write.
+constexpr int kExRowDw = 20;
+constexpr int kExBlkDw = kTileRows * kExRowDw;
+__host__ __device__ constexpr int ex_blk(int s, int t) { return (2 * s + t) * kExBlkDw + 8 * s; }
+constexpr int kExXchgDw = ex_blk(3, 1) + kExBlkDw;
+static_assert(kExXchgDw * 4 <= kExWaveLdsBytes, "the exchange region fits a wave's LDS part");
+
+struct ExXchg {
+    uint32_t* lds;  // the workgroup's LDS
+    uint32_t w;     // lane l of a load: its 16 bytes (row l / 16, step (l % 16) / 4, block l % 4), in dwords
+    uint32_t r;     // lane (n, g): its reads (row n, group g), in dwords
+};
+
+__device__ __forceinline__ ExXchg ex_xchg(float* lds, int wave, int lane) {
+    const uint32_t base = (uint32_t)wave * (kExWaveLdsBytes / 4);
+    const int st = (lane & 15) >> 2;
+    ExXchg x;
+    x.lds = reinterpret_cast<uint32_t*>(lds);
+    x.w = base + (uint32_t)(ex_blk(st, 0) + (lane >> 4) * kExRowDw + (lane & 3));
+    x.r = base + (uint32_t)((lane & 15) * kExRowDw + 4 * (lane >> 4));
+    return x;
+}
+
+// Load (q, t, h) of a window (rows 16t + 8h + 4q .. +3) into the region:
+// its groups g = 0..3 go 4 dwords apart ...
+__device__ __forceinline__ void weights_to_lds(const uint4& ld, const ExXchg& X, int q, int t, int h) {
+    uint32_t* w = X.lds + X.w + t * kExBlkDw + (8 * h + 4 * q) * kExRowDw;
+    w[0] = ld.x;
+    w[4] = ld.y;
+    w[8] = ld.z;
+    w[12] = ld.w;
+}
+
+// ... and back as the operands op[s][k] of steps 2q, 2q + 1 of tile t, as
+// weights_to_operands makes them.
+__device__ __forceinline__ void weights_from_lds(const ExXchg& X, int q, int t, uint32_t (&op)[2][4]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const uint4 v = *reinterpret_cast<const uint4*>(X.lds + X.r + ex_blk(2 * q + st, t));
+        op[st][0] = v.x;
+        op[st][1] = v.y;
+        op[st][2] = v.z;
+        op[st][3] = v.w;
+    }
 }
 
 template <int FMT, int R, int O, int WIN, bool ONE>
 __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE>& b, const ExScales<R, O, WIN>& S,
-                                                 int steps, int win, int q, int lane, v4f* acc) {
+                                                 int steps, int win, int q, int lane, const ExXchg& X, v4f* acc) {
     const int g = lane >> 4;
     uint32_t wop[R][2][4];
 #pragma unroll
-    for (int t = 0; t < R; ++t) weights_to_operands(b.b[q][t], wop[t]);
+    for (int t = 0; t < R; ++t) {
+        if constexpr (ONE)
+            weights_from_lds(X, q, t, wop[t]);  // stored by ex_stage
+        else
+            weights_to_operands(b.b[q][t], wop[t]);
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
         const int s = 2 * q + s2;
@@ -598,12 +708,19 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
         for (int o = 0; o < O; ++o) {
             uint2 ap[4];
             if constexpr (ONE) {
-                // lanes n = 0..3 of a lane group loaded (step, half) = (0, 0), (0, 1), (1, 0), (1, 1) of
-                // the pair; the token's rows (MXFP4: n = 0; NVFP4: n = 0, 1) take both halves of step s2
-                const uint4 R0 = b.a[q][0][0];
-                const uint4 lo = s2 == 0 ? (FMT == kMX ? R0 : quad_broadcast<0>(R0)) : quad_broadcast<2>(R0);
-                const uint4 half[2] = {lo, s2 == 0 ? quad_broadcast<1>(R0) : quad_broadcast<3>(R0)};
-                act_to_operands(half, ap);
+                // the token's rows (MXFP4: n = 0; NVFP4: n = 0, 1) take piece 4 s2 + k from lane 2(4 s2 + k)
+                const uint2 a0 = b.a[q][0][0];
+                if (s2 == 0) {
+                    ap[0] = row_shift<0>(a0);
+                    ap[1] = row_shift<2>(a0);
+                    ap[2] = row_shift<4>(a0);
+                    ap[3] = row_shift<6>(a0);
+                } else {
+                    ap[0] = row_shift<8>(a0);
+                    ap[1] = row_shift<10>(a0);
+                    ap[2] = row_shift<12>(a0);
+                    ap[3] = row_shift<14>(a0);
+                }
             } else {
                 act_to_operands(b.a[s][o], ap);
             }
@@ -706,6 +823,7 @@ __device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, co
 // for 16-byte stores), so the final writes load nothing but LDS.
 constexpr int kExLdsBytes = 80 * 1024;                      // per workgroup: at most 2 per compute unit
 constexpr int kExWaveLds = kExLdsBytes / kSeqWaves;         // per wave
+static_assert(kExWaveLds == kExWaveLdsBytes, "LDS part of a wave");
 constexpr int kExHoldMinM = 8;                              // smallest panel whose outputs are held back
 constexpr int kExUnitRows = ex_tiles(kMX, 1) * kTileRows;   // rows of a unit (both formats)
 static_assert(ex_tiles(kNV, 2) * kTileRows == kExUnitRows, "one unit height");
@@ -783,18 +901,43 @@ __device__ __forceinline__ void ex_flush(int lane, int M, const ExOut& o) {
 // (`last`), what LDS holds. `un` addresses the windows of `set`.
 template <int FMT, int R, int O, int WIN, bool ONE>
 __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnit<R, O, ONE>& un,
-                                         ExWin<FMT, R, O, WIN, ONE>& set, int lane, v4f* acc, ExOut& out) {
+                                         ExWin<FMT, R, O, WIN, ONE>& set, int lane, const ExXchg& X, v4f* acc,
+                                         ExOut& out) {
     constexpr int NACC = R * O;
     ExScales<R, O, WIN> S;
     ex_gather(set, S);
     if (nxt.win == 0 && nxt.more) ex_unit<FMT, R, O, WIN, ONE>(un, nxt.d, nxt.v, lane);
     const int csteps = ex_steps(cur.d), nsteps = ex_steps(nxt.d);
-#pragma unroll
-    for (int q = 0; q < WIN / 2; ++q) {
+    if constexpr (ONE) {
+        // every load of the window carries all its steps: the whole window
+        // goes to LDS, its registers take the weights of window nxt, then the
+        // matrix work, then the rest of nxt's loads
         __builtin_amdgcn_sched_barrier(0);
-        ex_compute_phase(set, S, csteps, cur.win, q, lane, acc);
-        __builtin_amdgcn_sched_barrier(0);  // the phase's registers are free: refill them
-        ex_issue_phase(set, un, nsteps, nxt.win, q);
+#pragma unroll
+        for (int q = 0; q < WIN / 2; ++q)
+#pragma unroll
+            for (int t = 0; t < R; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) weights_to_lds(set.b[q][t][h], X, q, t, h);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < WIN / 2; ++q) ex_issue_weights(set, un, nxt.win, q);
+#pragma unroll
+        for (int q = 0; q < WIN / 2; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            ex_compute_phase(set, S, csteps, cur.win, q, lane, X, acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < WIN / 2; ++q) ex_issue_rest(set, un, nsteps, nxt.win, q);
+    } else {
+#pragma unroll
+        for (int q = 0; q < WIN / 2; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            ex_compute_phase(set, S, csteps, cur.win, q, lane, X, acc);
+            __builtin_amdgcn_sched_barrier(0);  // the phase's registers are free: refill them
+            ex_issue_phase(set, un, nsteps, nxt.win, q);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (cur.win + 1 == ex_nwin<WIN>(cur.d)) {
@@ -818,13 +961,16 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     extern __shared__ __attribute__((aligned(16))) float ex_lds[];
     const int lane = threadIdx.x % kLanes;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const ExXchg X = ex_xchg(ex_lds, wave, lane);  // used by the single-token kernels (no outputs held in LDS)
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     ExPos p0;
     p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + wave;
     if (p0.u >= total) return;
     p0.win = 0;
     p0.j = 0;
-    p0.more = true;
+    p0.spare0 = 0;
+    p0.spare1 = p0.spare2 = p0.spare3 = p0.spare4 = 0;
+    p0.more = 1;
     if constexpr (LIST) {
         while (p0.u >= pre[p0.j + 1]) ++p0.j;
         p0.d = lin[p0.j];
@@ -856,11 +1002,11 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
         // continues that window's unit unless it starts a new one
         const ExPos p2 = ex_next<LIST, WIN>(p1, lin, pre, W, total);
         ua = ub;
-        ex_stage(p0, p2, !p1.more, ua, a, lane, acc, out);
+        ex_stage(p0, p2, !p1.more, ua, a, lane, X, acc, out);
         if (!p1.more) break;
         const ExPos p3 = ex_next<LIST, WIN>(p2, lin, pre, W, total);
         ub = ua;
-        ex_stage(p1, p3, !p2.more, ub, b, lane, acc, out);
+        ex_stage(p1, p3, !p2.more, ub, b, lane, X, acc, out);
         if (!p2.more) break;
         p0 = p2;
         p1 = p3;
