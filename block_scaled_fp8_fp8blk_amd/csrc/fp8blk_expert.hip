@@ -760,8 +760,10 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
                         v4f& a = acc[t * O + o];
                         a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
                         a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
-                        a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
-                        a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
+                        if constexpr (!ONE) {  // elements 2, 3: token 8o + 2(l / 16) + 1, past a single token
+                            a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
+                            a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
+                        }
                     }
                 }
             }
