@@ -825,7 +825,7 @@ def summarize_expert_trace(stats_csv, command, trace_csv=None):
     names = {"0": "MXFP4", "1": "NVFP4"}
     lines = ["# rocprofv3 kernel trace: native expert arm, routed-expert sweep (1032 FP4 linears), M=1", "",
              f"Command: `{command}`" if command else "", "",
-             "k_expert<format, tiles, token groups, steps per window, list>; format 0 = MXFP4, 1 = NVFP4. "
+             "k_expert<format, tiles, token groups, steps per window, list, single token>; format 0 = MXFP4, 1 = NVFP4. "
              "Each k_expert launch is one whole step (every linear of the sweep).", "",
              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(stats_csv)):

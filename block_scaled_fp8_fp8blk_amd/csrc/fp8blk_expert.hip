@@ -239,6 +239,10 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 // and exchanged likewise (permlane32, permlane16). Each lane group loads the
 // block scales (and the activation scale) of a different step of the window
 // and the exchanges hand every lane those of all the window's steps.
+// One activation row (template flag ONE, the decode case) reads the weights
+// differently: 4 rows x 256 bytes per load, through LDS (weights_to_lds), and
+// the activation as one 8-byte piece per lane and step pair, handed to the
+// token's rows by row shifts. Same operands, instructions and order.
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
