@@ -160,20 +160,24 @@ def native_parity(gpu, gu, L, M=None, what=""):
 
 @pytest.mark.parametrize("fmt", [MX, NV])
 @pytest.mark.parametrize("rows,cols,M", [(256, 512, 1), (1000, 384, 3), (17, 128, 16), (64, 1152, 2),
-                                         (200, 640, 5), (48, 256, 9), (2048, 4096, 1), (4096, 2048, 1)])
+                                         (200, 640, 5), (48, 256, 9), (2048, 4096, 1), (4096, 2048, 1),
+                                         # one activation row (its own load layout): a window shorter than 4
+                                         # steps, ragged rows and a last partial window
+                                         (17, 128, 1), (1000, 384, 1), (45, 1152, 1), (100, 2176, 1)])
 def test_native_gemv_parity(gpu, gu, fmt, rows, cols, M):
     L = I.host_fp4_linear(fmt, rows, cols, M, 1000 + rows + cols + M)
     native_parity(gpu, gu, L, what=f"{rows}x{cols}")
 
 
+@pytest.mark.parametrize("M", [1, 3])
 @pytest.mark.parametrize("fmt,lo,hi", [(MX, 0, 6), (MX, 230, 238), (NV, 0x01, 0x0F), (NV, 0x70, 0x7E)])
-def test_native_gemv_extreme_scales(gpu, gu, fmt, lo, hi):
+def test_native_gemv_extreme_scales(gpu, gu, fmt, lo, hi, M):
     """Block scales near the ends of the range the load check accepts: MXFP4
     codes 0..6 (2^-127..2^-121, code 0 included) and 230..238, NVFP4 e4m3
     subnormal and largest scales. (Larger MXFP4 codes are accepted too, but
     their outputs over 1024 columns can pass f32's largest value, where f32
     accumulation ends in infinity whatever the order.)"""
-    L = I.host_fp4_linear(fmt, 256, 1024, 3, 1500 + lo, scale_lo=lo, scale_hi=hi)
+    L = I.host_fp4_linear(fmt, 256, 1024, M, 1500 + lo, scale_lo=lo, scale_hi=hi)
     ws = torch.empty(256, dtype=torch.uint8, device=gu.DEV)
     assert gpu.fp4_load_check(fmt, dev(gu, L.codes), dev(gu, L.scales), ws, check=False) == (0, -1)
     native_parity(gpu, gu, L, what=f"scales {lo}..{hi}")
