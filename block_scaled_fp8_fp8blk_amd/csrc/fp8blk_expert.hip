@@ -265,6 +265,10 @@ static_assert(sizeof(ExLin) == kSeqDescBytes, "descriptor size of the plan");
 constexpr int ex_groups(int fmt, int M) { return fmt == kMX || M <= 8 ? 1 : 2; }
 constexpr int ex_tiles(int, int) { return 2; }
 constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
+// Kernels whose weights go through LDS as 4-row x 256-byte loads (ExXchg):
+// windows of 4 steps, MXFP4 at any panel height, NVFP4 at one activation row
+// (its panels need the registers the exchange would take).
+constexpr bool ex_xl(int fmt, int win, bool one) { return win == 4 && (fmt == kMX || one); }
 
 // A unit's loads go through buffer resources: a resource in scalar
 // registers (base, byte count) plus a 32-bit per-lane offset that is fixed for
@@ -284,7 +288,7 @@ struct ExUnit {
     int64_t sc_left;     // bytes of block scales from sc to the linear's end
     int32_t xq_bytes;    // M * K
     int32_t xs_bytes;    // M * K / 128
-    uint32_t woff[R][2]; // lane: offset of its row in tile t, load h (rows 8h .. 8h+7 of the tile) + its chunk
+    uint32_t woff[R][2]; // windows of 2 steps: lane's row in tile t, load h (rows 8h .. 8h+7) + its chunk
     uint32_t soff[R];    // lane: offset of the block scales of its row n of tile t + its lane group's step
     uint32_t xoff[O];    // lane: its token's codes + its 32-column block (kPastEnd: a row past M)
     uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step (likewise)
@@ -292,10 +296,10 @@ struct ExUnit {
     // the 8 codes of piece p = n / 2 (step p / 4 of the pair, columns
     // 32 (p % 4) + 8g .. +7); xhi selects the lanes of the pair's second step.
     uint32_t xoff1, xhi;
-    // ONE: weight load (q, t, h) reads rows 16t + 8h + 4q .. +3 of the unit,
-    // 256 bytes (the window's 4 steps) each; lane l: row l / 16, bytes
-    // 16 (l % 16) .. +15.
-    uint32_t wq[ONE ? 2 : 1][R][2];
+    // Windows of 4 steps: weight load (q, t, h) reads rows 16t + 8h + 4q ..
+    // +3 of the unit, 256 bytes (the window's 4 steps) each; lane l: row
+    // l / 16, bytes 16 (l % 16) .. +15.
+    uint32_t wq[2][R][2];
 };
 
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 on gfx9-family targets: raw 32-bit data
@@ -369,7 +373,7 @@ __device__ __forceinline__ void ex_unit(ExUnit<R, O, ONE>& U, const ExLin& d, in
         U.xoff[o] = live ? (uint32_t)(tok * d.K + 32 * g) : kPastEnd;
         U.xsoff[o] = live ? (uint32_t)(tok * nb) + g % WIN : kPastEnd;
     }
-    if constexpr (ONE) {
+    if constexpr (ex_xl(FMT, WIN, ONE)) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -379,6 +383,8 @@ __device__ __forceinline__ void ex_unit(ExUnit<R, O, ONE>& U, const ExLin& d, in
                     const int64_t row = min(r0 + 16 * t + 8 * h + 4 * q + (lane >> 4), d.rows - 1) - r0;
                     U.wq[q][t][h] = (uint32_t)(row * half) + 16 * (lane & 15);
                 }
+    }
+    if constexpr (ONE) {
         const int pc = n >> 1;
         U.xoff1 = (uint32_t)(32 * (pc & 3) + 8 * g);
         U.xhi = pc >= 4 ? ~0u : 0u;
@@ -424,8 +430,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 template <int FMT, int R, int O, int WIN, bool ONE>
 __device__ __forceinline__ void ex_issue_weights(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int win,
                                                  int q) {
-    if constexpr (ONE) {
-        static_assert(WIN == 4, "a single-token window is 4 steps (256 bytes of a row)");
+    if constexpr (ex_xl(FMT, WIN, ONE)) {  // 4 rows x 256 bytes per load (see ExXchg)
         const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 256 * win, U.w_left - 256 * win);
 #pragma unroll
         for (int t = 0; t < R; ++t)
@@ -695,7 +700,7 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
     uint32_t wop[R][2][4];
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-        if constexpr (ONE)
+        if constexpr (ex_xl(FMT, WIN, ONE))
             weights_from_lds(X, q, t, wop[t]);  // stored by ex_stage
         else
             weights_to_operands(b.b[q][t], wop[t]);
@@ -914,7 +919,7 @@ __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, boo
     ex_gather(set, S);
     if (nxt.win == 0 && nxt.more) ex_unit<FMT, R, O, WIN, ONE>(un, nxt.d, nxt.v, lane);
     const int csteps = ex_steps(cur.d), nsteps = ex_steps(nxt.d);
-    if constexpr (ONE) {
+    if constexpr (ex_xl(FMT, WIN, ONE)) {
         // every load of the window carries all its steps: the whole window
         // goes to LDS, its registers take the weights of window nxt, then the
         // matrix work, then the rest of nxt's loads
@@ -987,9 +992,11 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     }
     // Every linear of a list has the same M (the plan checks it).
     ExOut out;
-    out.lds = ex_lds + wave * (kExWaveLds / 4);
+    // the weight exchange takes the start of the wave's part
+    constexpr int xchg = ex_xl(FMT, WIN, ONE) ? kExXchgDw : 0;
+    out.lds = ex_lds + wave * (kExWaveLds / 4) + xchg;
     const int slot_floats = p0.d.M * kExUnitRows;
-    out.slots = p0.d.M >= kExHoldMinM ? min(kLanes, kExWaveLds / 4 / slot_floats) : 0;
+    out.slots = p0.d.M >= kExHoldMinM ? min(kLanes, (kExWaveLds / 4 - xchg) / slot_floats) : 0;
     out.k = 0;
     out.y_lo = out.y_hi = out.rows_lo = out.rows_hi = out.left_vec = 0;
     Unit ua, ub;
