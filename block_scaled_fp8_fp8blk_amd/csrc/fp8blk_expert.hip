@@ -266,9 +266,9 @@ constexpr int ex_groups(int fmt, int M) { return fmt == kMX || M <= 8 ? 1 : 2; }
 constexpr int ex_tiles(int, int) { return 2; }
 constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
 // Kernels whose weights go through LDS as 4-row x 256-byte loads (ExXchg):
-// windows of 4 steps, MXFP4 at any panel height, NVFP4 at one activation row
-// (its panels need the registers the exchange would take).
-constexpr bool ex_xl(int fmt, int win, bool one) { return win == 4 && (fmt == kMX || one); }
+// those with windows of 4 steps (all but NVFP4 panels of more than 8 rows,
+// whose windows are 2 steps).
+constexpr bool ex_xl(int, int win, bool) { return win == 4; }
 
 // A unit's loads go through buffer resources: a resource in scalar
 // registers (base, byte count) plus a 32-bit per-lane offset that is fixed for
@@ -278,7 +278,7 @@ constexpr bool ex_xl(int fmt, int win, bool one) { return win == 4 && (fmt == kM
 // a step past a row's end (in a last, partial window) reads the next row's
 // bytes, or zeros after the linear's last row, and never leaves the buffers.
 // Those steps are dropped in ex_compute_phase.
-template <int R, int O, bool ONE>
+template <int R, int O, bool ONE, bool WL>
 struct ExUnit {
     const uint8_t* w;    // the unit's first row of codes
     const uint8_t* sc;   // its first row of block scales
@@ -296,11 +296,20 @@ struct ExUnit {
     // the 8 codes of piece p = n / 2 (step p / 4 of the pair, columns
     // 32 (p % 4) + 8g .. +7); xhi selects the lanes of the pair's second step.
     uint32_t xoff1, xhi;
-    // Windows of 4 steps: weight load (q, t, h) reads rows 16t + 8h + 4q ..
-    // +3 of the unit, 256 bytes (the window's 4 steps) each; lane l: row
-    // l / 16, bytes 16 (l % 16) .. +15.
-    uint32_t wq[2][R][2];
+    // ex_xl kernels: weight load (q, t, h) reads rows 16t + 8h + 4q .. +3 of
+    // the unit, 256 bytes (the window's 4 steps) each; lane l: row l / 16,
+    // bytes 16 (l % 16) .. +15, at offset wq[q][t][h] (rows past the end
+    // repeat the last). NVFP4 panels, short of registers, keep one lane base
+    // instead and add (16t + 8h + 4q) half per load; their rows past the
+    // linear's end read zeros (the range check) and are not stored.
+    uint32_t wq[WL ? 0 : 2][R][2];
+    uint32_t wlane;
+    int32_t half;
 };
+
+// WL: the per-load lane base of NVFP4 panels (ExUnit::wlane).
+template <int FMT, int R, int O, bool ONE>
+using ExUnitT = ExUnit<R, O, ONE, FMT == kNV && !ONE>;
 
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 on gfx9-family targets: raw 32-bit data
 constexpr uint32_t kPastEnd = 0x40000000u;   // a lane offset past every resource's end (all are < 2^31 bytes)
@@ -338,7 +347,7 @@ template <int WIN>
 __device__ __forceinline__ int ex_nwin(const ExLin& d) { return (ex_steps(d) + WIN - 1) / WIN; }
 
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_unit(ExUnit<R, O, ONE>& U, const ExLin& d, int64_t v, int lane) {
+__device__ __forceinline__ void ex_unit(ExUnitT<FMT, R, O, ONE>& U, const ExLin& d, int64_t v, int lane) {
     const int64_t r0 = v * (R * kTileRows);
     const int n = lane & 15, g = lane >> 4, c = lane >> 3;
     const int64_t half = d.K / 2, sper = d.K / (FMT == kMX ? 32 : 16);
@@ -374,15 +383,20 @@ __device__ __forceinline__ void ex_unit(ExUnit<R, O, ONE>& U, const ExLin& d, in
         U.xsoff[o] = live ? (uint32_t)(tok * nb) + g % WIN : kPastEnd;
     }
     if constexpr (ex_xl(FMT, WIN, ONE)) {
+        if constexpr (FMT == kNV && !ONE) {
+            U.wlane = (uint32_t)((lane >> 4) * half) + 16 * (lane & 15);
+            U.half = (int32_t)half;
+        } else {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int t = 0; t < R; ++t)
+                for (int t = 0; t < R; ++t)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int64_t row = min(r0 + 16 * t + 8 * h + 4 * q + (lane >> 4), d.rows - 1) - r0;
-                    U.wq[q][t][h] = (uint32_t)(row * half) + 16 * (lane & 15);
-                }
+                    for (int h = 0; h < 2; ++h) {
+                        const int64_t row = min(r0 + 16 * t + 8 * h + 4 * q + (lane >> 4), d.rows - 1) - r0;
+                        U.wq[q][t][h] = (uint32_t)(row * half) + 16 * (lane & 15);
+                    }
+        }
     }
     if constexpr (ONE) {
         const int pc = n >> 1;
@@ -428,14 +442,18 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // the last step (uniformly); the weight and scale resources of a step past
 // the end read what ExUnit describes.
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_issue_weights(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int win,
+__device__ __forceinline__ void ex_issue_weights(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnitT<FMT, R, O, ONE>& U, int win,
                                                  int q) {
     if constexpr (ex_xl(FMT, WIN, ONE)) {  // 4 rows x 256 bytes per load (see ExXchg)
         const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 256 * win, U.w_left - 256 * win);
 #pragma unroll
         for (int t = 0; t < R; ++t)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) b.b[q][t][h] = buf_load16(wr, U.wq[q][t][h], 0, true);
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t off = FMT == kNV && !ONE ? U.wlane + (uint32_t)((16 * t + 8 * h + 4 * q) * U.half)
+                                                        : U.wq[q][t][h];
+                b.b[q][t][h] = buf_load16(wr, off, 0, true);
+            }
     } else {
         const int sp = win * WIN + 2 * q;  // first step of the phase
         const __amdgpu_buffer_rsrc_t wr = ex_rsrc(U.w + 64 * sp, U.w_left - 64 * sp);
@@ -449,7 +467,7 @@ __device__ __forceinline__ void ex_issue_weights(ExWin<FMT, R, O, WIN, ONE>& b, 
 // The rest of a phase's loads: block and activation scales (phase 0) and
 // activation codes.
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_issue_rest(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+__device__ __forceinline__ void ex_issue_rest(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnitT<FMT, R, O, ONE>& U, int steps,
                                               int win, int q) {
     const int s0 = win * WIN;
     const int sp = s0 + 2 * q;  // first step of the phase
@@ -492,14 +510,14 @@ __device__ __forceinline__ void ex_issue_rest(ExWin<FMT, R, O, WIN, ONE>& b, con
 }
 
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+__device__ __forceinline__ void ex_issue_phase(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnitT<FMT, R, O, ONE>& U, int steps,
                                                int win, int q) {
     ex_issue_weights(b, U, win, q);
     ex_issue_rest(b, U, steps, win, q);
 }
 
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnit<R, O, ONE>& U, int steps,
+__device__ __forceinline__ void ex_issue(ExWin<FMT, R, O, WIN, ONE>& b, const ExUnitT<FMT, R, O, ONE>& U, int steps,
                                          int win) {
 #pragma unroll
     for (int q = 0; q < WIN / 2; ++q) ex_issue_phase(b, U, steps, win, q);
@@ -911,7 +929,7 @@ __device__ __forceinline__ void ex_flush(int lane, int M, const ExOut& o) {
 // then, at the end of cur's unit, its outputs; after the wave's last window
 // (`last`), what LDS holds. `un` addresses the windows of `set`.
 template <int FMT, int R, int O, int WIN, bool ONE>
-__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnit<R, O, ONE>& un,
+__device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnitT<FMT, R, O, ONE>& un,
                                          ExWin<FMT, R, O, WIN, ONE>& set, int lane, const ExXchg& X, v4f* acc,
                                          ExOut& out) {
     constexpr int NACC = R * O;
@@ -968,7 +986,7 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
                                                                 ExLin one) {
     constexpr int NACC = R * O;
     using Win = ExWin<FMT, R, O, WIN, ONE>;
-    using Unit = ExUnit<R, O, ONE>;
+    using Unit = ExUnitT<FMT, R, O, ONE>;
     extern __shared__ __attribute__((aligned(16))) float ex_lds[];
     const int lane = threadIdx.x % kLanes;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
