@@ -215,12 +215,15 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 // stored); the instruction accumulates every block of every step into the
 // tile's f32 accumulator.
 // NVFP4: the e4m3 block scale of 16 columns cannot be folded into a bf16
-// operand exactly in one conversion, so A row s of token group o is token
-// 8o + s/2 restricted to 16-column block s % 2 of the instruction's 32
-// columns (zeros elsewhere): result element (s, n) is that block's sum for
-// weight row n. Each lane multiplies its results by their e4m3 scales in f32
-// (fused multiply-add) into one accumulator per (token, block parity); a
-// token's two accumulators are added at the end of the unit.
+// operand exactly in one conversion, so a row of A is a token restricted to
+// one 16-column block of the instruction's 32 columns (zeros elsewhere):
+// result element (row, n) is that block's sum for weight row n. Each lane
+// multiplies its results by their e4m3 scales in f32 (fused multiply-add)
+// into four accumulators per token, added at the end of the unit (the order
+// is stated at ex_compute_phase). Panels: A row s of token group o is token
+// 8o + s/2, block parity s % 2, one instruction per 32-column chunk. One
+// token: the four chunks of a step share one accumulator chain, each chunk
+// in rows of its own (ex_nv_one_phase).
 //
 // A unit is R tiles of 16 weight rows of one linear across all its columns,
 // 128 columns (a step) at a time, WIN steps per pipeline window. Units are
@@ -239,10 +242,11 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 // and exchanged likewise (permlane32, permlane16). Each lane group loads the
 // block scales (and the activation scale) of a different step of the window
 // and the exchanges hand every lane those of all the window's steps.
-// One activation row (template flag ONE, the decode case) reads the weights
-// differently: 4 rows x 256 bytes per load, through LDS (weights_to_lds), and
-// the activation as one 8-byte piece per lane and step pair, handed to the
-// token's rows by row shifts. Same operands, instructions and order.
+// One activation row (template flag ONE, the decode case) reads the
+// activation as one 8-byte piece per lane and step pair, handed to the
+// token's rows by row shifts. Kernels with 4-step windows read the weights
+// as 4 rows x 256 bytes per load, through LDS (weights_to_lds). Every
+// variant computes the same bits for a token.
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -269,6 +273,9 @@ constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
 // those with windows of 4 steps (all but NVFP4 panels of more than 8 rows,
 // whose windows are 2 steps).
 constexpr bool ex_xl(int, int win, bool) { return win == 4; }
+// f32 accumulators (v4f) of a wave: one per tile and token group; NVFP4
+// panels two (chunks k of even and of odd index, ex_compute_phase).
+constexpr int ex_nacc(int fmt, int R, int O, bool one) { return R * O * (fmt == kNV && !one ? 2 : 1); }
 
 // A unit's loads go through buffer resources: a resource in scalar
 // registers (base, byte count) plus a 32-bit per-lane offset that is fixed for
@@ -292,9 +299,10 @@ struct ExUnit {
     uint32_t soff[R];    // lane: offset of the block scales of its row n of tile t + its lane group's step
     uint32_t xoff[O];    // lane: its token's codes + its 32-column block (kPastEnd: a row past M)
     uint32_t xsoff[O];   // lane: its token's row of activation scales + its lane group's step (likewise)
-    // ONE (a single token): one 8-byte load per step pair; lane (n, g) reads
-    // the 8 codes of piece p = n / 2 (step p / 4 of the pair, columns
-    // 32 (p % 4) + 8g .. +7); xhi selects the lanes of the pair's second step.
+    // ONE (a single token): one 8-byte load per step pair. MXFP4: lane
+    // (n, g) reads the 8 codes of piece p = n / 2 (step p / 4 of the pair,
+    // columns 32 (p % 4) + 8g .. +7); NVFP4: see ex_nv_one_phase. xhi
+    // selects the lanes of the pair's second step.
     uint32_t xoff1, xhi;
     // ex_xl kernels: weight load (q, t, h) reads rows 16t + 8h + 4q .. +3 of
     // the unit, 256 bytes (the window's 4 steps) each; lane l: row l / 16,
@@ -398,10 +406,19 @@ __device__ __forceinline__ void ex_unit(ExUnitT<FMT, R, O, ONE>& U, const ExLin&
                     }
         }
     }
-    if constexpr (ONE) {
+    if constexpr (ONE && FMT == kMX) {
         const int pc = n >> 1;
         U.xoff1 = (uint32_t)(32 * (pc & 3) + 8 * g);
         U.xhi = pc >= 4 ? ~0u : 0u;
+    } else if constexpr (ONE) {
+        // lane n of groups 0, 1 (n of groups 2, 3 less 8), n < 8: chunk
+        // k = (0, 2, 1, 3)[n / 2] of step n % 2 of the pair; the other lanes
+        // read nothing
+        const bool mine = (g >> 1) == (n >> 3);
+        const int i = n & 7, kc = (i >> 1) == 1 ? 2 : (i >> 1) == 2 ? 1 : i >> 1;
+        U.xoff1 = mine ? (uint32_t)(32 * kc + 8 * g) : kPastEnd;
+        U.xhi = mine && (i & 1) ? ~0u : 0u;
+        U.xsoff[0] = (uint32_t)(g % WIN);  // every row of A carries the token
     }
 }
 
@@ -639,9 +656,15 @@ __device__ __forceinline__ void ex_gather(const ExWin<FMT, R, O, WIN, ONE>& b, E
 }
 
 // The matrix work of phase q (steps 2q, 2q + 1) of a window.
-// MXFP4: acc[t] holds token rows x weight rows of tile t. NVFP4: acc[t * O + o]
-// register e holds, for weight row l % 16, the accumulator of token
-// 8o + 2(l/16) + e/2 over the 16-column blocks of parity e % 2.
+// MXFP4: acc[t] holds token rows x weight rows of tile t.
+// NVFP4 accumulation order (every kernel, so every panel height gives the
+// same bits): each token has four f32 accumulators B(p, j), p the parity of a
+// 16-column block within its 32-column chunk k, j = k % 2. Step by step, and
+// within a step chunk j, then chunk j + 2, B(p, j) += s * c with c the
+// chunk's block sum (one matrix instruction's row) and s its e4m3 scale
+// (fused multiply-add). The output is g ((B(0,0) + B(0,1)) + (B(1,0) + B(1,1))).
+// Panels: acc[(t O + o) 2 + j] register e holds, for weight row l % 16,
+// B(e % 2, j) of token 8o + 2(l/16) + e/2.
 // Lane n + M of each row of 16 lanes into lane n (lanes past the row's end
 // read 0): the piece loaded by lane 2p reaches lanes 0 and 1 with M = 2p.
 template <int M>
@@ -711,6 +734,57 @@ __device__ __forceinline__ void weights_from_lds(const ExXchg& X, int q, int t, 
     }
 }
 
+// NVFP4, one token: the four matrix instructions of a step (chunks k) go
+// into one accumulator chain, each filling its own rows: row
+// 8p + 4(k % 2) + k / 2 of A holds the token restricted to block parity p of
+// chunk k (lane groups 2p, 2p + 1), every other row is zero. Result element e
+// of lane group h is then the block sum of chunk 2e + h % 2, parity h / 2, so
+// lane group h multiplies its two elements by their scales into
+// B(h / 2, h % 2), chunk h % 2 first (acc[t] element 0). The activation load
+// puts chunk k of step s2 in lane i = 2 idx(k) + s2, idx = (0, 2, 1, 3)[k], of
+// groups 0, 1 (lane i + 8 of groups 2, 3), where a row shift by i minus the
+// row above takes it.
+template <int R, int O, int WIN>
+__device__ __forceinline__ void ex_nv_one_phase(const uint2 a0, const uint32_t (&wop)[R][2][4],
+                                                const ExScales<R, O, WIN>& S, int steps, int win, int q, int lane,
+                                                v4f* acc) {
+    const int n = lane & 15, g = lane >> 4;
+    const uint32_t b = (uint32_t)(2 * (g & 1) + (g >> 1));  // block of element 0 (element 1: 4 + b)
+    const uint32_t sel = b | ((4u + b) << 8) | 0x0C0C0000u;  // bytes b of ws, then of ws_hi
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * q + s2;
+        if (win * WIN + s >= steps) continue;  // past the row's end: adds nothing (wave-uniform)
+        uint2 ap[4];
+        if (s2 == 0) {
+            ap[0] = row_shift<0>(a0);
+            ap[2] = row_shift<1>(a0);
+        } else {
+            ap[0] = row_shift<1>(a0);
+            ap[2] = row_shift<2>(a0);
+        }
+        ap[1] = ap[0];
+        ap[3] = ap[2];
+        const float sa = e8m0_cvt_scale<0>(S.as[0][s]);
+        v8bf A[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool row = n == 8 * (g >> 1) + 4 * (k & 1) + (k >> 1);
+            A[k] = fp8x8_operand(row ? ap[k] : make_uint2(0, 0), sa);
+        }
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k], fp4x8_operand(wop[t][s2][k], 1.0f), c, 0, 0, 0);
+            const v2f sc = e4m3_pair<false>(__builtin_amdgcn_perm(S.ws_hi[t][s], S.ws[t][s], sel));
+            acc[t][0] = __builtin_fmaf(sc.x, c[0], acc[t][0]);
+            acc[t][0] = __builtin_fmaf(sc.y, c[1], acc[t][0]);
+        }
+    }
+}
+
 template <int FMT, int R, int O, int WIN, bool ONE>
 __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE>& b, const ExScales<R, O, WIN>& S,
                                                  int steps, int win, int q, int lane, const ExXchg& X, v4f* acc) {
@@ -723,71 +797,73 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
         else
             weights_to_operands(b.b[q][t], wop[t]);
     }
+    if constexpr (FMT == kNV && ONE) {
+        ex_nv_one_phase<R, O, WIN>(b.a[q][0][0], wop, S, steps, win, q, lane, acc);
+    } else {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        const int s = 2 * q + s2;
-        const bool live = win * WIN + s < steps;  // wave-uniform
-        // MXFP4: a step past the row's end (in a last, partial window) adds
-        // nothing; a wave-uniform branch skips it.
-        if (FMT == kMX && !live) continue;
-        v8bf A[4][O];
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * q + s2;
+            const bool live = win * WIN + s < steps;  // wave-uniform
+            // MXFP4: a step past the row's end (in a last, partial window) adds
+            // nothing; a wave-uniform branch skips it.
+            if (FMT == kMX && !live) continue;
+            v8bf A[4][O];
 #pragma unroll
-        for (int o = 0; o < O; ++o) {
-            uint2 ap[4];
-            if constexpr (ONE) {
-                // the token's rows (MXFP4: n = 0; NVFP4: n = 0, 1) take piece 4 s2 + k from lane 2(4 s2 + k)
-                const uint2 a0 = b.a[q][0][0];
-                if (s2 == 0) {
-                    ap[0] = row_shift<0>(a0);
-                    ap[1] = row_shift<2>(a0);
-                    ap[2] = row_shift<4>(a0);
-                    ap[3] = row_shift<6>(a0);
+            for (int o = 0; o < O; ++o) {
+                uint2 ap[4];
+                if constexpr (ONE) {
+                    // the token's row n = 0 takes piece 4 s2 + k from lane 2(4 s2 + k)
+                    const uint2 a0 = b.a[q][0][0];
+                    if (s2 == 0) {
+                        ap[0] = row_shift<0>(a0);
+                        ap[1] = row_shift<2>(a0);
+                        ap[2] = row_shift<4>(a0);
+                        ap[3] = row_shift<6>(a0);
+                    } else {
+                        ap[0] = row_shift<8>(a0);
+                        ap[1] = row_shift<10>(a0);
+                        ap[2] = row_shift<12>(a0);
+                        ap[3] = row_shift<14>(a0);
+                    }
                 } else {
-                    ap[0] = row_shift<8>(a0);
-                    ap[1] = row_shift<10>(a0);
-                    ap[2] = row_shift<12>(a0);
-                    ap[3] = row_shift<14>(a0);
+                    act_to_operands(b.a[s][o], ap);
                 }
-            } else {
-                act_to_operands(b.a[s][o], ap);
+                const float sa = e8m0_cvt_scale<0>(S.as[o][s]);
+                if constexpr (FMT == kMX) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(ap[k], sa);
+                } else {
+                    // selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
+                    // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
+                    const bool keep = live && (g >> 1) == (lane & 1);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
+                }
             }
-            const float sa = e8m0_cvt_scale<0>(S.as[o][s]);
-            if constexpr (FMT == kMX) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(ap[k], sa);
-            } else {
-                // selector row s_ = lane % 16 keeps 16-column block s_ % 2 of
-                // each instruction, held by lane groups 2(s_ % 2) and 2(s_ % 2) + 1
-                const bool keep = live && (g >> 1) == (lane & 1);
+            for (int t = 0; t < R; ++t) {
+                if constexpr (FMT == kMX) {
+                    const uint32_t ws = S.ws[t][s];
+                    const float sw[4] = {e8m0_cvt_scale<0>(ws), e8m0_cvt_scale<1>(ws), e8m0_cvt_scale<2>(ws),
+                                         e8m0_cvt_scale<3>(ws)};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) A[k][o] = fp8x8_operand(keep ? ap[k] : make_uint2(0, 0), sa);
-            }
-        }
+                    for (int k = 0; k < 4; ++k)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            A[k][0], fp4x8_operand(wop[t][s2][k], sw[k]), acc[t], 0, 0, 0);
+                } else {
+                    // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + parity
+                    const v2f sc[4] = {e4m3_pair<false>(S.ws[t][s]), e4m3_pair<true>(S.ws[t][s]),
+                                       e4m3_pair<false>(S.ws_hi[t][s]), e4m3_pair<true>(S.ws_hi[t][s])};
 #pragma unroll
-        for (int t = 0; t < R; ++t) {
-            if constexpr (FMT == kMX) {
-                const uint32_t ws = S.ws[t][s];
-                const float sw[4] = {e8m0_cvt_scale<0>(ws), e8m0_cvt_scale<1>(ws), e8m0_cvt_scale<2>(ws),
-                                     e8m0_cvt_scale<3>(ws)};
+                    for (int k = 0; k < 4; ++k) {
+                        const v8bf B = fp4x8_operand(wop[t][s2][k], 1.0f);
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][0], fp4x8_operand(wop[t][s2][k], sw[k]),
-                                                                     acc[t], 0, 0, 0);
-            } else {
-                // e4m3 scales of the step's 8 blocks of 16 columns: block 2k + parity
-                const v2f sc[4] = {e4m3_pair<false>(S.ws[t][s]), e4m3_pair<true>(S.ws[t][s]),
-                                   e4m3_pair<false>(S.ws_hi[t][s]), e4m3_pair<true>(S.ws_hi[t][s])};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const v8bf B = fp4x8_operand(wop[t][s2][k], 1.0f);
-#pragma unroll
-                    for (int o = 0; o < O; ++o) {
-                        const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[k][o], B, v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                              0, 0, 0);
-                        v4f& a = acc[t * O + o];
-                        a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
-                        a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
-                        if constexpr (!ONE) {  // elements 2, 3: token 8o + 2(l / 16) + 1, past a single token
+                        for (int o = 0; o < O; ++o) {
+                            const v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                A[k][o], B, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                            v4f& a = acc[(t * O + o) * 2 + (k & 1)];
+                            a[0] = __builtin_fmaf(sc[k].x, c[0], a[0]);
+                            a[1] = __builtin_fmaf(sc[k].y, c[1], a[1]);
                             a[2] = __builtin_fmaf(sc[k].x, c[2], a[2]);
                             a[3] = __builtin_fmaf(sc[k].y, c[3], a[3]);
                         }
@@ -800,9 +876,11 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
 
 // The unit's outputs y = g * accumulator, handed one by one to put(token,
 // row within the unit, value). MXFP4: lane (n, g) holds tokens 4g .. 4g+3 of
-// weight row n. NVFP4: lane (n, g) holds tokens 8o + 2g and 8o + 2g + 1, each
-// as two block-parity accumulators, added here.
-template <int FMT, int R, int O, typename Put>
+// weight row n. NVFP4 (the order of ex_compute_phase): panels, lane (n, g)
+// holds tokens 8o + 2g and 8o + 2g + 1, each as four accumulators; one
+// token, lane group h holds B(h / 2, h % 2) and the groups are added across
+// lanes (every lane ends with the same sum).
+template <int FMT, int R, int O, bool ONE, typename Put>
 __device__ __forceinline__ void ex_outputs(const ExLin& d, int lane, const v4f* acc, Put put) {
     const int n = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -814,24 +892,31 @@ __device__ __forceinline__ void ex_outputs(const ExLin& d, int lane, const v4f* 
                 const int tok = 4 * g + e;
                 if (tok < d.M) put(tok, r, d.g * acc[t][e]);
             }
+        } else if constexpr (ONE) {
+            float v = acc[t][0];
+            v += __shfl_xor(v, 16);  // B(p, 0) + B(p, 1)
+            v += __shfl_xor(v, 32);
+            if (g == 0) put(0, r, d.g * v);
         } else {
 #pragma unroll
             for (int o = 0; o < O; ++o) {
-                const v4f& a = acc[t * O + o];
+                const v4f& a0 = acc[(t * O + o) * 2];
+                const v4f& a1 = acc[(t * O + o) * 2 + 1];
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int tok = 8 * o + 2 * g + k;
-                    if (tok < d.M) put(tok, r, d.g * (a[2 * k] + a[2 * k + 1]));
+                for (int j = 0; j < 2; ++j) {
+                    const int tok = 8 * o + 2 * g + j;
+                    const float v = (a0[2 * j] + a1[2 * j]) + (a0[2 * j + 1] + a1[2 * j + 1]);
+                    if (tok < d.M) put(tok, r, d.g * v);
                 }
             }
         }
     }
 }
 
-template <int FMT, int R, int O>
+template <int FMT, int R, int O, bool ONE>
 __device__ __forceinline__ void ex_store(const ExLin& d, int64_t v, int lane, const v4f* acc) {
     const int64_t r0 = v * (R * kTileRows);
-    ex_outputs<FMT, R, O>(d, lane, acc, [&](int tok, int r, float val) {
+    ex_outputs<FMT, R, O, ONE>(d, lane, acc, [&](int tok, int r, float val) {
         if (r0 + r < d.rows) store_global_f32(d.y + (int64_t)tok * d.rows + r0 + r, val);
     });
 }
@@ -866,7 +951,7 @@ struct ExOut {
     uint32_t y_lo, y_hi, rows_lo, rows_hi, left_vec;  // lane k: record of held unit k
 };
 
-template <int FMT, int R, int O>
+template <int FMT, int R, int O, bool ONE>
 __device__ __forceinline__ void ex_retire(const ExLin& d, int64_t v, int lane, const v4f* acc, ExOut& o) {
     if (o.k < o.slots) {
         const int64_t r0 = v * (R * kTileRows);
@@ -880,9 +965,10 @@ __device__ __forceinline__ void ex_retire(const ExLin& d, int64_t v, int lane, c
         o.rows_hi = mine ? (uint32_t)((uint64_t)d.rows >> 32) : o.rows_hi;
         o.left_vec = mine ? lv : o.left_vec;
         float* slot = o.lds + o.k * d.M * kExUnitRows;
-        ex_outputs<FMT, R, O>(d, lane, acc, [&](int tok, int r, float val) { slot[tok * kExUnitRows + r] = val; });
+        ex_outputs<FMT, R, O, ONE>(d, lane, acc,
+                                   [&](int tok, int r, float val) { slot[tok * kExUnitRows + r] = val; });
     } else {
-        ex_store<FMT, R, O>(d, v, lane, acc);
+        ex_store<FMT, R, O, ONE>(d, v, lane, acc);
     }
     ++o.k;
 }
@@ -932,7 +1018,7 @@ template <int FMT, int R, int O, int WIN, bool ONE>
 __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, bool last, ExUnitT<FMT, R, O, ONE>& un,
                                          ExWin<FMT, R, O, WIN, ONE>& set, int lane, const ExXchg& X, v4f* acc,
                                          ExOut& out) {
-    constexpr int NACC = R * O;
+    constexpr int NACC = ex_nacc(FMT, R, O, ONE);
     ExScales<R, O, WIN> S;
     ex_gather(set, S);
     if (nxt.win == 0 && nxt.more) ex_unit<FMT, R, O, WIN, ONE>(un, nxt.d, nxt.v, lane);
@@ -970,7 +1056,7 @@ __device__ __forceinline__ void ex_stage(const ExPos& cur, const ExPos& nxt, boo
     }
     __builtin_amdgcn_sched_barrier(0);
     if (cur.win + 1 == ex_nwin<WIN>(cur.d)) {
-        ex_retire<FMT, R, O>(cur.d, cur.v, lane, acc, out);
+        ex_retire<FMT, R, O, ONE>(cur.d, cur.v, lane, acc, out);
 #pragma unroll
         for (int k = 0; k < NACC; ++k) acc[k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         if (last) ex_flush(lane, cur.d.M, out);
@@ -984,7 +1070,7 @@ template <int FMT, int R, int O, int WIN, bool LIST, bool ONE>
 __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __restrict__ lin,
                                                                 const int64_t* __restrict__ pre, int64_t total,
                                                                 ExLin one) {
-    constexpr int NACC = R * O;
+    constexpr int NACC = ex_nacc(FMT, R, O, ONE);
     using Win = ExWin<FMT, R, O, WIN, ONE>;
     using Unit = ExUnitT<FMT, R, O, ONE>;
     extern __shared__ __attribute__((aligned(16))) float ex_lds[];
