@@ -242,11 +242,13 @@ __global__ __launch_bounds__(256) void k_fp4_dequant(const uint8_t* __restrict__
 // and exchanged likewise (permlane32, permlane16). Each lane group loads the
 // block scales (and the activation scale) of a different step of the window
 // and the exchanges hand every lane those of all the window's steps.
-// One activation row (template flag ONE, the decode case) reads the
+// Kernels with 4-step windows read the weights as 4 rows x 256 bytes per
+// load, through LDS (weights_to_lds); the MXFP4 panels among them read the
+// activation codes as whole lines too and hand them over through LDS
+// (ex_xa). One activation row (template flag ONE, the decode case) reads the
 // activation as one 8-byte piece per lane and step pair, handed to the
-// token's rows by row shifts. Kernels with 4-step windows read the weights
-// as 4 rows x 256 bytes per load, through LDS (weights_to_lds). Every
-// variant computes the same bits for a token.
+// token's rows by row shifts. Every variant computes the same bits for a
+// token.
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -273,6 +275,11 @@ constexpr int ex_win(int, int O) { return O == 1 ? 4 : 2; }
 // those with windows of 4 steps (all but NVFP4 panels of more than 8 rows,
 // whose windows are 2 steps).
 constexpr bool ex_xl(int, int win, bool) { return win == 4; }
+// MXFP4 panels of those kernels read the activation codes as whole 128-byte
+// lines (8 lanes per token and step, two loads of 8 tokens) and hand them
+// over through LDS too (ExXchg). NVFP4 panels keep their exchanges: the extra
+// operand registers would cost them their second wave per SIMD.
+constexpr bool ex_xa(int fmt, int win, bool one) { return fmt == kMX && ex_xl(fmt, win, one) && !one; }
 // f32 accumulators (v4f) of a wave: one per tile and token group; NVFP4
 // panels two (chunks k of even and of odd index, ex_compute_phase).
 constexpr int ex_nacc(int fmt, int R, int O, bool one) { return R * O * (fmt == kNV && !one ? 2 : 1); }
@@ -304,6 +311,10 @@ struct ExUnit {
     // columns 32 (p % 4) + 8g .. +7); NVFP4: see ex_nv_one_phase. xhi
     // selects the lanes of the pair's second step.
     uint32_t xoff1, xhi;
+    // ex_xa kernels: lane l of load i reads token 8i + l / 8, bytes
+    // 16 (l % 8) .. +15 of each step (kPastEnd: a token >= M, so that load 1
+    // reads nothing below 9 tokens)
+    uint32_t xline[ONE || WL ? 0 : 2];
     // ex_xl kernels: weight load (q, t, h) reads rows 16t + 8h + 4q .. +3 of
     // the unit, 256 bytes (the window's 4 steps) each; lane l: row l / 16,
     // bytes 16 (l % 16) .. +15, at offset wq[q][t][h] (rows past the end
@@ -404,6 +415,13 @@ __device__ __forceinline__ void ex_unit(ExUnitT<FMT, R, O, ONE>& U, const ExLin&
                         const int64_t row = min(r0 + 16 * t + 8 * h + 4 * q + (lane >> 4), d.rows - 1) - r0;
                         U.wq[q][t][h] = (uint32_t)(row * half) + 16 * (lane & 15);
                     }
+        }
+    }
+    if constexpr (ex_xa(FMT, WIN, ONE)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tok = 8 * i + (lane >> 3);
+            U.xline[i] = tok < d.M ? (uint32_t)(tok * d.K + 16 * (lane & 7)) : kPastEnd;
         }
     }
     if constexpr (ONE && FMT == kMX) {
@@ -508,6 +526,13 @@ __device__ __forceinline__ void ex_issue_rest(ExWin<FMT, R, O, WIN, ONE>& b, con
         const uint32_t d1 = (uint32_t)(min(sp + 1, steps - 1) - j0) * kStepCols;  // 0 or one step, uniform
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(xr, (int)(U.xoff1 + (U.xhi & d1)), kStepCols * j0, 0);
         b.a[q][0][0] = make_uint2(v[0], v[1]);
+    } else if constexpr (ex_xa(FMT, WIN, ONE)) {
+#pragma unroll
+        for (int s = 2 * q; s < 2 * q + 2; ++s) {
+            const int j = min(s0 + s, steps - 1);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) b.a[s][0][i] = buf_load16(xr, U.xline[i], kStepCols * j, false);
+        }
     } else {
 #pragma unroll
         for (int s = 2 * q; s < 2 * q + 2; ++s) {
@@ -695,20 +720,56 @@ __host__ __device__ constexpr int ex_blk(int s, int t) { return (2 * s + t) * kE
 constexpr int kExXchgDw = ex_blk(3, 1) + kExBlkDw;
 static_assert(kExXchgDw * 4 <= kExWaveLdsBytes, "the exchange region fits a wave's LDS part");
 
+// Activation region (ex_xa kernels), after the weights: the two steps of a
+// phase, [step][token (row stride kExActRowDw)][128 bytes], 8 tokens per load
+// that carries any; the 4-dword row padding spreads a step's 8-byte operand
+// reads over the banks.
+constexpr int kExActRowDw = 36;
+__host__ __device__ constexpr int ex_act_step_dw(int M) { return (M > 8 ? 16 : 8) * kExActRowDw; }
+static_assert((kExXchgDw + 2 * ex_act_step_dw(16)) * 4 <= kExWaveLdsBytes, "both regions fit a wave's LDS part");
+
 struct ExXchg {
     uint32_t* lds;  // the workgroup's LDS
     uint32_t w;     // lane l of a load: its 16 bytes (row l / 16, step (l % 16) / 4, block l % 4), in dwords
     uint32_t r;     // lane (n, g): its reads (row n, group g), in dwords
+    uint32_t a;     // the activation region
+    uint32_t astep; // its step stride, in dwords
+    int32_t an;     // loads per step that carry tokens (1 or 2)
 };
 
-__device__ __forceinline__ ExXchg ex_xchg(float* lds, int wave, int lane) {
+__device__ __forceinline__ ExXchg ex_xchg(float* lds, int wave, int lane, int M) {
     const uint32_t base = (uint32_t)wave * (kExWaveLdsBytes / 4);
     const int st = (lane & 15) >> 2;
     ExXchg x;
     x.lds = reinterpret_cast<uint32_t*>(lds);
     x.w = base + (uint32_t)(ex_blk(st, 0) + (lane >> 4) * kExRowDw + (lane & 3));
     x.r = base + (uint32_t)((lane & 15) * kExRowDw + 4 * (lane >> 4));
+    x.a = base + (uint32_t)kExXchgDw;
+    x.astep = (uint32_t)ex_act_step_dw(M);
+    x.an = M > 8 ? 2 : 1;
     return x;
+}
+
+// The activation lines of phase q (steps 2q, 2q + 1) into the region: lane l
+// of load i writes its 16 bytes at token 8i + l / 8, bytes 16 (l % 8) ...
+template <int FMT, int R, int O, int WIN, bool ONE>
+__device__ __forceinline__ void act_to_lds(const ExWin<FMT, R, O, WIN, ONE>& b, const ExXchg& X, int q, int lane) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (i >= X.an) break;
+            uint32_t* w = X.lds + X.a + s2 * X.astep + (8 * i + (lane >> 3)) * kExActRowDw + 4 * (lane & 7);
+            *reinterpret_cast<uint4*>(w) = b.a[2 * q + s2][0][i];
+        }
+}
+
+// ... and back as the operands of step 2q + s2 for token tok: piece k holds
+// its columns 32k + 8g .. +7 (g = l / 16), as act_to_operands makes them.
+__device__ __forceinline__ void act_from_lds(const ExXchg& X, int s2, int tok, int lane, uint2 (&op)[4]) {
+    const uint32_t* r = X.lds + X.a + s2 * X.astep + tok * kExActRowDw + 2 * (lane >> 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) op[k] = *reinterpret_cast<const uint2*>(r + 8 * k);
 }
 
 // Load (q, t, h) of a window (rows 16t + 8h + 4q .. +3) into the region:
@@ -800,6 +861,7 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
     if constexpr (FMT == kNV && ONE) {
         ex_nv_one_phase<R, O, WIN>(b.a[q][0][0], wop, S, steps, win, q, lane, acc);
     } else {
+        if constexpr (ex_xa(FMT, WIN, ONE)) act_to_lds(b, X, q, lane);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int s = 2 * q + s2;
@@ -825,6 +887,8 @@ __device__ __forceinline__ void ex_compute_phase(const ExWin<FMT, R, O, WIN, ONE
                         ap[2] = row_shift<12>(a0);
                         ap[3] = row_shift<14>(a0);
                     }
+                } else if constexpr (ex_xa(FMT, WIN, ONE)) {
+                    act_from_lds(X, s2, lane & 15, lane, ap);
                 } else {
                     act_to_operands(b.a[s][o], ap);
                 }
@@ -1076,7 +1140,6 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
     extern __shared__ __attribute__((aligned(16))) float ex_lds[];
     const int lane = threadIdx.x % kLanes;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-    const ExXchg X = ex_xchg(ex_lds, wave, lane);  // used by the single-token kernels (no outputs held in LDS)
     const int64_t W = (int64_t)gridDim.x * kSeqWaves;
     ExPos p0;
     p0.u = (int64_t)xcd_contiguous_block() * kSeqWaves + wave;
@@ -1095,9 +1158,10 @@ __global__ __launch_bounds__(kSeqWaves * kLanes) void k_expert(const ExLin* __re
         p0.v = p0.u;
     }
     // Every linear of a list has the same M (the plan checks it).
+    const ExXchg X = ex_xchg(ex_lds, wave, lane, p0.d.M);
     ExOut out;
-    // the weight exchange takes the start of the wave's part
-    constexpr int xchg = ex_xl(FMT, WIN, ONE) ? kExXchgDw : 0;
+    // the weight exchange (and the activation region) take the start of the wave's part
+    const int xchg = (ex_xl(FMT, WIN, ONE) ? kExXchgDw : 0) + (ex_xa(FMT, WIN, ONE) ? 2 * (int)X.astep : 0);
     out.lds = ex_lds + wave * (kExWaveLds / 4) + xchg;
     const int slot_floats = p0.d.M * kExUnitRows;
     out.slots = p0.d.M >= kExHoldMinM ? min(kLanes, (kExWaveLds / 4 - xchg) / slot_floats) : 0;
