@@ -803,8 +803,9 @@ __device__ __forceinline__ void weights_from_lds(const ExXchg& X, int q, int t, 
 // lane group h multiplies its two elements by their scales into
 // B(h / 2, h % 2), chunk h % 2 first (acc[t] element 0). The activation load
 // puts chunk k of step s2 in lane i = 2 idx(k) + s2, idx = (0, 2, 1, 3)[k], of
-// groups 0, 1 (lane i + 8 of groups 2, 3), where a row shift by i minus the
-// row above takes it.
+// groups 0, 1 (lane i + 8 of groups 2, 3): a row shift by
+// i - (4(k % 2) + k / 2), which is s2 for k = 0, 1 and s2 + 1 for k = 2, 3,
+// brings it to chunk k's row in both halves of the lane groups.
 template <int R, int O, int WIN>
 __device__ __forceinline__ void ex_nv_one_phase(const uint2 a0, const uint32_t (&wop)[R][2][4],
                                                 const ExScales<R, O, WIN>& S, int steps, int win, int q, int lane,
