@@ -111,8 +111,9 @@ def test_mfma_sequence_integer_exact(gpu):
 
 def test_mfma_sequence_whole_step_sweep(gpu):
     """The 259 linears of the whole-step sweep with a 16-row verify panel in one
-    matrix-core sequence: 128-row windows of several linears against the
-    oracle, and the FP8 arm against the twin on the first layer and the head."""
+    matrix-core sequence: every output of every linear against the oracle's
+    double GEMV (1e-5 * sum|w x|), and the FP8 arm against the twin on the
+    first layer and the head."""
     from gpu_util import DEV, DevLinear, assert_within_tolerance, say, u32
     sw = inputs.sweep_plan()
     xs = {c: inputs.device_x(c, 16, 7 + c, DEV) for c in {l.cols for l in sw.linears}}
@@ -135,15 +136,13 @@ def test_mfma_sequence_whole_step_sweep(gpu):
     torch.cuda.synchronize()
     for i in twin_idx:
         assert torch.equal(ys[i].view(torch.int32), yt[i].view(torch.int32)), lins[i][0].name
-    for i in twin_idx + [100, 200]:
-        spec, D = lins[i]
-        r0 = 128 * (spec.rows // 256)
-        ch = D.codes[r0:r0 + 128].cpu().numpy()
-        sh = D.scales[r0 // 128:r0 // 128 + 1].cpu().numpy()
+    for i, (spec, D) in enumerate(lins):
+        ch, sh = D.codes.cpu().numpy(), D.scales.cpu().numpy()
         xh = D.x.cpu().numpy().view(np.uint16)
-        yw = ys[i][:, r0:r0 + 128].cpu().numpy()
         y64, yabs = oracle.gemv_f64(ch, sh, xh, nthreads=NTHREADS)
-        assert_within_tolerance(yw, y64, yabs, what=f"{spec.name} rows {r0}.. M=16")
+        assert_within_tolerance(ys[i].cpu().numpy(), y64, yabs, what=f"{spec.name} M=16")
+        if i % 43 == 0 or spec.name == "head":
+            say(f"  sweep linear {i} {spec.name}: every output within tolerance")
     assert all(not torch.isnan(y).any() for y in ys)
     say(f"  {len(lins)} sweep linears at M=16 checked")
     # The decode / verify pairing of this arm ("Struct Dsv4Gpu" page,
