@@ -147,6 +147,30 @@ __device__ __forceinline__ int value_in_row(int row) { return row == 1 ? 2 : row
 // in every segment, so the running sums over segments are plain register adds,
 // and the lanes of a row store their own results. With sw > 1 each segment's
 // sums go to LDS and the first wave of the row stream adds them in order.
+// The fused multiply-add chains of one segment of the panel kernel: for each
+// activation row m (rows >= M repeat row M - 1) and weight row i, the lane's
+// 16 columns in increasing order from +0.0, into v[i * MT + m]; MASK: +0.0
+// where the lane is not live.
+template <bool MASK, int MT, int R>
+__device__ __forceinline__ void panel_tokens(const GemvArgs& a, const float (&w)[R][kChunk], int qc, bool live,
+                                             float* v) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int64_t xrow = min(m, a.M - 1);
+        const uint4* xp = reinterpret_cast<const uint4*>(a.x + xrow * a.K + (int64_t)qc * kChunk);
+        float xf[kChunk];
+        widen8_bf16(xp[0], xf);
+        widen8_bf16(xp[1], xf + 8);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[i][j], xf[j], s);
+            v[i * MT + m] = MASK && !live ? 0.0f : s;
+        }
+    }
+}
+
 template <int KIND, int MT, int R>
 __device__ __forceinline__ void panel_body(const GemvArgs& a, int64_t block) {
     constexpr int V = R * MT;
@@ -181,23 +205,16 @@ __device__ __forceinline__ void panel_body(const GemvArgs& a, int64_t block) {
         for (int i = 0; i < R; ++i) F::weights(raw[i][0], w[i], a.whole != 0);
         float v[VP];
 #pragma unroll
-        for (int k = 0; k < VP; ++k) v[k] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < a.M) {
-                const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)m * a.K + (int64_t)qc * kChunk);
-                float xf[kChunk];
-                widen8_bf16(xp[0], xf);
-                widen8_bf16(xp[1], xf + 8);
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    float s = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[i][j], xf[j], s);
-                    v[i * MT + m] = live ? s : 0.0f;
-                }
-            }
-        }
+        for (int k = V; k < VP; ++k) v[k] = 0.0f;
+        // Every activation row of the tile runs, rows >= M on a copy of row
+        // M - 1 (their outputs are never stored), so the x loads carry no
+        // branch and the compiler issues them ahead of the arithmetic. Lanes
+        // past the last column contribute +0.0; only a ragged last segment
+        // has any (wave-uniform test).
+        if ((t + 1) * kLanes - 1 <= last_q)
+            panel_tokens<false, MT, R>(a, w, qc, true, v);
+        else
+            panel_tokens<true, MT, R>(a, w, qc, live, v);
         float red[G];
         tree64xV<VP>(v, red);
         if (a.sw_log2 == 0) {
