@@ -485,15 +485,18 @@ int fp4_dequant_bf16(int fmt, const uint8_t *codes, const uint8_t *scales, int64
  * Every product is exact. Order: for each output, the 32-column blocks in
  * increasing order; MXFP4: each block's 32 products are summed by one matrix
  * instruction into the f32 accumulator; NVFP4: the instruction sums each
- * 16-column block, the sum times its e4m3 scale is added (one fused
- * multiply-add) into one of two f32 accumulators by block parity, and the
- * two are added at the end. Hence |y - exact| <= gamma_d * |g| * sum_c |q w|,
- * d = 33 + cols / 32 (gamma_d = d u / (1 - d u), u = 2^-24; below 1e-5 for
- * cols <= 4096), assuming the instruction's sum of 32 products is no worse
- * than 32 f32 additions (measured), while every product and partial sum is
- * in f32's normal range. The instruction may flush bf16 subnormal operands:
- * activation blocks with amax below about 2^-109 and MXFP4 scale codes below
- * 2 are outside the bound.
+ * 16-column block, and the sum times its e4m3 scale is added (one fused
+ * multiply-add) into one of four f32 accumulators B(p, j), p the block's
+ * parity inside its 32-column block k and j = k mod 2 (128 columns at a
+ * time, k = j before k = j + 2); the output is
+ * g * ((B(0,0) + B(0,1)) + (B(1,0) + B(1,1))). Hence
+ * |y - exact| <= gamma_d * |g| * sum_c |q w|, d = 33 + cols / 32
+ * (gamma_d = d u / (1 - d u), u = 2^-24; below 1e-5 for cols <= 4096),
+ * assuming the instruction's sum of 32 products is no worse than 32 f32
+ * additions (measured), while every partial sum stays in f32's range. The
+ * conversions and the matrix instruction keep bf16 subnormal operands and f32
+ * subnormal sums (tested at MXFP4 scale codes 0..6 and NVFP4's subnormal
+ * e4m3 scales).
  *   codes, xq: device, 16-byte aligned; scales: device, 4-byte (MXFP4) or
  *   8-byte (NVFP4) aligned; xs: device; y: device, 4-byte aligned.
  *   rows >= 1; 128 <= cols <= FP8BLK_MAX_COLS; cols % 128 == 0;
