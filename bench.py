@@ -968,7 +968,7 @@ def _config_blocks(rows_by_dispatch, manifest):
 
 def summarize_config_trace(trace_csv, manifest_path, command):
     """Markdown: per config block (linear, M, arm), the kernel, its grid and
-    the median / mean duration of the timed launches from a rocprofv3 kernel
+    the median, p10, p90 and mean duration of the timed launches from a rocprofv3 kernel
     trace of a --config-only run, with the weight GB/s the median gives."""
     import csv
     manifest = json.load(open(manifest_path))
@@ -980,18 +980,19 @@ def summarize_config_trace(trace_csv, manifest_path, command):
              "Timed launches: the graph replays (the eager warm-up pass and the first replay excluded). Weight "
              "bytes: codes + f32 grid (FP8 arms) or the bf16 slab (twins). vec = fp8blk_gemv, vec_twin = "
              "bf16_gemv_twin, mfma = fp8blk_gemv_mfma, mfma_twin = bf16_gemv_twin_mfma.", "",
-             "| linear | M | arm | kernel | grid (threads) | timed launches | median us | mean us | "
-             "weight GB/s (median) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+             "| linear | M | arm | kernel | grid (threads) | timed launches | median us | p10 us | p90 us | mean us | "
+             "weight GB/s (median) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for b, recs in zip(manifest, blocks):
         timed = recs[-b["timed_dispatches"]:]
         d = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed)
         med, mean = d[len(d) // 2] / 1e3, sum(d) / len(d) / 1e3
+        p10, p90 = d[len(d) // 10] / 1e3, d[(9 * len(d)) // 10] / 1e3
         gr, gc = -(-b["rows"] // 128), -(-b["cols"] // 128)
         wb = b["rows"] * b["cols"] + 4 * gr * gc if b["arm"] in ("vec", "mfma") else 2 * b["rows"] * b["cols"]
         names = {(_short(r["Kernel_Name"]), r.get("Grid_Size", r.get("Grid_Size_X", "?"))) for r in timed}
         k, g = sorted(names)[0]
-        lines.append(f"| {b['linear']} | {b['M']} | {b['arm']} | {k} | {g} | {len(d)} | {med:.2f} | {mean:.2f} | "
-                     f"{wb / med / 1e3:.1f} | {100 * wb / med / 1e3 / HBM_PEAK_GBS:.1f} |")
+        lines.append(f"| {b['linear']} | {b['M']} | {b['arm']} | {k} | {g} | {len(d)} | {med:.2f} | {p10:.2f} | "
+                     f"{p90:.2f} | {mean:.2f} | {wb / med / 1e3:.1f} | {100 * wb / med / 1e3 / HBM_PEAK_GBS:.1f} |")
     print("\n".join(lines))
 
 
