@@ -437,7 +437,7 @@ def expert_sweep(torch, fb, inputs, dev, steps, warmup, fmt, Ms=(1, 8)):
         # linear's activation codes and scales, and its f32 outputs
         algo = weight_bytes + sum(M * sp.cols + M * (sp.cols // 128) + 4 * M * sp.rows for sp, _, _ in lins)
         ach = algo * steps / t / 1e9
-        traffic = expert_traffic(fmt) if M == 1 else None
+        traffic = expert_traffic(fmt, M)
         r = {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
              "ms_per_step": round(t / steps * 1e3, 4),
              "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -538,15 +538,16 @@ def source_hash(sources):
     return h.hexdigest()[:16]
 
 
-def expert_counters_path():
-    return os.path.join(ROOT, "profiles", "expert_fp4_sweep_m1_counters.json")
+def expert_counters_path(M=1):
+    return os.path.join(ROOT, "profiles", f"expert_fp4_sweep_m{M}_counters.json")
 
 
-def expert_traffic(fmt):
-    """HBM bytes per M=1 launch of the expert kernel from the committed counter
-    summary (None when absent or taken on other kernel sources)."""
+def expert_traffic(fmt, M=1):
+    """HBM bytes per launch of the expert kernel at panel size M from the
+    committed counter summary (None when absent or taken on other kernel
+    sources)."""
     try:
-        with open(expert_counters_path()) as f:
+        with open(expert_counters_path(M)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -816,14 +817,14 @@ def summarize_trace(stats_csv, trace_csv, command, mode="sequence"):
     print("\n".join(lines))
 
 
-def summarize_expert_trace(stats_csv, command, trace_csv=None):
+def summarize_expert_trace(stats_csv, command, trace_csv=None, M=1):
     """Markdown: rocprofv3 --stats rows of the expert arm's kernels, and the
     median and minimum launch of the expert kernel per format from the
     per-dispatch trace (the stats average includes the warm-up launches)."""
     import csv
     import collections
     names = {"0": "MXFP4", "1": "NVFP4"}
-    lines = ["# rocprofv3 kernel trace: native expert arm, routed-expert sweep (1032 FP4 linears), M=1", "",
+    lines = [f"# rocprofv3 kernel trace: native expert arm, routed-expert sweep (1032 FP4 linears), M={M}", "",
              f"Command: `{command}`" if command else "", "",
              "k_expert<format, tiles, token groups, steps per window, list, single token>; format 0 = MXFP4, 1 = NVFP4. "
              "Each k_expert launch is one whole step (every linear of the sweep).", "",
@@ -848,10 +849,11 @@ def summarize_expert_trace(stats_csv, command, trace_csv=None):
     print("\n".join(lines))
 
 
-def summarize_expert_counters(fetch_csv, write_csv, command):
+def summarize_expert_counters(fetch_csv, write_csv, command, M=1):
     """Calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against the three
-    1 GiB copies of --copy-calibration and give the HBM bytes per M=1 launch of
-    the expert kernel, per format (median over its dispatches)."""
+    1 GiB copies of --copy-calibration and give the HBM bytes per launch of
+    the expert kernel at panel size M (one --expert-m value per run), per
+    format (median over its dispatches)."""
     import csv
     import collections
 
@@ -871,12 +873,13 @@ def summarize_expert_counters(fetch_csv, write_csv, command):
     f_factor = gib_kib / sorted(fc)[len(fc) // 2]
     w_factor = gib_kib / sorted(wc)[len(wc) // 2]
     per = {f: int((ff[f] * f_factor + wf[f] * w_factor) * 1024) for f in ff}
-    rec = {"source_hash": source_hash(EXPERT_SOURCES), "fetch_factor": round(f_factor, 4),
-           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": per, "kib": {f: {"fetch": ff[f], "write": wf[f]} for f in ff}, "command": command}
-    with open(expert_counters_path(), "w") as fh:
+    rec = {"source_hash": source_hash(EXPERT_SOURCES), "M": M, "fetch_factor": round(f_factor, 4),
+           "write_factor": round(w_factor, 4), "hbm_bytes_per_launch": per,
+           "kib": {f: {"fetch": ff[f], "write": wf[f]} for f in ff}, "command": command}
+    with open(expert_counters_path(M), "w") as fh:
         json.dump(rec, fh, indent=1)
     names = {"0": "MXFP4", "1": "NVFP4"}
-    lines = ["# rocprofv3 counters: native expert arm, routed-expert sweep (1032 FP4 linears), M=1", "",
+    lines = [f"# rocprofv3 counters: native expert arm, routed-expert sweep (1032 FP4 linears), M={M}", "",
              f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
              f"Calibration (1 GiB device copy in the same process): FETCH_SIZE x {f_factor:.3f}, "
              f"WRITE_SIZE x {w_factor:.3f} give bytes.", "",
@@ -1155,11 +1158,15 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.command, args.arm, args.mode)
         return
+    if args.summarize_expert_trace or args.summarize_expert_counters:
+        if "," in args.expert_m:
+            raise SystemExit("--summarize-expert-*: give the one --expert-m value the profiled runs used")
     if args.summarize_expert_trace:
-        summarize_expert_trace(args.summarize_expert_trace[0], args.command, args.summarize_expert_trace[1])
+        summarize_expert_trace(args.summarize_expert_trace[0], args.command, args.summarize_expert_trace[1],
+                               int(args.expert_m))
         return
     if args.summarize_expert_counters:
-        summarize_expert_counters(*args.summarize_expert_counters, args.command)
+        summarize_expert_counters(*args.summarize_expert_counters, args.command, int(args.expert_m))
         return
     if args.summarize_panel_trace:
         summarize_panel_trace(*args.summarize_panel_trace, args.command, int(args.panel_m))
