@@ -72,6 +72,9 @@ def parse():
     p.add_argument("--panel-only", action="store_true",
                    help="run only the M-row verify panel sweep (matrix-core sequence launch; for profiling) and "
                         "print its JSON")
+    p.add_argument("--chain-only", action="store_true",
+                   help="run only the dependent decode chain (graph of launches and the chained launch) and print "
+                        "its JSON")
     p.add_argument("--panel-m", default="1,2,4,8,16", help="panel rows of the verify panel sweep (comma-separated)")
     p.add_argument("--summarize-panel-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "KERNEL_TRACE_CSV"),
                    help="write the panel sweep kernel's rocprofv3 --stats summary (markdown) and exit")
@@ -290,6 +293,18 @@ class Chain:
         return [fb.prepared("fp8blk_gemv_grouped", [(m["w"], m["grid"], m["y"]) for m in a], b)]
 
 
+def persistent_chain(torch, fb, ch):
+    """The Chain's launch groups as a fp8blk_gemv_chain plan: group gi >= 1
+    reads bf16(c * y) of the first member of group gi - 1, with the glue scale
+    the calibration fixed; the first group reads the chain input."""
+    launches = [g for g in ch.groups if g[0] == "launch"]
+    groups = []
+    for gi, (_kind, members, _x) in enumerate(launches):
+        mem = [(m["w"], m["grid"], m["y"]) for m in members]
+        groups.append((mem, None if gi == 0 else (gi - 1, 0), 1.0 if gi == 0 else ch.c[gi - 1]))
+    return fb.fp8blk_chain_init(groups)
+
+
 def chain_sweep(torch, fb, sw, steps, warmup, dev):
     """Time the dependent chain (Chain) as one HIP graph replayed per step,
     events around `steps` replays on the replaying stream; and the same
@@ -326,15 +341,42 @@ def chain_sweep(torch, fb, sw, steps, warmup, dev):
     launches_only = lambda st: [c for (kind, _a, _b), c in zip(ch.groups, ch.calls(stream=st)) if kind == "launch"]  # noqa: E731
     t0 = graph_of(launches_only)
     v0 = sw.weight_bytes * steps / t0 / 1e9
+    # the same chain as one cooperative launch per step (fp8blk_gemv_chain)
+    pc = persistent_chain(torch, fb, ch)
+    pc_ms = None
+    if pc is not None:
+        run = lambda: fb.fp8blk_gemv_chain(pc, ch.x_in[0])  # noqa: E731
+        for _ in range(max(warmup, 20)):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pc_ms = e0.elapsed_time(e1) / steps
+        pc_status = fb.fp8blk_chain_status(pc)
+        pc_finite = all(bool(torch.isfinite(l["y"]).all()) for l in sw.lins)
     log(f"dependent chain ({ch.n_launches} GEMV launches + {ch.n_glue} glue kernels per step, graph): "
         f"{t / steps * 1e3:.4f} ms/step, {v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak); outputs finite: {finite}; "
-        f"the GEMV launches alone {t0 / steps * 1e3:.4f} ms/step, {v0:.1f} GB/s ({100 * v0 / HBM_PEAK_GBS:.1f}%)")
+        f"the GEMV launches alone {t0 / steps * 1e3:.4f} ms/step, {v0:.1f} GB/s ({100 * v0 / HBM_PEAK_GBS:.1f}%)"
+        + ("" if pc_ms is None else f"; one chained launch {pc_ms:.4f} ms/step, "
+           f"{sw.weight_bytes / (pc_ms / 1e3) / 1e9:.1f} GB/s "
+           f"({100 * sw.weight_bytes / (pc_ms / 1e3) / 1e9 / HBM_PEAK_GBS:.1f}%), status {pc_status}"))
     return {"value": round(v, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v / HBM_PEAK_GBS, 2),
             "ms_per_step": round(t / steps * 1e3, 4), "gemv_launches_per_step": ch.n_launches,
             "glue_kernels_per_step": ch.n_glue, "outputs_finite": finite,
             "gemv_launches_alone": {"value": round(v0, 1), "unit": "GB/s",
                                     "pct_hbm_peak": round(100 * v0 / HBM_PEAK_GBS, 2),
                                     "ms_per_step": round(t0 / steps * 1e3, 4)},
+            "one_launch": None if pc_ms is None else {
+                "value": round(sw.weight_bytes / (pc_ms / 1e3) / 1e9, 1), "unit": "GB/s",
+                "pct_hbm_peak": round(100 * sw.weight_bytes / (pc_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
+                "ms_per_step": round(pc_ms, 4), "launches_per_step": 1, "status": fb.fp8blk_strerror(pc_status),
+                "outputs_finite": pc_finite,
+                "note": "fp8blk_gemv_chain: the same groups, inputs x = bf16(c*y) formed inside the launch, one "
+                        "cooperative launch per step, events around the timed launches"},
             "workload": "the sweep's 259 linears as a dependent decode chain: per layer [q+kv] -> o -> [gate+up] "
                         "-> down -> next layer, then the head; one launch per group, x = bf16(c*y) between "
                         "groups (one torch kernel), one HIP graph per step"}
@@ -1219,6 +1261,11 @@ def main():
         if args.copy_calibration:
             copy_calibration(torch, dev)
         print(json.dumps({"panel_sweep_matrix_core_sequence": panel}), flush=True)
+        return
+    if args.chain_only:
+        sw = Sweep(torch, fb, inputs, dev, args.layers, "fp8")
+        chain = chain_sweep(torch, fb, sw, args.steps, args.warmup, dev)
+        print(json.dumps({"dependent_chain": chain}), flush=True)
         return
     log(f"setting up the sweep ({args.layers} layers + head, arm {args.arm})")
     t0 = time.perf_counter()

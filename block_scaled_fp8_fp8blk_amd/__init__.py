@@ -20,7 +20,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
 
-OK, ERR_ARG, ERR_SCALE_FF, ERR_NAN_CODE, ERR_INEXACT, ERR_WORKSPACE, ERR_HIP, ERR_BAD_SCALE = range(8)
+OK, ERR_ARG, ERR_SCALE_FF, ERR_NAN_CODE, ERR_INEXACT, ERR_WORKSPACE, ERR_HIP, ERR_BAD_SCALE, ERR_TIMEOUT = range(9)
 OP_LOAD_CHECK, OP_DEQUANT_BF16, OP_GEMV, OP_BF16_TWIN, OP_GEMM_STAGED, OP_BF16_GEMM = range(6)
 MIN_COLS, MAX_COLS, MAX_M, MAX_PANEL = 16, 65536, 16, 65536
 
@@ -32,9 +32,12 @@ EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "f
            "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
            "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin", "fp8blk_act_quant",
            "fp4_load_check", "fp4_dequant_bf16", "fp4_expert_gemv", "fp4_expert_sequence_init",
-           "fp4_expert_sequence")
+           "fp4_expert_sequence", "fp8blk_chain_bytes", "fp8blk_chain_init", "fp8blk_gemv_chain",
+           "fp8blk_chain_status")
 MAX_GROUP = 8
 MAX_SEQ = 65536
+MAX_CHAIN = 65536
+CHAIN_COLS = (1024, 2048, 3072, 4096)
 ARM_FP8, ARM_BF16, ARM_FP8_MFMA, ARM_BF16_MFMA, ARM_MXFP4, ARM_NVFP4 = 0, 1, 2, 3, 4, 5
 FMT_MXFP4, FMT_NVFP4 = 0, 1
 
@@ -64,6 +67,18 @@ class SequenceHandle(ctypes.Structure):
     _fields_ = [("plan", ctypes.c_void_p), ("units_dense", ctypes.c_int64), ("units_general", ctypes.c_int64),
                 ("n", ctypes.c_int32), ("arm", ctypes.c_int32), ("grid_dense", ctypes.c_int32),
                 ("grid_general", ctypes.c_int32), ("M", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ChainGroup(ctypes.Structure):
+    """fp8blk_chain_group: one group of a chained launch."""
+    _fields_ = [("first", ctypes.c_int32), ("n", ctypes.c_int32), ("cols", ctypes.c_int64), ("src", ctypes.c_int32),
+                ("c", ctypes.c_float)]
+
+
+class ChainHandle(ctypes.Structure):
+    """fp8blk_chain: the host-side record of a planned chained launch."""
+    _fields_ = [("plan", ctypes.c_void_p), ("units", ctypes.c_int64), ("n_linears", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("grid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -133,6 +148,13 @@ def load():
                                            i32, vp, sz, vp]
     L.fp4_expert_sequence_init.restype = i32
     L.fp4_expert_sequence.argtypes, L.fp4_expert_sequence.restype = [ctypes.POINTER(SequenceHandle), vp], i32
+    L.fp8blk_chain_bytes.argtypes = [ctypes.POINTER(Linear), i32, ctypes.POINTER(ChainGroup), i32]
+    L.fp8blk_chain_bytes.restype = sz
+    L.fp8blk_chain_init.argtypes = [ctypes.POINTER(ChainHandle), ctypes.POINTER(Linear), i32,
+                                    ctypes.POINTER(ChainGroup), i32, vp, sz, vp]
+    L.fp8blk_chain_init.restype = i32
+    L.fp8blk_gemv_chain.argtypes, L.fp8blk_gemv_chain.restype = [ctypes.POINTER(ChainHandle), vp, vp], i32
+    L.fp8blk_chain_status.argtypes, L.fp8blk_chain_status.restype = [ctypes.POINTER(ChainHandle), vp], i32
     _lib = L
     return L
 
@@ -423,6 +445,122 @@ def fp8blk_sequence_init(arm: int, linears, ws=None, stream=None, check=True):
     if check and st != OK:
         raise Fp8BlkError(st, "fp8blk_sequence_init")
     return Sequence(h, ws, keep) if st == OK else st
+
+
+class Chain:
+    """A planned chained launch (fp8blk_chain_init): the plan, the hand-off
+    words and the control words live in `ws` (a device byte tensor this object
+    keeps alive); `handle` is the host record; `keep` holds the tensors whose
+    addresses the plan records."""
+
+    def __init__(self, handle, ws, keep):
+        self.handle = handle
+        self.ws = ws
+        self.keep = keep
+
+
+def _chain_arrays(groups):
+    """groups: [(members, src, c), ...] with members [(codes, scales_f32, y), ...]
+    and src None (the chain input) or (g, k): member k of an earlier group g.
+    Returns the C arrays and the tensors they point at."""
+    import torch
+    lins, gs, keep = [], [], []
+    first = []
+    for gi, (members, src, c) in enumerate(groups):
+        if not members:
+            raise ValueError(f"group {gi}: no linears")
+        first.append(len(lins))
+        cols = None
+        for k, (w, grid, y) in enumerate(members):
+            if w.dim() != 2:
+                raise ValueError(f"group {gi} linear {k}: codes must be [rows, cols]")
+            rows, wc = int(w.shape[0]), int(w.shape[1])
+            cols = wc if cols is None else cols
+            if wc != cols:
+                raise ValueError(f"group {gi} linear {k}: cols {wc} differs from the group's {cols}")
+            if y.numel() != rows:
+                raise ValueError(f"group {gi} linear {k}: y holds {y.numel()} values, expected {rows}")
+            want = (-(-rows // 128)) * (-(-cols // 128))
+            if grid.numel() != want:
+                raise ValueError(f"group {gi} linear {k}: scale grid holds {grid.numel()} values, expected {want}")
+            lins.append((_dev(w, (torch.uint8,), "codes"), _dev(grid, (torch.float32,), "scales_f32"), rows,
+                         _dev(y, (torch.float32,), "y")))
+            keep.append((w, grid, y))
+        if src is None:
+            s = -1
+        else:
+            sg, sk = src
+            if not (0 <= sg < gi) or not (0 <= sk < len(groups[sg][0])):
+                raise ValueError(f"group {gi}: src {src} is not a linear of an earlier group")
+            s = first[sg] + sk
+        gs.append((first[-1], len(members), cols, s, float(c)))
+    devs = {t.device for trio in keep for t in trio}
+    if len(devs) != 1:
+        raise ValueError(f"the chain's tensors lie on {len(devs)} devices")
+    la = (Linear * len(lins))()
+    for k, (w, grid, rows, y) in enumerate(lins):
+        la[k].w, la[k].scales_f32, la[k].rows, la[k].y = w, grid, rows, y
+    ga = (ChainGroup * len(gs))()
+    for k, (f, n, cols, s, c) in enumerate(gs):
+        ga[k].first, ga[k].n, ga[k].cols, ga[k].src, ga[k].c = f, n, cols, s, c
+    x0_cols = max([g[2] for g in gs if g[3] < 0], default=0)
+    return la, len(lins), ga, len(gs), (keep, x0_cols)
+
+
+def fp8blk_chain_bytes(groups) -> int:
+    """Workspace bytes of a chained launch over `groups` (see fp8blk_chain_init);
+    0 if the library refuses the list."""
+    la, nl, ga, ng, _ = _chain_arrays(groups)
+    return int(load().fp8blk_chain_bytes(la, nl, ga, ng))
+
+
+def fp8blk_chain_init(groups, ws=None, stream=None, check=True):
+    """Plan a chained launch.
+    groups: [(members, src, c), ...] in order; members [(codes, scales_f32, y), ...]
+            share cols (1024, 2048, 3072 or 4096) and one input: the chain
+            input x0 (src None) or bf16(c * y) of member k of an earlier group g
+            (src (g, k)).
+    ws: a device uint8 tensor of at least fp8blk_chain_bytes(groups) bytes
+        (256-byte aligned), or None to allocate one here. Waits for `stream`."""
+    import torch
+    la, nl, ga, ng, (keep, x0_cols) = _chain_arrays(groups)
+    if ws is None:
+        nb = int(load().fp8blk_chain_bytes(la, nl, ga, ng))
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=groups[0][0][0][0].device)
+    wsp, wsb = _ws(ws)
+    h = ChainHandle()
+    st = load().fp8blk_chain_init(ctypes.byref(h), la, nl, ga, ng, wsp, wsb, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_chain_init")
+    if st != OK:
+        return st
+    ch = Chain(h, ws, keep)
+    ch.x0_cols = x0_cols
+    ch.device = keep[0][0].device
+    return ch
+
+
+def fp8blk_gemv_chain(chain, x0_bf16, stream=None, check=True):
+    """One cooperative launch of the whole chained list on x0 ([cols] bf16 of
+    the first group)."""
+    import torch
+    if x0_bf16.dtype not in _bf16_dtypes() or not x0_bf16.is_contiguous():
+        raise ValueError("x0_bf16 must be a contiguous bf16 (or int16/uint16) tensor")
+    if x0_bf16.numel() < chain.x0_cols:
+        raise ValueError(f"x0_bf16 holds {x0_bf16.numel()} values, the chain reads {chain.x0_cols}")
+    if x0_bf16.device != chain.device:
+        raise ValueError("x0_bf16 lies on another device than the chain")
+    st = load().fp8blk_gemv_chain(ctypes.byref(chain.handle), _dev(x0_bf16, _bf16_dtypes(), "x0_bf16"),
+                                  _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_chain")
+    return st
+
+
+def fp8blk_chain_status(chain, stream=None) -> int:
+    """Wait for `stream`; FP8BLK_OK, or ERR_TIMEOUT if a launch since the last
+    check stopped waiting for an input (the record is then cleared)."""
+    return int(load().fp8blk_chain_status(ctypes.byref(chain.handle), _stream(stream)))
 
 
 def fp8blk_gemv_sequence(seq, stream=None, check=True):

@@ -213,6 +213,7 @@ extern "C" const char* fp8blk_strerror(int status) {
         case FP8BLK_ERR_WORKSPACE: return "workspace missing or too small";
         case FP8BLK_ERR_HIP: return "HIP runtime error";
         case FP8BLK_ERR_BAD_SCALE: return "negative or NaN NVFP4 block scale refused";
+        case FP8BLK_ERR_TIMEOUT: return "chained launch stopped waiting for an earlier group's outputs";
         default: return "unknown status";
     }
 }

@@ -89,7 +89,8 @@ typedef enum fp8blk_status {
     FP8BLK_ERR_INEXACT = 4,   /* e4m3(code) * scale is not exactly a bf16 value */
     FP8BLK_ERR_WORKSPACE = 5, /* ws is NULL or ws_bytes is below fp8blk_workspace_bytes */
     FP8BLK_ERR_HIP = 6,       /* a HIP launch or runtime call failed */
-    FP8BLK_ERR_BAD_SCALE = 7  /* an NVFP4 block scale is negative or NaN */
+    FP8BLK_ERR_BAD_SCALE = 7, /* an NVFP4 block scale is negative or NaN */
+    FP8BLK_ERR_TIMEOUT = 8    /* a chained launch stopped waiting for an earlier group's outputs */
 } fp8blk_status;
 
 /* Operation ids for fp8blk_workspace_bytes. */
@@ -350,6 +351,80 @@ int fp8blk_gemv_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int bf16_gemv_twin_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int fp8blk_gemv_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
 int bf16_gemv_twin_mfma_sequence(const fp8blk_sequence *seq, fp8blk_stream_t stream);
+
+/*
+ * Chained launch: the projections of a decode step that feed one another
+ * ("Module dsv4_gpu" page, DecodePath: one launch per projection, each reading
+ * what the one before it wrote), as ONE persistent launch instead of one
+ * launch per link.
+ *
+ * The list is n_linears FP8-blk linears (fp8blk_linear: w = codes, scales_f32
+ * = the f32 grid, rows, y = [rows] f32; M = 1) in n_groups groups, in order.
+ * Group g is linears [first, first + n) (the groups tile the list in order),
+ * all with `cols` columns (1024, 2048, 3072 or 4096) and one input:
+ *   src = -1: the chain input x0_bf16 [cols] (bf16 bits, 16-byte aligned);
+ *   src >= 0: the output of linear `src` of an EARLIER group (its rows ==
+ *             cols), as x[c] = bf16(c_g * y_src[c]) -- the f32 product c_g *
+ *             y (one rounding) rounded to bf16 to nearest even (NaN: 0x7FC0).
+ *             The scale stands in for the elementwise work an engine does
+ *             between two projections; norms, attention and activations are
+ *             not part of this library.
+ * Every y_j is written, and equals fp8blk_gemv(w_j, scales_j, x_g) on that
+ * group's input bit for bit (the documented order of fp8blk_gemv).
+ *
+ *   fp8blk_chain_bytes  workspace bytes for this list (0: the list is
+ *                       invalid): descriptors, control words, and one 8-byte
+ *                       word per output row of every linear that is a src.
+ *   fp8blk_chain_init   validates the HOST arrays, writes the plan into the
+ *                       caller's device buffer ws (256-byte aligned, at least
+ *                       fp8blk_chain_bytes), zeroes its control words, fills
+ *                       the HOST struct *ch, and waits for `stream`. The plan
+ *                       holds the pointers: the buffers must stay allocated,
+ *                       at the same addresses, while ch is used.
+ *   fp8blk_gemv_chain   enqueues the whole list as one cooperative launch
+ *                       (one workgroup per compute unit, every workgroup
+ *                       resident at once) on `stream`; does not wait. The
+ *                       outputs of linears that feed later groups are handed
+ *                       on through ws, not through a kernel boundary: ws and
+ *                       the chain's y buffers must not be touched by other
+ *                       work until it completes, and two chained launches on
+ *                       one ws must not overlap (calls in stream order are
+ *                       fine, any number of times; not capturable in a HIP
+ *                       graph).
+ *   fp8blk_chain_status waits for `stream`, then returns FP8BLK_OK, or
+ *                       FP8BLK_ERR_TIMEOUT if a launch since the last check
+ *                       stopped waiting for an input (every wait is bounded,
+ *                       seconds; the outputs are then unspecified), and
+ *                       clears the record.
+ * Errors: FP8BLK_ERR_ARG (a bad list, struct or x0), FP8BLK_ERR_WORKSPACE (ws
+ * NULL, misaligned or too small), FP8BLK_ERR_HIP (including a device that
+ * cannot hold one workgroup per compute unit at once).
+ */
+#define FP8BLK_MAX_CHAIN 65536
+typedef struct fp8blk_chain_group {
+    int32_t first; /* the group's first linear */
+    int32_t n;     /* its linears, >= 1 */
+    int64_t cols;  /* shared by its linears */
+    int32_t src;   /* -1: x0; else the linear whose output is the input */
+    float c;       /* input scale (src >= 0) */
+} fp8blk_chain_group;
+
+typedef struct fp8blk_chain {
+    void *plan;        /* device: the plan inside ws */
+    int64_t units;     /* work units (16 chunk slots of one linear) over the list */
+    int32_t n_linears;
+    int32_t n_groups;
+    int32_t grid;      /* workgroups: the device's compute units */
+    int32_t reserved;
+} fp8blk_chain;
+
+size_t fp8blk_chain_bytes(const fp8blk_linear *linears, int n_linears, const fp8blk_chain_group *groups,
+                          int n_groups);
+int fp8blk_chain_init(fp8blk_chain *ch, const fp8blk_linear *linears, int n_linears,
+                      const fp8blk_chain_group *groups, int n_groups, void *ws, size_t ws_bytes,
+                      fp8blk_stream_t stream);
+int fp8blk_gemv_chain(const fp8blk_chain *ch, const uint16_t *x0_bf16, fp8blk_stream_t stream);
+int fp8blk_chain_status(const fp8blk_chain *ch, fp8blk_stream_t stream);
 
 /*
  * Staged prefill GEMM ("Module dsv4_gpu" page, rungs paragraph and

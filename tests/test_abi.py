@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_host_helpers(lib):
     assert fb.fp8blk_abi_version() == 1
-    for st in range(8):
+    for st in range(9):
         assert fb.fp8blk_strerror(st) != "unknown status"
     assert fb.fp8blk_strerror(99) == "unknown status"
     assert fb.fp8blk_workspace_bytes(fb.OP_LOAD_CHECK, 4096, 4096) >= 24
@@ -253,3 +253,60 @@ def test_expert_arm_refusals(lib):
     h.arm, h.M = fb.ARM_NVFP4, 17
     assert lib.fp4_expert_sequence(ctypes.byref(h), None) == fb.ERR_ARG
     assert lib.fp4_expert_sequence(None, None) == fb.ERR_ARG
+
+
+def _chain_arrays(specs, groups):
+    """C arrays for the chained-launch host checks: specs [(rows, cols)] with
+    fake, aligned device addresses (the checks never dereference them)."""
+    la = (fb.Linear * len(specs))()
+    for k, (rows, _cols) in enumerate(specs):
+        la[k].w, la[k].scales_f32, la[k].rows, la[k].y = 0x100000 * (k + 1), 0x7000000 + 0x10000 * k, rows, \
+            0x9000000 + 0x10000 * k
+    ga = (fb.ChainGroup * len(groups))()
+    for k, (first, n, cols, src, c) in enumerate(groups):
+        ga[k].first, ga[k].n, ga[k].cols, ga[k].src, ga[k].c = first, n, cols, src, c
+    return la, len(specs), ga, len(groups)
+
+
+def test_chain_plan_checks(lib):
+    """The chained launch's list checks run on the host, before any device
+    work: a valid list has a workspace size (descriptors + control words + one
+    8-byte word per output row of every linear that feeds a later group), and
+    each malformed list is refused (size 0, init FP8BLK_ERR_ARG)."""
+    specs = [(4096, 4096), (1024, 4096), (4096, 4096), (2048, 4096), (4096, 2048)]
+    good = [(0, 2, 4096, -1, 1.0), (2, 1, 4096, 0, 0.5), (3, 1, 4096, 2, 2.0), (4, 1, 2048, 3, 1.0)]
+    n = lib.fp8blk_chain_bytes(*_chain_arrays(specs, good))
+    # 256 control bytes, 4 x 16-byte groups, one 48-byte record per work unit (4 rows of a 4096-column linear,
+    # 8 rows of a 2048-column one), then one 8-byte word per output row of linears 0, 2 and 3 (the inputs of
+    # groups 1, 2 and 3)
+    units = 4096 // 4 + 1024 // 4 + 4096 // 4 + 2048 // 4 + 4096 // 8
+    recs_end = 256 + 64 + 48 * units
+    assert n == -(-recs_end // 64) * 64 + 8 * (4096 + 4096 + 2048)
+    bad = {
+        "a gap between groups": [(0, 2, 4096, -1, 1.0), (3, 1, 4096, 0, 0.5), (4, 1, 2048, 3, 1.0)],
+        "groups not covering the list": good[:3],
+        "src in the same group": [(0, 2, 4096, 1, 1.0)] + good[1:],
+        "src in a later group": [(0, 2, 4096, 2, 1.0)] + good[1:],
+        "src rows != cols": [good[0], (2, 1, 4096, 1, 0.5)] + good[2:],
+        "cols 8192": [good[0], good[1], good[2], (4, 1, 8192, 3, 1.0)],
+        "cols 1536": [good[0], good[1], good[2], (4, 1, 1536, 3, 1.0)],
+        "NaN scale": [good[0], (2, 1, 4096, 0, float("nan"))] + good[2:],
+        "src -2": [good[0], (2, 1, 4096, -2, 1.0)] + good[2:],
+        "empty group": [good[0], (2, 0, 4096, 0, 1.0), (2, 1, 4096, 0, 1.0)] + good[2:],
+    }
+    for what, groups in bad.items():
+        assert lib.fp8blk_chain_bytes(*_chain_arrays(specs, groups)) == 0, what
+        h = fb.ChainHandle()
+        la, nl, ga, ng = _chain_arrays(specs, groups)
+        st = lib.fp8blk_chain_init(ctypes.byref(h), la, nl, ga, ng, ctypes.c_void_p(0x10000000), 1 << 30, None)
+        assert st == fb.ERR_ARG, what
+    # a list whose cols do not match its linears' rows where it says so, with a
+    # misaligned code pointer
+    la, nl, ga, ng = _chain_arrays(specs, good)
+    la[1].w = 0x100008
+    assert lib.fp8blk_chain_bytes(la, nl, ga, ng) == 0
+    # a launch without a planned chain, or with a misaligned x0, is refused
+    assert lib.fp8blk_gemv_chain(None, ctypes.c_void_p(0x1000), None) == fb.ERR_ARG
+    h = fb.ChainHandle()
+    assert lib.fp8blk_gemv_chain(ctypes.byref(h), ctypes.c_void_p(0x1000), None) == fb.ERR_ARG
+    assert lib.fp8blk_chain_status(ctypes.byref(h), None) == fb.ERR_ARG
