@@ -281,18 +281,44 @@ __device__ __forceinline__ void mf_compute(MfCallWindow<KIND, TILES, XR> b, cons
                                                                  acc[t], 0, 0, 0);
 }
 
-// A wave owns TILES tiles of 16 consecutive rows and one part of the windows;
-// the loads of the next DEPTH - 1 windows are in flight while a window is
-// multiplied. Loads are unconditional: past the end of the part they re-read
-// its last window, which is then not used.
-template <int KIND, int TILES, int XR, int DEPTH>
-__global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
-    using Win = MfCallWindow<KIND, TILES, XR>;
-    __shared__ v4f part[kMfMaxWaves][TILES][kLanes];
+// After the windows: the sw parts of a row group meet in LDS and the wave of
+// part 0 adds them in part order; then lane l writes D[4 (l / 16) + e][l % 16]
+// (row 4 (l / 16) + e of the tile, panel row l % 16).
+template <int TILES>
+__device__ __forceinline__ void mf_finish(const MfArgs& a, const MfLane& L, int wave, int sp, v4f* acc,
+                                          v4f (*part)[TILES][kLanes]) {
+    const int lane = L.lane;
+    if (a.sw_log2 > 0) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) part[wave][t][lane] = acc[t];
+        __syncthreads();
+        if (sp != 0) return;
+        const int nsw = 1 << a.sw_log2;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+            v4f s = part[wave][t][lane];
+            for (int k = 1; k < nsw; ++k) {
+                const v4f o = part[wave + k][t][lane];
+                s = v4f{s[0] + o[0], s[1] + o[1], s[2] + o[2], s[3] + o[3]};
+            }
+            acc[t] = s;
+        }
+    }
+    const int n = lane & 15, kg = lane >> 4;
+    if (n < a.M) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t r = L.r0 + t * kTile + 4 * kg + e;
+                if (r < a.rows) a.y[(int64_t)n * a.rows + r] = acc[t][e];
+            }
+    }
+}
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-    const int lane = threadIdx.x % kLanes;
-    const int rs = wave >> a.sw_log2, sp = wave & ((1 << a.sw_log2) - 1);
+template <int TILES>
+__device__ __forceinline__ MfLane mf_lane(const MfArgs& a, int wave, int lane) {
+    const int rs = wave >> a.sw_log2;
     MfLane L;
     L.r0 = (((int64_t)blockIdx.x << a.streams_log2) + rs) * (TILES * kTile);
     L.r = lane & 7;
@@ -305,6 +331,22 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
     L.b1 = (lane & 2) != 0;
     L.b3 = (lane & 8) != 0;
     L.lane = lane;
+    return L;
+}
+
+// A wave owns TILES tiles of 16 consecutive rows and one part of the windows;
+// the loads of the next DEPTH - 1 windows are in flight while a window is
+// multiplied. Loads are unconditional: past the end of the part they re-read
+// its last window, which is then not used.
+template <int KIND, int TILES, int XR, int DEPTH>
+__global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
+    using Win = MfCallWindow<KIND, TILES, XR>;
+    __shared__ v4f part[kMfMaxWaves][TILES][kLanes];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const int lane = threadIdx.x % kLanes;
+    const int sp = wave & ((1 << a.sw_log2) - 1);
+    const MfLane L = mf_lane<TILES>(a, wave, lane);
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), (short)0, a.M * a.K * 2, kBufferWord3);
     const int wb = sp * a.bpp;
@@ -328,34 +370,43 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
             }
         }
     }
+    mf_finish<TILES>(a, L, wave, sp, acc, part);
+}
 
-    if (a.sw_log2 > 0) {
+// One shot: every load of a wave's part (at most NW windows) is issued before
+// any matrix work, so that a compute unit has its whole share of a cold
+// linear in flight at once; a single launch is then bound by how fast HBM
+// answers, not by how many loads each wave keeps waiting. A part shorter
+// than NW re-reads its last window for the missing ones (not used). WAVES is
+// the workgroup's wave count, which sets the register budget.
+template <int KIND, int TILES, int XR, int NW, int WAVES>
+__global__ __launch_bounds__(WAVES * kLanes) void k_mfma_shot(const MfArgs a) {
+    using Win = MfCallWindow<KIND, TILES, XR>;
+    __shared__ v4f part[WAVES][TILES][kLanes];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const int lane = threadIdx.x % kLanes;
+    const int sp = wave & ((1 << a.sw_log2) - 1);
+    const MfLane L = mf_lane<TILES>(a, wave, lane);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), (short)0, a.M * a.K * 2, kBufferWord3);
+    const int wb = sp * a.bpp;
+    const int we = min(a.nwin, wb + a.bpp);
+
+    v4f acc[TILES];
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) part[wave][t][lane] = acc[t];
-        __syncthreads();
-        if (sp != 0) return;
-        const int nsw = 1 << a.sw_log2;
+    for (int t = 0; t < TILES; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (wb < we) {
+        Win buf[NW];
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-            v4f s = part[wave][t][lane];
-            for (int k = 1; k < nsw; ++k) {
-                const v4f o = part[wave + k][t][lane];
-                s = v4f{s[0] + o[0], s[1] + o[1], s[2] + o[2], s[3] + o[3]};
-            }
-            acc[t] = s;
-        }
+        for (int d = 0; d < NW; ++d) mf_issue(buf[d], a, L, xr, min(wb + d, we - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < NW; ++d)
+            if (wb + d < we) mf_compute(buf[d], a, L, wb + d, acc);
     }
-    // lane l holds D[4 (l / 16) + e][l % 16]: row 4 (l / 16) + e of the tile, panel row l % 16
-    const int n = lane & 15, kg = lane >> 4;
-    if (n < a.M) {
-#pragma unroll
-        for (int t = 0; t < TILES; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t r = L.r0 + t * kTile + 4 * kg + e;
-                if (r < a.rows) a.y[(int64_t)n * a.rows + r] = acc[t][e];
-            }
-    }
+    mf_finish<TILES>(a, L, wave, sp, acc, part);
 }
 
 // Plan. The split sw is a function of (rows, cols) only -- it fixes the
@@ -371,10 +422,19 @@ __global__ __launch_bounds__(kMfMaxThreads) void k_mfma(const MfArgs a) {
 // tiles (256 workgroups): 42 -> 50% of HBM peak at M = 16, 45 -> 53% at
 // M = 8, against 4 tiles (192 workgroups, a quarter of the compute units
 // idle) and 1 tile (768 workgroups, three times the activation loads).
+// The loads are issued in one shot (nw = windows per part, FP8 arm) where a
+// part is 2, 4 or 8 windows, M <= 8, and either M <= 2 or the waves take one
+// tile anyway: a wave then has all of its part in flight at once instead of
+// two windows. Measured on cold single launches (same bits): M = 1 on
+// 4096 x 4096 6.5 -> 5.4 us, 16384 x 4096 15.8 -> 14.2 us, 12288 x 4096 11.6
+// -> 11.3 us, 1024 x 4096 4.9 -> 4.65 us; M = 8 on 4096 x 4096 7.0 -> 6.8 us.
+// With more activation rows and several tiles per wave the two-deep pipeline
+// stays faster (12288 x 4096 at M = 8: 11.6 us against 13.3), and at M = 16
+// too (4096 x 4096: 7.25 against 7.6).
 struct MfPlan {
-    int tiles, sw, depth;
+    int tiles, sw, nw;  // nw: windows per wave loaded in one shot (0: the two-deep pipeline)
 };
-MfPlan mf_plan(int64_t rows, int64_t K, int cus) {
+MfPlan mf_plan(int64_t rows, int64_t K, int64_t M, int cus, bool fp8) {
     MfPlan p;
     const int64_t nwin = ceil_div(K, (int64_t)kBlock);
     const int64_t groups1 = ceil_div(rows, (int64_t)kTile);
@@ -387,12 +447,36 @@ MfPlan mf_plan(int64_t rows, int64_t K, int cus) {
             p.tiles = t;
             break;
         }
-    p.depth = 2;
+    const int64_t bpp = ceil_div(nwin, (int64_t)p.sw);
+    p.nw = 0;
+    if (fp8 && (bpp == 2 || bpp == 4 || bpp == 8) && M <= 8 && (M <= 2 || p.tiles == 1)) {
+        p.nw = (int)bpp;
+        p.tiles = 1;
+    }
     return p;
 }
 
 template <int KIND, int XR>
 void mf_launch(const MfPlan& p, dim3 nb, dim3 nt, hipStream_t s, const MfArgs& a) {
+    if constexpr (KIND == 0) {
+        if (p.nw > 0) {
+            const bool w4 = nt.x == 4 * kLanes;
+            switch (p.nw) {
+                case 8:
+                    if (w4) k_mfma_shot<0, 1, XR, 8, 4><<<nb, nt, 0, s>>>(a);
+                    else k_mfma_shot<0, 1, XR, 8, 8><<<nb, nt, 0, s>>>(a);
+                    return;
+                case 4:
+                    if (w4) k_mfma_shot<0, 1, XR, 4, 4><<<nb, nt, 0, s>>>(a);
+                    else k_mfma_shot<0, 1, XR, 4, 8><<<nb, nt, 0, s>>>(a);
+                    return;
+                default:
+                    if (w4) k_mfma_shot<0, 1, XR, 2, 4><<<nb, nt, 0, s>>>(a);
+                    else k_mfma_shot<0, 1, XR, 2, 8><<<nb, nt, 0, s>>>(a);
+                    return;
+            }
+        }
+    }
     switch (p.tiles) {
         case 4: k_mfma<KIND, 4, XR, 2><<<nb, nt, 0, s>>>(a); break;
         case 3: k_mfma<KIND, 3, XR, 2><<<nb, nt, 0, s>>>(a); break;
@@ -406,7 +490,7 @@ int mf_run(const void* w, const float* grid, int64_t rows, int64_t cols, const u
            hipStream_t s) {
     const int cus = device_cus();
     if (cus <= 0) return FP8BLK_ERR_HIP;
-    const MfPlan p = mf_plan(rows, cols, cus);
+    const MfPlan p = mf_plan(rows, cols, M, cus, KIND == 0);
     MfArgs a;
     a.w = w;
     a.grid = grid;

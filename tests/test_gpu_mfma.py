@@ -47,8 +47,13 @@ def _check(L, Ms=None, nthreads=None):
         assert_within_tolerance(y8, y64, yabs, what=f"mfma {L.rows}x{L.cols} M={M}")
 
 
+# The one-shot single calls (each wave's 2, 4 or 8 windows loaded at once) are
+# among these: (1000, 1024, 4) with two row groups per workgroup, (300, 1008, 3)
+# and (500, 4080, 2) with a ragged last window, (4099, 4080, 1) with four-wave
+# workgroups and a ragged last row group; the others take the two-deep pipeline.
 CASES = [(1, 16, 1), (3, 48, 2), (17, 1040, 3), (129, 2064, 16), (130, 3088, 5), (257, 4112, 8),
-         (64, 16400, 2), (100, 4096, 16), (2, 65536, 1), (33, 65536, 16), (1000, 1024, 4), (4097, 272, 9)]
+         (64, 16400, 2), (100, 4096, 16), (2, 65536, 1), (33, 65536, 16), (1000, 1024, 4), (4097, 272, 9),
+         (300, 1008, 3), (500, 4080, 2), (4099, 4080, 1)]
 
 
 @pytest.mark.parametrize("rows,cols,M", CASES)
