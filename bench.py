@@ -636,7 +636,7 @@ def counted_traffic(arm, mode):
 
 
 # Kernels of the single-linear GEMV entry points (one dispatch per call).
-CONFIG_KERNELS = ("k_gemv_m1<", "k_panel<", "k_mfma<")
+CONFIG_KERNELS = ("k_gemv_m1<", "k_panel<", "k_mfma<", "k_mfma_shot<")
 CONFIG_SOURCES = ("block_scaled_fp8_fp8blk_amd/csrc/fp8blk_gemv.hip", "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_mfma.hip",
                   "block_scaled_fp8_fp8blk_amd/csrc/fp8blk_device.hpp")
 CONFIG_ARMS = (("vec", "fp8blk_gemv"), ("vec_twin", "bf16_gemv_twin"), ("mfma", "fp8blk_gemv_mfma"),
