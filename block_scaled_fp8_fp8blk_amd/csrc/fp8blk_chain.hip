@@ -48,13 +48,24 @@
 namespace fp8blk {
 namespace {
 
-constexpr int kChWaves = 8;                  // waves per workgroup: kChWaves - 1 compute waves and one polling wave
+constexpr int kChWaves = 12;                 // waves per workgroup: kChWaves - 1 compute waves and one polling wave
 constexpr int kChCompute = kChWaves - 1;
 constexpr int kChPoller = kChWaves - 1;      // the polling wave's index
-constexpr int kChSlots = 16;                 // 16-byte code chunks per lane per unit
+constexpr int kChSlots = 8;                  // 16-byte code chunks per lane per unit
 constexpr int kChMaxCols = 4096;
 constexpr int kChSpin = 1 << 21;             // polls before a wait gives up (seconds, far beyond any group)
 constexpr int kChErrCheck = 64;              // polls between checks of the error record
+// The polling wave reads a group's input no sooner than kChPollDelay ticks of
+// the 100 MHz real-time counter after the barrier that released the group
+// before it: the outputs it waits for take about that long to be computed
+// and written (one unit of vector work and the write-through), and device-
+// coherent polls issued earlier only slow every workgroup's weight loads.
+// Measured on the 173-group decode chain (8-slot units): 1.15 ms per launch
+// waiting 3.4 us, 1.10 ms waiting 2.0-2.7 us; with 16-slot units: 1.39 ms
+// polling at once, 1.23-1.26 ms waiting 3.0-3.8 us, 1.41 ms waiting 5 us,
+// and 1.46-1.57 ms waiting instead for the workgroup's own units to be
+// stored.
+constexpr uint64_t kChPollDelay = 240;
 constexpr int kBufferWord3 = 0x00020000;     // buffer resource word 3: raw 32-bit data
 constexpr int kCoherent = 16;                // cache policy of a device-coherent load (sc1)
 
@@ -62,7 +73,7 @@ constexpr int kCoherent = 16;                // cache policy of a device-coheren
 constexpr int kCtlEpoch = 0, kCtlDone = 16, kCtlErr = 32;
 constexpr size_t kCtlBytes = 256;
 
-// One work unit (16 chunk slots of one linear, 16 / T4 consecutive rows):
+// One work unit (8 chunk slots of one linear, 8 / T4 consecutive rows):
 // everything its loads, arithmetic and stores need, precomputed on the host,
 // so that the loop reads no descriptor (a scalar load would be waited for at
 // every barrier).
@@ -71,7 +82,7 @@ struct alignas(16) ChRec {
     const float* grid;   // the unit's row of block scales
     float* y;            // output of the unit's first row
     int32_t ll;          // word index of that output among the linked outputs, -1: none
-    int32_t left;        // rows of the unit that exist (<= 16 / T4)
+    int32_t left;        // rows of the unit that exist (<= 8 / T4)
     int32_t cols;        // 1024, 2048, 3072 or 4096
     int32_t group;
 };
@@ -95,7 +106,7 @@ struct ChArgs {
     int32_t n_groups;
 };
 
-// Rows per unit: 16 chunk slots per lane, T4 segments per row (T4 = 1, 2 or 4;
+// Rows per unit: 8 chunk slots per lane, T4 segments per row (T4 = 1, 2 or 4;
 // cols 3072 use four slots per row, the last one unused).
 __host__ __device__ constexpr int seg_slots(int cols) { return cols <= 1024 ? 1 : cols <= 2048 ? 2 : 4; }
 
@@ -275,15 +286,27 @@ __device__ __forceinline__ void ch_poll_words(const ChArgs& a, int src_ll, float
         __builtin_amdgcn_s_sleep(1);
     }
     for (int it = 0;; ++it) {
-        uint4 v[NP];
-#pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + kLanes * k) * 16, 0, kCoherent);
-            v[k] = make_uint4(t[0], t[1], t[2], t[3]);
-        }
+        // in halves of at most 16 pieces per lane (registers); each half's bf16
+        // input goes to LDS as it is read, and counts only if every half carried
+        // the epoch in the same pass
         bool ok = true;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) ok = ok && v[k].y == epoch && v[k].w == epoch;
+        for (int h = 0; h < NP; h += 16) {
+            uint4 v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (h + k < NP) {
+                    const auto t =
+                        __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + kLanes * (h + k)) * 16, 0, kCoherent);
+                    v[k] = make_uint4(t[0], t[1], t[2], t[3]);
+                }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (h + k < NP) {
+                    ok = ok && v[k].y == epoch && v[k].w == epoch;
+                    x32[lane + kLanes * (h + k)] = bf16_of_scaled(c, v[k].x) | (bf16_of_scaled(c, v[k].z) << 16);
+                }
+        }
         bool stop = __all(ok);
         if (!stop && it >= kChSpin) {
             if (lane == 0) __hip_atomic_fetch_or(a.ctl + kCtlErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -291,12 +314,7 @@ __device__ __forceinline__ void ch_poll_words(const ChArgs& a, int src_ll, float
         }
         if (!stop && it % kChErrCheck == kChErrCheck - 1)
             stop = __builtin_amdgcn_readfirstlane(ld_coherent_u32(a.ctl + kCtlErr)) != 0;
-        if (stop) {
-#pragma unroll
-            for (int k = 0; k < NP; ++k)
-                x32[lane + kLanes * k] = bf16_of_scaled(c, v[k].x) | (bf16_of_scaled(c, v[k].z) << 16);
-            return;
-        }
+        if (stop) return;
         __builtin_amdgcn_s_sleep(1);
     }
 }
@@ -304,6 +322,7 @@ __device__ __forceinline__ void ch_poll_words(const ChArgs& a, int src_ll, float
 // The polling wave: group g's bf16 input into LDS slot xs. gd: lane l holds
 // the descriptor of group g - g % 64 + l.
 __device__ __forceinline__ void ch_poll(const ChArgs& a, int g, const uint4& gd, uint4* xs, int lane, uint32_t epoch) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const int l = g % kLanes;
     const int cols = __builtin_amdgcn_readlane((int)gd.x, l);
     const int src_ll = __builtin_amdgcn_readlane((int)gd.y, l);
@@ -313,6 +332,7 @@ __device__ __forceinline__ void ch_poll(const ChArgs& a, int g, const uint4& gd,
         for (int p = lane; p < cols / 8; p += kLanes) xs[p] = load_global16(src + p);
         return;
     }
+    while (__builtin_amdgcn_s_memrealtime() - t0 < kChPollDelay) __builtin_amdgcn_s_sleep(8);
     switch (cols) {
         case 1024: ch_poll_words<8>(a, src_ll, c, xs, lane, epoch); break;
         case 2048: ch_poll_words<16>(a, src_ll, c, xs, lane, epoch); break;

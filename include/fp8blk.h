@@ -411,7 +411,7 @@ typedef struct fp8blk_chain_group {
 
 typedef struct fp8blk_chain {
     void *plan;        /* device: the plan inside ws */
-    int64_t units;     /* work units (16 chunk slots of one linear) over the list */
+    int64_t units;     /* work units (8 chunk slots of one linear) over the list */
     int32_t n_linears;
     int32_t n_groups;
     int32_t grid;      /* workgroups: the device's compute units */

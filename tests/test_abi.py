@@ -276,10 +276,10 @@ def test_chain_plan_checks(lib):
     specs = [(4096, 4096), (1024, 4096), (4096, 4096), (2048, 4096), (4096, 2048)]
     good = [(0, 2, 4096, -1, 1.0), (2, 1, 4096, 0, 0.5), (3, 1, 4096, 2, 2.0), (4, 1, 2048, 3, 1.0)]
     n = lib.fp8blk_chain_bytes(*_chain_arrays(specs, good))
-    # 256 control bytes, 4 x 16-byte groups, one 48-byte record per work unit (4 rows of a 4096-column linear,
-    # 8 rows of a 2048-column one), then one 8-byte word per output row of linears 0, 2 and 3 (the inputs of
+    # 256 control bytes, 4 x 16-byte groups, one 48-byte record per work unit (2 rows of a 4096-column linear,
+    # 4 rows of a 2048-column one), then one 8-byte word per output row of linears 0, 2 and 3 (the inputs of
     # groups 1, 2 and 3)
-    units = 4096 // 4 + 1024 // 4 + 4096 // 4 + 2048 // 4 + 4096 // 8
+    units = 4096 // 2 + 1024 // 2 + 4096 // 2 + 2048 // 2 + 4096 // 4
     recs_end = 256 + 64 + 48 * units
     assert n == -(-recs_end // 64) * 64 + 8 * (4096 + 4096 + 2048)
     bad = {
