@@ -144,7 +144,7 @@ __device__ __forceinline__ ChItem ch_item(ChRecs& R, const ChArgs& a, int64_t gw
                                           int lane) {
     ChItem it;
     it.more = k < n_items;
-    const int64_t kk = it.more ? k : n_items - 1;
+    const int64_t kk = it.more ? k : n_items > 0 ? n_items - 1 : 0;  // a wave with no unit reads record 0 of its list
     if (kk < R.k0 || kk >= R.k0 + kLanes) ch_recs_load(R, a, gw, W, kk - kk % kLanes, lane);
     const int l = (int)(kk - R.k0);
     it.w = reinterpret_cast<const uint8_t*>(rl64(R.a.x, R.a.y, l));
