@@ -263,12 +263,12 @@ __device__ __forceinline__ void panel_body(const GemvArgs& a, int64_t block) {
 // TPW segments they are split over sw = 2 or 4 waves of the workgroup, which
 // leave their segment sums in LDS; one wave then adds them in order. Lanes
 // whose chunk lies past the last column load a valid chunk and contribute +0.0.
-template <int KIND, int R, int TPW>
+template <int KIND, int R, int TPW, int MT>
 __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
-    constexpr int V = R * TPW;
+    constexpr int V = R * TPW * MT;
     constexpr int VP = V < 4 ? 4 : V;  // reductions run in groups of four values
     using F = Fetch<KIND>;
-    extern __shared__ float part[];  // [row stream][segment][R], used when sw > 1
+    extern __shared__ float part[];  // [row stream][segment][R][MT], used when sw > 1
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);  // uniform: scalar branches below
     const int lane = threadIdx.x % kLanes;
@@ -282,9 +282,11 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
     // so the compiler can wait for each segment alone (no branch merges the
     // outstanding-load counts). A segment past this wave's range re-reads
     // its last one, a chunk past the last column re-reads the last chunk;
-    // both are discarded below.
+    // both are discarded below. With MT = 2 activation rows (M = 2), each
+    // chunk of weights is decoded once and feeds both rows; a second row past
+    // M (M = 1 never takes MT = 2) would repeat row M - 1.
     typename F::Raw raw[R][TPW];
-    uint4 xr[TPW][2];
+    uint4 xr[TPW][MT][2];
     const int t_last = max(0, min(t0 + nseg, a.T) - 1);
     // FP8: the wave's rows share one 128-row block, and its TPW segments need
     // 8 * TPW consecutive block scales: lanes load one each (one instruction
@@ -298,9 +300,12 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
     for (int u = 0; u < TPW; ++u) {
         const int q = min(min(t0 + u, t_last) * kLanes + lane, last_q);
         F::load_codes(a, r0, q, raw, u);
-        const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)q * kChunk);
-        xr[u][0] = xp[0];
-        xr[u][1] = xp[1];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)min(m, a.M - 1) * a.K + (int64_t)q * kChunk);
+            xr[u][m][0] = xp[0];
+            xr[u][m][1] = xp[1];
+        }
     }
     // Keep every load ahead of the arithmetic: with one shot of data per wave,
     // the bytes in flight per CU are what sets the streaming rate.
@@ -319,56 +324,73 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const bool live = u < nseg && (t0 + u) * kLanes + lane <= last_q;
-        float xf[kChunk];
-        widen8_bf16(xr[u][0], xf);
-        widen8_bf16(xr[u][1], xf + 8);
+        float xf[MT][kChunk];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            widen8_bf16(xr[u][m][0], xf[m]);
+            widen8_bf16(xr[u][m][1], xf[m] + 8);
+        }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             float w[kChunk];
             F::weights(raw[i][u], w, a.whole != 0);
-            float s = 0.0f;
 #pragma unroll
-            for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[j], xf[j], s);
-            v[i * TPW + u] = live ? s : 0.0f;
+            for (int m = 0; m < MT; ++m) {
+                float s = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j) s = __builtin_fmaf(w[j], xf[m][j], s);
+                v[(i * TPW + u) * MT + m] = live ? s : 0.0f;
+            }
         }
     }
     float red[VP / 4];
     tree64xV<VP>(v, red);
-    // segment sum of (row i, segment u): value k = i * TPW + u
-#define FP8BLK_P(i, u) lane_value(red[((i) * TPW + (u)) / 4], 16 * kRowOf4[((i) * TPW + (u)) % 4])
+    // segment sum of (row i, segment u, activation row m): value k = (i * TPW + u) * MT + m
+#define FP8BLK_P(i, u, m) \
+    lane_value(red[(((i) * TPW + (u)) * MT + (m)) / 4], 16 * kRowOf4[(((i) * TPW + (u)) * MT + (m)) % 4])
 
-    float y[R];
+    float y[R][MT];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        y[i] = FP8BLK_P(i, 0);
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int u = 1; u < TPW; ++u)
-            if (u < nseg) y[i] = y[i] + FP8BLK_P(i, u);
-    }
+        for (int m = 0; m < MT; ++m) {
+            y[i][m] = FP8BLK_P(i, 0, m);
+#pragma unroll
+            for (int u = 1; u < TPW; ++u)
+                if (u < nseg) y[i][m] = y[i][m] + FP8BLK_P(i, u, m);
+        }
     if (a.sw_log2 > 0) {
         if (lane == 0)
 #pragma unroll
             for (int i = 0; i < R; ++i)
 #pragma unroll
                 for (int u = 0; u < TPW; ++u)
-                    if (u < nseg) part[((int64_t)rs * a.T + t0 + u) * R + i] = FP8BLK_P(i, u);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        if (u < nseg) part[(((int64_t)rs * a.T + t0 + u) * R + i) * MT + m] = FP8BLK_P(i, u, m);
         __syncthreads();
         if (sp != 0) return;
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float* p = part + (int64_t)rs * a.T * R + i;
-            float v = p[0];
-            for (int t = 1; t < a.T; ++t) v = v + p[t * R];
-            y[i] = v;
-        }
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float* p = part + ((int64_t)rs * a.T * R + i) * MT + m;
+                float v = p[0];
+                for (int t = 1; t < a.T; ++t) v = v + p[t * R * MT];
+                y[i][m] = v;
+            }
     }
 #undef FP8BLK_P
-    if (lane < R && r0 + lane < a.rows) {
-        float out = y[0];
+    // lane i * MT + m stores output (m, r0 + i)
+    if (lane < R * MT) {
+        const int i = lane / MT, m = lane % MT;
+        float out = y[0][0];
 #pragma unroll
-        for (int i = 1; i < R; ++i)
-            if (lane == i) out = y[i];
-        a.y[r0 + lane] = out;
+        for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+                if (lane == ii * MT + mm) out = y[ii][mm];
+        if (m < a.M && r0 + i < a.rows) a.y[(int64_t)m * a.rows + r0 + i] = out;
     }
 }
 
@@ -402,15 +424,15 @@ __host__ __device__ __forceinline__ GemvArgs group_args(const GroupArgs& g, int 
     return a;
 }
 
-template <int KIND, int R, int TPW>
+template <int KIND, int R, int TPW, int MT>
 __global__ __launch_bounds__(kThreads) void k_gemv_m1(const GemvArgs a) {
-    m1_body<KIND, R, TPW>(a, blockIdx.x);
+    m1_body<KIND, R, TPW, MT>(a, blockIdx.x);
 }
 
-template <int KIND, int R, int TPW>
+template <int KIND, int R, int TPW, int MT>
 __global__ __launch_bounds__(kThreads) void k_gemv_m1_group(const GroupArgs g) {
     const int j = __builtin_amdgcn_readfirstlane(group_of(g, blockIdx.x));
-    m1_body<KIND, R, TPW>(group_args(g, j), (int64_t)blockIdx.x - g.start[j]);
+    m1_body<KIND, R, TPW, MT>(group_args(g, j), (int64_t)blockIdx.x - g.start[j]);
 }
 
 template <int KIND, int MT, int R>
@@ -430,7 +452,7 @@ struct Plan {
 };
 
 // Plan: a pure function of (rows, cols, M); it never changes bits.
-// M = 1 and at most 16 segments: the single-row kernel, TPW segments per wave
+// M = 1 and at most 16 segments: the one-shot kernel, TPW segments per wave
 // and the rest of a row over sw waves (T <= TPW * sw):
 // - T <= 2: TPW = T, R = 4 / TPW rows (four chunks per lane).
 // - T >= 3 and fewer than 4096 rows: TPW = 4, R = 1. Small linears want the
@@ -442,13 +464,19 @@ struct Plan {
 //   launches at cols 4096: 4096 rows 42.0% -> 43.2% of HBM peak, 12288 rows
 //   60.9% -> 65.0%, 16384 rows 63.2% -> 67.6%, 129280 rows 75.7% -> 89.3%;
 //   4096 x 16384 (split over 4 waves) 48.5% -> 56.7%.
+// M = 2 and at most 4 segments: the same kernel with two activation rows
+// (each weight chunk decoded once for both), the same R and TPW except TPW = 4
+// from 4096 rows on. Measured, single cold launches at M = 2 against the
+// panel kernel (same bits): 4096 x 4096 6.02 -> 5.71 us, 12288 x 4096 13.1 ->
+// 11.5 us, 16384 x 4096 18.6 -> 15.1 us, 4096 x 2048 4.22 -> 3.96 us; with 16
+// segments (4096 x 16384) the panel kernel stays faster, 19.1 against 21.0 us.
 // Otherwise the panel kernel with R = 4 rows per wave, splitting the segments
 // of a row over 2 or 4 waves while fewer than 4096 waves would run.
 Plan make_plan(int64_t rows, int64_t K, int64_t M) {
     Plan p;
     const int64_t T = ceil_div(K, kSegCols);
     p.MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
-    if (p.MT == 1 && T <= 16) {
+    if ((p.MT == 1 && T <= 16) || (p.MT == 2 && T <= 4)) {
         p.m1 = true;
         if (T <= 2) {
             p.tpw = (int)T;
@@ -457,7 +485,7 @@ Plan make_plan(int64_t rows, int64_t K, int64_t M) {
             p.tpw = 4;
             p.R = 1;
         } else {
-            p.tpw = rows >= 16384 && T <= 8 ? 2 : 4;
+            p.tpw = p.MT == 1 && rows >= 16384 && T <= 8 ? 2 : 4;
             p.R = 2;
         }
         p.sw = T <= p.tpw ? 1 : T <= 2 * p.tpw ? 2 : 4;
@@ -485,14 +513,14 @@ void launch_panel(const GroupArgs& g, int64_t blocks, hipStream_t s) {
         k_panel_group<KIND, MT, R><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(g);
 }
 
-template <int KIND, int R, int TPW>
+template <int KIND, int R, int TPW, int MT>
 void launch_m1(const GroupArgs& g, int64_t blocks, hipStream_t s) {
     const int streams = kWaves / g.base.sw;
-    const size_t lds = g.base.sw > 1 ? (size_t)streams * g.base.T * R * sizeof(float) : 0;
+    const size_t lds = g.base.sw > 1 ? (size_t)streams * g.base.T * R * MT * sizeof(float) : 0;
     if (g.n == 1)
-        k_gemv_m1<KIND, R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(group_args(g, 0));
+        k_gemv_m1<KIND, R, TPW, MT><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(group_args(g, 0));
     else
-        k_gemv_m1_group<KIND, R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(g);
+        k_gemv_m1_group<KIND, R, TPW, MT><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(g);
 }
 
 // One launch for g.n linears that share cols, x and M (g.w, g.grid, g.y and
@@ -522,9 +550,10 @@ int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s)
     if (blocks > 0x7fffffff) return FP8BLK_ERR_ARG;
     (void)hipGetLastError();
     if (p.m1) {
-#define FP8BLK_M1(RR, TT) \
-    if (p.R == RR && p.tpw == TT) launch_m1<KIND, RR, TT>(g, blocks, s)
-        FP8BLK_M1(1, 4); else FP8BLK_M1(2, 4); else FP8BLK_M1(2, 2); else FP8BLK_M1(4, 1);
+#define FP8BLK_M1(RR, TT, MM) \
+    if (p.R == RR && p.tpw == TT && p.MT == MM) launch_m1<KIND, RR, TT, MM>(g, blocks, s)
+        FP8BLK_M1(1, 4, 1); else FP8BLK_M1(2, 4, 1); else FP8BLK_M1(2, 2, 1); else FP8BLK_M1(4, 1, 1);
+        else FP8BLK_M1(1, 4, 2); else FP8BLK_M1(2, 4, 2); else FP8BLK_M1(2, 2, 2); else FP8BLK_M1(4, 1, 2);
 #undef FP8BLK_M1
     } else {
         switch (p.MT) {

@@ -51,6 +51,22 @@ def test_gemv_parity(gpu, rows, cols, M, kind):
 PLAN_CASES = [(4097, 3088), (8191, 8192), (16385, 2064), (16391, 5136)]
 
 
+# M = 2 with at most 4 segments runs the same one-shot kernel with two
+# activation rows: two rows per wave and four segments per wave from 4096
+# rows (ragged rows and cols, 3 and 4 segments), two segments (cols 2048,
+# ragged rows) and one (cols 1008, four rows per wave).
+M2_CASES = [(4097, 3088), (5003, 2064), (4099, 2048), (257, 1008), (12288, 4096)]
+
+
+@pytest.mark.parametrize("rows,cols", M2_CASES)
+def test_gemv_parity_two_activation_rows(gpu, rows, cols):
+    from gpu_util import full_parity, say
+    say(f"gemv parity rows={rows} cols={cols} M=2 (one-shot, two activation rows)")
+    L = inputs.host_linear(rows, cols, 2, 13 * rows + cols)
+    _D, _s, y8, yt = _run(L)
+    full_parity(L, L.codes, L.scales, L.x, y8, yt, nthreads=16, what=f"{rows}x{cols} M=2")
+
+
 @pytest.mark.parametrize("rows,cols", PLAN_CASES)
 def test_gemv_parity_two_rows_per_wave(gpu, rows, cols):
     from gpu_util import full_parity, say
