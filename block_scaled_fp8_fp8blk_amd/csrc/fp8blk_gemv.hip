@@ -470,6 +470,9 @@ struct Plan {
 // panel kernel (same bits): 4096 x 4096 6.02 -> 5.71 us, 12288 x 4096 13.1 ->
 // 11.5 us, 16384 x 4096 18.6 -> 15.1 us, 4096 x 2048 4.22 -> 3.96 us; with 16
 // segments (4096 x 16384) the panel kernel stays faster, 19.1 against 21.0 us.
+// Four activation rows in the one-shot kernel (M = 3, 4) measured slower than
+// the panel kernel on every shape (12288 x 4096 at M = 4: 18.8-25.6 us over
+// the row and segment splits against 17.2 us).
 // Otherwise the panel kernel with R = 4 rows per wave, splitting the segments
 // of a row over 2 or 4 waves while fewer than 4096 waves would run.
 Plan make_plan(int64_t rows, int64_t K, int64_t M) {
