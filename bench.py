@@ -849,7 +849,7 @@ def summarize_trace(stats_csv, trace_csv, command, mode="sequence"):
     for r in csv.DictReader(open(trace_csv)):
         if "k_gemv_m1" in r["Kernel_Name"] or "k_panel" in r["Kernel_Name"] or "k_seq" in r["Kernel_Name"]:
             by[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines += ["", "Per launch shape (kernel<arm, rows per wave, segments per wave>, grid = threads; one launch per "
+    lines += ["", "Per launch shape (kernel<arm, rows per wave, segments per wave, activation rows>, grid = threads; one launch per "
               "linear: q/o 4096x4096, kv 1024x4096, gate/up 2048x4096, down 4096x2048, head 129280x4096; the "
               "sequence kernel: its persistent grid):", "",
               "| kernel | grid | launches | median us | min us |", "|---|---|---|---|---|"]
@@ -1101,7 +1101,7 @@ def m1_launch_key(rows, cols):
         tpw, R = (2 if rows >= 16384 and T <= 8 else 4), 2
     sw = 1 if T <= tpw else 2 if T <= 2 * tpw else 4
     blocks = -(-(-(-rows // R)) // (4 // sw))
-    return (f"k_gemv_m1<0, {R}, {tpw}>", blocks * 256)
+    return (f"k_gemv_m1<0, {R}, {tpw}, 1>", blocks * 256)
 
 
 def summarize_counters(fetch_csv, write_csv, command, arm="fp8", mode="sequence"):
