@@ -270,6 +270,27 @@ class Chain:
                 gi += 1
         return out
 
+    def scaled_calls(self, stream=None):
+        """The chain's launches with the glue inside them: group gi >= 1 reads
+        x = bf16(c * y) of the first member of group gi - 1, formed in the
+        kernel's x loads (fp8blk_gemv_scaled_input and its grouped form); the
+        first group reads the chain input. No glue kernels."""
+        fb = self.fb
+        launches = [g for g in self.groups if g[0] == "launch"]
+        out = []
+        for gi, (_kind, a, x) in enumerate(launches):
+            if gi == 0:
+                out += self._one("launch", a, x, stream)
+                continue
+            src, c = launches[gi - 1][1][0]["y"], self.c[gi - 1]
+            if len(a) == 1:
+                out.append(fb.prepared("fp8blk_gemv_scaled_input", a[0]["w"], a[0]["grid"], src, c, a[0]["y"],
+                                       stream=stream))
+            else:
+                out.append(fb.prepared("fp8blk_gemv_grouped_scaled_input", [(m["w"], m["grid"], m["y"]) for m in a],
+                                       src, c, stream=stream))
+        return out
+
     def calibrate(self):
         """Run the chain eagerly once, fixing each glue step's scale so that
         its output has unit root mean square."""
@@ -286,11 +307,11 @@ class Chain:
                 gi += 1
         torch.cuda.synchronize()
 
-    def _one(self, kind, a, b):
+    def _one(self, kind, a, b, stream=None):
         fb = self.fb
         if len(a) == 1:
-            return [fb.prepared("fp8blk_gemv", a[0]["w"], a[0]["grid"], b, a[0]["y"])]
-        return [fb.prepared("fp8blk_gemv_grouped", [(m["w"], m["grid"], m["y"]) for m in a], b)]
+            return [fb.prepared("fp8blk_gemv", a[0]["w"], a[0]["grid"], b, a[0]["y"], stream=stream)]
+        return [fb.prepared("fp8blk_gemv_grouped", [(m["w"], m["grid"], m["y"]) for m in a], b, stream=stream)]
 
 
 def persistent_chain(torch, fb, ch):
@@ -341,6 +362,10 @@ def chain_sweep(torch, fb, sw, steps, warmup, dev):
     launches_only = lambda st: [c for (kind, _a, _b), c in zip(ch.groups, ch.calls(stream=st)) if kind == "launch"]  # noqa: E731
     t0 = graph_of(launches_only)
     v0 = sw.weight_bytes * steps / t0 / 1e9
+    # the glue inside the launches: each group's kernel forms its x = bf16(c * y) itself
+    t1 = graph_of(lambda st: ch.scaled_calls(stream=st))
+    v1 = sw.weight_bytes * steps / t1 / 1e9
+    f1 = all(bool(torch.isfinite(l["y"]).all()) for l in sw.lins)
     # the same chain as one cooperative launch per step (fp8blk_gemv_chain)
     pc = persistent_chain(torch, fb, ch)
     pc_ms = None
@@ -360,7 +385,9 @@ def chain_sweep(torch, fb, sw, steps, warmup, dev):
         pc_finite = all(bool(torch.isfinite(l["y"]).all()) for l in sw.lins)
     log(f"dependent chain ({ch.n_launches} GEMV launches + {ch.n_glue} glue kernels per step, graph): "
         f"{t / steps * 1e3:.4f} ms/step, {v:.1f} GB/s ({100 * v / HBM_PEAK_GBS:.1f}% of peak); outputs finite: {finite}; "
-        f"the GEMV launches alone {t0 / steps * 1e3:.4f} ms/step, {v0:.1f} GB/s ({100 * v0 / HBM_PEAK_GBS:.1f}%)"
+        f"the GEMV launches alone {t0 / steps * 1e3:.4f} ms/step, {v0:.1f} GB/s ({100 * v0 / HBM_PEAK_GBS:.1f}%); "
+        f"glue inside the launches (graph) {t1 / steps * 1e3:.4f} ms/step, {v1:.1f} GB/s "
+        f"({100 * v1 / HBM_PEAK_GBS:.1f}%)"
         + ("" if pc_ms is None else f"; one chained launch {pc_ms:.4f} ms/step, "
            f"{sw.weight_bytes / (pc_ms / 1e3) / 1e9:.1f} GB/s "
            f"({100 * sw.weight_bytes / (pc_ms / 1e3) / 1e9 / HBM_PEAK_GBS:.1f}%), status {pc_status}"))
@@ -370,6 +397,12 @@ def chain_sweep(torch, fb, sw, steps, warmup, dev):
             "gemv_launches_alone": {"value": round(v0, 1), "unit": "GB/s",
                                     "pct_hbm_peak": round(100 * v0 / HBM_PEAK_GBS, 2),
                                     "ms_per_step": round(t0 / steps * 1e3, 4)},
+            "glue_in_launches": {"value": round(v1, 1), "unit": "GB/s", "pct_hbm_peak": round(100 * v1 / HBM_PEAK_GBS, 2),
+                                 "ms_per_step": round(t1 / steps * 1e3, 4), "launches_per_step": ch.n_launches,
+                                 "outputs_finite": f1,
+                                 "note": "the same groups, each launch after the first reading x = bf16(c*y) of the "
+                                         "previous group's output inside its x loads (fp8blk_gemv_scaled_input, "
+                                         "fp8blk_gemv_grouped_scaled_input), no glue kernels, one HIP graph per step"},
             "one_launch": None if pc_ms is None else {
                 "value": round(sw.weight_bytes / (pc_ms / 1e3) / 1e9, 1), "unit": "GB/s",
                 "pct_hbm_peak": round(100 * sw.weight_bytes / (pc_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),

@@ -28,6 +28,7 @@ MIN_COLS, MAX_COLS, MAX_M, MAX_PANEL = 16, 65536, 16, 65536
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
            "fp8blk_load_check_noalloc",
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
+           "fp8blk_gemv_scaled_input", "fp8blk_gemv_grouped_scaled_input",
            "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
            "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
            "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin", "fp8blk_act_quant",
@@ -119,6 +120,10 @@ def load():
     L.fp8blk_gemv_grouped.restype = i32
     L.bf16_gemv_twin_grouped.argtypes = [ctypes.POINTER(Linear), i32, i64, vp, i64, vp]
     L.bf16_gemv_twin_grouped.restype = i32
+    L.fp8blk_gemv_scaled_input.argtypes = [vp, vp, i64, i64, vp, ctypes.c_float, vp, vp]
+    L.fp8blk_gemv_scaled_input.restype = i32
+    L.fp8blk_gemv_grouped_scaled_input.argtypes = [ctypes.POINTER(Linear), i32, i64, vp, ctypes.c_float, vp]
+    L.fp8blk_gemv_grouped_scaled_input.restype = i32
     L.fp8blk_gemv_mfma.argtypes, L.fp8blk_gemv_mfma.restype = [vp, vp, i64, i64, vp, i64, vp, vp], i32
     L.bf16_gemv_twin_mfma.argtypes, L.bf16_gemv_twin_mfma.restype = [vp, i64, i64, vp, i64, vp, vp], i32
     L.fp8blk_sequence_bytes.argtypes, L.fp8blk_sequence_bytes.restype = [i32], sz
@@ -344,6 +349,48 @@ def _group(members, fp8, x):
         arr[k].rows = rows
         arr[k].y = _dev(y, (torch.float32,), "y")
     return arr, cols
+
+
+def _scaled(members, src_f32):
+    """Descriptors of FP8 linears [(codes, scales_f32, y), ...] that read
+    x = bf16(c * src_f32) (M = 1, y of rows values), and src's pointer."""
+    import torch
+    arr = (Linear * len(members))()
+    cols = None
+    for k, (w, grid, y) in enumerate(members):
+        rows, c = _weights(w, "codes")
+        cols = c if cols is None else cols
+        if c != cols:
+            raise ValueError("grouped linears must share cols")
+        _numel(grid, _grid_cells(rows, cols), "scales_f32", "the ceil(rows/128) x ceil(cols/128) grid")
+        _numel(y, rows, "y", "rows outputs (one activation row)")
+        _one_device(w, grid, y, src_f32)
+        arr[k].w = _dev(w, (torch.uint8,), "codes")
+        arr[k].scales_f32 = _dev(grid, (torch.float32,), "scales_f32")
+        arr[k].rows = rows
+        arr[k].y = _dev(y, (torch.float32,), "y")
+    _numel(src_f32, cols, "src_f32", "cols values")
+    return arr, cols, _dev(src_f32, (torch.float32,), "src_f32")
+
+
+def fp8blk_gemv_scaled_input(codes, scales_f32, src_f32, c, y, stream=None, check=True):
+    """y[rows] = fp8blk_gemv on x = bf16(c * src_f32) (one activation row),
+    the conversion done inside the kernel's x loads (same bits)."""
+    arr, cols, srcp = _scaled([(codes, scales_f32, y)], src_f32)
+    st = load().fp8blk_gemv_scaled_input(arr[0].w, arr[0].scales_f32, arr[0].rows, cols, srcp, float(c), arr[0].y,
+                                         _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_scaled_input")
+    return st
+
+
+def fp8blk_gemv_grouped_scaled_input(members, src_f32, c, stream=None, check=True):
+    """fp8blk_gemv_grouped on x = bf16(c * src_f32), formed in the kernel."""
+    arr, cols, srcp = _scaled(members, src_f32)
+    st = load().fp8blk_gemv_grouped_scaled_input(arr, len(members), cols, srcp, float(c), _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_grouped_scaled_input")
+    return st
 
 
 def fp8blk_gemv_grouped(members, x_bf16, stream=None, check=True):
@@ -756,8 +803,9 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
     (benchmarks, graph capture), where per-call tensor inspection would
     dominate. Supported: "fp8blk_gemv" and "fp8blk_gemv_mfma" (codes,
     scales_f32, x_bf16, y), "bf16_gemv_twin" and "bf16_gemv_twin_mfma" (w_bf16,
-    x_bf16, y), the grouped launches (members, x_bf16), the staged GEMMs (...,
-    ws) and the sequence launches (a planned Sequence)."""
+    x_bf16, y), the grouped launches (members, x_bf16), the scaled-input
+    launches (codes, scales_f32, src_f32, c, y) and (members, src_f32, c), the
+    staged GEMMs (..., ws) and the sequence launches (a planned Sequence)."""
     import torch
     fn = getattr(load(), name)
     s = _stream(stream)
@@ -785,6 +833,14 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         members, x = tensors_and_sizes
         arr, cols = _group(members, name == "fp8blk_gemv_grouped", x)
         args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), x.shape[0], s)
+    elif name == "fp8blk_gemv_scaled_input":
+        codes, grid, src, c, y = tensors_and_sizes
+        arr, cols, srcp = _scaled([(codes, grid, y)], src)
+        args = (arr[0].w, arr[0].scales_f32, arr[0].rows, cols, srcp, float(c), arr[0].y, s)
+    elif name == "fp8blk_gemv_grouped_scaled_input":
+        members, src, c = tensors_and_sizes
+        arr, cols, srcp = _scaled(members, src)
+        args = (arr, len(members), cols, srcp, float(c), s)
     elif name == "fp8blk_gemm_staged":
         codes, grid, x, y, ws = tensors_and_sizes
         rows, cols, _N = _check_linear(codes, grid, x, y)

@@ -250,14 +250,6 @@ __device__ __forceinline__ void ch_compute_any(const ChRaw& r, const ChItem& I, 
         ch_compute<1>(r, I, xs, lane, epoch, ll);
 }
 
-// bf16 of the f32 product c * v, rounded to nearest even (NaN: the quiet NaN).
-__device__ __forceinline__ uint32_t bf16_of_scaled(float c, uint32_t vbits) {
-    const float f = c * as_f32(vbits);
-    const uint32_t u = as_u32(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ uint32_t ld_coherent_u32(uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

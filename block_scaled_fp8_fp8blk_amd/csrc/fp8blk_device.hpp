@@ -133,6 +133,15 @@ __device__ __forceinline__ void widen2_bf16(uint32_t d, float* w) {
     w[1] = as_f32(d & 0xffff0000u);
 }
 
+// bf16 of the f32 product c * v, rounded to nearest even (NaN: the quiet NaN):
+// the input a dependent linear reads from an earlier linear's f32 output.
+__device__ __forceinline__ uint32_t bf16_of_scaled(float c, uint32_t vbits) {
+    const float f = c * as_f32(vbits);
+    const uint32_t u = as_u32(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ void widen8_bf16(const uint4& v, float* w) {
     widen2_bf16(v.x, w + 0);
     widen2_bf16(v.y, w + 2);

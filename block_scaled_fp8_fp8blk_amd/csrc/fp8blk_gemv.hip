@@ -38,6 +38,8 @@ struct GemvArgs {
     const void* w;       // uint8 codes [rows, K] or uint16 bf16 slab [rows, K]
     const float* grid;   // f32 block scales [ceil(rows/128), GC] (FP8 arm only)
     const uint16_t* x;   // bf16 [M, K]
+    const float* xs;     // f32 [K] (scaled-input launches: x = bf16(xc * xs), M = 1)
+    float xc;
     float* y;            // f32 [M, rows]
     int64_t rows;
     int K, M, T, GC;
@@ -263,8 +265,9 @@ __device__ __forceinline__ void panel_body(const GemvArgs& a, int64_t block) {
 // TPW segments they are split over sw = 2 or 4 waves of the workgroup, which
 // leave their segment sums in LDS; one wave then adds them in order. Lanes
 // whose chunk lies past the last column load a valid chunk and contribute +0.0.
-template <int KIND, int R, int TPW, int MT>
+template <int KIND, int R, int TPW, int MT, bool XS = false>
 __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
+    static_assert(!XS || MT == 1, "a scaled input is one activation row");
     constexpr int V = R * TPW * MT;
     constexpr int VP = V < 4 ? 4 : V;  // reductions run in groups of four values
     using F = Fetch<KIND>;
@@ -286,7 +289,8 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
     // chunk of weights is decoded once and feeds both rows; a second row past
     // M (M = 1 never takes MT = 2) would repeat row M - 1.
     typename F::Raw raw[R][TPW];
-    uint4 xr[TPW][MT][2];
+    constexpr int NX = XS ? 4 : 2;  // 16-byte loads per x chunk: 16 bf16, or 16 f32 to be scaled and rounded
+    uint4 xr[TPW][MT][NX];
     const int t_last = max(0, min(t0 + nseg, a.T) - 1);
     // FP8: the wave's rows share one 128-row block, and its TPW segments need
     // 8 * TPW consecutive block scales: lanes load one each (one instruction
@@ -302,9 +306,10 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
         F::load_codes(a, r0, q, raw, u);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const uint4* xp = reinterpret_cast<const uint4*>(a.x + (int64_t)min(m, a.M - 1) * a.K + (int64_t)q * kChunk);
-            xr[u][m][0] = xp[0];
-            xr[u][m][1] = xp[1];
+            const uint4* xp = XS ? reinterpret_cast<const uint4*>(a.xs + (int64_t)q * kChunk)
+                                 : reinterpret_cast<const uint4*>(a.x + (int64_t)min(m, a.M - 1) * a.K + (int64_t)q * kChunk);
+#pragma unroll
+            for (int h = 0; h < NX; ++h) xr[u][m][h] = xp[h];
         }
     }
     // Keep every load ahead of the arithmetic: with one shot of data per wave,
@@ -327,8 +332,18 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
         float xf[MT][kChunk];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            widen8_bf16(xr[u][m][0], xf[m]);
-            widen8_bf16(xr[u][m][1], xf[m] + 8);
+            if constexpr (XS) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    xf[m][4 * h + 0] = as_f32(bf16_of_scaled(a.xc, xr[u][m][h].x) << 16);
+                    xf[m][4 * h + 1] = as_f32(bf16_of_scaled(a.xc, xr[u][m][h].y) << 16);
+                    xf[m][4 * h + 2] = as_f32(bf16_of_scaled(a.xc, xr[u][m][h].z) << 16);
+                    xf[m][4 * h + 3] = as_f32(bf16_of_scaled(a.xc, xr[u][m][h].w) << 16);
+                }
+            } else {
+                widen8_bf16(xr[u][m][0], xf[m]);
+                widen8_bf16(xr[u][m][1], xf[m] + 8);
+            }
         }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -435,6 +450,18 @@ __global__ __launch_bounds__(kThreads) void k_gemv_m1_group(const GroupArgs g) {
     m1_body<KIND, R, TPW, MT>(group_args(g, j), (int64_t)blockIdx.x - g.start[j]);
 }
 
+// The same kernels reading x as bf16(xc * xs) from an f32 vector (M = 1).
+template <int R, int TPW>
+__global__ __launch_bounds__(kThreads) void k_gemv_m1_scaled(const GemvArgs a) {
+    m1_body<kFp8, R, TPW, 1, true>(a, blockIdx.x);
+}
+
+template <int R, int TPW>
+__global__ __launch_bounds__(kThreads) void k_gemv_m1_group_scaled(const GroupArgs g) {
+    const int j = __builtin_amdgcn_readfirstlane(group_of(g, blockIdx.x));
+    m1_body<kFp8, R, TPW, 1, true>(group_args(g, j), (int64_t)blockIdx.x - g.start[j]);
+}
+
 template <int KIND, int MT, int R>
 __global__ __launch_bounds__(kThreads) void k_panel(const GemvArgs a) {
     panel_body<KIND, MT, R>(a, blockIdx.x);
@@ -520,6 +547,15 @@ template <int KIND, int R, int TPW, int MT>
 void launch_m1(const GroupArgs& g, int64_t blocks, hipStream_t s) {
     const int streams = kWaves / g.base.sw;
     const size_t lds = g.base.sw > 1 ? (size_t)streams * g.base.T * R * MT * sizeof(float) : 0;
+    if constexpr (KIND == kFp8 && MT == 1) {
+        if (g.base.xs) {
+            if (g.n == 1)
+                k_gemv_m1_scaled<R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(group_args(g, 0));
+            else
+                k_gemv_m1_group_scaled<R, TPW><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(g);
+            return;
+        }
+    }
     if (g.n == 1)
         k_gemv_m1<KIND, R, TPW, MT><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(group_args(g, 0));
     else
@@ -529,7 +565,8 @@ void launch_m1(const GroupArgs& g, int64_t blocks, hipStream_t s) {
 // One launch for g.n linears that share cols, x and M (g.w, g.grid, g.y and
 // g.rows filled in). The plan is that of a single linear with all the rows.
 template <int KIND>
-int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s) {
+int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s, const float* xs = nullptr,
+        float xc = 1.0f) {
     int64_t all_rows = 0;
     for (int j = 0; j < g.n; ++j) all_rows += g.rows[j];
     const Plan p = make_plan(all_rows, cols, M);
@@ -539,6 +576,8 @@ int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s)
     a.y = nullptr;
     a.rows = 0;
     a.x = x;
+    a.xs = xs;
+    a.xc = xc;
     a.K = (int)cols;
     a.M = (int)M;
     a.T = (int)ceil_div(cols, kSegCols);
@@ -608,6 +647,27 @@ int run_grouped(const fp8blk_linear* lin, int n, int64_t cols, const uint16_t* x
     return run<KIND>(g, cols, x, M, s);
 }
 
+// Scaled input: x = bf16(c * src) for one activation row, formed inside the
+// single-row kernel's x loads. Only shapes that the single-row kernel takes
+// at M = 1 (at most 16 segments) are accepted.
+int run_scaled(const fp8blk_linear* lin, int n, int64_t cols, const float* src, float c, hipStream_t s) {
+    if (!lin || n < 1 || n > FP8BLK_MAX_GROUP || !src || !aligned(src, 16) || ceil_div(cols, kSegCols) > 16)
+        return FP8BLK_ERR_ARG;
+    const uint16_t* xchk = reinterpret_cast<const uint16_t*>(src);  // for the common null / alignment checks
+    GroupArgs g;
+    g.n = n;
+    for (int j = 0; j < n; ++j) {
+        const int st = check_common(lin[j].w, lin[j].rows, cols, xchk, 1, lin[j].y, 0, nullptr, 0);
+        if (st != FP8BLK_OK) return st;
+        if (!lin[j].scales_f32 || !aligned(lin[j].scales_f32, 4)) return FP8BLK_ERR_ARG;
+        g.w[j] = lin[j].w;
+        g.grid[j] = lin[j].scales_f32;
+        g.y[j] = lin[j].y;
+        g.rows[j] = lin[j].rows;
+    }
+    return run<kFp8>(g, cols, nullptr, 1, s, src, c);
+}
+
 static_assert(kMaxGroup == FP8BLK_MAX_GROUP, "group size of the ABI");
 
 }  // namespace
@@ -641,4 +701,19 @@ extern "C" int fp8blk_gemv_grouped(const fp8blk_linear* linears, int n, int64_t 
 extern "C" int bf16_gemv_twin_grouped(const fp8blk_linear* linears, int n, int64_t cols, const uint16_t* x_bf16,
                                       int64_t M, fp8blk_stream_t stream) {
     return run_grouped<kBf16>(linears, n, cols, x_bf16, M, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8blk_gemv_scaled_input(const uint8_t* codes, const float* scales_f32, int64_t rows, int64_t cols,
+                                        const float* src_f32, float c, float* y, fp8blk_stream_t stream) {
+    fp8blk_linear l;
+    l.w = codes;
+    l.scales_f32 = scales_f32;
+    l.rows = rows;
+    l.y = y;
+    return run_scaled(&l, 1, cols, src_f32, c, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8blk_gemv_grouped_scaled_input(const fp8blk_linear* linears, int n, int64_t cols,
+                                                const float* src_f32, float c, fp8blk_stream_t stream) {
+    return run_scaled(linears, n, cols, src_f32, c, reinterpret_cast<hipStream_t>(stream));
 }

@@ -234,6 +234,33 @@ int bf16_gemv_twin_grouped(const fp8blk_linear *linears, int n, int64_t cols, co
                            int64_t M, fp8blk_stream_t stream);
 
 /*
+ * Scaled input: one decode-step linear (or a group of them) whose input is an
+ * earlier linear's f32 output, x = bf16(c * src) with the f32 product rounded
+ * to nearest even (a NaN product gives the quiet NaN 0x7fc0), formed inside
+ * the kernel's activation loads instead of by a separate kernel. This is the
+ * step between the dependent launches of the device decode path ("Module
+ * dsv4_gpu" page, DecodePath: one launch per projection, each projection
+ * reading the previous one's output), the same conversion that
+ * fp8blk_gemv_chain applies between its groups. For every output:
+ * fp8blk_gemv_scaled_input(L, src, c) == fp8blk_gemv(L, x) and
+ * fp8blk_gemv_grouped_scaled_input({L1, ...}, src, c) ==
+ * fp8blk_gemv_grouped({L1, ...}, x) bit for bit, with x[k] = bf16(c * src[k])
+ * and M = 1.
+ *   codes, scales_f32, y / linears: as for fp8blk_gemv / fp8blk_gemv_grouped
+ *     (M = 1; y = [rows]).
+ *   src_f32: device, 16-byte aligned, cols f32 values; it may be another
+ *     linear's y, but not one that this call writes.
+ *   c: any f32 (the caller's scale).
+ *   cols: as for fp8blk_gemv, and at most 16 * 1024 (the single-row kernel's
+ *     range); larger cols return FP8BLK_ERR_ARG.
+ * No workspace. Enqueued on `stream`; does not wait.
+ */
+int fp8blk_gemv_scaled_input(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,
+                             const float *src_f32, float c, float *y, fp8blk_stream_t stream);
+int fp8blk_gemv_grouped_scaled_input(const fp8blk_linear *linears, int n, int64_t cols, const float *src_f32,
+                                     float c, fp8blk_stream_t stream);
+
+/*
  * Matrix-core arm ("Module dsv4_gpu" page, Fp8Dense; "Struct Dsv4Gpu" page,
  * dense_fp8 and spec_greedy_batched_with). The same y as fp8blk_gemv, with the
  * products run on gfx950's matrix cores (v_mfma_f32_16x16x32_bf16): the

@@ -310,3 +310,27 @@ def test_chain_plan_checks(lib):
     h = fb.ChainHandle()
     assert lib.fp8blk_gemv_chain(ctypes.byref(h), ctypes.c_void_p(0x1000), None) == fb.ERR_ARG
     assert lib.fp8blk_chain_status(ctypes.byref(h), None) == fb.ERR_ARG
+
+
+def test_scaled_input_refusals(lib):
+    """The scaled-input launches check their arguments on the host before any
+    device work: more than 16 segments of columns, a NULL or misaligned src, a
+    bad group size, no rows or no scale grid are refused with FP8BLK_ERR_ARG
+    (the pointers here are never dereferenced)."""
+    P = ctypes.c_void_p
+    codes, grid, src, y = P(0x10000000), P(0x20000000), P(0x30000000), P(0x40000000)
+    one = lambda rows, cols, g, s: lib.fp8blk_gemv_scaled_input(codes, g, rows, cols, s, 1.0, y, None)
+    assert one(4096, 17 * 1024, grid, src) == fb.ERR_ARG
+    assert one(4096, 16 * 1024 + 16, grid, src) == fb.ERR_ARG
+    assert one(4096, 4096, grid, P(0x30000008)) == fb.ERR_ARG
+    assert one(4096, 4096, grid, None) == fb.ERR_ARG
+    assert one(0, 4096, grid, src) == fb.ERR_ARG
+    assert one(4096, 4100, grid, src) == fb.ERR_ARG
+    assert one(4096, 4096, None, src) == fb.ERR_ARG
+    arr = (fb.Linear * 9)()
+    for k in range(9):
+        arr[k].w, arr[k].scales_f32, arr[k].rows, arr[k].y = 0x10000000, 0x20000000, 128, 0x40000000
+    assert lib.fp8blk_gemv_grouped_scaled_input(arr, 0, 4096, src, 1.0, None) == fb.ERR_ARG
+    assert lib.fp8blk_gemv_grouped_scaled_input(arr, 9, 4096, src, 1.0, None) == fb.ERR_ARG
+    arr[1].rows = 0
+    assert lib.fp8blk_gemv_grouped_scaled_input(arr, 2, 4096, src, 1.0, None) == fb.ERR_ARG

@@ -162,3 +162,37 @@ def test_chained_launch_shapes_against_oracle(gpu):
                 assert nd == 0, f"group {gi} linear {k} ({L.rows}x{L.cols}): {nd} outputs differ from O7"
                 y64, yabs = oracle.gemv_f64(L.codes, L.scales, x)
                 assert_within_tolerance(y, y64, yabs, what=f"group {gi} linear {k}")
+
+
+def test_chain_with_glue_in_launches(gpu):
+    """The chain's launches with the glue inside them (scaled-input launches,
+    captured in a graph and replayed three times): every output equals, bit
+    for bit, the graph chain's (its x formed by a torch kernel between the
+    launches) and the chained launch's."""
+    import bench
+    from gpu_util import DEV, say
+    sw = bench.Sweep(torch, fb, inputs, DEV, 2, "fp8")
+    ch = bench.Chain(torch, fb, sw, DEV)
+    ch.calibrate()
+    graph_ys = [l["y"].clone() for l in sw.lins]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        bench.run_calls(ch.scaled_calls(stream=cap))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"  glue-in-launch chain replay {rep}")
+        for l in sw.lins:
+            l["y"].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a.view(torch.int32), l["y"].view(torch.int32)) for a, l in zip(graph_ys, sw.lins)), rep
+        _ = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+    pc = bench.persistent_chain(torch, fb, ch)
+    for l in sw.lins:
+        l["y"].fill_(float("nan"))
+    fb.fp8blk_gemv_chain(pc, ch.x_in[0])
+    assert fb.fp8blk_chain_status(pc) == fb.OK
+    assert all(torch.equal(a.view(torch.int32), l["y"].view(torch.int32)) for a, l in zip(graph_ys, sw.lins))
