@@ -28,7 +28,8 @@ MIN_COLS, MAX_COLS, MAX_M, MAX_PANEL = 16, 65536, 16, 65536
 EXPORTS = ("fp8blk_abi_version", "fp8blk_strerror", "fp8blk_workspace_bytes", "fp8blk_load_check",
            "fp8blk_load_check_noalloc",
            "fp8blk_dequant_bf16", "fp8blk_gemv", "bf16_gemv_twin", "fp8blk_gemv_grouped", "bf16_gemv_twin_grouped",
-           "fp8blk_gemv_scaled_input", "fp8blk_gemv_grouped_scaled_input",
+           "fp8blk_gemv_scaled_input", "fp8blk_gemv_grouped_scaled_input", "fp8blk_gemv_next_input",
+           "fp8blk_gemv_grouped_next_input",
            "fp8blk_gemv_mfma", "bf16_gemv_twin_mfma", "fp8blk_sequence_bytes", "fp8blk_sequence_init",
            "fp8blk_gemv_sequence", "bf16_gemv_twin_sequence", "fp8blk_gemv_mfma_sequence",
            "bf16_gemv_twin_mfma_sequence", "fp8blk_gemm_staged", "bf16_gemm_twin", "fp8blk_act_quant",
@@ -124,6 +125,10 @@ def load():
     L.fp8blk_gemv_scaled_input.restype = i32
     L.fp8blk_gemv_grouped_scaled_input.argtypes = [ctypes.POINTER(Linear), i32, i64, vp, ctypes.c_float, vp]
     L.fp8blk_gemv_grouped_scaled_input.restype = i32
+    L.fp8blk_gemv_next_input.argtypes = [vp, vp, i64, i64, vp, vp, ctypes.c_float, vp, vp]
+    L.fp8blk_gemv_next_input.restype = i32
+    L.fp8blk_gemv_grouped_next_input.argtypes = [ctypes.POINTER(Linear), i32, i64, vp, i32, ctypes.c_float, vp, vp]
+    L.fp8blk_gemv_grouped_next_input.restype = i32
     L.fp8blk_gemv_mfma.argtypes, L.fp8blk_gemv_mfma.restype = [vp, vp, i64, i64, vp, i64, vp, vp], i32
     L.bf16_gemv_twin_mfma.argtypes, L.bf16_gemv_twin_mfma.restype = [vp, i64, i64, vp, i64, vp, vp], i32
     L.fp8blk_sequence_bytes.argtypes, L.fp8blk_sequence_bytes.restype = [i32], sz
@@ -390,6 +395,41 @@ def fp8blk_gemv_grouped_scaled_input(members, src_f32, c, stream=None, check=Tru
     st = load().fp8blk_gemv_grouped_scaled_input(arr, len(members), cols, srcp, float(c), _stream(stream))
     if check and st != OK:
         raise Fp8BlkError(st, "fp8blk_gemv_grouped_scaled_input")
+    return st
+
+
+def _next(members, x_bf16, k, x_next):
+    """Descriptors for a next-input launch (M = 1): x_next holds rows of
+    linear k bf16 values."""
+    import torch
+    arr, cols = _group(members, True, x_bf16)
+    if x_bf16.shape[0] != 1:
+        raise ValueError("a next-input launch takes one activation row")
+    if not 0 <= k < len(members):
+        raise ValueError(f"k = {k} names no linear of the group")
+    _numel(x_next, arr[k].rows, "x_next", "the rows of linear k")
+    _one_device(x_bf16, x_next)
+    return arr, cols, _dev(x_next, _bf16_dtypes(), "x_next")
+
+
+def fp8blk_gemv_next_input(codes, scales_f32, x_bf16, y, c, x_next, stream=None, check=True):
+    """fp8blk_gemv at M = 1 that also writes x_next = bf16(c * y)."""
+    arr, cols, xnp = _next([(codes, scales_f32, y)], x_bf16, 0, x_next)
+    st = load().fp8blk_gemv_next_input(arr[0].w, arr[0].scales_f32, arr[0].rows, cols,
+                                       _dev(x_bf16, _bf16_dtypes(), "x_bf16"), arr[0].y, float(c), xnp,
+                                       _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_next_input")
+    return st
+
+
+def fp8blk_gemv_grouped_next_input(members, x_bf16, k, c, x_next, stream=None, check=True):
+    """fp8blk_gemv_grouped at M = 1; linear k also writes x_next = bf16(c * y_k)."""
+    arr, cols, xnp = _next(members, x_bf16, k, x_next)
+    st = load().fp8blk_gemv_grouped_next_input(arr, len(members), cols, _dev(x_bf16, _bf16_dtypes(), "x_bf16"), k,
+                                               float(c), xnp, _stream(stream))
+    if check and st != OK:
+        raise Fp8BlkError(st, "fp8blk_gemv_grouped_next_input")
     return st
 
 
@@ -805,7 +845,8 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
     scales_f32, x_bf16, y), "bf16_gemv_twin" and "bf16_gemv_twin_mfma" (w_bf16,
     x_bf16, y), the grouped launches (members, x_bf16), the scaled-input
     launches (codes, scales_f32, src_f32, c, y) and (members, src_f32, c), the
-    staged GEMMs (..., ws) and the sequence launches (a planned Sequence)."""
+    next-input launches (codes, scales_f32, x_bf16, y, c, x_next) and
+    (members, x_bf16, k, c, x_next), the staged GEMMs (..., ws) and the sequence launches (a planned Sequence)."""
     import torch
     fn = getattr(load(), name)
     s = _stream(stream)
@@ -841,6 +882,15 @@ def prepared(name: str, *tensors_and_sizes, stream=None):
         members, src, c = tensors_and_sizes
         arr, cols, srcp = _scaled(members, src)
         args = (arr, len(members), cols, srcp, float(c), s)
+    elif name == "fp8blk_gemv_next_input":
+        codes, grid, x, y, c, xn = tensors_and_sizes
+        arr, cols, xnp = _next([(codes, grid, y)], x, 0, xn)
+        args = (arr[0].w, arr[0].scales_f32, arr[0].rows, cols, _dev(x, _bf16_dtypes(), "x_bf16"), arr[0].y,
+                float(c), xnp, s)
+    elif name == "fp8blk_gemv_grouped_next_input":
+        members, x, k, c, xn = tensors_and_sizes
+        arr, cols, xnp = _next(members, x, k, xn)
+        args = (arr, len(members), cols, _dev(x, _bf16_dtypes(), "x_bf16"), k, float(c), xnp, s)
     elif name == "fp8blk_gemm_staged":
         codes, grid, x, y, ws = tensors_and_sizes
         rows, cols, _N = _check_linear(codes, grid, x, y)

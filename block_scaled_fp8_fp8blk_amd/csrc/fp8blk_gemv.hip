@@ -40,6 +40,8 @@ struct GemvArgs {
     const uint16_t* x;   // bf16 [M, K]
     const float* xs;     // f32 [K] (scaled-input launches: x = bf16(xc * xs), M = 1)
     float xc;
+    uint16_t* xn;        // when set (M = 1): also write bf16(xnc * y) [rows], the next linear's input
+    float xnc;
     float* y;            // f32 [M, rows]
     int64_t rows;
     int K, M, T, GC;
@@ -405,7 +407,10 @@ __device__ __forceinline__ void m1_body(const GemvArgs& a, int64_t block) {
 #pragma unroll
             for (int mm = 0; mm < MT; ++mm)
                 if (lane == ii * MT + mm) out = y[ii][mm];
-        if (m < a.M && r0 + i < a.rows) a.y[(int64_t)m * a.rows + r0 + i] = out;
+        if (m < a.M && r0 + i < a.rows) {
+            a.y[(int64_t)m * a.rows + r0 + i] = out;
+            if (a.xn) a.xn[r0 + i] = (uint16_t)bf16_of_scaled(a.xnc, as_u32(out));
+        }
     }
 }
 
@@ -418,6 +423,7 @@ struct GroupArgs {
     const void* w[kMaxGroup];
     const float* grid[kMaxGroup];
     float* y[kMaxGroup];
+    uint16_t* xn[kMaxGroup];  // per linear: the next input written beside y, or null
     int64_t rows[kMaxGroup];
     int64_t start[kMaxGroup + 1];
     int n;
@@ -435,6 +441,7 @@ __host__ __device__ __forceinline__ GemvArgs group_args(const GroupArgs& g, int 
     a.w = g.w[j];
     a.grid = g.grid[j];
     a.y = g.y[j];
+    a.xn = g.xn[j];
     a.rows = g.rows[j];
     return a;
 }
@@ -578,6 +585,7 @@ int run(GroupArgs& g, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s,
     a.x = x;
     a.xs = xs;
     a.xc = xc;
+    a.xn = nullptr;
     a.K = (int)cols;
     a.M = (int)M;
     a.T = (int)ceil_div(cols, kSegCols);
@@ -621,7 +629,7 @@ int check_common(const void* w, int64_t rows, int64_t cols, const uint16_t* x, i
 template <int KIND>
 int run_single(const void* w, const float* grid, int64_t rows, int64_t cols, const uint16_t* x, int64_t M,
                float* y, hipStream_t s) {
-    GroupArgs g;
+    GroupArgs g = {};
     g.n = 1;
     g.w[0] = w;
     g.grid[0] = grid;
@@ -633,7 +641,7 @@ int run_single(const void* w, const float* grid, int64_t rows, int64_t cols, con
 template <int KIND>
 int run_grouped(const fp8blk_linear* lin, int n, int64_t cols, const uint16_t* x, int64_t M, hipStream_t s) {
     if (!lin || n < 1 || n > FP8BLK_MAX_GROUP) return FP8BLK_ERR_ARG;
-    GroupArgs g;
+    GroupArgs g = {};
     g.n = n;
     for (int j = 0; j < n; ++j) {
         const int st = check_common(lin[j].w, lin[j].rows, cols, x, M, lin[j].y, 0, nullptr, 0);
@@ -654,7 +662,7 @@ int run_scaled(const fp8blk_linear* lin, int n, int64_t cols, const float* src, 
     if (!lin || n < 1 || n > FP8BLK_MAX_GROUP || !src || !aligned(src, 16) || ceil_div(cols, kSegCols) > 16)
         return FP8BLK_ERR_ARG;
     const uint16_t* xchk = reinterpret_cast<const uint16_t*>(src);  // for the common null / alignment checks
-    GroupArgs g;
+    GroupArgs g = {};
     g.n = n;
     for (int j = 0; j < n; ++j) {
         const int st = check_common(lin[j].w, lin[j].rows, cols, xchk, 1, lin[j].y, 0, nullptr, 0);
@@ -666,6 +674,30 @@ int run_scaled(const fp8blk_linear* lin, int n, int64_t cols, const float* src, 
         g.rows[j] = lin[j].rows;
     }
     return run<kFp8>(g, cols, nullptr, 1, s, src, c);
+}
+
+// Next input: as run_grouped at M = 1, and linear k also writes
+// x_next[r] = bf16(c * y_k[r]) beside its output (the input of a dependent
+// linear that follows), in the single-row kernel's final stores.
+int run_next(const fp8blk_linear* lin, int n, int64_t cols, const uint16_t* x, int k, float c, uint16_t* x_next,
+             hipStream_t s) {
+    if (!lin || n < 1 || n > FP8BLK_MAX_GROUP || k < 0 || k >= n || !x_next || !aligned(x_next, 2) ||
+        ceil_div(cols, kSegCols) > 16)
+        return FP8BLK_ERR_ARG;
+    GroupArgs g = {};
+    g.n = n;
+    for (int j = 0; j < n; ++j) {
+        const int st = check_common(lin[j].w, lin[j].rows, cols, x, 1, lin[j].y, 0, nullptr, 0);
+        if (st != FP8BLK_OK) return st;
+        if (!lin[j].scales_f32 || !aligned(lin[j].scales_f32, 4)) return FP8BLK_ERR_ARG;
+        g.w[j] = lin[j].w;
+        g.grid[j] = lin[j].scales_f32;
+        g.y[j] = lin[j].y;
+        g.rows[j] = lin[j].rows;
+    }
+    g.xn[k] = x_next;
+    g.base.xnc = c;
+    return run<kFp8>(g, cols, x, 1, s);
 }
 
 static_assert(kMaxGroup == FP8BLK_MAX_GROUP, "group size of the ABI");
@@ -716,4 +748,21 @@ extern "C" int fp8blk_gemv_scaled_input(const uint8_t* codes, const float* scale
 extern "C" int fp8blk_gemv_grouped_scaled_input(const fp8blk_linear* linears, int n, int64_t cols,
                                                 const float* src_f32, float c, fp8blk_stream_t stream) {
     return run_scaled(linears, n, cols, src_f32, c, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8blk_gemv_next_input(const uint8_t* codes, const float* scales_f32, int64_t rows, int64_t cols,
+                                      const uint16_t* x_bf16, float* y, float c, uint16_t* x_next,
+                                      fp8blk_stream_t stream) {
+    fp8blk_linear l;
+    l.w = codes;
+    l.scales_f32 = scales_f32;
+    l.rows = rows;
+    l.y = y;
+    return run_next(&l, 1, cols, x_bf16, 0, c, x_next, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fp8blk_gemv_grouped_next_input(const fp8blk_linear* linears, int n, int64_t cols,
+                                              const uint16_t* x_bf16, int k, float c, uint16_t* x_next,
+                                              fp8blk_stream_t stream) {
+    return run_next(linears, n, cols, x_bf16, k, c, x_next, reinterpret_cast<hipStream_t>(stream));
 }

@@ -261,6 +261,29 @@ int fp8blk_gemv_grouped_scaled_input(const fp8blk_linear *linears, int n, int64_
                                      float c, fp8blk_stream_t stream);
 
 /*
+ * Next input: the same step done by the producer instead. One activation row
+ * (M = 1); besides its f32 output the linear (for the grouped form, linear k
+ * of the group) writes x_next[r] = bf16(c * y[r]), the f32 product rounded to
+ * nearest even (a NaN gives 0x7fc0), the bf16 input of the dependent linear
+ * that follows ("Module dsv4_gpu" page, DecodePath). y is exactly
+ * fp8blk_gemv's (fp8blk_gemv_grouped's) and x_next is exactly what
+ * fp8blk_gemv_scaled_input forms from y, so a chain of these launches gives
+ * every output bit for bit as separate launches with the conversion between
+ * them.
+ *   codes, scales_f32, x_bf16, y / linears: as for fp8blk_gemv /
+ *     fp8blk_gemv_grouped with M = 1; cols at most 16 * 1024 (else
+ *     FP8BLK_ERR_ARG).
+ *   k: 0 <= k < n, the linear whose output feeds x_next.
+ *   c: any f32. x_next: device, 2-byte aligned, rows (of linear k) bf16
+ *     values; it must not overlap x_bf16 or any output.
+ * No workspace. Enqueued on `stream`; does not wait.
+ */
+int fp8blk_gemv_next_input(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,
+                           const uint16_t *x_bf16, float *y, float c, uint16_t *x_next, fp8blk_stream_t stream);
+int fp8blk_gemv_grouped_next_input(const fp8blk_linear *linears, int n, int64_t cols, const uint16_t *x_bf16,
+                                   int k, float c, uint16_t *x_next, fp8blk_stream_t stream);
+
+/*
  * Matrix-core arm ("Module dsv4_gpu" page, Fp8Dense; "Struct Dsv4Gpu" page,
  * dense_fp8 and spec_greedy_batched_with). The same y as fp8blk_gemv, with the
  * products run on gfx950's matrix cores (v_mfma_f32_16x16x32_bf16): the

@@ -334,3 +334,23 @@ def test_scaled_input_refusals(lib):
     assert lib.fp8blk_gemv_grouped_scaled_input(arr, 9, 4096, src, 1.0, None) == fb.ERR_ARG
     arr[1].rows = 0
     assert lib.fp8blk_gemv_grouped_scaled_input(arr, 2, 4096, src, 1.0, None) == fb.ERR_ARG
+
+
+def test_next_input_refusals(lib):
+    """The next-input launches refuse, on the host: more than 16 segments of
+    columns, a NULL or odd x_next, k outside the group, a bad group size."""
+    P = ctypes.c_void_p
+    codes, grid, x, y, xn = P(0x10000000), P(0x20000000), P(0x30000000), P(0x40000000), P(0x50000000)
+    one = lambda cols, n: lib.fp8blk_gemv_next_input(codes, grid, 4096, cols, x, y, 1.0, n, None)
+    assert one(17 * 1024, xn) == fb.ERR_ARG
+    assert one(4096, None) == fb.ERR_ARG
+    assert one(4096, P(0x50000001)) == fb.ERR_ARG
+    assert one(4100, xn) == fb.ERR_ARG
+    arr = (fb.Linear * 9)()
+    for k in range(9):
+        arr[k].w, arr[k].scales_f32, arr[k].rows, arr[k].y = 0x10000000, 0x20000000, 128, 0x40000000
+    grp = lambda n, k: lib.fp8blk_gemv_grouped_next_input(arr, n, 4096, x, k, 1.0, xn, None)
+    assert grp(2, 2) == fb.ERR_ARG
+    assert grp(2, -1) == fb.ERR_ARG
+    assert grp(0, 0) == fb.ERR_ARG
+    assert grp(9, 0) == fb.ERR_ARG

@@ -196,3 +196,35 @@ def test_chain_with_glue_in_launches(gpu):
     fb.fp8blk_gemv_chain(pc, ch.x_in[0])
     assert fb.fp8blk_chain_status(pc) == fb.OK
     assert all(torch.equal(a.view(torch.int32), l["y"].view(torch.int32)) for a, l in zip(graph_ys, sw.lins))
+
+
+def test_chain_with_glue_in_producer(gpu):
+    """The chain's launches with the glue in the producer (next-input
+    launches, captured in a graph and replayed three times): every output and
+    every group input equals, bit for bit, the graph chain's."""
+    import bench
+    from gpu_util import DEV, say
+    sw = bench.Sweep(torch, fb, inputs, DEV, 2, "fp8")
+    ch = bench.Chain(torch, fb, sw, DEV)
+    ch.calibrate()
+    graph_ys = [l["y"].clone() for l in sw.lins]
+    xs = [g[2] for g in ch.groups if g[0] == "launch"]
+    graph_xs = [x.clone() for x in xs]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        bench.run_calls(ch.next_calls(stream=cap))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"  glue-in-producer chain replay {rep}")
+        for l in sw.lins:
+            l["y"].fill_(float("nan"))
+        for x in xs[1:]:
+            x.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a.view(torch.int32), l["y"].view(torch.int32)) for a, l in zip(graph_ys, sw.lins)), rep
+        assert all(torch.equal(a.view(torch.int16), x.view(torch.int16)) for a, x in zip(graph_xs, xs)), rep
+        _ = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()

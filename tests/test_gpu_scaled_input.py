@@ -1,7 +1,8 @@
 """GPU: the scaled-input launches (fp8blk_gemv_scaled_input and its grouped
 form), where a dependent linear reads x = bf16(c * src) of an earlier
 linear's f32 output ("Module dsv4_gpu" page, DecodePath), formed inside the
-kernel's x loads.
+kernel's x loads; and the next-input launches (fp8blk_gemv_next_input and its
+grouped form), where the producer writes that x beside its output.
 
 Checked: every output equals, bit for bit, fp8blk_gemv / fp8blk_gemv_grouped
 on x formed on the host from the same src and c (the f32 product rounded to
@@ -121,3 +122,54 @@ def test_grouped_scaled_input(gpu):
             torch.cuda.synchronize()
             for D, y, r in zip(Ds, ys, ref):
                 assert _same(y, r.view(-1)), (cols, D.rows, rep)
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_next_input_equals_gemv(gpu, rows, cols):
+    """y equals fp8blk_gemv's bit for bit and x_next equals the host's
+    bf16(c * y) (nearest even) bit for bit, with a c that makes some products
+    overflow to infinity."""
+    from gpu_util import DEV, DevLinear, say
+    say(f"  next input {rows}x{cols}")
+    L = inputs.host_linear(rows, cols, 1, 1500 + rows % 89 + cols)
+    D = DevLinear(L.codes, L.scales, L.x)
+    assert D.check()[0] == fb.OK
+    x = D.x[:1].contiguous()
+    y_ref = torch.full((1, rows), float("nan"), dtype=torch.float32, device=DEV)
+    fb.fp8blk_gemv(D.codes, D.grid, x, y_ref)
+    torch.cuda.synchronize()
+    amax = float(y_ref.abs().max())
+    for c in (0.75, min(1.0e39 / max(amax, 1e-30), 1.0e38)):
+        y = torch.full((1, rows), float("nan"), dtype=torch.float32, device=DEV)
+        xn = torch.full((rows,), -1, dtype=torch.int16, device=DEV)
+        fb.fp8blk_gemv_next_input(D.codes, D.grid, x, y, c, xn)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), (rows, cols, c)
+        want = inputs.round_to_bf16_bits(np.float32(c) * y.cpu().numpy().reshape(-1))
+        assert np.array_equal(xn.cpu().numpy().view(np.uint16), want), (rows, cols, c)
+
+
+def test_grouped_next_input(gpu):
+    """A group of three (ragged rows): the outputs equal fp8blk_gemv_grouped's,
+    and x_next is bf16(c * y) of the chosen linear, for each choice k."""
+    from gpu_util import DEV, DevLinear, say
+    cols, rows_list = 4096, [1024, 77, 600]
+    Ds = []
+    for j, rows in enumerate(rows_list):
+        L = inputs.host_linear(rows, cols, 1, 1600 + 7 * j)
+        D = DevLinear(L.codes, L.scales, L.x)
+        assert D.check()[0] == fb.OK
+        Ds.append(D)
+    x = Ds[0].x[:1].contiguous()
+    ref = [torch.full((1, D.rows), float("nan"), dtype=torch.float32, device=DEV) for D in Ds]
+    fb.fp8blk_gemv_grouped([(D.codes, D.grid, r) for D, r in zip(Ds, ref)], x)
+    for k in range(3):
+        say(f"  grouped next input k={k}")
+        ys = [torch.full((1, D.rows), float("nan"), dtype=torch.float32, device=DEV) for D in Ds]
+        xn = torch.full((Ds[k].rows,), -1, dtype=torch.int16, device=DEV)
+        fb.fp8blk_gemv_grouped_next_input([(D.codes, D.grid, y) for D, y in zip(Ds, ys)], x, k, 0.5, xn)
+        torch.cuda.synchronize()
+        for y, r in zip(ys, ref):
+            assert torch.equal(y.view(torch.int32), r.view(torch.int32)), k
+        want = inputs.round_to_bf16_bits(np.float32(0.5) * ys[k].cpu().numpy().reshape(-1))
+        assert np.array_equal(xn.cpu().numpy().view(np.uint16), want), k
