@@ -655,6 +655,12 @@ int run_grouped(const fp8blk_linear* lin, int n, int64_t cols, const uint16_t* x
     return run<KIND>(g, cols, x, M, s);
 }
 
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
 // Scaled input: x = bf16(c * src) for one activation row, formed inside the
 // single-row kernel's x loads. Only shapes that the single-row kernel takes
 // at M = 1 (at most 16 segments) are accepted.
@@ -672,6 +678,8 @@ int run_scaled(const fp8blk_linear* lin, int n, int64_t cols, const float* src, 
         g.grid[j] = lin[j].scales_f32;
         g.y[j] = lin[j].y;
         g.rows[j] = lin[j].rows;
+        if (overlaps(src, (size_t)cols * sizeof(float), lin[j].y, (size_t)lin[j].rows * sizeof(float)))
+            return FP8BLK_ERR_ARG;  // an output would overwrite the input it is read from
     }
     return run<kFp8>(g, cols, nullptr, 1, s, src, c);
 }
@@ -695,6 +703,10 @@ int run_next(const fp8blk_linear* lin, int n, int64_t cols, const uint16_t* x, i
         g.y[j] = lin[j].y;
         g.rows[j] = lin[j].rows;
     }
+    const size_t xn_bytes = (size_t)lin[k].rows * sizeof(uint16_t);
+    if (overlaps(x_next, xn_bytes, x, (size_t)cols * sizeof(uint16_t))) return FP8BLK_ERR_ARG;
+    for (int j = 0; j < n; ++j)
+        if (overlaps(x_next, xn_bytes, lin[j].y, (size_t)lin[j].rows * sizeof(float))) return FP8BLK_ERR_ARG;
     g.xn[k] = x_next;
     g.base.xnc = c;
     return run<kFp8>(g, cols, x, 1, s);

@@ -249,7 +249,8 @@ int bf16_gemv_twin_grouped(const fp8blk_linear *linears, int n, int64_t cols, co
  *   codes, scales_f32, y / linears: as for fp8blk_gemv / fp8blk_gemv_grouped
  *     (M = 1; y = [rows]).
  *   src_f32: device, 16-byte aligned, cols f32 values; it may be another
- *     linear's y, but not one that this call writes.
+ *     linear's y, but not one that this call writes (an overlap with any
+ *     output returns FP8BLK_ERR_ARG).
  *   c: any f32 (the caller's scale).
  *   cols: as for fp8blk_gemv, and at most 16 * 1024 (the single-row kernel's
  *     range); larger cols return FP8BLK_ERR_ARG.
@@ -275,7 +276,7 @@ int fp8blk_gemv_grouped_scaled_input(const fp8blk_linear *linears, int n, int64_
  *     FP8BLK_ERR_ARG).
  *   k: 0 <= k < n, the linear whose output feeds x_next.
  *   c: any f32. x_next: device, 2-byte aligned, rows (of linear k) bf16
- *     values; it must not overlap x_bf16 or any output.
+ *     values; an overlap with x_bf16 or any output returns FP8BLK_ERR_ARG.
  * No workspace. Enqueued on `stream`; does not wait.
  */
 int fp8blk_gemv_next_input(const uint8_t *codes, const float *scales_f32, int64_t rows, int64_t cols,

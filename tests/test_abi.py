@@ -354,3 +354,22 @@ def test_next_input_refusals(lib):
     assert grp(2, -1) == fb.ERR_ARG
     assert grp(0, 0) == fb.ERR_ARG
     assert grp(9, 0) == fb.ERR_ARG
+
+
+def test_glue_launch_overlap_refusals(lib):
+    """An output range that overlaps the input it is formed from is refused on
+    the host: a scaled-input src overlapping an output, a next-input x_next
+    overlapping x or an output (the pointers are never dereferenced)."""
+    P = ctypes.c_void_p
+    codes, grid = P(0x10000000), P(0x20000000)
+    # scaled input: src (4096 f32 = 16 KB at 0x30000000) against y (4096 f32)
+    sc = lambda y: lib.fp8blk_gemv_scaled_input(codes, grid, 4096, 4096, P(0x30000000), 1.0, P(y), None)
+    assert sc(0x30000000) == fb.ERR_ARG
+    assert sc(0x30000000 + 16384 - 4) == fb.ERR_ARG
+    assert sc(0x30000000 - 16384 + 4) == fb.ERR_ARG
+    # next input: x (4096 bf16 = 8 KB at 0x30000000), y (4096 f32 at 0x40000000), x_next (4096 bf16)
+    nx = lambda xn: lib.fp8blk_gemv_next_input(codes, grid, 4096, 4096, P(0x30000000), P(0x40000000), 1.0, P(xn), None)
+    assert nx(0x30000000 + 8192 - 2) == fb.ERR_ARG
+    assert nx(0x30000000 - 8192 + 2) == fb.ERR_ARG
+    assert nx(0x40000000 + 16384 - 2) == fb.ERR_ARG
+    assert nx(0x40000000 - 8192 + 2) == fb.ERR_ARG
